@@ -1,0 +1,105 @@
+/*
+ * CPU ORACLE for the top-k MoE SwiGLU layer forward pass.
+ *
+ * TEST INFRASTRUCTURE ONLY. This is the plain, slow, obviously-correct
+ * reference the GPU path is checked against. Only the test suite, the smoke
+ * check and the benchmark's CPU-baseline leg may load it; the product library
+ * never links, calls or falls back to it.
+ *
+ * All arithmetic is IEEE double unless a rounding step is stated. Inputs are
+ * the exact values the GPU sees (fp32 arrays, or bf16 bit patterns decoded
+ * exactly). Outputs are plain host arrays. No blocking, fusion or reordering
+ * beyond what each definition states.
+ *
+ * Sources (page titles as printed on the pages):
+ *   [UP]  "Llama 3 Meets MoE: Efficient Upcycling" (paper review), section 3
+ *         core formulas: MoE output y = sum_i G(x)_i E_i(x); noisy top-k
+ *         router G = Softmax(KeepTopK(H, k)) with
+ *         H_i = (x W_g)_i + StandardNormal() * Softplus((x W_noise)_i);
+ *         KeepTopK; expert capacity = tokens per batch / N * CF with
+ *         overflow tokens skipping the experts; section 5 router ablation
+ *         (Mixtral order vs ST order).
+ *   [V2]  "LLaMA-MoE v2" article: gating-mechanism section (noisy gate,
+ *         balance loss L = lambda * sum f_i P_i), rescaling section
+ *         (y = N/k * sum G_i E_i), and its code example (SwiGLU expert
+ *         down(SiLU(gate x) * up x), noise = randn * softplus(noise_linear)).
+ *
+ * Parity status: every function here is pinned by CPU tests (brute force on
+ * tiny inputs, closed forms, library routines, invariants); none is
+ * "parity unpinned".
+ */
+#ifndef MOE_ORACLE_H
+#define MOE_ORACLE_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { ORC_F32 = 0, ORC_BF16 = 1 };                 /* storage of x / expert weights */
+enum { ORC_H_EXACT = 0, ORC_H_F32 = 1, ORC_H_BF16 = 2 }; /* rounding of the SwiGLU product h */
+enum { ORC_KEEPTOPK_SOFTMAX = 0, ORC_SOFTMAX_TOPK = 1 };
+
+typedef struct {
+  int64_t T;          /* tokens */
+  int32_t H;          /* hidden size */
+  int32_t F;          /* per-expert intermediate size */
+  int32_t N;          /* experts */
+  int32_t k;          /* experts per token */
+  int64_t capacity;   /* per-expert cap on kept assignments; < 0 means no cap */
+  int32_t order;      /* ORC_KEEPTOPK_SOFTMAX (Mixtral) or ORC_SOFTMAX_TOPK (ST) */
+  int32_t noisy;      /* add eps * softplus(x W_noise) to the logits */
+  double out_scale;   /* s in y = s * sum_j w_j E_j  (1, or N/k) */
+  int32_t h_round;    /* ORC_H_* */
+  int32_t x_dtype;    /* ORC_F32 / ORC_BF16 */
+  int32_t w_dtype;    /* ORC_F32 / ORC_BF16 (expert weights) */
+} oracle_cfg;
+
+/* Router + KeepTopK + gate weights for every token.
+ * x [T,H] (x_dtype), Wg [H,N] fp32, Wn [H,N] fp32 and eps [T,N] fp32 (used iff noisy).
+ * Out: logits [T,N] fp32 = fl32(x.Wg) (clean), Hv [T,N] fp32 = selection scores,
+ *      topk_idx [T,k] (sorted by Hv descending, ties to the lower index),
+ *      topk_w [T,k] double, min_gap [T] double (smallest gap between adjacent
+ *      sorted scores among the first min(k+1, N); +inf when N == 1). */
+int oracle_route(const oracle_cfg* c, const void* x, const float* Wg, const float* Wn, const float* eps,
+                 float* logits, float* Hv, int32_t* topk_idx, double* topk_w, double* min_gap);
+
+/* Gate load / importance / balance statistics (before capacity).
+ * load[N], importance[N], P[N], f[N]; balance = sum f_i P_i;
+ * balance_code = the article's code variant (gate-weighted frequency with a
+ * 1e-6 guard, times N), reported for information only. */
+int oracle_stats(const oracle_cfg* c, const float* logits, const int32_t* topk_idx, const double* topk_w,
+                 int64_t* load, double* importance, double* P, double* f, double* balance,
+                 double* balance_code);
+
+/* Capacity clip and expert-contiguous permutation.
+ * counts[N] (before capacity), kept[N] = min(counts, C), offsets[N+1] =
+ * exclusive scan of kept, slot[T,k] = row of (t,j) or -1 when dropped,
+ * row_token[T*k] = token of each row, -1 past the last kept row. */
+int oracle_capacity(const oracle_cfg* c, const int32_t* topk_idx, int64_t* counts, int64_t* kept,
+                    int64_t* offsets, int64_t* slot, int64_t* row_token);
+
+/* One expert applied to selected tokens: h_out [n,F] (after rounding, may be
+ * NULL) and E_out [n,H] = down(round(SiLU(gate x) * up x)). */
+int oracle_expert_rows(const oracle_cfg* c, const void* x, const void* Wgate, const void* Wup,
+                       const void* Wdown, int32_t e, const int64_t* tokens, int64_t n, int32_t nthreads,
+                       double* h_out, double* E_out);
+
+/* Layer output for selected tokens, given routing and slots:
+ * y_t = s * sum_{j=0..k-1, slot>=0} w_j E_{idx_j}(x_t), summed in j order.
+ * y64 [n,H] double (may be NULL), y32 [n,H] = fl32(y64) (may be NULL). */
+int oracle_combine_tokens(const oracle_cfg* c, const void* x, const void* Wgate, const void* Wup,
+                          const void* Wdown, const int32_t* topk_idx, const double* topk_w,
+                          const int64_t* slot, const int64_t* tokens, int64_t n, int32_t nthreads,
+                          double* y64, float* y32);
+
+/* Scalar pieces, exported so tests can pin them against library routines. */
+double oracle_round_bf16(double v);   /* round to nearest bf16, ties to even */
+double oracle_round_f32(double v);    /* round to nearest fp32, ties to even */
+double oracle_silu(double z);
+double oracle_softplus(double z);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

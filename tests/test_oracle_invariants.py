@@ -1,0 +1,200 @@
+"""Invariants the method fixes, checked on the oracle.
+
+I1  gate weights sum to 1 (Mixtral order) / to the top-k softmax mass (ST).
+I2a the experts of a non-overlapping split sum to the dense FFN.
+I2b zero router, k = N, s = N: the layer reproduces the dense FFN.
+I3  identical (upcycled) experts reproduce the dense FFN for any router;
+    with capacity, y_t = (sum of kept w) * FFN(x_t).
+I4  kept_i = min(load_i, C) <= C and sum kept = number of rows.
+I5  slot and row_token are inverse; rows of an expert are in token order.
+I6  dropless equals a capacity >= T; capacity 0 gives y = 0.
+I7  eps = 0 makes the noisy gate equal the clean one.
+I8  stats closed form at a zero router.
+I9  k = 1 Mixtral gives w = 1; all-equal scores give w = 1/k on 0..k-1.
+I10 dropless outputs are equivariant under token permutation.
+I11 relabelling the experts leaves y unchanged (no score ties).
+"""
+import numpy as np
+import torch
+
+import oracle
+import synth
+
+
+def dense_ffn(x, Wg_d, Wu_d, Wd_d):
+    x = torch.from_numpy(x).double()
+    g = x @ torch.from_numpy(Wg_d).double().T
+    u = x @ torch.from_numpy(Wu_d).double().T
+    return ((torch.nn.functional.silu(g) * u) @ torch.from_numpy(Wd_d).double().T).numpy()
+
+
+def f32_split(seed, T=24, H=32, Ftot=96, N=6, k=2, **kw):
+    return synth.make_split("inv", seed, T, H, Ftot, N, k, act="f32", wt="f32", **kw)
+
+
+def test_I1_gate_sums():
+    for order in (0, 1):
+        w = f32_split(1, order=order, N=8, k=3)
+        r = oracle.route(w)
+        s = r["topk_w"].sum(axis=1)
+        if order == 0:
+            np.testing.assert_allclose(s, 1.0, atol=1e-14)
+        else:
+            p = torch.softmax(torch.from_numpy(r["H"]).double(), dim=1).numpy()
+            top = np.sort(p, axis=1)[:, ::-1][:, :3].sum(axis=1)
+            np.testing.assert_allclose(s, top, atol=1e-14)
+            assert np.all(s <= 1.0 + 1e-15)
+
+
+def test_I2a_split_identity():
+    w = f32_split(2)
+    Wg_d, Wu_d, Wd_d = w.meta["dense"]
+    tokens = np.arange(w.T)
+    tot = sum(oracle.expert_rows(w, e, tokens, h_round=oracle.H_EXACT) for e in range(w.N))
+    ref = dense_ffn(w.x, Wg_d, Wu_d, Wd_d)
+    np.testing.assert_allclose(tot, ref, rtol=1e-12, atol=1e-13)
+
+
+def test_I2b_zero_router_all_experts_is_dense():
+    w = f32_split(3, k=6, N=6, out_scale=6.0)
+    w.Wg = np.zeros_like(w.Wg)
+    out = oracle.forward(w, h_round=oracle.H_EXACT)
+    assert np.all(out["topk_w"] == 1.0 / 6.0)
+    ref = dense_ffn(w.x, *w.meta["dense"])
+    np.testing.assert_allclose(out["y64"], ref, rtol=1e-12, atol=1e-13)
+    # fp32 h rounding stays within fp32 relative accuracy
+    out32 = oracle.forward(w, h_round=oracle.H_F32)
+    np.testing.assert_allclose(out32["y64"], ref, rtol=1e-5, atol=1e-6)
+
+
+def _upcycled_f32(seed, T=20, H=16, F=12, N=4, k=2, capacity=-1):
+    base = synth.make_independent("up", seed, T, H, F, 1, 1, act="f32", wt="f32")
+    w = synth.make_independent("up", seed, T, H, F, N, k, act="f32", wt="f32", capacity=capacity)
+    w.Wgate = np.ascontiguousarray(np.repeat(base.Wgate, N, axis=0))
+    w.Wup = np.ascontiguousarray(np.repeat(base.Wup, N, axis=0))
+    w.Wdown = np.ascontiguousarray(np.repeat(base.Wdown, N, axis=0))
+    w.Wg = synth.normal_f32(seed, 99, (H, N), 1.0)  # any router
+    return w, base
+
+
+def test_I3_upcycled_identical_experts_reproduce_dense():
+    w, base = _upcycled_f32(4)
+    out = oracle.forward(w, h_round=oracle.H_EXACT)
+    ref = dense_ffn(w.x, base.Wgate[0], base.Wup[0], base.Wdown[0])
+    np.testing.assert_allclose(out["y64"], ref, rtol=1e-12, atol=1e-13)
+
+
+def test_I3_upcycled_with_capacity_scales_by_kept_weight():
+    w, base = _upcycled_f32(5, T=40, capacity=6)
+    out = oracle.forward(w, h_round=oracle.H_EXACT)
+    ref = dense_ffn(w.x, base.Wgate[0], base.Wup[0], base.Wdown[0])
+    kept_w = np.where(out["slot"] >= 0, out["topk_w"], 0.0).sum(axis=1)
+    assert (kept_w < 1 - 1e-9).any()  # some assignments were dropped
+    np.testing.assert_allclose(out["y64"], kept_w[:, None] * ref, rtol=1e-12, atol=1e-13)
+
+
+def test_I4_I5_capacity_and_permutation_structure():
+    for cap in (-1, 0, 1, 5, 9, 1000):
+        w = f32_split(6, T=60, N=8, k=3, capacity=cap)
+        r = oracle.route(w)
+        c = oracle.capacity(w, r["topk_idx"])
+        load = np.bincount(r["topk_idx"].ravel(), minlength=w.N)
+        assert np.array_equal(c["counts"], load)
+        C = cap if cap >= 0 else 10 ** 9
+        assert np.array_equal(c["kept"], np.minimum(load, C))
+        assert np.all(c["kept"] <= C)
+        A = int(c["kept"].sum())
+        assert c["offsets"][-1] == A
+        assert np.array_equal(np.diff(c["offsets"]), c["kept"])
+        rows = c["slot"][c["slot"] >= 0]
+        assert np.array_equal(np.sort(rows), np.arange(A))
+        for t in range(w.T):
+            for j in range(w.k):
+                s = c["slot"][t, j]
+                if s >= 0:
+                    assert c["row_token"][s] == t
+                    e = r["topk_idx"][t, j]
+                    assert c["offsets"][e] <= s < c["offsets"][e + 1]
+        assert np.all(c["row_token"][A:] == -1)
+        for e in range(w.N):
+            seg = c["row_token"][c["offsets"][e]:c["offsets"][e + 1]]
+            assert np.all(np.diff(seg) > 0)
+            # the kept tokens are the first ones routed to e, in token order
+            routed = np.nonzero((r["topk_idx"] == e).any(axis=1))[0]
+            assert np.array_equal(seg, routed[:len(seg)])
+
+
+def test_I6_dropless_equals_large_capacity_and_zero_capacity_is_zero():
+    w = f32_split(7)
+    a = oracle.forward(w)
+    w.capacity = w.T
+    b = oracle.forward(w)
+    assert np.array_equal(a["y"], b["y"]) and np.array_equal(a["slot"], b["slot"])
+    w.capacity = 0
+    z = oracle.forward(w)
+    assert np.all(z["y"] == 0) and np.all(z["slot"] == -1)
+
+
+def test_I7_zero_noise_equals_clean_gate():
+    w = f32_split(8, noisy=True, N=8, k=2)
+    w.eps = np.zeros_like(w.eps)
+    a = oracle.forward(w)
+    w.noisy = False
+    b = oracle.forward(w)
+    assert np.array_equal(a["H"], b["H"]) and np.array_equal(a["y"], b["y"])
+
+
+def test_I8_stats_closed_form_at_zero_router():
+    for N, k in ((8, 2), (16, 4), (5, 5)):
+        w = f32_split(9, N=N, k=k, Ftot=N * 4)
+        w.Wg = np.zeros_like(w.Wg)
+        r = oracle.route(w)
+        st = oracle.stats(w, r)
+        np.testing.assert_allclose(st["P"], 1.0 / N, atol=1e-15)
+        f = np.where(np.arange(N) < k, 1.0 / k, 0.0)
+        np.testing.assert_allclose(st["f"], f, atol=1e-15)
+        assert abs(st["balance"] - 1.0 / N) < 1e-15
+        assert st["load"].sum() == w.T * k
+        assert abs(st["importance"].sum() - w.T) < 1e-12
+
+
+def test_I9_k1_and_equal_scores():
+    w = f32_split(10, k=1)
+    r = oracle.route(w)
+    assert np.all(r["topk_w"] == 1.0)
+    w = f32_split(11, k=4, N=6, Ftot=24)
+    w.Wg = np.zeros_like(w.Wg)
+    r = oracle.route(w)
+    assert np.all(r["topk_idx"] == np.arange(4)) and np.all(r["topk_w"] == 0.25)
+
+
+def test_I10_token_permutation_equivariance():
+    w = f32_split(12, T=32)
+    a = oracle.forward(w)
+    p = np.random.default_rng(0).permutation(w.T)
+    w.x = np.ascontiguousarray(w.x[p])
+    b = oracle.forward(w)
+    assert np.array_equal(a["y"][p], b["y"])
+    assert np.array_equal(a["topk_idx"][p], b["topk_idx"])
+
+
+def test_I11_expert_relabelling_invariance():
+    w = f32_split(13, T=32, N=6, k=2)
+    a = oracle.forward(w)
+    assert np.all(a["min_gap"] > 0)
+    q = np.random.default_rng(1).permutation(w.N)
+    w.Wg = np.ascontiguousarray(w.Wg[:, q])
+    w.Wgate = np.ascontiguousarray(w.Wgate[q])
+    w.Wup = np.ascontiguousarray(w.Wup[q])
+    w.Wdown = np.ascontiguousarray(w.Wdown[q])
+    b = oracle.forward(w)
+    np.testing.assert_allclose(a["y64"], b["y64"], rtol=1e-13, atol=1e-14)
+    assert np.array_equal(q[b["topk_idx"]], a["topk_idx"])
+
+
+def test_empty_batch():
+    w = f32_split(14, T=0)
+    w.x = np.zeros((0, w.H), np.float32)
+    out = oracle.forward(w)
+    assert out["y"].shape == (0, w.H)
+    assert np.all(out["counts"] == 0) and np.all(out["offsets"] == 0)
