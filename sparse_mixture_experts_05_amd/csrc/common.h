@@ -1,0 +1,97 @@
+// Device helpers shared by the gfx950 kernels of the MoE layer.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+namespace moe {
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(static_cast<uint32_t>(b) << 16); }
+
+// fp32 -> bf16 bits, round to nearest, ties to even; NaN stays NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// Element access for the two activation / weight storage types.
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  __device__ __forceinline__ static float load(const float* p, int64_t i) { return p[i]; }
+  __device__ __forceinline__ static void store(float* p, int64_t i, float v) { p[i] = v; }
+};
+template <> struct Elem<uint16_t> {
+  __device__ __forceinline__ static float load(const uint16_t* p, int64_t i) { return bf16_to_f32(p[i]); }
+  __device__ __forceinline__ static void store(uint16_t* p, int64_t i, float v) { p[i] = f32_to_bf16(v); }
+};
+
+// Butterfly sum over the 64 lanes. Every lane ends with the bitwise-same
+// value: at each level lanes i and i^m add the same two numbers, and fp32
+// addition is commutative.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
+  return v;
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+
+__device__ __forceinline__ float softplus(float z) { return fmaxf(z, 0.0f) + log1pf(expf(-fabsf(z))); }
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+  const int lane = threadIdx.x & (kWave - 1);
+  return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+}
+
+struct TileInfo {
+  int expert;
+  int row0;   // first permuted row of the tile
+  int rows;   // valid rows in the tile (<= BM)
+};
+
+// Map a linear m-tile index to (expert, first row, valid rows). Lane e reads
+// expert e's row count; a lane-wise inclusive scan of the per-expert tile
+// counts locates the expert. Returns false past the last tile.
+template <int BM>
+__device__ __forceinline__ bool find_tile(const int32_t* __restrict__ offsets, int N, int mt, TileInfo& ti) {
+  const int lane = threadIdx.x & 63;
+  int off = 0, cnt = 0;
+  if (lane < N) {
+    off = offsets[lane];
+    cnt = offsets[lane + 1] - off;
+  }
+  const int tl = (cnt + BM - 1) / BM;
+  int incl = tl;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int v = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += v;
+  }
+  const int total = __shfl(incl, 63, 64);
+  if (mt >= total) return false;
+  const int e = __popcll(__ballot(incl <= mt));
+  const int start = __shfl(incl - tl, e, 64);
+  const int eoff = __shfl(off, e, 64);
+  const int ecnt = __shfl(cnt, e, 64);
+  const int local = mt - start;
+  ti.expert = e;
+  ti.row0 = eoff + local * BM;
+  ti.rows = min(BM, ecnt - local * BM);
+  return true;
+}
+
+}  // namespace moe

@@ -1,0 +1,443 @@
+// C ABI of the MoE layer: host-side validation, workspace layout and the
+// launch sequence of each entry point (declared and documented in moe.h).
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <utility>
+#include <vector>
+
+#include "kernels.h"
+#include "moe.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+moe_status fail(moe_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+// ---- kernel timing -----------------------------------------------------------
+std::mutex g_prof_mu;
+int g_prof_kernel = -1;
+std::vector<std::pair<hipEvent_t, hipEvent_t>> g_prof_events;
+
+class ProfScope {
+ public:
+  ProfScope(int kernel, hipStream_t s) : s_(s) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    if (kernel != g_prof_kernel) return;
+    if (hipEventCreate(&a_) != hipSuccess || hipEventCreate(&b_) != hipSuccess) return;
+    hipEventRecord(a_, s_);
+    on_ = true;
+  }
+  ~ProfScope() {
+    if (!on_) return;
+    hipEventRecord(b_, s_);
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    g_prof_events.emplace_back(a_, b_);
+  }
+
+ private:
+  hipStream_t s_;
+  hipEvent_t a_ = nullptr, b_ = nullptr;
+  bool on_ = false;
+};
+
+#define MOE_LAUNCH(KID, STREAM, CALL)                                                   \
+  do {                                                                                  \
+    hipError_t e_;                                                                      \
+    {                                                                                   \
+      ProfScope ps_(KID, STREAM);                                                       \
+      e_ = (CALL);                                                                      \
+    }                                                                                   \
+    if (e_ != hipSuccess)                                                               \
+      return fail(MOE_ERR_DEVICE, "%s launch failed: %s", #KID, hipGetErrorString(e_)); \
+  } while (0)
+
+// ---- configuration -----------------------------------------------------------
+constexpr size_t kAlign = 256;
+size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+struct Layout {
+  int64_t A_max = 0;     // upper bound on kept rows
+  int hist_tokens = 0;
+  int hist_blocks = 0;
+  int splits = 1;        // K splits of the down projection in moe_forward
+  bool mfma = false;
+  size_t hist = 0, stat = 0, h = 0, yperm = 0, idx = 0, w = 0, slot = 0, rowtok = 0, counts = 0, kept = 0,
+         offsets = 0, total = 0;
+};
+
+bool use_mfma(const moe_cfg* c) { return c->act == MOE_BF16 && c->F % 8 == 0; }
+
+Layout layout(const moe_cfg* c) {
+  Layout L;
+  const int64_t T = c->T, Tk = c->T * c->k;
+  L.A_max = c->capacity < 0 ? Tk : std::min<int64_t>(Tk, static_cast<int64_t>(c->N) * c->capacity);
+  L.hist_tokens = moe::router_tokens_per_block(c->N, c->noisy);
+  L.hist_blocks = static_cast<int>((T + L.hist_tokens - 1) / L.hist_tokens);
+  L.mfma = use_mfma(c);
+  if (L.mfma) {
+    // the down projection splits K when there are too few output tiles to
+    // occupy 256 compute units
+    const int64_t avg = L.A_max / c->N;
+    const int bm = avg <= 48 ? 32 : 128, bn = avg <= 48 ? 256 : 128;
+    const int64_t tiles = ((L.A_max + bm - 1) / bm + std::min<int64_t>(c->N, L.A_max)) * ((c->H + bn - 1) / bn);
+    if (tiles > 0 && tiles < 512) {
+      int64_t s = (1024 + tiles - 1) / tiles;
+      s = std::min<int64_t>(s, 8);
+      s = std::min<int64_t>(s, std::max<int64_t>(1, c->F / 512));
+      L.splits = static_cast<int>(std::max<int64_t>(1, s));
+    }
+  }
+  const size_t act = c->act == MOE_BF16 ? 2 : 4;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += up(bytes);
+    return at;
+  };
+  L.hist = take(static_cast<size_t>(L.hist_blocks) * c->N * 4);
+  L.stat = take(static_cast<size_t>(L.hist_blocks) * c->N * 2 * 4);
+  L.h = take(static_cast<size_t>(L.A_max) * c->F * act);
+  L.yperm = take(static_cast<size_t>(L.splits) * L.A_max * c->H * 4);
+  L.idx = take(static_cast<size_t>(Tk) * 4);
+  L.w = take(static_cast<size_t>(Tk) * 4);
+  L.slot = take(static_cast<size_t>(Tk) * 4);
+  L.rowtok = take(static_cast<size_t>(Tk) * 4);
+  L.counts = take(static_cast<size_t>(c->N) * 4);
+  L.kept = take(static_cast<size_t>(c->N) * 4);
+  L.offsets = take(static_cast<size_t>(c->N + 1) * 4);
+  L.total = o;
+  return L;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+moe_status check_ws(const moe_cfg* c, const void* ws, size_t ws_bytes) {
+  const size_t need = layout(c).total;
+  if (ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, need);
+  if (need > 0 && !ws) return fail(MOE_ERR_INVALID, "workspace pointer is NULL");
+  if (ws && !aligned(ws, 256)) return fail(MOE_ERR_INVALID, "workspace must be 256-byte aligned");
+  return MOE_OK;
+}
+
+#define MOE_REQUIRE(COND, ...)                                 \
+  do {                                                         \
+    if (!(COND)) return fail(MOE_ERR_INVALID, __VA_ARGS__);    \
+  } while (0)
+
+moe_status zero_expert_outputs(const moe_cfg* c, int32_t* a, int32_t* b, int32_t* offsets, float* f0, float* f1,
+                               float* bal, hipStream_t s) {
+  const int N = c->N;
+  hipError_t e = hipSuccess;
+  if (a && e == hipSuccess) e = moe::launch_fill_i32(a, N, 0, s);
+  if (b && e == hipSuccess) e = moe::launch_fill_i32(b, N, 0, s);
+  if (offsets && e == hipSuccess) e = moe::launch_fill_i32(offsets, N + 1, 0, s);
+  if (f0 && e == hipSuccess) e = moe::launch_fill_f32(f0, N, 0.0f, s);
+  if (f1 && e == hipSuccess) e = moe::launch_fill_f32(f1, N, 0.0f, s);
+  if (bal && e == hipSuccess) e = moe::launch_fill_f32(bal, 1, 0.0f, s);
+  if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "fill launch failed: %s", hipGetErrorString(e));
+  return MOE_OK;
+}
+
+moe_status run_gemms(const moe_cfg* c, const Layout& L, const void* a, const int32_t* row_token,
+                     const int32_t* offsets, const void* Wgate, const void* Wup, const void* Wdown, float* y_perm,
+                     int splits, void* ws, hipStream_t s) {
+  const int bf16 = c->act == MOE_BF16;
+  moe::GemmParams g1{};
+  g1.A = a;
+  g1.lda = c->H;
+  g1.row_token = row_token;
+  g1.offsets = offsets;
+  g1.N = c->N;
+  g1.B0 = Wgate;
+  g1.B1 = Wup;
+  g1.b_expert_stride = static_cast<int64_t>(c->F) * c->H;
+  g1.ldb = c->H;
+  g1.K = c->H;
+  g1.Nout = c->F;
+  g1.C = at<char>(ws, L.h);
+  g1.ldc = c->F;
+  g1.c_split_stride = 0;
+  g1.splits = 1;
+  g1.rows_max = L.A_max;
+  g1.swiglu = 1;
+  moe::GemmParams g2 = g1;
+  g2.A = at<char>(ws, L.h);
+  g2.lda = c->F;
+  g2.row_token = nullptr;
+  g2.B0 = Wdown;
+  g2.B1 = nullptr;
+  g2.b_expert_stride = static_cast<int64_t>(c->H) * c->F;
+  g2.ldb = c->F;
+  g2.K = c->F;
+  g2.Nout = c->H;
+  g2.C = y_perm;
+  g2.ldc = c->H;
+  g2.c_split_stride = L.A_max * static_cast<int64_t>(c->H);
+  g2.splits = splits;
+  g2.swiglu = 0;
+  if (L.mfma) {
+    MOE_LAUNCH(MOE_KERNEL_GEMM1, s, moe::launch_gemm_bf16_mfma(g1, s));
+    MOE_LAUNCH(MOE_KERNEL_GEMM2, s, moe::launch_gemm_bf16_mfma(g2, s));
+  } else {
+    MOE_LAUNCH(MOE_KERNEL_GEMM1, s, moe::launch_gemm_simple(g1, bf16, s));
+    MOE_LAUNCH(MOE_KERNEL_GEMM2, s, moe::launch_gemm_simple(g2, bf16, s));
+  }
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t moe_capacity(int64_t T, int32_t N, int32_t k, double cf, int32_t count_assignments) {
+  if (cf < 0 || N <= 0 || T < 0 || k <= 0 || !std::isfinite(cf)) return -1;
+  const double num = count_assignments ? static_cast<double>(T) * k : static_cast<double>(T);
+  const double c = std::ceil(cf * num / N - 1e-9);
+  if (c > 2147483647.0) return -1;
+  return static_cast<int32_t>(c < 0 ? 0 : c);
+}
+
+moe_status moe_check(const moe_cfg* c) {
+  g_err.clear();
+  if (!c) return fail(MOE_ERR_INVALID, "cfg is NULL");
+  if (c->T < 0) return fail(MOE_ERR_INVALID, "T = %lld < 0", static_cast<long long>(c->T));
+  if (c->T > (int64_t(1) << 26)) return fail(MOE_ERR_UNSUPPORTED, "T above 2^26");
+  if (c->H < 1 || c->F < 1) return fail(MOE_ERR_INVALID, "H and F must be >= 1");
+  if (c->N < 1 || c->k < 1 || c->k > c->N) return fail(MOE_ERR_INVALID, "need 1 <= k <= N (N=%d, k=%d)", c->N, c->k);
+  if (c->N > 64) return fail(MOE_ERR_UNSUPPORTED, "N = %d above 64", c->N);
+  if (c->H % 8 != 0) return fail(MOE_ERR_UNSUPPORTED, "H = %d is not a multiple of 8", c->H);
+  if (c->order != MOE_TOPK_THEN_SOFTMAX && c->order != MOE_SOFTMAX_THEN_TOPK)
+    return fail(MOE_ERR_INVALID, "unknown order %d", c->order);
+  if ((c->noisy != 0 && c->noisy != 1) || (c->want_stats != 0 && c->want_stats != 1))
+    return fail(MOE_ERR_INVALID, "noisy and want_stats must be 0 or 1");
+  if (!std::isfinite(c->out_scale)) return fail(MOE_ERR_INVALID, "out_scale is not finite");
+  const bool dt_ok = (c->act == MOE_BF16 || c->act == MOE_F32) && (c->wt == MOE_BF16 || c->wt == MOE_F32) &&
+                     (c->out == MOE_BF16 || c->out == MOE_F32);
+  if (!dt_ok) return fail(MOE_ERR_INVALID, "unknown dtype code");
+  if (c->act != c->wt) return fail(MOE_ERR_UNSUPPORTED, "activations and expert weights must share a dtype");
+  const int64_t Tk = c->T * c->k;
+  if (Tk > INT32_MAX || static_cast<double>(Tk) * c->H > 9.0e18) return fail(MOE_ERR_UNSUPPORTED, "too large");
+  return MOE_OK;
+}
+
+size_t moe_workspace_bytes(const moe_cfg* c) {
+  if (moe_check(c) != MOE_OK) return 0;
+  return layout(c).total;
+}
+
+moe_status moe_route(const moe_cfg* c, const void* x, const float* Wg, const float* Wn, const float* eps,
+                     float* logits_opt, int32_t* topk_idx, float* topk_w, int32_t* load_opt,
+                     float* importance_opt, float* P_opt, float* balance_opt, void* ws, size_t ws_bytes,
+                     hipStream_t s) {
+  moe_status st = moe_check(c);
+  if (st != MOE_OK) return st;
+  const bool stats = c->want_stats && (load_opt || importance_opt || P_opt || balance_opt);
+  if (c->T == 0) {
+    if (stats) return zero_expert_outputs(c, load_opt, nullptr, nullptr, importance_opt, P_opt, balance_opt, s);
+    return MOE_OK;
+  }
+  MOE_REQUIRE(x && Wg && topk_idx && topk_w, "x, Wg, topk_idx and topk_w are required");
+  MOE_REQUIRE(!c->noisy || (Wn && eps), "noisy routing needs Wn and eps");
+  MOE_REQUIRE(aligned(x, 16) && aligned(Wg, 16) && (!Wn || aligned(Wn, 16)), "x, Wg and Wn must be 16-byte aligned");
+  if (stats) {
+    st = check_ws(c, ws, ws_bytes);
+    if (st != MOE_OK) return st;
+  }
+  const Layout L = layout(c);
+  moe::RouterParams rp{};
+  rp.x = x;
+  rp.act_bf16 = c->act == MOE_BF16;
+  rp.Wg = Wg;
+  rp.Wn = Wn;
+  rp.eps = eps;
+  rp.T = c->T;
+  rp.H = c->H;
+  rp.N = c->N;
+  rp.k = c->k;
+  rp.order = c->order;
+  rp.noisy = c->noisy;
+  rp.logits = logits_opt;
+  rp.topk_idx = topk_idx;
+  rp.topk_w = topk_w;
+  rp.hist = stats ? at<int32_t>(ws, L.hist) : nullptr;
+  rp.stat_part = stats ? at<float>(ws, L.stat) : nullptr;
+  MOE_LAUNCH(MOE_KERNEL_ROUTER, s, moe::launch_router(rp, s));
+  if (stats) {
+    moe::StatsParams sp{at<int32_t>(ws, L.hist), at<float>(ws, L.stat), L.hist_blocks, c->T, c->N, c->k,
+                        load_opt, importance_opt, P_opt, balance_opt};
+    MOE_LAUNCH(MOE_KERNEL_STATS, s, moe::launch_stats(sp, s));
+  }
+  return MOE_OK;
+}
+
+moe_status moe_permute(const moe_cfg* c, const void* x, const int32_t* topk_idx, int32_t* counts,
+                       int32_t* offsets, int32_t* slot, int32_t* row_token, void* x_perm, void* ws,
+                       size_t ws_bytes, hipStream_t s) {
+  moe_status st = moe_check(c);
+  if (st != MOE_OK) return st;
+  MOE_REQUIRE(counts && offsets, "counts and offsets are required");
+  if (c->T == 0) return zero_expert_outputs(c, counts, nullptr, offsets, nullptr, nullptr, nullptr, s);
+  MOE_REQUIRE(topk_idx && slot && row_token, "topk_idx, slot and row_token are required");
+  MOE_REQUIRE(!x_perm || (x && aligned(x, 16) && aligned(x_perm, 16)), "gather needs 16-byte aligned x and x_perm");
+  st = check_ws(c, ws, ws_bytes);
+  if (st != MOE_OK) return st;
+  const Layout L = layout(c);
+  moe::HistParams hp{topk_idx, c->T, c->N, c->k, L.hist_tokens, at<int32_t>(ws, L.hist)};
+  MOE_LAUNCH(MOE_KERNEL_HIST, s, moe::launch_hist(hp, s));
+  moe::ScatterParams sp{topk_idx, at<int32_t>(ws, L.hist), L.hist_tokens, c->T, c->N, c->k, c->capacity,
+                        counts, nullptr, offsets, slot, row_token};
+  MOE_LAUNCH(MOE_KERNEL_SCATTER, s, moe::launch_scatter(sp, s));
+  if (x_perm) {
+    moe::GatherParams gp{x, x_perm, row_token, offsets, c->T * c->k, c->H, c->N, c->act == MOE_BF16 ? 2 : 4};
+    MOE_LAUNCH(MOE_KERNEL_GATHER, s, moe::launch_gather(gp, s));
+  }
+  return MOE_OK;
+}
+
+moe_status moe_grouped_swiglu(const moe_cfg* c, const void* a, const int32_t* row_token_opt,
+                              const int32_t* offsets, const void* Wgate, const void* Wup, const void* Wdown,
+                              float* y_perm, void* ws, size_t ws_bytes, hipStream_t s) {
+  moe_status st = moe_check(c);
+  if (st != MOE_OK) return st;
+  if (c->T == 0) return MOE_OK;
+  MOE_REQUIRE(a && offsets && Wgate && Wup && Wdown && y_perm, "inputs and y_perm are required");
+  MOE_REQUIRE(aligned(a, 16) && aligned(Wgate, 16) && aligned(Wup, 16) && aligned(Wdown, 16) && aligned(y_perm, 16),
+              "activations, weights and y_perm must be 16-byte aligned");
+  st = check_ws(c, ws, ws_bytes);
+  if (st != MOE_OK) return st;
+  const Layout L = layout(c);
+  return run_gemms(c, L, a, row_token_opt, offsets, Wgate, Wup, Wdown, y_perm, 1, ws, s);
+}
+
+moe_status moe_combine(const moe_cfg* c, const float* y_perm, const int32_t* slot, const float* topk_w, void* y,
+                       hipStream_t s) {
+  moe_status st = moe_check(c);
+  if (st != MOE_OK) return st;
+  if (c->T == 0) return MOE_OK;
+  MOE_REQUIRE(y_perm && slot && topk_w && y, "y_perm, slot, topk_w and y are required");
+  MOE_REQUIRE(aligned(y_perm, 16) && aligned(y, 16), "y_perm and y must be 16-byte aligned");
+  moe::CombineParams cp{y_perm, 0, 1, slot, topk_w, y, c->out == MOE_BF16, c->T, c->H, c->k, c->out_scale};
+  MOE_LAUNCH(MOE_KERNEL_COMBINE, s, moe::launch_combine(cp, s));
+  return MOE_OK;
+}
+
+moe_status moe_forward(const moe_cfg* c, const void* x, const float* Wg, const float* Wn, const float* eps,
+                       const void* Wgate, const void* Wup, const void* Wdown, void* y, int32_t* topk_idx_opt,
+                       float* topk_w_opt, int32_t* kept_opt, int32_t* load_opt, float* importance_opt,
+                       float* P_opt, float* balance_opt, void* ws, size_t ws_bytes, hipStream_t s) {
+  moe_status st = moe_check(c);
+  if (st != MOE_OK) return st;
+  const bool stats = c->want_stats && (load_opt || importance_opt || P_opt || balance_opt);
+  if (c->T == 0)
+    return zero_expert_outputs(c, kept_opt, load_opt, nullptr, stats ? importance_opt : nullptr,
+                               stats ? P_opt : nullptr, stats ? balance_opt : nullptr, s);
+  MOE_REQUIRE(x && Wg && Wgate && Wup && Wdown && y, "x, Wg, expert weights and y are required");
+  MOE_REQUIRE(!c->noisy || (Wn && eps), "noisy routing needs Wn and eps");
+  MOE_REQUIRE(aligned(x, 16) && aligned(Wg, 16) && (!Wn || aligned(Wn, 16)) && aligned(Wgate, 16) &&
+                  aligned(Wup, 16) && aligned(Wdown, 16) && aligned(y, 16),
+              "x, router and expert weights and y must be 16-byte aligned");
+  st = check_ws(c, ws, ws_bytes);
+  if (st != MOE_OK) return st;
+  const Layout L = layout(c);
+  int32_t* topk_idx = topk_idx_opt ? topk_idx_opt : at<int32_t>(ws, L.idx);
+  float* topk_w = topk_w_opt ? topk_w_opt : at<float>(ws, L.w);
+  int32_t* slot = at<int32_t>(ws, L.slot);
+  int32_t* row_token = at<int32_t>(ws, L.rowtok);
+  int32_t* offsets = at<int32_t>(ws, L.offsets);
+
+  moe::RouterParams rp{};
+  rp.x = x;
+  rp.act_bf16 = c->act == MOE_BF16;
+  rp.Wg = Wg;
+  rp.Wn = Wn;
+  rp.eps = eps;
+  rp.T = c->T;
+  rp.H = c->H;
+  rp.N = c->N;
+  rp.k = c->k;
+  rp.order = c->order;
+  rp.noisy = c->noisy;
+  rp.logits = nullptr;
+  rp.topk_idx = topk_idx;
+  rp.topk_w = topk_w;
+  rp.hist = at<int32_t>(ws, L.hist);
+  rp.stat_part = stats ? at<float>(ws, L.stat) : nullptr;
+  MOE_LAUNCH(MOE_KERNEL_ROUTER, s, moe::launch_router(rp, s));
+  if (stats) {
+    moe::StatsParams sp{at<int32_t>(ws, L.hist), at<float>(ws, L.stat), L.hist_blocks, c->T, c->N, c->k,
+                        load_opt, importance_opt, P_opt, balance_opt};
+    MOE_LAUNCH(MOE_KERNEL_STATS, s, moe::launch_stats(sp, s));
+  }
+  moe::ScatterParams sc{topk_idx, at<int32_t>(ws, L.hist), L.hist_tokens, c->T, c->N, c->k, c->capacity,
+                        (!stats && load_opt) ? load_opt : at<int32_t>(ws, L.counts), kept_opt, offsets, slot,
+                        row_token};
+  MOE_LAUNCH(MOE_KERNEL_SCATTER, s, moe::launch_scatter(sc, s));
+  float* y_perm = at<float>(ws, L.yperm);
+  st = run_gemms(c, L, x, row_token, offsets, Wgate, Wup, Wdown, y_perm, L.splits, ws, s);
+  if (st != MOE_OK) return st;
+  moe::CombineParams cp{y_perm, L.A_max * static_cast<int64_t>(c->H), L.splits, slot, topk_w, y,
+                        c->out == MOE_BF16, c->T, c->H, c->k, c->out_scale};
+  MOE_LAUNCH(MOE_KERNEL_COMBINE, s, moe::launch_combine(cp, s));
+  return MOE_OK;
+}
+
+const char* moe_status_str(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID: return "MOE_ERR_INVALID";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_DEVICE: return "MOE_ERR_DEVICE";
+  }
+  return "unknown moe_status";
+}
+
+const char* moe_last_error(void) { return g_err.c_str(); }
+
+moe_status moe_profile_select(int32_t kernel_id) {
+  if (kernel_id < -1 || kernel_id >= MOE_KERNEL_COUNT) return fail(MOE_ERR_INVALID, "unknown kernel id %d", kernel_id);
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_kernel = kernel_id;
+  return MOE_OK;
+}
+
+moe_status moe_profile_read(double* total_ms, int64_t* launches) {
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> ev;
+  {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    ev.swap(g_prof_events);
+  }
+  double tot = 0.0;
+  moe_status st = MOE_OK;
+  for (auto& p : ev) {
+    float ms = 0.0f;
+    if (hipEventSynchronize(p.second) != hipSuccess || hipEventElapsedTime(&ms, p.first, p.second) != hipSuccess)
+      st = fail(MOE_ERR_DEVICE, "event timing failed");
+    tot += ms;
+    hipEventDestroy(p.first);
+    hipEventDestroy(p.second);
+  }
+  if (total_ms) *total_ms = tot;
+  if (launches) *launches = static_cast<int64_t>(ev.size());
+  return st;
+}
+
+}  // extern "C"

@@ -1,0 +1,161 @@
+// Capacity clip and permutation of (token, expert) assignments into
+// expert-contiguous order, without atomics.
+//
+// Each expert keeps its assignments in token order up to its capacity; the
+// rest overflow and are dropped ("Llama 3 Meets MoE" review, section 3,
+// capacity factor). The rank of an assignment inside its expert's queue is
+//   (assignments to that expert in earlier router blocks, from the per-block
+//    histogram) + (earlier waves of this block) + (earlier lanes of this wave)
+// where the last two come from wave ballots and popcounts. Ranks are unique
+// and exact, so the whole permutation is deterministic.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kScatterThreads = 256;
+
+// Histogram of topk_idx with the router's block granularity (one block of
+// 64 threads per router block; thread n counts expert n).
+__global__ __launch_bounds__(64) void k_hist(HistParams p) {
+  const int n = threadIdx.x;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * p.tokens_per_block;
+  int64_t t1 = t0 + p.tokens_per_block;
+  if (t1 > p.T) t1 = p.T;
+  int c = 0;
+  for (int64_t t = t0; t < t1; ++t)
+    for (int j = 0; j < p.k; ++j) c += (p.topk_idx[t * p.k + j] == n) ? 1 : 0;
+  if (n < p.N) p.hist[static_cast<int64_t>(blockIdx.x) * p.N + n] = c;
+}
+
+template <int KMAX>
+__global__ __launch_bounds__(kScatterThreads) void k_scatter(ScatterParams p) {
+  __shared__ int s_part[4][64][2];
+  __shared__ int s_base[64], s_kept[64], s_off[65];
+  __shared__ int s_wcnt[4][64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int N = p.N, k = p.k;
+  const int64_t T = p.T;
+  const int64_t tb0 = static_cast<int64_t>(blockIdx.x) * kScatterThreads;
+  const int64_t nhb = (T + p.hist_tokens - 1) / p.hist_tokens;
+  const int64_t hb0 = tb0 / p.hist_tokens;
+
+  // per-expert totals and the count before this block, over the histogram
+  int base = 0, tot = 0;
+  if (lane < N) {
+    for (int64_t hb = wave; hb < nhb; hb += 4) {
+      const int v = p.hist[hb * N + lane];
+      tot += v;
+      if (hb < hb0) base += v;
+    }
+  }
+  s_part[wave][lane][0] = base;
+  s_part[wave][lane][1] = tot;
+  __syncthreads();
+  if (tid < N) {
+    int b = 0, c = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      b += s_part[w][tid][0];
+      c += s_part[w][tid][1];
+    }
+    s_base[tid] = b;
+    s_kept[tid] = p.capacity < 0 ? c : (c < p.capacity ? c : p.capacity);
+    if (blockIdx.x == 0) {
+      if (p.counts) p.counts[tid] = c;
+      if (p.kept) p.kept[tid] = s_kept[tid];
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    s_off[0] = 0;
+    for (int e = 0; e < N; ++e) s_off[e + 1] = s_off[e] + s_kept[e];
+  }
+  __syncthreads();
+  if (blockIdx.x == 0 && tid <= N) p.offsets[tid] = s_off[tid];
+
+  // this thread's token
+  const int64_t t = tb0 + tid;
+  const bool tv = t < T;
+  int idx[KMAX], pre[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    idx[j] = (tv && j < k) ? p.topk_idx[t * k + j] : -1;
+    pre[j] = 0;
+  }
+  // rank among earlier lanes of the wave, per expert, by ballot
+  for (int e = 0; e < N; ++e) {
+    bool has = false;
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) has = has || (idx[j] == e);
+    const uint64_t m = __ballot(has);
+    if (lane == 0) s_wcnt[wave][e] = __popcll(m);
+    const int before = __popcll(m & lanemask_lt());
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j)
+      if (idx[j] == e) pre[j] = before;
+  }
+  __syncthreads();
+  if (tv) {
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      if (j >= k) break;
+      const int e = idx[j];
+      int woff = 0;
+      for (int w = 0; w < wave; ++w) woff += s_wcnt[w][e];
+      const int rank = s_base[e] + woff + pre[j];
+      const bool keep = p.capacity < 0 || rank < p.capacity;
+      const int row = keep ? s_off[e] + rank : -1;
+      p.slot[t * k + j] = row;
+      if (keep) p.row_token[row] = static_cast<int32_t>(t);
+    }
+  }
+  // rows past the last kept one
+  const int64_t A = s_off[N];
+  for (int64_t r = A + tb0 + tid; r < T * k; r += static_cast<int64_t>(gridDim.x) * kScatterThreads)
+    p.row_token[r] = -1;
+}
+
+// x_perm[r] = x[row_token[r]] for r < offsets[N]; one wave per row.
+__global__ __launch_bounds__(256) void k_gather(GatherParams p) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int64_t A = p.offsets[p.N];
+  if (r >= A) return;
+  const int64_t src = p.row_token[r];
+  const int64_t row_bytes = static_cast<int64_t>(p.H) * p.elem_bytes;
+  const char* s = static_cast<const char*>(p.x) + src * row_bytes;
+  char* d = static_cast<char*>(p.x_perm) + r * row_bytes;
+  for (int64_t o = lane * 16; o < row_bytes; o += 64 * 16)
+    *reinterpret_cast<u32x4_t*>(d + o) = *reinterpret_cast<const u32x4_t*>(s + o);
+}
+
+}  // namespace
+
+hipError_t launch_hist(const HistParams& p, hipStream_t s) {
+  const int64_t blocks = (p.T + p.tokens_per_block - 1) / p.tokens_per_block;
+  if (blocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_hist, dim3(static_cast<unsigned>(blocks)), dim3(64), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_scatter(const ScatterParams& p, hipStream_t s) {
+  const int64_t blocks = (p.T + kScatterThreads - 1) / kScatterThreads;
+  if (blocks <= 0) return hipSuccess;
+  if (p.k <= 8)
+    hipLaunchKernelGGL(k_scatter<8>, dim3(static_cast<unsigned>(blocks)), dim3(kScatterThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL(k_scatter<64>, dim3(static_cast<unsigned>(blocks)), dim3(kScatterThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather(const GatherParams& p, hipStream_t s) {
+  const int64_t blocks = (p.rows_max + 3) / 4;
+  if (blocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_gather, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace moe

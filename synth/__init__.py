@@ -156,7 +156,7 @@ def capacity_from_cf(T: int, N: int, k: int, cf: float, count_assignments: bool 
     review, section 3, capacity-factor equation). With count_assignments the
     numerator counts (token, expert) assignments, T*k, instead of tokens."""
     num = T * k if count_assignments else T
-    return int(np.ceil(cf * num / N - 1e-12))
+    return int(np.ceil(cf * num / N - 1e-9))
 
 
 def _rand_w(seed, stream, shape, sigma, dtype):

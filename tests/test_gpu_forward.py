@@ -1,0 +1,133 @@
+"""moe_forward (the whole layer in one call) against the oracle.
+
+Small shapes of every workload family check every output element; the five
+named workloads run at full size in the same launch configuration as the
+benchmark and are checked on sampled tokens (routing, capacity and kept
+counts on all tokens)."""
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import check_forward, log, run_forward, sample_tokens, upload
+
+pytestmark = pytest.mark.gpu
+
+SMALL = {
+    "split_bf16_s4": lambda: synth.make_split("split_bf16_s4", 21, 333, 512, 8 * 48, 8, 2, out_scale=4.0),
+    "split_noisy_stats": lambda: synth.make_split("split_noisy", 22, 400, 512, 16 * 24, 16, 4, noisy=True,
+                                                  want_stats=True, out_scale=4.0),
+    "upcycled_cf1": lambda: synth.make_upcycled("up_cf1", 23, 512, 256, 128, 8, 2,
+                                                capacity=synth.capacity_from_cf(512, 8, 2, 1.0)),
+    "upcycled_cf4": lambda: synth.make_upcycled("up_cf4", 24, 512, 256, 128, 8, 2,
+                                                capacity=synth.capacity_from_cf(512, 8, 2, 4.0)),
+    "upcycled_dropless": lambda: synth.make_upcycled("up_dl", 25, 300, 256, 192, 8, 2),
+    "decode_skewed": lambda: synth.apply_skew(synth.make_independent("dec", 26, 64, 512, 1024, 8, 2), n_pref=32),
+    "fp32_split": lambda: synth.make_split("fp32", 27, 200, 128, 8 * 40, 8, 2, act="f32", wt="f32"),
+    "st_order": lambda: synth.make_split("st", 28, 150, 256, 8 * 32, 8, 2, order=synth.ST),
+    "bf16_f_not_mult8": lambda: synth.make_independent("f86", 29, 100, 256, 86, 8, 2, out_scale=4.0),
+    "one_expert": lambda: synth.make_independent("n1", 30, 70, 128, 64, 1, 1),
+    "k_equals_n": lambda: synth.make_independent("keqn", 31, 90, 128, 64, 4, 4),
+    "one_token": lambda: synth.make_independent("t1", 32, 1, 256, 64, 8, 2),
+    "capacity_zero": lambda: synth.make_independent("c0", 33, 50, 128, 32, 8, 2, capacity=0),
+    "n64_k8": lambda: synth.make_independent("n64", 34, 200, 256, 64, 64, 8),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_forward_small(name):
+    w = SMALL[name]()
+    g, ora, cap = check_forward(w)
+    if w.capacity == 0:
+        assert np.all(g["y"] == 0.0)
+    if w.want_stats:
+        st = oracle.stats(w, ora)
+        np.testing.assert_allclose(g["importance"], st["importance"], rtol=1e-5, atol=1e-4)
+        np.testing.assert_allclose(g["P"], st["P"], rtol=1e-5, atol=1e-7)
+        np.testing.assert_allclose(g["balance"][0], st["balance"], rtol=1e-5)
+
+
+def test_forward_bf16_output_within_one_ulp():
+    w = SMALL["split_bf16_s4"]()
+    g = run_forward(w, out="bf16")
+    ora = oracle.forward(w)
+    ref = ora["y"].astype(np.float64)
+    ulp = np.spacing(np.abs(synth.bf16_to_f32(synth.f32_to_bf16(ora["y"])))).astype(np.float64) * 65536.0
+    # one bf16 step plus the fp32 error of the layer before rounding
+    assert np.all(np.abs(g["y"] - ref) <= ulp + 2e-2)
+    assert np.mean(np.abs(g["y"] - ref) <= ulp) > 0.99
+
+
+def test_forward_empty_batch():
+    w = synth.make_independent("t0", 35, 0, 128, 64, 8, 2, want_stats=True)
+    w.x = np.zeros((0, 128), np.uint16)
+    w.eps = None
+    g = run_forward(w)
+    assert g["y"].shape == (0, 128)
+    assert np.all(g["kept"] == 0) and np.all(g["load"] == 0)
+
+
+def test_forward_is_deterministic():
+    w = SMALL["split_noisy_stats"]()
+    d = upload(w)
+    a = run_forward(w, d=d)
+    b = run_forward(w, d=d)
+    for key in a:
+        assert np.array_equal(a[key], b[key]), key
+
+
+# ---- the five named workloads at full size --------------------------------------
+
+@functools.lru_cache(maxsize=1)
+def _c4_base():
+    return synth.c4("dropless")
+
+
+def _c4(variant):
+    w = _c4_base()
+    cap = {"cf4": synth.capacity_from_cf(w.T, 8, 2, 4.0), "cf1": synth.capacity_from_cf(w.T, 8, 2, 1.0),
+           "dropless": -1, "cf1_assign": synth.capacity_from_cf(w.T, 8, 2, 1.0, True)}[variant]
+    return synth.Workload(f"C4_{variant}", w.T, w.H, w.F, w.N, w.k, cap, w.order, False, False, 1.0, "bf16", "bf16",
+                          w.x, w.Wg, None, None, w.Wgate, w.Wup, w.Wdown, dict(w.meta))
+
+
+def test_full_C1():
+    check_forward(synth.c1())
+
+
+def test_full_C2():
+    w = synth.c2()
+    check_forward(w, sample_tokens(w, 40))
+
+
+def test_full_C3():
+    w = synth.c3()
+    g, ora, _ = check_forward(w, sample_tokens(w, 24))
+    st = oracle.stats(w, ora)
+    np.testing.assert_allclose(g["importance"], st["importance"], rtol=1e-5)
+    np.testing.assert_allclose(g["P"], st["P"], rtol=1e-5)
+    np.testing.assert_allclose(g["balance"][0], st["balance"], rtol=1e-5)
+
+
+@pytest.mark.parametrize("variant", ["cf4", "cf1", "dropless", "cf1_assign"])
+def test_full_C4(variant):
+    w = _c4(variant)
+    ora = oracle.route(w)
+    cap = oracle.capacity(w, ora["topk_idx"])
+    # include tokens that lost a slot to the capacity clip
+    dropped = np.nonzero(np.any(cap["slot"] < 0, axis=1))[0]
+    g, _, cap2 = check_forward(w, sample_tokens(w, 12, extra=dropped[:4]))
+    log(f"  kept per expert {g['kept'].tolist()} (capacity {w.capacity})")
+    if w.capacity >= 0:
+        assert np.all(g["kept"] <= w.capacity)
+
+
+def test_full_C5():
+    w = synth.c5()
+    g, _, _ = check_forward(w)
+    frac = float(np.mean(g["topk_idx"][:, 0] == 0))
+    log(f"  C5 top-1 fraction on expert 0: {frac:.3f}; rows per expert {g['kept'].tolist()}")
+    assert frac >= 0.5
