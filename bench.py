@@ -1,0 +1,229 @@
+"""Benchmark: forward pass of one LLaMA-MoE-3.5B (2/8) MoE layer on one MI355X.
+
+Workload: T = 4096 tokens (batch 1 x sequence 4096), hidden 4096, LLaMA-2-7B
+intermediate 11008 split into 8 experts of 1376, top-2 Mixtral routing,
+dropless, output rescaled by N/k = 4; bf16 activations and expert weights,
+fp32 router. Seeded synthetic inputs (no checkpoint or dataset), resident in
+HBM before timing. A step is one moe_forward call (router, KeepTopK and gates,
+permutation, both grouped expert GEMMs, combine). Steps rotate over several
+copies of the layer's inputs so the 256 MB last-level cache cannot keep a
+step's weights from the previous step.
+
+Prints one JSON line (rank 0). `value` is tokens/s of the whole job; the
+`roofline` object covers the dominant kernel (the fused gate/up GEMM with the
+SwiGLU epilogue), timed with HIP events on its launch stream inside the timed
+region; `cpu_baseline` is the CPU oracle timed on this host on a sample of the
+same workload.
+"""
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/sec and % of bf16 MFMA peak, LLaMA-MoE-3.5B 2/8 shape"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "gemm1_swiglu_C2_counters.txt")
+GEMM_SOURCE = os.path.join(ROOT, "sparse_mixture_experts_05_amd", "csrc", "gemm_mfma.hip")
+
+
+def parse_args():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--copies", type=int, default=3, help="input copies the steps rotate over")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="run one plain 512 MiB device copy first (counter calibration under rocprofv3)")
+    ap.add_argument("--no-detail", action="store_true")
+    return ap.parse_args()
+
+
+def counters_traffic():
+    """HBM bytes per GEMM1 launch from the committed rocprofv3 counter summary,
+    or None if there is none or the kernel source changed since it was taken."""
+    if not os.path.exists(COUNTERS_FILE):
+        return None
+    txt = open(COUNTERS_FILE).read()
+    kv = dict(re.findall(r"^([a-z_0-9]+):\s*(\S+)\s*$", txt, flags=re.M))
+    src_hash = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
+    if kv.get("gemm_source_sha256") != src_hash:
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build runs the MoE layer on a single MI355X and has no "
+              f"multi-GPU path (asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    from sparse_mixture_experts_05_amd import abi
+
+    torch.cuda.set_device(0)
+    abi.load_library()
+    dev_name = torch.cuda.get_device_name(0)
+
+    if args.calib_copy:
+        n = 512 * 1024 * 1024
+        src = torch.empty(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    w = synth.c2()
+    T, H, F, N, k = w.T, w.H, w.F, w.N, w.k
+    cfg = abi.MoEConfig(T=T, H=H, F=F, N=N, k=k, capacity=-1, order=0, out_scale=w.out_scale)
+
+    def dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(a).cuda()
+
+    base = dict(x=dev(w.x), Wg=dev(w.Wg), Wgate=dev(w.Wgate), Wup=dev(w.Wup), Wdown=dev(w.Wdown))
+    copies = [base] + [{k_: v.clone() for k_, v in base.items()} for _ in range(max(0, args.copies - 1))]
+    y = torch.empty(T, H, dtype=torch.float32, device="cuda")
+    ws = abi.workspace(cfg)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        d = copies[i % len(copies)]
+        abi.moe_forward(cfg, d["x"], d["Wg"], None, None, d["Wgate"], d["Wup"], d["Wdown"], y, ws=ws,
+                        stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # timed region; GEMM1 bracketed by HIP events on the launch stream
+    abi.moe_profile_select(abi.MOE_KERNEL_GEMM1)
+    abi.moe_profile_read()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    abi.moe_profile_select(-1)
+    g1_ms, g1_n = abi.moe_profile_read()
+
+    ms_per_step = elapsed * 1e3 / args.steps
+    tokens_per_s = T * args.steps / elapsed
+
+    A = T * k
+    gemm1_flops = 4.0 * A * H * F            # gate and up projections of the kept rows
+    gemm1_avg_s = g1_ms / 1e3 / max(1, g1_n)
+    achieved = gemm1_flops / gemm1_avg_s / 1e12
+    traffic = counters_traffic()
+
+    # layer roofline (algorithmic work of the kept assignments)
+    f_bf16 = 6.0 * A * H * F
+    f_fp32 = 2.0 * T * H * N
+    b_alg = T * H * 2 + H * N * 4 + N * 3 * F * H * 2 + T * k * 8 + T * H * 4
+    t_roof = max(f_bf16 / (PEAK_BF16_TFLOPS * 1e12) + f_fp32 / (PEAK_FP32_TFLOPS * 1e12), b_alg / (PEAK_HBM_GBS * 1e9))
+    t_layer = elapsed / args.steps
+
+    detail = None
+    if not args.no_detail:
+        per_kernel = {}
+        names = {abi.MOE_KERNEL_ROUTER: "router_topk", abi.MOE_KERNEL_SCATTER: "permute_scatter",
+                 abi.MOE_KERNEL_GEMM1: "gemm1_gate_up_swiglu", abi.MOE_KERNEL_GEMM2: "gemm2_down",
+                 abi.MOE_KERNEL_COMBINE: "combine"}
+        for kid, name in names.items():
+            abi.moe_profile_select(kid)
+            for i in range(10):
+                step(i)
+            torch.cuda.synchronize()
+            ms, n = abi.moe_profile_read()
+            per_kernel[name] = round(ms * 1e3 / max(1, n), 2)
+        abi.moe_profile_select(-1)
+        # same data every step: weights can stay in the last-level cache
+        d0 = copies[0]
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for _ in range(args.steps):
+            abi.moe_forward(cfg, d0["x"], d0["Wg"], None, None, d0["Wgate"], d0["Wup"], d0["Wdown"], y, ws=ws,
+                            stream=stream)
+        torch.cuda.synchronize()
+        warm_ms = (time.perf_counter() - t1) * 1e3 / args.steps
+        detail = dict(device=dev_name, kernel_avg_us=per_kernel, layer_us=round(t_layer * 1e6, 2),
+                      layer_tflops=round((f_bf16 + f_fp32) / t_layer / 1e12, 1),
+                      layer_roofline_us=round(t_roof * 1e6, 2), layer_frac_of_roofline=round(t_roof / t_layer, 4),
+                      gemm2_tflops=round(2.0 * A * F * H / (per_kernel["gemm2_down"] * 1e-6) / 1e12, 1),
+                      same_inputs_every_step_ms=round(warm_ms, 4), input_copies=len(copies))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights; no checkpoint)",
+        "config": {"workload": "LLaMA-MoE-3.5B (2/8) MoE layer forward: T=4096 tokens, hidden 4096, "
+                               "11008 split into 8 experts of 1376, top-2 Mixtral, dropless, s=N/k=4, "
+                               "bf16 experts, fp32 router",
+                   "T": T, "H": H, "F": F, "N": N, "k": k, "out_scale": w.out_scale},
+        "roofline": {"bound": "mfma", "kernel": "gemm1_gate_up_swiglu", "achieved": round(achieved, 1),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic, "launches_timed": g1_n,
+                     "avg_launch_us": round(gemm1_avg_s * 1e6, 2), "flops_per_launch": gemm1_flops},
+        "cpu_baseline": cpu,
+    }
+    if detail is not None:
+        out["detail"] = detail
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(w, target_s: float):
+    """The CPU oracle, as it is, on the first S tokens of the workload (same
+    weights): routing, capacity and the expert FFNs of those tokens, with the
+    token loop on this host's cores. S is sized for about target_s seconds."""
+    import oracle
+    import synth
+
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    cores = max(1, min(16, cores))
+
+    def sample(S):
+        return synth.Workload(w.name, S, w.H, w.F, w.N, w.k, w.capacity, w.order, w.noisy, False, w.out_scale,
+                              w.act, w.wt, w.x[:S].copy(), w.Wg, None, None, w.Wgate, w.Wup, w.Wdown)
+
+    S0 = max(cores, 16)
+    t0 = time.perf_counter()
+    oracle.forward(sample(S0), nthreads=cores)
+    dt0 = time.perf_counter() - t0
+    S = int(min(w.T, max(S0, S0 * target_s / max(dt0, 1e-3))))
+    S = max(cores, S // cores * cores)
+    t1 = time.perf_counter()
+    oracle.forward(sample(S), nthreads=cores)
+    dt = time.perf_counter() - t1
+    return {"value": round(S / dt, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {S} of {w.T} tokens of the same layer (routing, capacity and experts of those "
+                      f"tokens), fp64 accumulation, {dt:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()
