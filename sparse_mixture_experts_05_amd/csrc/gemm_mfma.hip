@@ -3,8 +3,8 @@
 // Rows of expert e occupy [offsets[e], offsets[e+1]) of the permuted order.
 // A workgroup owns one BM x BN output tile of one expert; it finds its expert
 // on the device from `offsets` (no host synchronisation), stages A and B
-// tiles of BK = 64 through LDS with double buffering, and issues
-// v_mfma_f32_32x32x16_bf16 with fp32 accumulation.
+// tiles of BK = 64 through LDS, and issues v_mfma_f32_32x32x16_bf16 with fp32
+// accumulation.
 //
 //   swiglu: B rows [0, BN/2) are Wgate rows, [BN/2, BN) the matching Wup rows;
 //           each wave holds gate and up accumulators of the same columns, so
@@ -19,6 +19,13 @@
 // chunk c of row r is stored at chunk c ^ (r & 7), which keeps both the
 // row-wise global->LDS writes and the column-wise MFMA operand reads free of
 // bank conflicts.
+//
+// Two load paths share the tile order and the epilogue:
+//   k_gemm_dma : buffer loads straight into LDS (no register staging), STAGES
+//                deep, so several K steps of loads stay in flight; rows past
+//                the expert's segment and K past the range read as zero
+//                through the buffer's range check, without branches.
+//   k_gemm_reg : global loads into registers, then LDS stores, two buffers.
 #include "common.h"
 #include "kernels.h"
 
@@ -27,15 +34,321 @@ namespace moe {
 namespace {
 
 constexpr int BK = 64;
+constexpr uint32_t kOOB = 0xFFFFFFF0u;       // byte offset past any buffer: loads return zero
+constexpr int kBufferFlags = 0x00020000;     // raw buffer, 32-bit data
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * BK + ((chunk ^ (row & 7)) << 3); }
 
+// Linear tile order: XCD-aware remap of blockIdx.x (workgroups are dealt to
+// the 8 XCDs round-robin, so XCD x runs blocks x, x+8, ...; the remap gives each
+// XCD a contiguous range of the order below, and so a compact group of tiles
+// that shares operands in its own L2), then groups of GM m-tiles with the
+// m-tile index varying fastest, so tiles that read the same expert's weight
+// tile run together.
+__device__ __forceinline__ int xcd_remap(int bid, int G) {
+  const int xcd = bid & 7, base = G >> 3, rem = G & 7;
+  return xcd * base + min(xcd, rem) + (bid >> 3);
+}
+
+struct TilePos {
+  TileInfo ti;
+  int nt, split, kb0, kb1, KT;
+};
+
+// Decode this workgroup's tile; false when it has none (uniform over the
+// workgroup).
+template <int BM, int NO>
+__device__ __forceinline__ bool decode_tile(const GemmParams& p, TilePos& tp) {
+  constexpr int GM = BM >= 256 ? 4 : 8;  // m-tiles per group
+  const int lane = threadIdx.x & 63;
+  const int ntiles = (p.Nout + NO - 1) / NO;
+  // per-expert m-tile counts (lane e = expert e), inclusive scan over lanes
+  int eoff = 0, ecnt = 0;
+  if (lane < p.N) {
+    eoff = p.offsets[lane];
+    ecnt = p.offsets[lane + 1] - eoff;
+  }
+  const int etl = (ecnt + BM - 1) / BM;
+  int incl = etl;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int v = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += v;
+  }
+  const int mtot = __shfl(incl, 63, 64);
+  const int per_split = mtot * ntiles;
+  int L = xcd_remap(blockIdx.x, gridDim.x);
+  if (L >= per_split * p.splits) return false;
+  tp.split = L / per_split;
+  L -= tp.split * per_split;
+  const int g = L / (GM * ntiles);
+  const int gm = min(GM, mtot - g * GM);
+  const int r_in = L - g * GM * ntiles;
+  const int mt = g * GM + r_in % gm;
+  tp.nt = r_in / gm;
+  const int e = __popcll(__ballot(incl <= mt));
+  const int local = mt - __shfl(incl - etl, e, 64);
+  // the values are wave-uniform; saying so keeps them (and the buffer
+  // descriptors built from them) in scalar registers
+  tp.ti.expert = __builtin_amdgcn_readfirstlane(e);
+  tp.ti.row0 = __builtin_amdgcn_readfirstlane(__shfl(eoff, e, 64) + local * BM);
+  tp.ti.rows = __builtin_amdgcn_readfirstlane(min(BM, __shfl(ecnt, e, 64) - local * BM));
+  tp.nt = __builtin_amdgcn_readfirstlane(tp.nt);
+  tp.split = __builtin_amdgcn_readfirstlane(tp.split);
+  // K range of this split
+  const int kper = ((p.K + p.splits - 1) / p.splits + BK - 1) / BK * BK;
+  tp.kb0 = tp.split * kper;
+  tp.kb1 = min(p.K, tp.kb0 + kper);
+  tp.KT = tp.kb1 > tp.kb0 ? (tp.kb1 - tp.kb0 + BK - 1) / BK : 0;
+  return true;
+}
+
+// LDS rows read by a wave's MFMA blocks; swiglu pairs gate block j with up
+// block j + NB/2 over the same output columns.
+template <int WM, int WN, int MB, int NB, int BN, bool SWIGLU>
+__device__ __forceinline__ void frag_rows(int wm, int wn, int lane, int (&arow)[MB], int (&brow)[NB]) {
+#pragma unroll
+  for (int i = 0; i < MB; ++i) arow[i] = wm * WM + i * 32 + (lane & 31);
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    if (SWIGLU) {
+      const int half = NB / 2;
+      const int jj = j < half ? j : j - half;
+      brow[j] = (j < half ? 0 : BN / 2) + wn * (WN / 2) + jj * 32 + (lane & 31);
+    } else {
+      brow[j] = wn * WN + j * 32 + (lane & 31);
+    }
+  }
+}
+
+// One BK step of MFMAs from an LDS stage.
+template <int MB, int NB>
+__device__ __forceinline__ void mma_stage(const uint16_t* __restrict__ a, const uint16_t* __restrict__ b,
+                                          const int (&arow)[MB], const int (&brow)[NB], int khalf,
+                                          f32x16_t (&acc)[MB][NB]) {
+#pragma unroll
+  for (int ks = 0; ks < BK / 16; ++ks) {
+    const int chunk = ks * 2 + khalf;
+    bf16x8_t af[MB], bfr[NB];
+#pragma unroll
+    for (int i = 0; i < MB; ++i) af[i] = *reinterpret_cast<const bf16x8_t*>(&a[swz(arow[i], chunk)]);
+#pragma unroll
+    for (int j = 0; j < NB; ++j) bfr[j] = *reinterpret_cast<const bf16x8_t*>(&b[swz(brow[j], chunk)]);
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+  }
+}
+
+// Accumulator layout of a 32x32 block: lane holds column (lane & 31) and rows
+// 8*(r/4) + 4*(lane/32) + r%4 for r = 0..15.
+template <int WM, int WN, int MB, int NB, bool SWIGLU>
+__device__ __forceinline__ void epilogue(const GemmParams& p, const TilePos& tp, int wm, int wn, int lane, int NO,
+                                         f32x16_t (&acc)[MB][NB]) {
+  const int col_l = lane & 31, khalf = lane >> 5;
+  if (SWIGLU) {
+    uint16_t* __restrict__ C = static_cast<uint16_t*>(p.C);
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int j = 0; j < NB / 2; ++j) {
+        const int f = tp.nt * NO + wn * (WN / 2) + j * 32 + col_l;
+        if (f >= p.Nout) continue;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int tr = wm * WM + i * 32 + (r >> 2) * 8 + khalf * 4 + (r & 3);
+          if (tr < tp.ti.rows) {
+            const float g = acc[i][j][r], u = acc[i][j + NB / 2][r];
+            C[static_cast<int64_t>(tp.ti.row0 + tr) * p.ldc + f] = f32_to_bf16(silu(g) * u);
+          }
+        }
+      }
+  } else {
+    float* __restrict__ C = static_cast<float*>(p.C) + tp.split * p.c_split_stride;
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const int n = tp.nt * NO + wn * WN + j * 32 + col_l;
+        if (n >= p.Nout) continue;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int tr = wm * WM + i * 32 + (r >> 2) * 8 + khalf * 4 + (r & 3);
+          if (tr < tp.ti.rows) C[static_cast<int64_t>(tp.ti.row0 + tr) * p.ldc + n] = acc[i][j][r];
+        }
+      }
+  }
+}
+
+template <int MB, int NB>
+__device__ __forceinline__ void zero_acc(f32x16_t (&acc)[MB][NB]) {
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+}
+
+// ---- buffer loads straight into LDS ------------------------------------------
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Wait until at most `later` stages of LPS loads each are still in flight.
+template <int LPS, int MAXLATER>
+__device__ __forceinline__ void wait_stage(int later) {
+  if constexpr (MAXLATER >= 3) {
+    if (later >= 3) { wait_vm<3 * LPS>(); return; }
+  }
+  if constexpr (MAXLATER >= 2) {
+    if (later >= 2) { wait_vm<2 * LPS>(); return; }
+  }
+  if constexpr (MAXLATER >= 1) {
+    if (later >= 1) { wait_vm<LPS>(); return; }
+  }
+  wait_vm<0>();
+}
+
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// A wave-uniform buffer descriptor: the base address passes through
+// readfirstlane so the descriptor lives in scalar registers (a descriptor in
+// vector registers makes every load a per-lane loop).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* base, int64_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
+  void* p = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
+  const int num = __builtin_amdgcn_readfirstlane(static_cast<int>(bytes < 0x7FFFFFF0 ? bytes : 0x7FFFFFF0));
+  return __builtin_amdgcn_make_buffer_rsrc(p, 0, num, kBufferFlags);
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// One pipeline step: issue the loads of a later stage, then run the MFMAs of
+// the current one. The restrict-qualified stage pointers tell the compiler the
+// two stages are disjoint, so it does not hold the current stage's LDS reads
+// until the just-issued loads land (the explicit waits and barrier at the top
+// of each step order the stages).
+template <int MB, int NB, class Issue>
+__device__ __forceinline__ void dma_step(Issue& issue, bool do_issue, int kt_next, const uint16_t* __restrict__ a_cur,
+                                         const uint16_t* __restrict__ b_cur, uint16_t* __restrict__ a_nxt,
+                                         uint16_t* __restrict__ b_nxt, const int (&arow)[MB], const int (&brow)[NB],
+                                         int khalf, f32x16_t (&acc)[MB][NB]) {
+  if (do_issue) issue(a_nxt, b_nxt, kt_next);
+  mma_stage<MB, NB>(a_cur, b_cur, arow, brow, khalf, acc);
+}
+
+template <int BM, int BN, int WGM, int WGN, int STAGES, bool SWIGLU, bool GATHER>
+__global__ __launch_bounds__(WGM * WGN * 64) void k_gemm_dma(GemmParams p) {
+  constexpr int NW = WGM * WGN;
+  constexpr int WM = BM / WGM, WN = BN / WGN;
+  constexpr int MB = WM / 32, NB = WN / 32;
+  constexpr int IA = BM / 8 / NW, IB = BN / 8 / NW;  // 1-KB LDS segments a wave fills per stage
+  constexpr int LPS = IA + IB;
+  constexpr int NO = SWIGLU ? BN / 2 : BN;
+  static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be a multiple of 32");
+  static_assert(!SWIGLU || NB % 2 == 0, "swiglu needs gate/up block pairs");
+  static_assert(IA * NW * 8 == BM && IB * NW * 8 == BN, "segments must divide among waves");
+  static_assert(STAGES >= 2 && STAGES <= 5 && (STAGES - 2) * LPS <= 63, "stage count");
+
+  // one LDS object for every stage of A and B: with a single object the
+  // compiler's alias scopes can tell the stages apart
+  __shared__ __attribute__((aligned(16))) uint16_t smem[STAGES * (BM + BN) * BK];
+  auto sA = [&](int st) { return smem + st * (BM + BN) * BK; };
+  auto sB = [&](int st) { return smem + st * (BM + BN) * BK + BM * BK; };
+
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave / WGN, wn = wave % WGN;
+  TilePos tp;
+  if (!decode_tile<BM, NO>(p, tp)) return;
+
+  // lane q of a 1-KB segment s holds row 8s + q/8 and logical chunk (q%8) ^ (q/8)
+  const int lrow = lane >> 3;
+  const int lchunk = (lane & 7) ^ lrow;
+  uint32_t aoff[IA];
+#pragma unroll
+  for (int i = 0; i < IA; ++i) {
+    const int r = (i * NW + wave) * 8 + lrow;
+    const bool v = r < tp.ti.rows;
+    int src = tp.ti.row0 + r;
+    if (GATHER) src = v ? p.row_token[src] : 0;
+    aoff[i] = v ? static_cast<uint32_t>(src) * static_cast<uint32_t>(p.lda) * 2u + lchunk * 16u : kOOB;
+  }
+  // B segment of load i: for swiglu the first IB/2 loads of every wave fill
+  // gate rows [0, BN/2) and the rest the matching up rows, so the weight
+  // matrix of each load is known at compile time
+  constexpr int IBH = SWIGLU ? IB / 2 : IB;
+  static_assert(!SWIGLU || IB % 2 == 0, "swiglu splits the B loads in halves");
+  uint32_t boff[IB];
+#pragma unroll
+  for (int i = 0; i < IB; ++i) {
+    const int r = ((i % IBH) * NW + wave) * 8 + lrow;  // row within the gate (or plain) block
+    const int f = tp.nt * NO + r;
+    boff[i] = f < p.Nout ? static_cast<uint32_t>(f) * static_cast<uint32_t>(p.ldb) * 2u + lchunk * 16u : kOOB;
+  }
+  const int64_t b_bytes = static_cast<int64_t>(p.Nout) * p.ldb * 2;
+  const __amdgpu_buffer_rsrc_t ra = uniform_rsrc(p.A, p.a_rows * p.lda * 2);
+  const uint16_t* b0 = static_cast<const uint16_t*>(p.B0) + tp.ti.expert * p.b_expert_stride;
+  const uint16_t* b1 = SWIGLU ? static_cast<const uint16_t*>(p.B1) + tp.ti.expert * p.b_expert_stride : b0;
+  const __amdgpu_buffer_rsrc_t rb0 = uniform_rsrc(b0, b_bytes);
+  const __amdgpu_buffer_rsrc_t rb1 = uniform_rsrc(b1, b_bytes);
+
+  // One K step of loads into the LDS stage at (a_dst, b_dst).
+  auto issue = [&](uint16_t* a_dst, uint16_t* b_dst, int kt) {
+    const int kb = tp.kb0 + kt * BK;
+    const bool kval = kb + lchunk * 8 < tp.kb1;
+    const uint32_t kbyte = static_cast<uint32_t>(kb) * 2u;
+#pragma unroll
+    for (int i = 0; i < IA; ++i) {
+      const uint32_t vo = (kval && aoff[i] != kOOB) ? aoff[i] + kbyte : kOOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(a_dst + (i * NW + wave) * 512), 16, vo, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < IB; ++i) {
+      const uint32_t vo = (kval && boff[i] != kOOB) ? boff[i] + kbyte : kOOB;
+      const int seg = (i % IBH) * NW + wave + (i >= IBH ? (BN / 16) : 0);
+      if (i < IBH)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb0, (lds_ptr_t)(b_dst + seg * 512), 16, vo, 0, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb1, (lds_ptr_t)(b_dst + seg * 512), 16, vo, 0, 0, 0);
+    }
+  };
+
+  f32x16_t acc[MB][NB];
+  zero_acc(acc);
+  int arow[MB], brow[NB];
+  frag_rows<WM, WN, MB, NB, BN, SWIGLU>(wm, wn, lane, arow, brow);
+  const int khalf = lane >> 5;
+
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s)
+    if (s < tp.KT) issue(sA(s), sB(s), s);
+  for (int kt = 0; kt < tp.KT; ++kt) {
+    const int later = min(STAGES - 2, tp.KT - 1 - kt);
+    wait_stage<LPS, STAGES - 2>(later);
+    lds_barrier();  // stage kt is complete for every wave; stage kt-1 is free
+    const int st = kt % STAGES, nx = (kt + STAGES - 1) % STAGES;
+    dma_step<MB, NB>(issue, kt + STAGES - 1 < tp.KT, kt + STAGES - 1, sA(st), sB(st), sA(nx), sB(nx), arow, brow,
+                     khalf, acc);
+  }
+  epilogue<WM, WN, MB, NB, SWIGLU>(p, tp, wm, wn, lane, NO, acc);
+}
+
+// ---- register-staged loads -------------------------------------------------------
+
 template <int BM, int BN, int WGM, int WGN, bool SWIGLU, bool GATHER>
-__global__ __launch_bounds__(WGM * WGN * 64) void k_gemm_mfma(GemmParams p) {
+__global__ __launch_bounds__(WGM * WGN * 64) void k_gemm_reg(GemmParams p) {
   constexpr int NT = WGM * WGN * 64;
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int MB = WM / 32, NB = WN / 32;
   constexpr int CA = BM * 8 / NT, CB = BN * 8 / NT;  // 16-byte chunks per thread per K step
+  constexpr int NO = SWIGLU ? BN / 2 : BN;
   static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be a multiple of 32");
   static_assert(!SWIGLU || NB % 2 == 0, "swiglu needs gate/up block pairs");
   static_assert(CA >= 1 && CB >= 1 && (BM * 8) % NT == 0 && (BN * 8) % NT == 0, "load split");
@@ -43,195 +356,120 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm_mfma(GemmParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * BK];
   __shared__ __attribute__((aligned(16))) uint16_t sB[2][BN * BK];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WGN, wn = wave % WGN;
-  const int NO = SWIGLU ? BN / 2 : BN;  // output columns per tile
-  const int ntiles = (p.Nout + NO - 1) / NO;
-  const int mtiles = static_cast<int>((p.rows_max + BM - 1) / BM) + p.N;
-  int bid = blockIdx.x;
-  const int nt = bid % ntiles;
-  bid /= ntiles;
-  const int mt = bid % mtiles;
-  const int split = bid / mtiles;
+  TilePos tp;
+  if (!decode_tile<BM, NO>(p, tp)) return;
 
-  TileInfo ti;
-  if (!find_tile<BM>(p.offsets, p.N, mt, ti)) return;  // uniform over the workgroup
-
-  // K range of this split
-  const int kper = ((p.K + p.splits - 1) / p.splits + BK - 1) / BK * BK;
-  const int kb0 = split * kper;
-  const int kb1 = min(p.K, kb0 + kper);
-  const int KT = kb1 > kb0 ? (kb1 - kb0 + BK - 1) / BK : 0;
-
-  // per-thread global source rows
   const uint16_t* __restrict__ Ab = static_cast<const uint16_t*>(p.A);
-  const uint16_t* arow[CA];
-  int achunk[CA];
+  int aoff[CA], achunk[CA];
   bool aval[CA];
 #pragma unroll
   for (int i = 0; i < CA; ++i) {
     const int ci = tid + i * NT;
     const int r = ci >> 3;
     achunk[i] = ci & 7;
-    aval[i] = r < ti.rows;
-    int64_t src = ti.row0 + r;
+    aval[i] = r < tp.ti.rows;
+    int src = tp.ti.row0 + r;
     if (GATHER) src = aval[i] ? p.row_token[src] : 0;
-    arow[i] = Ab + (aval[i] ? src : 0) * p.lda;
+    aoff[i] = (aval[i] ? src : 0) * static_cast<int>(p.lda) + achunk[i] * 8;
   }
-  const uint16_t* __restrict__ B0 = static_cast<const uint16_t*>(p.B0) + ti.expert * p.b_expert_stride;
-  const uint16_t* __restrict__ B1 = SWIGLU ? static_cast<const uint16_t*>(p.B1) + ti.expert * p.b_expert_stride : nullptr;
-  const uint16_t* brow[CB];
-  int bchunk[CB];
-  bool bval[CB];
+  const uint16_t* __restrict__ B0 = static_cast<const uint16_t*>(p.B0) + tp.ti.expert * p.b_expert_stride;
+  const uint16_t* __restrict__ B1 =
+      SWIGLU ? static_cast<const uint16_t*>(p.B1) + tp.ti.expert * p.b_expert_stride : nullptr;
+  int boff[CB], bchunk[CB];
+  bool bval[CB], bup[CB];
 #pragma unroll
   for (int i = 0; i < CB; ++i) {
     const int ci = tid + i * NT;
     const int r = ci >> 3;
     bchunk[i] = ci & 7;
-    int f;
-    const uint16_t* base;
-    if (SWIGLU) {
-      const bool up = r >= BN / 2;
-      f = nt * NO + (up ? r - BN / 2 : r);
-      base = up ? B1 : B0;
-    } else {
-      f = nt * NO + r;
-      base = B0;
-    }
+    bup[i] = SWIGLU && r >= BN / 2;
+    const int f = tp.nt * NO + (bup[i] ? r - BN / 2 : r);
     bval[i] = f < p.Nout;
-    brow[i] = base + static_cast<int64_t>(bval[i] ? f : 0) * p.ldb;
+    boff[i] = (bval[i] ? f : 0) * static_cast<int>(p.ldb) + bchunk[i] * 8;
   }
 
   u32x4_t ra[CA], rb[CB];
   auto gload = [&](int kt) {
-    const int kb = kb0 + kt * BK;
+    const int kb = tp.kb0 + kt * BK;
 #pragma unroll
     for (int i = 0; i < CA; ++i) {
       const int kk = kb + achunk[i] * 8;
-      if (aval[i] && kk < kb1) ra[i] = *reinterpret_cast<const u32x4_t*>(arow[i] + kk);
+      if (aval[i] && kk < tp.kb1) ra[i] = *reinterpret_cast<const u32x4_t*>(Ab + aoff[i] + kb);
       else ra[i] = u32x4_t{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int i = 0; i < CB; ++i) {
       const int kk = kb + bchunk[i] * 8;
-      if (bval[i] && kk < kb1) rb[i] = *reinterpret_cast<const u32x4_t*>(brow[i] + kk);
+      const uint16_t* bb = bup[i] ? B1 : B0;
+      if (bval[i] && kk < tp.kb1) rb[i] = *reinterpret_cast<const u32x4_t*>(bb + boff[i] + kb);
       else rb[i] = u32x4_t{0u, 0u, 0u, 0u};
     }
   };
   auto lstore = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < CA; ++i) {
-      const int r = (tid + i * NT) >> 3;
-      *reinterpret_cast<u32x4_t*>(&sA[buf][swz(r, achunk[i])]) = ra[i];
-    }
+    for (int i = 0; i < CA; ++i)
+      *reinterpret_cast<u32x4_t*>(&sA[buf][swz((tid + i * NT) >> 3, achunk[i])]) = ra[i];
 #pragma unroll
-    for (int i = 0; i < CB; ++i) {
-      const int r = (tid + i * NT) >> 3;
-      *reinterpret_cast<u32x4_t*>(&sB[buf][swz(r, bchunk[i])]) = rb[i];
-    }
+    for (int i = 0; i < CB; ++i)
+      *reinterpret_cast<u32x4_t*>(&sB[buf][swz((tid + i * NT) >> 3, bchunk[i])]) = rb[i];
   };
 
   f32x16_t acc[MB][NB];
-#pragma unroll
-  for (int i = 0; i < MB; ++i)
-#pragma unroll
-    for (int j = 0; j < NB; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-  // B rows read by this wave's blocks
-  int brow_l[NB];
-#pragma unroll
-  for (int j = 0; j < NB; ++j) {
-    if (SWIGLU) {
-      const int half = NB / 2;
-      const int jj = j < half ? j : j - half;
-      brow_l[j] = (j < half ? 0 : BN / 2) + wn * (WN / 2) + jj * 32 + (lane & 31);
-    } else {
-      brow_l[j] = wn * WN + j * 32 + (lane & 31);
-    }
-  }
-  int arow_l[MB];
-#pragma unroll
-  for (int i = 0; i < MB; ++i) arow_l[i] = wm * WM + i * 32 + (lane & 31);
+  zero_acc(acc);
+  int arow[MB], brow[NB];
+  frag_rows<WM, WN, MB, NB, BN, SWIGLU>(wm, wn, lane, arow, brow);
   const int khalf = lane >> 5;
 
-  if (KT > 0) {
+  if (tp.KT > 0) {
     gload(0);
     lstore(0);
   }
   __syncthreads();
-  for (int kt = 0; kt < KT; ++kt) {
+  for (int kt = 0; kt < tp.KT; ++kt) {
     const int cur = kt & 1;
-    if (kt + 1 < KT) gload(kt + 1);
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      const int chunk = ks * 2 + khalf;
-      bf16x8_t af[MB], bfr[NB];
-#pragma unroll
-      for (int i = 0; i < MB; ++i) af[i] = *reinterpret_cast<const bf16x8_t*>(&sA[cur][swz(arow_l[i], chunk)]);
-#pragma unroll
-      for (int j = 0; j < NB; ++j) bfr[j] = *reinterpret_cast<const bf16x8_t*>(&sB[cur][swz(brow_l[j], chunk)]);
-#pragma unroll
-      for (int i = 0; i < MB; ++i)
-#pragma unroll
-        for (int j = 0; j < NB; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
-    if (kt + 1 < KT) lstore(cur ^ 1);
+    if (kt + 1 < tp.KT) gload(kt + 1);
+    mma_stage<MB, NB>(sA[cur], sB[cur], arow, brow, khalf, acc);
+    if (kt + 1 < tp.KT) lstore(cur ^ 1);
     __syncthreads();
   }
-
-  // epilogue: lane holds column (lane & 31) and rows 8*(r/4) + 4*(lane/32) + r%4
-  const int col_l = lane & 31;
-  if (SWIGLU) {
-    uint16_t* __restrict__ C = static_cast<uint16_t*>(p.C);
-#pragma unroll
-    for (int i = 0; i < MB; ++i)
-#pragma unroll
-      for (int j = 0; j < NB / 2; ++j) {
-        const int f = nt * NO + wn * (WN / 2) + j * 32 + col_l;
-        if (f >= p.Nout) continue;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int tr = wm * WM + i * 32 + (r >> 2) * 8 + khalf * 4 + (r & 3);
-          if (tr < ti.rows) {
-            const float g = acc[i][j][r], u = acc[i][j + NB / 2][r];
-            C[static_cast<int64_t>(ti.row0 + tr) * p.ldc + f] = f32_to_bf16(silu(g) * u);
-          }
-        }
-      }
-  } else {
-    float* __restrict__ C = static_cast<float*>(p.C) + split * p.c_split_stride;
-#pragma unroll
-    for (int i = 0; i < MB; ++i)
-#pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        const int n = nt * NO + wn * WN + j * 32 + col_l;
-        if (n >= p.Nout) continue;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int tr = wm * WM + i * 32 + (r >> 2) * 8 + khalf * 4 + (r & 3);
-          if (tr < ti.rows) C[static_cast<int64_t>(ti.row0 + tr) * p.ldc + n] = acc[i][j][r];
-        }
-      }
-  }
+  epilogue<WM, WN, MB, NB, SWIGLU>(p, tp, wm, wn, lane, NO, acc);
 }
 
-template <int BM, int BN, int WGM, int WGN>
-hipError_t launch_cfg(const GemmParams& p, hipStream_t s) {
+int64_t grid_blocks(const GemmParams& p, int BM, int BN) {
   const int NO = p.swiglu ? BN / 2 : BN;
   const int64_t ntiles = (p.Nout + NO - 1) / NO;
   const int64_t mtiles = (p.rows_max + BM - 1) / BM + p.N;
-  const int64_t blocks = ntiles * mtiles * p.splits;
+  return ntiles * mtiles * p.splits;
+}
+
+template <int BM, int BN, int WGM, int WGN>
+hipError_t launch_reg(const GemmParams& p, hipStream_t s) {
+  const int64_t blocks = grid_blocks(p, BM, BN);
   if (blocks <= 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>(blocks)), block(WGM * WGN * 64);
   if (p.swiglu) {
-    if (p.row_token) hipLaunchKernelGGL((k_gemm_mfma<BM, BN, WGM, WGN, true, true>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((k_gemm_mfma<BM, BN, WGM, WGN, true, false>), grid, block, 0, s, p);
+    if (p.row_token) hipLaunchKernelGGL((k_gemm_reg<BM, BN, WGM, WGN, true, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((k_gemm_reg<BM, BN, WGM, WGN, true, false>), grid, block, 0, s, p);
   } else {
-    if (p.row_token) hipLaunchKernelGGL((k_gemm_mfma<BM, BN, WGM, WGN, false, true>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((k_gemm_mfma<BM, BN, WGM, WGN, false, false>), grid, block, 0, s, p);
+    if (p.row_token) hipLaunchKernelGGL((k_gemm_reg<BM, BN, WGM, WGN, false, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((k_gemm_reg<BM, BN, WGM, WGN, false, false>), grid, block, 0, s, p);
+  }
+  return hipGetLastError();
+}
+
+template <int BM, int BN, int WGM, int WGN, int STAGES>
+hipError_t launch_dma(const GemmParams& p, hipStream_t s) {
+  const int64_t blocks = grid_blocks(p, BM, BN);
+  if (blocks <= 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>(blocks)), block(WGM * WGN * 64);
+  if (p.swiglu) {
+    if (p.row_token) hipLaunchKernelGGL((k_gemm_dma<BM, BN, WGM, WGN, STAGES, true, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((k_gemm_dma<BM, BN, WGM, WGN, STAGES, true, false>), grid, block, 0, s, p);
+  } else {
+    if (p.row_token) hipLaunchKernelGGL((k_gemm_dma<BM, BN, WGM, WGN, STAGES, false, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((k_gemm_dma<BM, BN, WGM, WGN, STAGES, false, false>), grid, block, 0, s, p);
   }
   return hipGetLastError();
 }
@@ -240,11 +478,24 @@ hipError_t launch_cfg(const GemmParams& p, hipStream_t s) {
 
 bool gemm_bf16_mfma_supported(int K, int Nout) { return K % 8 == 0 && K > 0 && Nout > 0; }
 
+// Tile shape by the average rows per expert: short, wide tiles when experts
+// get few rows (decode), large square tiles otherwise.
+void gemm_bf16_mfma_tile(int64_t rows_max, int N, int* bm, int* bn) {
+  const int64_t avg_rows = rows_max / (N > 0 ? N : 1);
+  if (avg_rows <= 48) {
+    *bm = 32;
+    *bn = 256;
+  } else {
+    *bm = 256;
+    *bn = 256;
+  }
+}
+
 hipError_t launch_gemm_bf16_mfma(const GemmParams& p, hipStream_t s) {
-  // few rows per expert: short, wide tiles; otherwise square tiles
-  const int64_t avg_rows = p.rows_max / (p.N > 0 ? p.N : 1);
-  if (avg_rows <= 48) return launch_cfg<32, 256, 1, 4>(p, s);
-  return launch_cfg<128, 128, 2, 2>(p, s);
+  int bm, bn;
+  gemm_bf16_mfma_tile(p.rows_max, p.N, &bm, &bn);
+  if (bm == 32) return launch_reg<32, 256, 1, 4>(p, s);
+  return launch_dma<256, 256, 4, 2, 2>(p, s);
 }
 
 }  // namespace moe

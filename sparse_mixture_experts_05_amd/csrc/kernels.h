@@ -102,10 +102,12 @@ struct GemmParams {
   int64_t c_split_stride;     // elements between split-K partial outputs
   int splits;
   int64_t rows_max;           // upper bound on offsets[N] (grid sizing)
+  int64_t a_rows;             // rows of A (bounds of the gathered or permuted operand)
   int swiglu;
 };
 hipError_t launch_gemm_bf16_mfma(const GemmParams& p, hipStream_t s);
 bool gemm_bf16_mfma_supported(int K, int Nout);
+void gemm_bf16_mfma_tile(int64_t rows_max, int N, int* bm, int* bn);
 hipError_t launch_gemm_simple(const GemmParams& p, int bf16, hipStream_t s);
 
 // ---- combine (combine.hip) --------------------------------------------------

@@ -90,8 +90,8 @@ Layout layout(const moe_cfg* c) {
   if (L.mfma) {
     // the down projection splits K when there are too few output tiles to
     // occupy 256 compute units
-    const int64_t avg = L.A_max / c->N;
-    const int bm = avg <= 48 ? 32 : 128, bn = avg <= 48 ? 256 : 128;
+    int bm, bn;
+    moe::gemm_bf16_mfma_tile(L.A_max, c->N, &bm, &bn);
     const int64_t tiles = ((L.A_max + bm - 1) / bm + std::min<int64_t>(c->N, L.A_max)) * ((c->H + bn - 1) / bn);
     if (tiles > 0 && tiles < 512) {
       int64_t s = (1024 + tiles - 1) / tiles;
@@ -177,6 +177,7 @@ moe_status run_gemms(const moe_cfg* c, const Layout& L, const void* a, const int
   g1.c_split_stride = 0;
   g1.splits = 1;
   g1.rows_max = L.A_max;
+  g1.a_rows = row_token ? c->T : c->T * c->k;
   g1.swiglu = 1;
   moe::GemmParams g2 = g1;
   g2.A = at<char>(ws, L.h);
@@ -191,6 +192,7 @@ moe_status run_gemms(const moe_cfg* c, const Layout& L, const void* a, const int
   g2.C = y_perm;
   g2.ldc = c->H;
   g2.c_split_stride = L.A_max * static_cast<int64_t>(c->H);
+  g2.a_rows = L.A_max;
   g2.splits = splits;
   g2.swiglu = 0;
   if (L.mfma) {
@@ -233,8 +235,12 @@ moe_status moe_check(const moe_cfg* c) {
                      (c->out == MOE_BF16 || c->out == MOE_F32);
   if (!dt_ok) return fail(MOE_ERR_INVALID, "unknown dtype code");
   if (c->act != c->wt) return fail(MOE_ERR_UNSUPPORTED, "activations and expert weights must share a dtype");
+  // the kernels address each operand with 32-bit byte offsets below 2^31
   const int64_t Tk = c->T * c->k;
-  if (Tk > INT32_MAX || static_cast<double>(Tk) * c->H > 9.0e18) return fail(MOE_ERR_UNSUPPORTED, "too large");
+  const int64_t lim = int64_t(1) << 29;  // elements, so that fp32 operands stay below 2 GiB
+  if (c->T * static_cast<int64_t>(c->H) >= lim || Tk * static_cast<int64_t>(c->F) >= lim ||
+      Tk * static_cast<int64_t>(c->H) >= lim || static_cast<int64_t>(c->F) * c->H >= lim)
+    return fail(MOE_ERR_UNSUPPORTED, "T*H, T*k*F, T*k*H and F*H must stay below 2^29 elements");
   return MOE_OK;
 }
 
