@@ -12,7 +12,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libmoe.so")
-SOURCES = ["router.hip", "permute.hip", "gemm_mfma.hip", "gemm_simple.hip", "combine.hip", "moe_abi.cpp"]
+SOURCES = ["router.hip", "router_mma.hip", "permute.hip", "gemm_mfma.hip", "gemm_simple.hip", "combine.hip", "moe_abi.cpp"]
 OBJDIR = os.path.join(HERE, "_build")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -32,8 +32,7 @@ __global__ __launch_bounds__(64) void k_hist(HistParams p) {
 
 template <int KMAX>
 __global__ __launch_bounds__(kScatterThreads) void k_scatter(ScatterParams p) {
-  __shared__ int s_part[4][64][2];
-  __shared__ int s_base[64], s_kept[64], s_off[65];
+  __shared__ int s_base[64], s_tot[64], s_kept[64], s_off[65];
   __shared__ int s_wcnt[4][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int N = p.N, k = p.k;
@@ -42,26 +41,30 @@ __global__ __launch_bounds__(kScatterThreads) void k_scatter(ScatterParams p) {
   const int64_t nhb = (T + p.hist_tokens - 1) / p.hist_tokens;
   const int64_t hb0 = tb0 / p.hist_tokens;
 
-  // per-expert totals and the count before this block, over the histogram
-  int base = 0, tot = 0;
-  if (lane < N) {
-    for (int64_t hb = wave; hb < nhb; hb += 4) {
-      const int v = p.hist[hb * N + lane];
-      tot += v;
-      if (hb < hb0) base += v;
+  // per-expert totals and the count before this block: every thread reads
+  // its share of the histogram at once and adds it into LDS (integer sums,
+  // so the order of the adds does not matter)
+  if (tid < 64) {
+    s_base[tid] = 0;
+    s_tot[tid] = 0;
+  }
+  __syncthreads();
+  {
+    const int64_t nel = nhb * N;
+    const int64_t split = hb0 * N;  // elements before this block's first histogram row
+#pragma unroll 8
+    for (int64_t i = tid; i < nel; i += kScatterThreads) {
+      const int v = p.hist[i];
+      const int n = static_cast<int>(i % N);
+      if (v) {
+        atomicAdd(&s_tot[n], v);
+        if (i < split) atomicAdd(&s_base[n], v);
+      }
     }
   }
-  s_part[wave][lane][0] = base;
-  s_part[wave][lane][1] = tot;
   __syncthreads();
   if (tid < N) {
-    int b = 0, c = 0;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      b += s_part[w][tid][0];
-      c += s_part[w][tid][1];
-    }
-    s_base[tid] = b;
+    const int c = s_tot[tid];
     s_kept[tid] = p.capacity < 0 ? c : (c < p.capacity ? c : p.capacity);
     if (blockIdx.x == 0) {
       if (p.counts) p.counts[tid] = c;

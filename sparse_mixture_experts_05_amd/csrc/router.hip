@@ -222,7 +222,7 @@ __global__ __launch_bounds__(kRouterWaves * kWave) void k_router(RouterParams p)
 
 template <int NMAX>
 hipError_t launch_router_n(const RouterParams& p, hipStream_t s) {
-  const dim3 grid(router_blocks(p.T, p.N, p.noisy)), block(kRouterWaves * kWave);
+  const dim3 grid(router_blocks(p.T, p.N, p.noisy, 0)), block(kRouterWaves * kWave);
   const bool vec4 = (p.N % 4) == 0;
 #define MOE_ROUTER_LAUNCH(NOISY, XT, V4) \
   hipLaunchKernelGGL((k_router<NMAX, NOISY, XT, V4>), grid, block, 0, s, p)
@@ -291,18 +291,20 @@ __global__ void k_fill_f32(float* p, int64_t n, float v) {
 
 }  // namespace
 
-int router_tokens_per_block(int N, int /*noisy*/) {
+int router_tokens_per_block(int N, int /*noisy*/, int act_bf16) {
+  if (act_bf16) return 16;  // the matrix-core router (router_mma.hip)
   const int nm = nmax_for(N);
   const int tpw = nm <= 16 ? 4 : (nm == 32 ? 2 : 1);
   return tpw * kRouterWaves;
 }
 
-int router_blocks(int64_t T, int N, int noisy) {
-  const int tpb = router_tokens_per_block(N, noisy);
+int router_blocks(int64_t T, int N, int noisy, int act_bf16) {
+  const int tpb = router_tokens_per_block(N, noisy, act_bf16);
   return static_cast<int>((T + tpb - 1) / tpb);
 }
 
 hipError_t launch_router(const RouterParams& p, hipStream_t s) {
+  if (p.act_bf16) return launch_router_mma(p, s);
   switch (nmax_for(p.N)) {
     case 8: return launch_router_n<8>(p, s);
     case 16: return launch_router_n<16>(p, s);

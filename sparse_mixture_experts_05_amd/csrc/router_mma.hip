@@ -1,0 +1,240 @@
+// Router on the matrix cores for bf16 activations.
+//
+// The router product x.W_g (and x.W_noise) is a skinny GEMM: T x H times
+// H x N with N <= 64. The fp32 router weights are split exactly into three
+// bf16 parts, W = W1 + W2 + W3 (each part holds the next 8 significant bits),
+// so every product x * W_i of a bf16 activation is exact in fp32 and
+// v_mfma_f32_16x16x32_bf16 forms x.W with fp32 accumulation. The hi part and
+// the two lower parts go to separate accumulators and the four waves of a
+// block each cover a quarter of H, which keeps the accumulated rounding error
+// near that of a plain fp32 dot product.
+//
+// A block owns 16 tokens. After the product, one thread per token applies the
+// noise term, KeepTopK (ties to the lower expert index; "Llama 3 Meets MoE"
+// review, section 3) and the gate of the chosen order (Mixtral: softmax over
+// the kept scores; ST: softmax over all scores, section 5), and threads of
+// the block then sum the per-expert counts, gate weights and softmax(logit)
+// values over the block's tokens in token order for the permutation and the
+// balance statistics.
+#include "common.h"
+#include "kernels.h"
+
+#include <algorithm>
+
+typedef float f32x4_mma_t __attribute__((ext_vector_type(4)));
+
+namespace moe {
+
+namespace {
+
+constexpr int kTok = 16;    // tokens per block (M of the MFMA)
+constexpr int kWaves = 4;   // waves per block, each over a quarter of H
+
+// Ws[p][c][h], p = 0..2, c < N2p (columns: W_g, then W_noise, then zero
+// padding), K-contiguous bf16 bits.
+__global__ __launch_bounds__(256) void k_router_wsplit(const float* __restrict__ Wg, const float* __restrict__ Wn,
+                                                       int H, int N, int noisy, int N2p, uint16_t* __restrict__ Ws) {
+  const int64_t total = static_cast<int64_t>(N2p) * H;
+  for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < total;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int c = static_cast<int>(i / H), h = static_cast<int>(i % H);
+    float w = 0.0f;
+    if (c < N) w = Wg[static_cast<int64_t>(h) * N + c];
+    else if (noisy && c < 2 * N) w = Wn[static_cast<int64_t>(h) * N + (c - N)];
+    const uint16_t w1 = f32_to_bf16(w);
+    const float r1 = w - bf16_to_f32(w1);
+    const uint16_t w2 = f32_to_bf16(r1);
+    const float r2 = r1 - bf16_to_f32(w2);
+    const uint16_t w3 = f32_to_bf16(r2);
+    Ws[i] = w1;
+    Ws[total + i] = w2;
+    Ws[2 * total + i] = w3;
+  }
+}
+
+template <int NB16>
+__global__ __launch_bounds__(kWaves * 64) void k_router_mma(RouterParams p, int N2p) {
+  constexpr int NC = NB16 * 16;
+  __shared__ float s_part[kWaves][kTok][NC];
+  __shared__ float s_log[kTok][NC];       // clean logits, then noise logits
+  __shared__ float s_h[kTok][64];         // selection scores
+  __shared__ float s_p[kTok][64];         // softmax of the clean logits
+  __shared__ int s_idx[kTok][64];
+  __shared__ float s_w[kTok][64];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int N = p.N, H = p.H, k = p.k;
+  const int64_t T = p.T;
+  const int64_t tok0 = static_cast<int64_t>(blockIdx.x) * kTok;
+  const uint16_t* __restrict__ x = static_cast<const uint16_t*>(p.x);
+  const uint16_t* __restrict__ Ws = p.wsplit;
+  const int64_t part = static_cast<int64_t>(N2p) * H;
+
+  // this wave's K range, in steps of 32
+  const int steps = (H + 31) / 32;
+  const int s0 = wave * steps / kWaves, s1 = (wave + 1) * steps / kWaves;
+  const int row = lane & 15, kg = lane >> 4;  // A: token row; B: column; kg selects 8 of the 32 K
+  const int64_t tok = tok0 + row;
+  const bool tok_ok = tok < T;
+  const uint16_t* xrow = x + (tok_ok ? tok : 0) * H;
+
+  f32x4_mma_t acc_hi[NB16], acc_lo[NB16];
+#pragma unroll
+  for (int c = 0; c < NB16; ++c)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc_hi[c][r] = acc_lo[c][r] = 0.0f;
+
+  constexpr int U = NB16 <= 1 ? 4 : (NB16 <= 2 ? 2 : 1);  // K steps whose loads are issued together
+  for (int s = s0; s < s1; s += U) {
+    bf16x8_t a[U], b[U][NB16][3];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int kk = (s + u) * 32 + kg * 8;
+      const bool kin = (s + u) < s1 && kk < H;
+      u32x4_t v = {0u, 0u, 0u, 0u};
+      if (kin && tok_ok) v = *reinterpret_cast<const u32x4_t*>(xrow + kk);
+      a[u] = __builtin_bit_cast(bf16x8_t, v);
+#pragma unroll
+      for (int c = 0; c < NB16; ++c)
+#pragma unroll
+        for (int q = 0; q < 3; ++q) {
+          u32x4_t wv = {0u, 0u, 0u, 0u};
+          if (kin) wv = *reinterpret_cast<const u32x4_t*>(Ws + q * part + static_cast<int64_t>(c * 16 + row) * H + kk);
+          b[u][c][q] = __builtin_bit_cast(bf16x8_t, wv);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int c = 0; c < NB16; ++c) {
+        acc_hi[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], b[u][c][0], acc_hi[c], 0, 0, 0);
+        acc_lo[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], b[u][c][1], acc_lo[c], 0, 0, 0);
+        acc_lo[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], b[u][c][2], acc_lo[c], 0, 0, 0);
+      }
+  }
+  // lane holds column (lane & 15) and token rows 4*(lane/16) + r
+#pragma unroll
+  for (int c = 0; c < NB16; ++c)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s_part[wave][kg * 4 + r][c * 16 + row] = acc_hi[c][r] + acc_lo[c][r];
+  __syncthreads();
+  for (int i = threadIdx.x; i < kTok * NC; i += kWaves * 64) {
+    const int t = i / NC, c = i % NC;
+    float v = s_part[0][t][c];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) v += s_part[w][t][c];
+    s_log[t][c] = v;
+  }
+  __syncthreads();
+
+  // one thread per token: noise, KeepTopK, gates
+  if (threadIdx.x < kTok) {
+    const int t = threadIdx.x;
+    const int64_t g = tok0 + t;
+    if (g < T) {
+      float lmax = -INFINITY;
+      for (int n = 0; n < N; ++n) {
+        const float l = s_log[t][n];
+        float hv = l;
+        // H_i = (x W_g)_i + StandardNormal() * Softplus((x W_noise)_i), the
+        // normal draw being the input eps[t, i]
+        if (p.noisy) hv = fmaf(p.eps[g * N + n], softplus(s_log[t][N + n]), l);
+        s_h[t][n] = hv;
+        if (p.logits) p.logits[g * N + n] = l;
+        lmax = fmaxf(lmax, l);
+      }
+      // KeepTopK: k rounds of argmax, strict comparison keeps the lower index
+      uint64_t taken = 0;
+      for (int j = 0; j < k; ++j) {
+        int bi = -1;
+        float bv = -INFINITY;
+        for (int n = 0; n < N; ++n) {
+          const float v = s_h[t][n];
+          if (!((taken >> n) & 1ull) && (bi < 0 || v > bv)) {
+            bv = v;
+            bi = n;
+          }
+        }
+        taken |= 1ull << bi;
+        s_idx[t][j] = bi;
+        s_w[t][j] = bv;  // score for now
+      }
+      const float hmax = s_w[t][0];
+      float den = 0.0f;
+      if (p.order == 0) {
+        for (int j = 0; j < k; ++j) den += expf(s_w[t][j] - hmax);  // Mixtral: softmax over the kept scores
+      } else {
+        for (int n = 0; n < N; ++n) den += expf(s_h[t][n] - hmax);  // ST: softmax over all scores
+      }
+      for (int j = 0; j < k; ++j) {
+        const float wj = expf(s_w[t][j] - hmax) / den;
+        s_w[t][j] = wj;
+        p.topk_idx[g * k + j] = s_idx[t][j];
+        p.topk_w[g * k + j] = wj;
+      }
+      if (p.stat_part) {
+        float dl = 0.0f;
+        for (int n = 0; n < N; ++n) dl += expf(s_log[t][n] - lmax);
+        for (int n = 0; n < N; ++n) s_p[t][n] = expf(s_log[t][n] - lmax) / dl;
+      }
+    }
+  }
+  __syncthreads();
+
+  // per-block sums over the tokens, in token order
+  if (p.hist && threadIdx.x < N) {
+    const int n = threadIdx.x;
+    int cnt = 0;
+    float imp = 0.0f, ps = 0.0f;
+    for (int t = 0; t < kTok; ++t) {
+      if (tok0 + t >= T) break;
+      for (int j = 0; j < k; ++j)
+        if (s_idx[t][j] == n) {
+          ++cnt;
+          imp += s_w[t][j];
+        }
+      if (p.stat_part) ps += s_p[t][n];
+    }
+    p.hist[static_cast<int64_t>(blockIdx.x) * N + n] = cnt;
+    if (p.stat_part) {
+      p.stat_part[static_cast<int64_t>(blockIdx.x) * 2 * N + 2 * n] = imp;
+      p.stat_part[static_cast<int64_t>(blockIdx.x) * 2 * N + 2 * n + 1] = ps;
+    }
+  }
+}
+
+}  // namespace
+
+int router_mma_columns(int N, int noisy) {
+  const int n2 = N * (noisy ? 2 : 1);
+  return (n2 + 15) / 16 * 16;
+}
+
+size_t router_wsplit_bytes(int H, int N, int noisy) {
+  return static_cast<size_t>(3) * router_mma_columns(N, noisy) * H * sizeof(uint16_t);
+}
+
+hipError_t launch_router_mma(const RouterParams& p, hipStream_t s) {
+  const int N2p = router_mma_columns(p.N, p.noisy);
+  {
+    const int64_t total = static_cast<int64_t>(N2p) * p.H;
+    const int blocks = static_cast<int>(std::min<int64_t>((total + 255) / 256, 2048));
+    hipLaunchKernelGGL(k_router_wsplit, dim3(blocks), dim3(256), 0, s, p.Wg, p.Wn, p.H, p.N, p.noisy, N2p, p.wsplit);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const dim3 grid(static_cast<unsigned>((p.T + kTok - 1) / kTok)), block(kWaves * 64);
+  switch (N2p / 16) {
+    case 1: hipLaunchKernelGGL(k_router_mma<1>, grid, block, 0, s, p, N2p); break;
+    case 2: hipLaunchKernelGGL(k_router_mma<2>, grid, block, 0, s, p, N2p); break;
+    case 3: hipLaunchKernelGGL(k_router_mma<3>, grid, block, 0, s, p, N2p); break;
+    case 4: hipLaunchKernelGGL(k_router_mma<4>, grid, block, 0, s, p, N2p); break;
+    case 5: hipLaunchKernelGGL(k_router_mma<5>, grid, block, 0, s, p, N2p); break;
+    case 6: hipLaunchKernelGGL(k_router_mma<6>, grid, block, 0, s, p, N2p); break;
+    case 7: hipLaunchKernelGGL(k_router_mma<7>, grid, block, 0, s, p, N2p); break;
+    default: hipLaunchKernelGGL(k_router_mma<8>, grid, block, 0, s, p, N2p); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe
