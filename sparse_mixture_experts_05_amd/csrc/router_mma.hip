@@ -9,13 +9,13 @@
 // block each cover a quarter of H, which keeps the accumulated rounding error
 // near that of a plain fp32 dot product.
 //
-// A block owns 16 tokens. After the product, one thread per token applies the
-// noise term, KeepTopK (ties to the lower expert index; "Llama 3 Meets MoE"
-// review, section 3) and the gate of the chosen order (Mixtral: softmax over
-// the kept scores; ST: softmax over all scores, section 5), and threads of
-// the block then sum the per-expert counts, gate weights and softmax(logit)
-// values over the block's tokens in token order for the permutation and the
-// balance statistics.
+// A block owns 16 tokens. After the product, one wave per token applies the
+// noise term, KeepTopK by k rounds of a wave-wide argmax (ties to the lower
+// expert index; "Llama 3 Meets MoE" review, section 3) and the gate of the
+// chosen order (Mixtral: softmax over the kept scores; ST: softmax over all
+// scores, section 5); threads of the block then sum the per-expert counts,
+// gate weights and softmax(logit) values over the block's tokens in token
+// order for the permutation and the balance statistics.
 #include "common.h"
 #include "kernels.h"
 
@@ -28,16 +28,19 @@ namespace moe {
 namespace {
 
 constexpr int kTok = 16;    // tokens per block (M of the MFMA)
-constexpr int kWaves = 4;   // waves per block, each over a quarter of H
+// waves per block, each over 1/W of H: more waves for fewer output columns
+// (shorter dependent load chains per wave), fewer when the partial sums of
+// every wave would not fit in LDS
+template <int NB16>
+constexpr int router_waves() { return NB16 <= 2 ? 16 : (NB16 <= 4 ? 8 : 4); }
 
 // Ws[p][c][h], p = 0..2, c < N2p (columns: W_g, then W_noise, then zero
 // padding), K-contiguous bf16 bits.
 __global__ __launch_bounds__(256) void k_router_wsplit(const float* __restrict__ Wg, const float* __restrict__ Wn,
                                                        int H, int N, int noisy, int N2p, uint16_t* __restrict__ Ws) {
-  const int64_t total = static_cast<int64_t>(N2p) * H;
-  for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < total;
-       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    const int c = static_cast<int>(i / H), h = static_cast<int>(i % H);
+  const int total = N2p * H;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < total; i += gridDim.x * blockDim.x) {
+    const int c = i / H, h = i - c * H;
     float w = 0.0f;
     if (c < N) w = Wg[static_cast<int64_t>(h) * N + c];
     else if (noisy && c < 2 * N) w = Wn[static_cast<int64_t>(h) * N + (c - N)];
@@ -53,14 +56,11 @@ __global__ __launch_bounds__(256) void k_router_wsplit(const float* __restrict__
 }
 
 template <int NB16>
-__global__ __launch_bounds__(kWaves * 64) void k_router_mma(RouterParams p, int N2p) {
+__global__ __launch_bounds__(router_waves<NB16>() * 64) void k_router_mma(RouterParams p, int N2p) {
+  constexpr int kWaves = router_waves<NB16>();
   constexpr int NC = NB16 * 16;
   __shared__ float s_part[kWaves][kTok][NC];
   __shared__ float s_log[kTok][NC];       // clean logits, then noise logits
-  __shared__ float s_h[kTok][64];         // selection scores
-  __shared__ float s_p[kTok][64];         // softmax of the clean logits
-  __shared__ int s_idx[kTok][64];
-  __shared__ float s_w[kTok][64];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int N = p.N, H = p.H, k = p.k;
@@ -69,6 +69,7 @@ __global__ __launch_bounds__(kWaves * 64) void k_router_mma(RouterParams p, int 
   const uint16_t* __restrict__ x = static_cast<const uint16_t*>(p.x);
   const uint16_t* __restrict__ Ws = p.wsplit;
   const int64_t part = static_cast<int64_t>(N2p) * H;
+  const int n2 = N * (p.noisy ? 2 : 1);  // real columns; the padding stays zero without loads
 
   // this wave's K range, in steps of 32
   const int steps = (H + 31) / 32;
@@ -99,7 +100,7 @@ __global__ __launch_bounds__(kWaves * 64) void k_router_mma(RouterParams p, int 
 #pragma unroll
         for (int q = 0; q < 3; ++q) {
           u32x4_t wv = {0u, 0u, 0u, 0u};
-          if (kin) wv = *reinterpret_cast<const u32x4_t*>(Ws + q * part + static_cast<int64_t>(c * 16 + row) * H + kk);
+          if (kin && c * 16 + row < n2) wv = *reinterpret_cast<const u32x4_t*>(Ws + q * part + static_cast<int64_t>(c * 16 + row) * H + kk);
           b[u][c][q] = __builtin_bit_cast(bf16x8_t, wv);
         }
     }
@@ -127,56 +128,62 @@ __global__ __launch_bounds__(kWaves * 64) void k_router_mma(RouterParams p, int 
   }
   __syncthreads();
 
-  // one thread per token: noise, KeepTopK, gates
-  if (threadIdx.x < kTok) {
-    const int t = threadIdx.x;
+  // one wave per token, lane n holding expert n: noise, KeepTopK, gates
+  __shared__ float s_sel[kTok][64];  // gate weight of expert n if kept, else 0
+  __shared__ int s_take[kTok][64];   // 1 if expert n is among the token's top k
+  __shared__ float s_p[kTok][64];    // softmax of the clean logits
+  const bool valid = lane < N;
+  for (int t = wave; t < kTok; t += kWaves) {
     const int64_t g = tok0 + t;
-    if (g < T) {
-      float lmax = -INFINITY;
-      for (int n = 0; n < N; ++n) {
-        const float l = s_log[t][n];
-        float hv = l;
-        // H_i = (x W_g)_i + StandardNormal() * Softplus((x W_noise)_i), the
-        // normal draw being the input eps[t, i]
-        if (p.noisy) hv = fmaf(p.eps[g * N + n], softplus(s_log[t][N + n]), l);
-        s_h[t][n] = hv;
-        if (p.logits) p.logits[g * N + n] = l;
-        lmax = fmaxf(lmax, l);
-      }
-      // KeepTopK: k rounds of argmax, strict comparison keeps the lower index
-      uint64_t taken = 0;
-      for (int j = 0; j < k; ++j) {
-        int bi = -1;
-        float bv = -INFINITY;
-        for (int n = 0; n < N; ++n) {
-          const float v = s_h[t][n];
-          if (!((taken >> n) & 1ull) && (bi < 0 || v > bv)) {
-            bv = v;
-            bi = n;
-          }
+    if (g >= T) break;  // wave-uniform
+    const float lv = valid ? s_log[t][lane] : -INFINITY;
+    float hv = lv;
+    // H_i = (x W_g)_i + StandardNormal() * Softplus((x W_noise)_i), the
+    // normal draw being the input eps[t, i]
+    if (p.noisy && valid) hv = fmaf(p.eps[g * N + lane], softplus(s_log[t][N + lane]), lv);
+    if (p.logits && valid) p.logits[g * N + lane] = lv;
+    // KeepTopK: k rounds of a wave-wide (score desc, index asc) argmax
+    float cur = valid ? hv : -INFINITY;
+    int curi = valid ? lane : 4096 + lane;
+    bool taken = false;
+    float my_v = 0.0f;
+    int my_i = 0;
+    for (int jj = 0; jj < k; ++jj) {
+      float bv = cur;
+      int bi = curi;
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) {
+        const float ov = __shfl_xor(bv, m, 64);
+        const int oi = __shfl_xor(bi, m, 64);
+        if (ov > bv || (ov == bv && oi < bi)) {
+          bv = ov;
+          bi = oi;
         }
-        taken |= 1ull << bi;
-        s_idx[t][j] = bi;
-        s_w[t][j] = bv;  // score for now
       }
-      const float hmax = s_w[t][0];
-      float den = 0.0f;
-      if (p.order == 0) {
-        for (int j = 0; j < k; ++j) den += expf(s_w[t][j] - hmax);  // Mixtral: softmax over the kept scores
-      } else {
-        for (int n = 0; n < N; ++n) den += expf(s_h[t][n] - hmax);  // ST: softmax over all scores
+      if (lane == jj) {
+        my_v = bv;
+        my_i = bi;
       }
-      for (int j = 0; j < k; ++j) {
-        const float wj = expf(s_w[t][j] - hmax) / den;
-        s_w[t][j] = wj;
-        p.topk_idx[g * k + j] = s_idx[t][j];
-        p.topk_w[g * k + j] = wj;
+      if (curi == bi) {
+        taken = true;
+        cur = -INFINITY;
+        curi = 8192 + lane;
       }
-      if (p.stat_part) {
-        float dl = 0.0f;
-        for (int n = 0; n < N; ++n) dl += expf(s_log[t][n] - lmax);
-        for (int n = 0; n < N; ++n) s_p[t][n] = expf(s_log[t][n] - lmax) / dl;
-      }
+    }
+    const float hmax = __shfl(my_v, 0, 64);
+    // Mixtral order: softmax over the kept scores; ST: over all N scores
+    const float den = p.order == 0 ? wave_sum(lane < k ? expf(my_v - hmax) : 0.0f)
+                                   : wave_sum(valid ? expf(hv - hmax) : 0.0f);
+    if (lane < k) {
+      p.topk_idx[g * k + lane] = my_i;
+      p.topk_w[g * k + lane] = expf(my_v - hmax) / den;
+    }
+    s_take[t][lane] = taken ? 1 : 0;
+    s_sel[t][lane] = taken ? expf(hv - hmax) / den : 0.0f;  // the value written for this expert
+    if (p.stat_part) {
+      const float lmax = wave_max(lv);
+      const float el = valid ? expf(lv - lmax) : 0.0f;
+      s_p[t][lane] = el / wave_sum(el);
     }
   }
   __syncthreads();
@@ -188,11 +195,8 @@ __global__ __launch_bounds__(kWaves * 64) void k_router_mma(RouterParams p, int 
     float imp = 0.0f, ps = 0.0f;
     for (int t = 0; t < kTok; ++t) {
       if (tok0 + t >= T) break;
-      for (int j = 0; j < k; ++j)
-        if (s_idx[t][j] == n) {
-          ++cnt;
-          imp += s_w[t][j];
-        }
+      cnt += s_take[t][n];
+      imp += s_sel[t][n];
       if (p.stat_part) ps += s_p[t][n];
     }
     p.hist[static_cast<int64_t>(blockIdx.x) * N + n] = cnt;
@@ -223,17 +227,20 @@ hipError_t launch_router_mma(const RouterParams& p, hipStream_t s) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const dim3 grid(static_cast<unsigned>((p.T + kTok - 1) / kTok)), block(kWaves * 64);
+  const dim3 grid(static_cast<unsigned>((p.T + kTok - 1) / kTok));
+#define MOE_ROUTER_MMA(NB) \
+  hipLaunchKernelGGL(k_router_mma<NB>, grid, dim3(router_waves<NB>() * 64), 0, s, p, N2p)
   switch (N2p / 16) {
-    case 1: hipLaunchKernelGGL(k_router_mma<1>, grid, block, 0, s, p, N2p); break;
-    case 2: hipLaunchKernelGGL(k_router_mma<2>, grid, block, 0, s, p, N2p); break;
-    case 3: hipLaunchKernelGGL(k_router_mma<3>, grid, block, 0, s, p, N2p); break;
-    case 4: hipLaunchKernelGGL(k_router_mma<4>, grid, block, 0, s, p, N2p); break;
-    case 5: hipLaunchKernelGGL(k_router_mma<5>, grid, block, 0, s, p, N2p); break;
-    case 6: hipLaunchKernelGGL(k_router_mma<6>, grid, block, 0, s, p, N2p); break;
-    case 7: hipLaunchKernelGGL(k_router_mma<7>, grid, block, 0, s, p, N2p); break;
-    default: hipLaunchKernelGGL(k_router_mma<8>, grid, block, 0, s, p, N2p); break;
+    case 1: MOE_ROUTER_MMA(1); break;
+    case 2: MOE_ROUTER_MMA(2); break;
+    case 3: MOE_ROUTER_MMA(3); break;
+    case 4: MOE_ROUTER_MMA(4); break;
+    case 5: MOE_ROUTER_MMA(5); break;
+    case 6: MOE_ROUTER_MMA(6); break;
+    case 7: MOE_ROUTER_MMA(7); break;
+    default: MOE_ROUTER_MMA(8); break;
   }
+#undef MOE_ROUTER_MMA
   return hipGetLastError();
 }
 
