@@ -45,6 +45,8 @@ def parse_args():
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one plain 512 MiB device copy first (counter calibration under rocprofv3)")
     ap.add_argument("--no-detail", action="store_true")
+    ap.add_argument("--config", default="C2",
+                    help="workload: C2 (the headline LLaMA-MoE-3.5B 2/8 layer) or one of the other layer shapes")
     return ap.parse_args()
 
 
@@ -64,11 +66,34 @@ def counters_traffic():
         return None
 
 
+WORKLOADS = {
+    "C1": ("tiny fp32 MoE layer: T=256, hidden 256, 688 split into 8 experts of 86, top-2 Mixtral, dropless",
+           lambda synth: synth.c1()),
+    "C2": ("LLaMA-MoE-3.5B (2/8) MoE layer forward: T=4096 tokens, hidden 4096, 11008 split into 8 experts of "
+           "1376, top-2 Mixtral, dropless, s=N/k=4, bf16 experts, fp32 router", lambda synth: synth.c2()),
+    "C3": ("LLaMA-MoE-3.5B (4/16) MoE layer forward: T=4096, hidden 4096, 11008 split into 16 experts of 688, "
+           "top-4 noisy gate with stats, dropless, s=4", lambda synth: synth.c3()),
+    "C4cf4": ("Llama-3-8B upcycled E8T2 layer: T=8192, hidden 4096, 8 experts of 14336, top-2 Mixtral, "
+              "capacity factor 4 (C=4096)", lambda synth: synth.c4("cf4")),
+    "C4cf1": ("Llama-3-8B upcycled E8T2 layer: T=8192, 8 experts of 14336, top-2, capacity factor 1 (C=1024)",
+              lambda synth: synth.c4("cf1")),
+    "C4dropless": ("Llama-3-8B upcycled E8T2 layer: T=8192, 8 experts of 14336, top-2, dropless",
+                   lambda synth: synth.c4("dropless")),
+    "C4cf1_assign": ("Llama-3-8B upcycled E8T2 layer: T=8192, 8 experts of 14336, top-2, capacity factor 1 "
+                     "counted per assignment (C=2048)", lambda synth: synth.c4("cf1_assign")),
+    "C5": ("decode-shaped E8T2 layer: T=64 tokens, hidden 4096, 8 experts of 14336, top-2, half the tokens "
+           "steered to expert 0, dropless", lambda synth: synth.c5()),
+}
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build runs the MoE layer on a single MI355X and has no "
               f"multi-GPU path (asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+    if args.config not in WORKLOADS:
+        print(f"unknown --config {args.config}; one of {', '.join(WORKLOADS)}", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -89,29 +114,45 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    w = synth.c2()
+    headline = args.config == "C2"
+    desc, make = WORKLOADS[args.config]
+    w = make(synth)
     T, H, F, N, k = w.T, w.H, w.F, w.N, w.k
-    cfg = abi.MoEConfig(T=T, H=H, F=F, N=N, k=k, capacity=-1, order=0, out_scale=w.out_scale)
+    cfg = abi.MoEConfig(T=T, H=H, F=F, N=N, k=k, capacity=w.capacity, order=w.order, noisy=w.noisy,
+                        want_stats=w.want_stats, out_scale=w.out_scale, act=w.act, wt=w.wt)
+    bf16 = w.act == "bf16"
 
     def dev(a):
+        if a is None:
+            return None
         if a.dtype == np.uint16:
             return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
         return torch.from_numpy(a).cuda()
 
-    base = dict(x=dev(w.x), Wg=dev(w.Wg), Wgate=dev(w.Wgate), Wup=dev(w.Wup), Wdown=dev(w.Wdown))
-    copies = [base] + [{k_: v.clone() for k_, v in base.items()} for _ in range(max(0, args.copies - 1))]
+    base = dict(x=dev(w.x), Wg=dev(w.Wg), Wn=dev(w.Wn), eps=dev(w.eps), Wgate=dev(w.Wgate), Wup=dev(w.Wup),
+                Wdown=dev(w.Wdown))
+    copies = [base] + [{k_: (v.clone() if v is not None else None) for k_, v in base.items()}
+                       for _ in range(max(0, args.copies - 1))]
     y = torch.empty(T, H, dtype=torch.float32, device="cuda")
+    kept = torch.zeros(N, dtype=torch.int32, device="cuda")
+    stats = dict(load=torch.empty(N, dtype=torch.int32, device="cuda"),
+                 importance=torch.empty(N, dtype=torch.float32, device="cuda"),
+                 P=torch.empty(N, dtype=torch.float32, device="cuda"),
+                 balance=torch.empty(1, dtype=torch.float32, device="cuda")) if w.want_stats else {}
     ws = abi.workspace(cfg)
     stream = torch.cuda.current_stream()
 
-    def step(i):
-        d = copies[i % len(copies)]
-        abi.moe_forward(cfg, d["x"], d["Wg"], None, None, d["Wgate"], d["Wup"], d["Wdown"], y, ws=ws,
-                        stream=stream)
+    def step(i, d=None):
+        d = d if d is not None else copies[i % len(copies)]
+        abi.moe_forward(cfg, d["x"], d["Wg"], d["Wn"], d["eps"], d["Wgate"], d["Wup"], d["Wdown"], y, kept=kept,
+                        ws=ws, stream=stream, **stats)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+    kept_h = kept.cpu().numpy().astype(np.int64)
+    A = int(kept_h.sum())                    # kept (token, expert) rows
+    active = int((kept_h > 0).sum())          # experts with at least one row
 
     # timed region; GEMM1 bracketed by HIP events on the launch stream
     abi.moe_profile_select(abi.MOE_KERNEL_GEMM1)
@@ -127,47 +168,68 @@ def main():
 
     ms_per_step = elapsed * 1e3 / args.steps
     tokens_per_s = T * args.steps / elapsed
-
-    A = T * k
-    gemm1_flops = 4.0 * A * H * F            # gate and up projections of the kept rows
-    gemm1_avg_s = g1_ms / 1e3 / max(1, g1_n)
-    achieved = gemm1_flops / gemm1_avg_s / 1e12
-    traffic = counters_traffic()
-
-    # layer roofline (algorithmic work of the kept assignments)
-    f_bf16 = 6.0 * A * H * F
-    f_fp32 = 2.0 * T * H * N
-    b_alg = T * H * 2 + H * N * 4 + N * 3 * F * H * 2 + T * k * 8 + T * H * 4
-    t_roof = max(f_bf16 / (PEAK_BF16_TFLOPS * 1e12) + f_fp32 / (PEAK_FP32_TFLOPS * 1e12), b_alg / (PEAK_HBM_GBS * 1e9))
     t_layer = elapsed / args.steps
+    gemm1_avg_s = g1_ms / 1e3 / max(1, g1_n)
+
+    # layer roofline over the kept assignments: expert flops on the matrix
+    # cores plus the fp32 router, or the bytes of reading x, the router
+    # weights, the active experts' weights once, the routing outputs, and
+    # writing fp32 y once, whichever takes longer
+    eb = 2 if bf16 else 4
+    f_expert = 6.0 * A * H * F
+    f_router = 2.0 * T * H * N * (2 if w.noisy else 1)
+    b_alg = (T * H * eb + H * N * 4 * (2 if w.noisy else 1) + (T * N * 4 if w.noisy else 0)
+             + active * 3 * F * H * eb + T * k * 8 + T * H * 4)
+    peak_expert = PEAK_BF16_TFLOPS if bf16 else PEAK_FP32_TFLOPS
+    t_compute = f_expert / (peak_expert * 1e12) + f_router / (PEAK_FP32_TFLOPS * 1e12)
+    t_mem = b_alg / (PEAK_HBM_GBS * 1e9)
+    t_roof = max(t_compute, t_mem)
+
+    # dominant kernel: the gate/up GEMM with the SwiGLU epilogue
+    gemm1_flops = 4.0 * A * H * F
+    gemm1_bytes = active * 2 * F * H * eb + A * H * eb + A * F * eb
+    if t_mem > t_compute:
+        achieved = gemm1_bytes / gemm1_avg_s / 1e9
+        roof = {"bound": "hbm", "kernel": "gemm1_gate_up_swiglu", "achieved": round(achieved, 1),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                "traffic": None, "bytes_per_launch": gemm1_bytes}
+    else:
+        achieved = gemm1_flops / gemm1_avg_s / 1e12
+        roof = {"bound": "mfma" if bf16 else "alu", "kernel": "gemm1_gate_up_swiglu", "achieved": round(achieved, 1),
+                "peak": peak_expert, "unit": "TFLOP/s", "frac": round(achieved / peak_expert, 4),
+                "traffic": counters_traffic() if headline else None, "flops_per_launch": gemm1_flops}
+    roof.update(launches_timed=g1_n, avg_launch_us=round(gemm1_avg_s * 1e6, 2))
 
     detail = None
     if not args.no_detail:
         per_kernel = {}
-        names = {abi.MOE_KERNEL_ROUTER: "router_topk", abi.MOE_KERNEL_SCATTER: "permute_scatter",
-                 abi.MOE_KERNEL_GEMM1: "gemm1_gate_up_swiglu", abi.MOE_KERNEL_GEMM2: "gemm2_down",
-                 abi.MOE_KERNEL_COMBINE: "combine"}
+        names = {abi.MOE_KERNEL_ROUTER: "router_topk", abi.MOE_KERNEL_STATS: "router_stats",
+                 abi.MOE_KERNEL_SCATTER: "permute_scatter", abi.MOE_KERNEL_GEMM1: "gemm1_gate_up_swiglu",
+                 abi.MOE_KERNEL_GEMM2: "gemm2_down", abi.MOE_KERNEL_COMBINE: "combine"}
         for kid, name in names.items():
             abi.moe_profile_select(kid)
             for i in range(10):
                 step(i)
             torch.cuda.synchronize()
             ms, n = abi.moe_profile_read()
-            per_kernel[name] = round(ms * 1e3 / max(1, n), 2)
+            if n:
+                per_kernel[name] = round(ms * 1e3 / n, 2)
         abi.moe_profile_select(-1)
         # same data every step: weights can stay in the last-level cache
-        d0 = copies[0]
         torch.cuda.synchronize()
         t1 = time.perf_counter()
-        for _ in range(args.steps):
-            abi.moe_forward(cfg, d0["x"], d0["Wg"], None, None, d0["Wgate"], d0["Wup"], d0["Wdown"], y, ws=ws,
-                            stream=stream)
+        for i in range(args.steps):
+            step(i, copies[0])
         torch.cuda.synchronize()
         warm_ms = (time.perf_counter() - t1) * 1e3 / args.steps
-        detail = dict(device=dev_name, kernel_avg_us=per_kernel, layer_us=round(t_layer * 1e6, 2),
-                      layer_tflops=round((f_bf16 + f_fp32) / t_layer / 1e12, 1),
-                      layer_roofline_us=round(t_roof * 1e6, 2), layer_frac_of_roofline=round(t_roof / t_layer, 4),
-                      gemm2_tflops=round(2.0 * A * F * H / (per_kernel["gemm2_down"] * 1e-6) / 1e12, 1),
+        g2 = per_kernel.get("gemm2_down")
+        detail = dict(device=dev_name, kept_rows=A, active_experts=active, kept_per_expert=kept_h.tolist(),
+                      kernel_avg_us=per_kernel, layer_us=round(t_layer * 1e6, 2),
+                      layer_tflops=round((f_expert + f_router) / t_layer / 1e12, 1),
+                      layer_hbm_gbs=round(b_alg / t_layer / 1e9, 1),
+                      layer_roofline_us=round(t_roof * 1e6, 2), layer_bound="hbm" if t_mem > t_compute else "compute",
+                      layer_frac_of_roofline=round(t_roof / t_layer, 4),
+                      gemm2_tflops=round(2.0 * A * F * H / (g2 * 1e-6) / 1e12, 1) if g2 else None,
                       same_inputs_every_step_ms=round(warm_ms, 4), input_copies=len(copies))
 
     cpu = None
@@ -177,16 +239,11 @@ def main():
     out = {
         "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if bf16 else "f32",
         "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights; no checkpoint)",
-        "config": {"workload": "LLaMA-MoE-3.5B (2/8) MoE layer forward: T=4096 tokens, hidden 4096, "
-                               "11008 split into 8 experts of 1376, top-2 Mixtral, dropless, s=N/k=4, "
-                               "bf16 experts, fp32 router",
-                   "T": T, "H": H, "F": F, "N": N, "k": k, "out_scale": w.out_scale},
-        "roofline": {"bound": "mfma", "kernel": "gemm1_gate_up_swiglu", "achieved": round(achieved, 1),
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic, "launches_timed": g1_n,
-                     "avg_launch_us": round(gemm1_avg_s * 1e6, 2), "flops_per_launch": gemm1_flops},
+        "config": {"workload": desc, "T": T, "H": H, "F": F, "N": N, "k": k, "capacity": w.capacity,
+                   "out_scale": w.out_scale},
+        "roofline": roof,
         "cpu_baseline": cpu,
     }
     if detail is not None:
@@ -209,7 +266,8 @@ def cpu_baseline(w, target_s: float):
 
     def sample(S):
         return synth.Workload(w.name, S, w.H, w.F, w.N, w.k, w.capacity, w.order, w.noisy, False, w.out_scale,
-                              w.act, w.wt, w.x[:S].copy(), w.Wg, None, None, w.Wgate, w.Wup, w.Wdown)
+                              w.act, w.wt, w.x[:S].copy(), w.Wg, w.Wn, None if w.eps is None else w.eps[:S].copy(),
+                              w.Wgate, w.Wup, w.Wdown)
 
     S0 = max(cores, 16)
     t0 = time.perf_counter()

@@ -15,10 +15,10 @@
 //           fixed order.
 //
 // Both operands are K-contiguous ("TN"): a 16-byte LDS read gives a lane its
-// 8 bf16 MFMA operand elements. LDS rows are 128 bytes (BK bf16); the 16-byte
-// chunk c of row r is stored at chunk c ^ (r & 7), which keeps both the
-// row-wise global->LDS writes and the column-wise MFMA operand reads free of
-// bank conflicts.
+// 8 bf16 MFMA operand elements. An LDS row holds BK bf16 (128 bytes for
+// BK = 64, 64 bytes for BK = 32) and its 16-byte chunks are XOR-swizzled by
+// row (see swz), which keeps both the row-wise global->LDS writes and the
+// column-wise MFMA operand reads free of bank conflicts.
 //
 // Two load paths share the tile order and the epilogue:
 //   k_gemm_dma : buffer loads straight into LDS (no register staging), STAGES
@@ -33,11 +33,29 @@ namespace moe {
 
 namespace {
 
-constexpr int BK = 64;
+constexpr int kBKReg = 64;                   // K step of the register-staged kernel
 constexpr uint32_t kOOB = 0xFFFFFFF0u;       // byte offset past any buffer: loads return zero
 constexpr int kBufferFlags = 0x00020000;     // raw buffer, 32-bit data
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * BK + ((chunk ^ (row & 7)) << 3); }
+// Element offset of 16-byte chunk `chunk` of LDS row `row`. The LDS serves a
+// 16-byte read (ds_read_b128) for 16 lanes at a time over 64 four-byte banks
+// (256 bytes), and the MFMA operand reads have 16 consecutive lanes read 16
+// consecutive rows at one logical chunk, so those 16 rows must land in 16
+// different 16-byte bank slots.
+//   BK = 64 (128-byte rows): slot = 8*(r & 1) + position; the position is
+//     c ^ ((r >> 1) & 7), distinct over the 8 rows of each parity.
+//   BK = 32 (64-byte rows):  slot = 4*(r & 3) + position; the position is
+//     c ^ ((r >> 2) & 3), distinct over the 4 rows of each r & 3.
+template <int BK>
+__device__ __forceinline__ int swz_key(int row) {
+  static_assert(BK == 64 || BK == 32, "K step");
+  if constexpr (BK == 64) return (row >> 1) & 7;
+  else return (row >> 2) & 3;
+}
+template <int BK>
+__device__ __forceinline__ int swz(int row, int chunk) {
+  return row * BK + ((chunk ^ swz_key<BK>(row)) << 3);
+}
 
 // Linear tile order: XCD-aware remap of blockIdx.x (workgroups are dealt to
 // the 8 XCDs round-robin, so XCD x runs blocks x, x+8, ...; the remap gives each
@@ -57,7 +75,7 @@ struct TilePos {
 
 // Decode this workgroup's tile; false when it has none (uniform over the
 // workgroup).
-template <int BM, int NO>
+template <int BM, int NO, int BK>
 __device__ __forceinline__ bool decode_tile(const GemmParams& p, TilePos& tp) {
   constexpr int GM = BM >= 256 ? 4 : 8;  // m-tiles per group
   const int lane = threadIdx.x & 63;
@@ -122,7 +140,7 @@ __device__ __forceinline__ void frag_rows(int wm, int wn, int lane, int (&arow)[
 }
 
 // One BK step of MFMAs from an LDS stage.
-template <int MB, int NB>
+template <int MB, int NB, int BK>
 __device__ __forceinline__ void mma_stage(const uint16_t* __restrict__ a, const uint16_t* __restrict__ b,
                                           const int (&arow)[MB], const int (&brow)[NB], int khalf,
                                           f32x16_t (&acc)[MB][NB]) {
@@ -131,9 +149,9 @@ __device__ __forceinline__ void mma_stage(const uint16_t* __restrict__ a, const 
     const int chunk = ks * 2 + khalf;
     bf16x8_t af[MB], bfr[NB];
 #pragma unroll
-    for (int i = 0; i < MB; ++i) af[i] = *reinterpret_cast<const bf16x8_t*>(&a[swz(arow[i], chunk)]);
+    for (int i = 0; i < MB; ++i) af[i] = *reinterpret_cast<const bf16x8_t*>(&a[swz<BK>(arow[i], chunk)]);
 #pragma unroll
-    for (int j = 0; j < NB; ++j) bfr[j] = *reinterpret_cast<const bf16x8_t*>(&b[swz(brow[j], chunk)]);
+    for (int j = 0; j < NB; ++j) bfr[j] = *reinterpret_cast<const bf16x8_t*>(&b[swz<BK>(brow[j], chunk)]);
 #pragma unroll
     for (int i = 0; i < MB; ++i)
 #pragma unroll
@@ -235,26 +253,28 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 // two stages are disjoint, so it does not hold the current stage's LDS reads
 // until the just-issued loads land (the explicit waits and barrier at the top
 // of each step order the stages).
-template <int MB, int NB, class Issue>
+template <int MB, int NB, int BK, class Issue>
 __device__ __forceinline__ void dma_step(Issue& issue, bool do_issue, int kt_next, const uint16_t* __restrict__ a_cur,
                                          const uint16_t* __restrict__ b_cur, uint16_t* __restrict__ a_nxt,
                                          uint16_t* __restrict__ b_nxt, const int (&arow)[MB], const int (&brow)[NB],
                                          int khalf, f32x16_t (&acc)[MB][NB]) {
   if (do_issue) issue(a_nxt, b_nxt, kt_next);
-  mma_stage<MB, NB>(a_cur, b_cur, arow, brow, khalf, acc);
+  mma_stage<MB, NB, BK>(a_cur, b_cur, arow, brow, khalf, acc);
 }
 
-template <int BM, int BN, int WGM, int WGN, int STAGES, bool SWIGLU, bool GATHER>
+template <int BM, int BN, int WGM, int WGN, int STAGES, int BK, bool SWIGLU, bool GATHER>
 __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm_dma(GemmParams p) {
   constexpr int NW = WGM * WGN;
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int MB = WM / 32, NB = WN / 32;
-  constexpr int IA = BM / 8 / NW, IB = BN / 8 / NW;  // 1-KB LDS segments a wave fills per stage
+  constexpr int CPR = BK / 8;                          // 16-byte chunks per LDS row
+  constexpr int RPS = 64 / CPR;                        // rows per 1-KB segment (one load per wave)
+  constexpr int IA = BM / RPS / NW, IB = BN / RPS / NW;  // segments a wave fills per stage
   constexpr int LPS = IA + IB;
   constexpr int NO = SWIGLU ? BN / 2 : BN;
   static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be a multiple of 32");
   static_assert(!SWIGLU || NB % 2 == 0, "swiglu needs gate/up block pairs");
-  static_assert(IA * NW * 8 == BM && IB * NW * 8 == BN, "segments must divide among waves");
+  static_assert(IA * NW * RPS == BM && IB * NW * RPS == BN, "segments must divide among waves");
   static_assert(STAGES >= 2 && STAGES <= 5 && (STAGES - 2) * LPS <= 63, "stage count");
 
   // one LDS object for every stage of A and B: with a single object the
@@ -266,15 +286,20 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm_dma(GemmParams p) {
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / WGN, wn = wave % WGN;
   TilePos tp;
-  if (!decode_tile<BM, NO>(p, tp)) return;
+  if (!decode_tile<BM, NO, BK>(p, tp)) return;
 
-  // lane q of a 1-KB segment s holds row 8s + q/8 and logical chunk (q%8) ^ (q/8)
-  const int lrow = lane >> 3;
-  const int lchunk = (lane & 7) ^ lrow;
+  // lane q of 1-KB segment s holds row RPS*s + q/CPR at physical chunk q%CPR,
+  // which stores logical chunk (q%CPR) ^ key(row) (the swizzle is an XOR, so
+  // the same map in both directions). The key reads row bits 1..3, and every
+  // segment this wave fills starts at a row congruent to wave*RPS modulo 16,
+  // so one chunk per lane serves all of its loads.
+  static_assert((NW * RPS) % 16 == 0 && (BN / 2) % 16 == 0, "segment rows must keep the swizzle key");
+  const int lrow = lane / CPR;
+  const int lchunk = (lane % CPR) ^ swz_key<BK>(wave * RPS + lrow);
   uint32_t aoff[IA];
 #pragma unroll
   for (int i = 0; i < IA; ++i) {
-    const int r = (i * NW + wave) * 8 + lrow;
+    const int r = (i * NW + wave) * RPS + lrow;
     const bool v = r < tp.ti.rows;
     int src = tp.ti.row0 + r;
     if (GATHER) src = v ? p.row_token[src] : 0;
@@ -288,7 +313,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm_dma(GemmParams p) {
   uint32_t boff[IB];
 #pragma unroll
   for (int i = 0; i < IB; ++i) {
-    const int r = ((i % IBH) * NW + wave) * 8 + lrow;  // row within the gate (or plain) block
+    const int r = ((i % IBH) * NW + wave) * RPS + lrow;  // row within the gate (or plain) block
     const int f = tp.nt * NO + r;
     boff[i] = f < p.Nout ? static_cast<uint32_t>(f) * static_cast<uint32_t>(p.ldb) * 2u + lchunk * 16u : kOOB;
   }
@@ -312,7 +337,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm_dma(GemmParams p) {
 #pragma unroll
     for (int i = 0; i < IB; ++i) {
       const uint32_t vo = (kval && boff[i] != kOOB) ? boff[i] + kbyte : kOOB;
-      const int seg = (i % IBH) * NW + wave + (i >= IBH ? (BN / 16) : 0);
+      const int seg = (i % IBH) * NW + wave + (i >= IBH ? (BN / 2 / RPS) : 0);
       if (i < IBH)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rb0, (lds_ptr_t)(b_dst + seg * 512), 16, vo, 0, 0, 0);
       else
@@ -334,7 +359,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm_dma(GemmParams p) {
     wait_stage<LPS, STAGES - 2>(later);
     lds_barrier();  // stage kt is complete for every wave; stage kt-1 is free
     const int st = kt % STAGES, nx = (kt + STAGES - 1) % STAGES;
-    dma_step<MB, NB>(issue, kt + STAGES - 1 < tp.KT, kt + STAGES - 1, sA(st), sB(st), sA(nx), sB(nx), arow, brow,
+    dma_step<MB, NB, BK>(issue, kt + STAGES - 1 < tp.KT, kt + STAGES - 1, sA(st), sB(st), sA(nx), sB(nx), arow, brow,
                      khalf, acc);
   }
   epilogue<WM, WN, MB, NB, SWIGLU>(p, tp, wm, wn, lane, NO, acc);
@@ -353,13 +378,13 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm_reg(GemmParams p) {
   static_assert(!SWIGLU || NB % 2 == 0, "swiglu needs gate/up block pairs");
   static_assert(CA >= 1 && CB >= 1 && (BM * 8) % NT == 0 && (BN * 8) % NT == 0, "load split");
 
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * BK];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[2][BN * BK];
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * kBKReg];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[2][BN * kBKReg];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WGN, wn = wave % WGN;
   TilePos tp;
-  if (!decode_tile<BM, NO>(p, tp)) return;
+  if (!decode_tile<BM, NO, kBKReg>(p, tp)) return;
 
   const uint16_t* __restrict__ Ab = static_cast<const uint16_t*>(p.A);
   int aoff[CA], achunk[CA];
@@ -392,7 +417,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm_reg(GemmParams p) {
 
   u32x4_t ra[CA], rb[CB];
   auto gload = [&](int kt) {
-    const int kb = tp.kb0 + kt * BK;
+    const int kb = tp.kb0 + kt * kBKReg;
 #pragma unroll
     for (int i = 0; i < CA; ++i) {
       const int kk = kb + achunk[i] * 8;
@@ -410,10 +435,10 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm_reg(GemmParams p) {
   auto lstore = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < CA; ++i)
-      *reinterpret_cast<u32x4_t*>(&sA[buf][swz((tid + i * NT) >> 3, achunk[i])]) = ra[i];
+      *reinterpret_cast<u32x4_t*>(&sA[buf][swz<kBKReg>((tid + i * NT) >> 3, achunk[i])]) = ra[i];
 #pragma unroll
     for (int i = 0; i < CB; ++i)
-      *reinterpret_cast<u32x4_t*>(&sB[buf][swz((tid + i * NT) >> 3, bchunk[i])]) = rb[i];
+      *reinterpret_cast<u32x4_t*>(&sB[buf][swz<kBKReg>((tid + i * NT) >> 3, bchunk[i])]) = rb[i];
   };
 
   f32x16_t acc[MB][NB];
@@ -430,7 +455,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm_reg(GemmParams p) {
   for (int kt = 0; kt < tp.KT; ++kt) {
     const int cur = kt & 1;
     if (kt + 1 < tp.KT) gload(kt + 1);
-    mma_stage<MB, NB>(sA[cur], sB[cur], arow, brow, khalf, acc);
+    mma_stage<MB, NB, kBKReg>(sA[cur], sB[cur], arow, brow, khalf, acc);
     if (kt + 1 < tp.KT) lstore(cur ^ 1);
     __syncthreads();
   }
@@ -459,17 +484,17 @@ hipError_t launch_reg(const GemmParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int BM, int BN, int WGM, int WGN, int STAGES>
+template <int BM, int BN, int WGM, int WGN, int STAGES, int BK>
 hipError_t launch_dma(const GemmParams& p, hipStream_t s) {
   const int64_t blocks = grid_blocks(p, BM, BN);
   if (blocks <= 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>(blocks)), block(WGM * WGN * 64);
   if (p.swiglu) {
-    if (p.row_token) hipLaunchKernelGGL((k_gemm_dma<BM, BN, WGM, WGN, STAGES, true, true>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((k_gemm_dma<BM, BN, WGM, WGN, STAGES, true, false>), grid, block, 0, s, p);
+    if (p.row_token) hipLaunchKernelGGL((k_gemm_dma<BM, BN, WGM, WGN, STAGES, BK, true, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((k_gemm_dma<BM, BN, WGM, WGN, STAGES, BK, true, false>), grid, block, 0, s, p);
   } else {
-    if (p.row_token) hipLaunchKernelGGL((k_gemm_dma<BM, BN, WGM, WGN, STAGES, false, true>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((k_gemm_dma<BM, BN, WGM, WGN, STAGES, false, false>), grid, block, 0, s, p);
+    if (p.row_token) hipLaunchKernelGGL((k_gemm_dma<BM, BN, WGM, WGN, STAGES, BK, false, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((k_gemm_dma<BM, BN, WGM, WGN, STAGES, BK, false, false>), grid, block, 0, s, p);
   }
   return hipGetLastError();
 }
@@ -495,7 +520,7 @@ hipError_t launch_gemm_bf16_mfma(const GemmParams& p, hipStream_t s) {
   int bm, bn;
   gemm_bf16_mfma_tile(p.rows_max, p.N, &bm, &bn);
   if (bm == 32) return launch_reg<32, 256, 1, 4>(p, s);
-  return launch_dma<256, 256, 4, 2, 2>(p, s);
+  return launch_dma<256, 256, 4, 2, 2, 64>(p, s);
 }
 
 }  // namespace moe
