@@ -154,8 +154,17 @@ def main():
     A = int(kept_h.sum())                    # kept (token, expert) rows
     active = int((kept_h > 0).sum())          # experts with at least one row
 
-    # timed region; GEMM1 bracketed by HIP events on the launch stream
-    abi.moe_profile_select(abi.MOE_KERNEL_GEMM1)
+    # the dominant kernel: both expert GEMMs in one persistent launch where the
+    # library fuses them, else the gate/up GEMM with the SwiGLU epilogue
+    abi.moe_profile_select(abi.MOE_KERNEL_EXPERTS)
+    abi.moe_profile_read()
+    step(0)
+    torch.cuda.synchronize()
+    fused = abi.moe_profile_read()[1] > 0
+    dom_id = abi.MOE_KERNEL_EXPERTS if fused else abi.MOE_KERNEL_GEMM1
+
+    # timed region; the dominant kernel bracketed by HIP events on the launch stream
+    abi.moe_profile_select(dom_id)
     abi.moe_profile_read()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -164,12 +173,12 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     abi.moe_profile_select(-1)
-    g1_ms, g1_n = abi.moe_profile_read()
+    dom_ms, dom_n = abi.moe_profile_read()
 
     ms_per_step = elapsed * 1e3 / args.steps
     tokens_per_s = T * args.steps / elapsed
     t_layer = elapsed / args.steps
-    gemm1_avg_s = g1_ms / 1e3 / max(1, g1_n)
+    dom_avg_s = dom_ms / 1e3 / max(1, dom_n)
 
     # layer roofline over the kept assignments: expert flops on the matrix
     # cores plus the fp32 router, or the bytes of reading x, the router
@@ -185,27 +194,36 @@ def main():
     t_mem = b_alg / (PEAK_HBM_GBS * 1e9)
     t_roof = max(t_compute, t_mem)
 
-    # dominant kernel: the gate/up GEMM with the SwiGLU epilogue
-    gemm1_flops = 4.0 * A * H * F
-    gemm1_bytes = active * 2 * F * H * eb + A * H * eb + A * F * eb
-    if t_mem > t_compute:
-        achieved = gemm1_bytes / gemm1_avg_s / 1e9
-        roof = {"bound": "hbm", "kernel": "gemm1_gate_up_swiglu", "achieved": round(achieved, 1),
-                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                "traffic": None, "bytes_per_launch": gemm1_bytes}
+    # dominant kernel's algorithmic work per launch: the fused launch does
+    # 6*A*H*F flops and reads the active experts' three matrices; the gate/up
+    # GEMM alone does 4*A*H*F and reads two of them
+    if fused:
+        dom_name = "experts_gate_up_swiglu_down"
+        dom_flops = 6.0 * A * H * F
+        dom_bytes = active * 3 * F * H * eb + A * H * eb + A * H * 4
     else:
-        achieved = gemm1_flops / gemm1_avg_s / 1e12
-        roof = {"bound": "mfma" if bf16 else "alu", "kernel": "gemm1_gate_up_swiglu", "achieved": round(achieved, 1),
+        dom_name = "gemm1_gate_up_swiglu"
+        dom_flops = 4.0 * A * H * F
+        dom_bytes = active * 2 * F * H * eb + A * H * eb + A * F * eb
+    if t_mem > t_compute:
+        achieved = dom_bytes / dom_avg_s / 1e9
+        roof = {"bound": "hbm", "kernel": dom_name, "achieved": round(achieved, 1),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                "traffic": None, "bytes_per_launch": dom_bytes}
+    else:
+        achieved = dom_flops / dom_avg_s / 1e12
+        roof = {"bound": "mfma" if bf16 else "alu", "kernel": dom_name, "achieved": round(achieved, 1),
                 "peak": peak_expert, "unit": "TFLOP/s", "frac": round(achieved / peak_expert, 4),
-                "traffic": counters_traffic() if headline else None, "flops_per_launch": gemm1_flops}
-    roof.update(launches_timed=g1_n, avg_launch_us=round(gemm1_avg_s * 1e6, 2))
+                "traffic": counters_traffic() if headline else None, "flops_per_launch": dom_flops}
+    roof.update(launches_timed=dom_n, avg_launch_us=round(dom_avg_s * 1e6, 2))
 
     detail = None
     if not args.no_detail:
         per_kernel = {}
         names = {abi.MOE_KERNEL_ROUTER: "router_topk", abi.MOE_KERNEL_STATS: "router_stats",
                  abi.MOE_KERNEL_SCATTER: "permute_scatter", abi.MOE_KERNEL_GEMM1: "gemm1_gate_up_swiglu",
-                 abi.MOE_KERNEL_GEMM2: "gemm2_down", abi.MOE_KERNEL_COMBINE: "combine"}
+                 abi.MOE_KERNEL_GEMM2: "gemm2_down", abi.MOE_KERNEL_EXPERTS: "experts_fused",
+                 abi.MOE_KERNEL_COMBINE: "combine"}
         for kid, name in names.items():
             abi.moe_profile_select(kid)
             for i in range(10):

@@ -181,7 +181,8 @@ enum {
   MOE_KERNEL_GEMM2 = 5,
   MOE_KERNEL_COMBINE = 6,
   MOE_KERNEL_STATS = 7,
-  MOE_KERNEL_COUNT = 8
+  MOE_KERNEL_EXPERTS = 8,  /* both expert GEMMs in one persistent launch (bf16, prefill shapes) */
+  MOE_KERNEL_COUNT = 9
 };
 moe_status moe_profile_select(int32_t kernel_id);
 moe_status moe_profile_read(double* total_ms, int64_t* launches);

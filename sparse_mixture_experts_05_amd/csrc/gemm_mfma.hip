@@ -262,8 +262,15 @@ __device__ __forceinline__ void dma_step(Issue& issue, bool do_issue, int kt_nex
   mma_stage<MB, NB, BK>(a_cur, b_cur, arow, brow, khalf, acc);
 }
 
+// LDS elements of one workgroup's operand stages.
+template <int BM, int BN, int STAGES, int BK>
+constexpr int dma_lds_elems() { return STAGES * (BM + BN) * BK; }
+
+// One output tile with buffer loads straight into LDS: the operand stages
+// live in `smem` (dma_lds_elems elements, one LDS object). The caller makes
+// sure no wave still reads `smem` from an earlier tile.
 template <int BM, int BN, int WGM, int WGN, int STAGES, int BK, bool SWIGLU, bool GATHER>
-__global__ __launch_bounds__(WGM * WGN * 64) void k_gemm_dma(GemmParams p) {
+__device__ __forceinline__ void gemm_tile(const GemmParams& p, const TilePos& tp, uint16_t* smem) {
   constexpr int NW = WGM * WGN;
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int MB = WM / 32, NB = WN / 32;
@@ -277,16 +284,11 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm_dma(GemmParams p) {
   static_assert(IA * NW * RPS == BM && IB * NW * RPS == BN, "segments must divide among waves");
   static_assert(STAGES >= 2 && STAGES <= 5 && (STAGES - 2) * LPS <= 63, "stage count");
 
-  // one LDS object for every stage of A and B: with a single object the
-  // compiler's alias scopes can tell the stages apart
-  __shared__ __attribute__((aligned(16))) uint16_t smem[STAGES * (BM + BN) * BK];
   auto sA = [&](int st) { return smem + st * (BM + BN) * BK; };
   auto sB = [&](int st) { return smem + st * (BM + BN) * BK + BM * BK; };
 
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / WGN, wn = wave % WGN;
-  TilePos tp;
-  if (!decode_tile<BM, NO, BK>(p, tp)) return;
 
   // lane q of 1-KB segment s holds row RPS*s + q/CPR at physical chunk q%CPR,
   // which stores logical chunk (q%CPR) ^ key(row) (the swizzle is an XOR, so
@@ -363,6 +365,140 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm_dma(GemmParams p) {
                      khalf, acc);
   }
   epilogue<WM, WN, MB, NB, SWIGLU>(p, tp, wm, wn, lane, NO, acc);
+}
+
+template <int BM, int BN, int WGM, int WGN, int STAGES, int BK, bool SWIGLU, bool GATHER>
+__global__ __launch_bounds__(WGM * WGN * 64) void k_gemm_dma(GemmParams p) {
+  // one LDS object for every stage of A and B: with a single object the
+  // compiler's alias scopes can tell the stages apart
+  __shared__ __attribute__((aligned(16))) uint16_t smem[dma_lds_elems<BM, BN, STAGES, BK>()];
+  constexpr int NO = SWIGLU ? BN / 2 : BN;
+  TilePos tp;
+  if (!decode_tile<BM, NO, BK>(p, tp)) return;
+  gemm_tile<BM, BN, WGM, WGN, STAGES, BK, SWIGLU, GATHER>(p, tp, smem);
+}
+
+// ---- both expert GEMMs in one persistent launch ---------------------------------
+//
+// A row block is BM consecutive permuted rows of one expert. The gate/up
+// GEMM of a row block is NT1 tiles (one per 128-column slice of h); its down
+// projection is NT2 tiles, and those read every column of the row block's h,
+// so they may start only once all NT1 gate/up tiles of that row block are
+// done. Workgroups stay resident and take work items from one queue in
+// ticket order: first every gate/up tile (grouped GM row blocks at a time, as
+// in the separate launch), then the down tiles in row-block order, so the
+// down tiles of the first row blocks fill the compute units that the last
+// round of gate/up tiles leaves idle. The first tickets are remapped as the
+// separate launch remaps blockIdx: workgroups start in dispatch order, dealt
+// round-robin to the 8 XCDs, so the first round's tiles that share weight
+// panels land on one XCD and its L2. A down tile waits, with a bounded spin,
+// on its row block's count of finished gate/up tiles; all gate/up tickets
+// come before any down ticket, so every tile it waits on is already held by
+// a running workgroup that waits on nothing, and the wait always ends.
+
+constexpr int kSchedTicket = 0;     // sched[kSchedTicket]: next ticket
+constexpr int kSchedError = 8;      // sched[kSchedError] = 1 if a wait gave up
+constexpr int kSchedDone = 16;      // sched[kSchedDone + rb]: finished gate/up tiles of row block rb
+constexpr int kFusedBM = 256, kFusedBN = 256;
+
+// Row block rb's expert and rows (lane e holds expert e's segment and its
+// inclusive prefix count of row blocks).
+template <int BM>
+__device__ __forceinline__ TileInfo row_block(int rb, int eoff, int ecnt, int etl, int incl) {
+  const int e = __popcll(__ballot(incl <= rb));
+  const int local = rb - __shfl(incl - etl, e, 64);
+  TileInfo ti;
+  ti.expert = __builtin_amdgcn_readfirstlane(e);
+  ti.row0 = __builtin_amdgcn_readfirstlane(__shfl(eoff, e, 64) + local * BM);
+  ti.rows = __builtin_amdgcn_readfirstlane(min(BM, __shfl(ecnt, e, 64) - local * BM));
+  return ti;
+}
+
+// Spin until *ctr reaches target. The loads are relaxed: an acquire load
+// invalidates the caches every time round the loop, under the tiles that run
+// beside it; the caller issues one acquire fence after the wait.
+__device__ __forceinline__ void wait_count(int32_t* ctr, int target, int32_t* err) {
+  for (int it = 0; __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target; ++it) {
+    if (it >= (1 << 22)) {  // about a second: never reached unless a producer failed
+      __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(8);
+  }
+}
+
+template <int BM, int BN, int WGM, int WGN, int STAGES, int BK, bool GATHER>
+__global__ __launch_bounds__(WGM * WGN * 64) void k_experts_fused(FusedParams fp) {
+  constexpr int kElems = dma_lds_elems<BM, BN, STAGES, BK>();
+  // the operand stages and, after them, the broadcast work item: one LDS object
+  __shared__ __attribute__((aligned(16))) uint16_t smem[kElems + 8];
+  int* s_item = reinterpret_cast<int*>(smem + kElems);
+  constexpr int GM = 4;  // row blocks per group of gate/up tiles
+  const GemmParams& g1 = fp.g1;
+  const GemmParams& g2 = fp.g2;
+  const int lane = threadIdx.x & 63;
+
+  // per-expert row blocks (lane e = expert e), inclusive scan over lanes
+  int eoff = 0, ecnt = 0;
+  if (lane < g1.N) {
+    eoff = g1.offsets[lane];
+    ecnt = g1.offsets[lane + 1] - eoff;
+  }
+  const int etl = (ecnt + BM - 1) / BM;
+  int incl = etl;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int v = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += v;
+  }
+  const int RB = __builtin_amdgcn_readfirstlane(__shfl(incl, 63, 64));
+  const int NT1 = (g1.Nout + BN / 2 - 1) / (BN / 2);
+  const int NT2 = (g2.Nout + BN - 1) / BN;
+  const int n1 = RB * NT1, ntot = RB * (NT1 + NT2);
+  const int G = gridDim.x;
+  const int S = min(n1, G);  // tickets below S are remapped XCD-aware
+
+  for (;;) {
+    __syncthreads();  // every wave is done with the LDS stages and the last item
+    if (threadIdx.x == 0) *s_item = atomicAdd(&fp.sched[kSchedTicket], 1);
+    __syncthreads();
+    const int ticket = __builtin_amdgcn_readfirstlane(*s_item);
+    if (ticket >= ntot) break;
+    const int it = ticket < S ? xcd_remap(ticket, S) : ticket;
+    TilePos tp{};
+    if (it < n1) {
+      const int g = it / (GM * NT1);
+      const int gm = min(GM, RB - g * GM);
+      const int r_in = it - g * GM * NT1;
+      const int rb = g * GM + r_in % gm;
+      tp.nt = r_in / gm;
+      tp.ti = row_block<BM>(rb, eoff, ecnt, etl, incl);
+      tp.kb1 = g1.K;
+      tp.KT = (g1.K + BK - 1) / BK;
+      gemm_tile<BM, BN, WGM, WGN, STAGES, BK, true, GATHER>(g1, tp, smem);
+      // publish: every wave's h stores complete, then one device-scope
+      // release (a single write-back) before the count
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        __hip_atomic_fetch_add(&fp.sched[kSchedDone + rb], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    } else {
+      const int j = it - n1;
+      const int rb = j / NT2;
+      tp.nt = j % NT2;
+      if (threadIdx.x == 0) {
+        wait_count(&fp.sched[kSchedDone + rb], NT1, &fp.sched[kSchedError]);
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      }
+      __syncthreads();
+      tp.ti = row_block<BM>(rb, eoff, ecnt, etl, incl);
+      tp.kb1 = g2.K;
+      tp.KT = (g2.K + BK - 1) / BK;
+      gemm_tile<BM, BN, WGM, WGN, STAGES, BK, false, false>(g2, tp, smem);
+    }
+  }
 }
 
 // ---- register-staged loads -------------------------------------------------------
@@ -514,6 +650,31 @@ void gemm_bf16_mfma_tile(int64_t rows_max, int N, int* bm, int* bn) {
     *bm = 256;
     *bn = 256;
   }
+}
+
+int fused_sched_ints(int64_t rows_max, int N) {
+  return kSchedDone + static_cast<int>((rows_max + kFusedBM - 1) / kFusedBM) + N + 1;
+}
+
+bool gemm_fused_supported(int64_t rows_max, int N, int K1, int F) {
+  int bm, bn;
+  gemm_bf16_mfma_tile(rows_max, N, &bm, &bn);
+  return bm == kFusedBM && bn == kFusedBN && gemm_bf16_mfma_supported(K1, F);
+}
+
+hipError_t launch_experts_fused(const FusedParams& fp, hipStream_t s) {
+  if (fp.g1.rows_max <= 0) return hipSuccess;
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  // one resident workgroup per compute unit (the LDS stages fill most of a CU)
+  const dim3 grid(static_cast<unsigned>(cus > 0 ? cus : 256)), block(4 * 2 * 64);
+  if (fp.g1.row_token)
+    hipLaunchKernelGGL((k_experts_fused<kFusedBM, kFusedBN, 4, 2, 2, 64, true>), grid, block, 0, s, fp);
+  else
+    hipLaunchKernelGGL((k_experts_fused<kFusedBM, kFusedBN, 4, 2, 2, 64, false>), grid, block, 0, s, fp);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm_bf16_mfma(const GemmParams& p, hipStream_t s) {

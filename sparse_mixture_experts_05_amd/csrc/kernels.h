@@ -113,6 +113,17 @@ bool gemm_bf16_mfma_supported(int K, int Nout);
 void gemm_bf16_mfma_tile(int64_t rows_max, int N, int* bm, int* bn);
 hipError_t launch_gemm_simple(const GemmParams& p, int bf16, hipStream_t s);
 
+// Both expert GEMMs in one persistent launch: g1 is the gate/up GEMM with the
+// SwiGLU epilogue (writing h), g2 the down projection reading h (no K split).
+// sched: fused_sched_ints(rows_max, N) int32 of workspace, zero on entry.
+struct FusedParams {
+  GemmParams g1, g2;
+  int32_t* sched;
+};
+int fused_sched_ints(int64_t rows_max, int N);
+bool gemm_fused_supported(int64_t rows_max, int N, int K1, int F);
+hipError_t launch_experts_fused(const FusedParams& fp, hipStream_t s);
+
 // ---- combine (combine.hip) --------------------------------------------------
 struct CombineParams {
   const float* y_perm;       // [splits][rows][H]

@@ -74,8 +74,9 @@ struct Layout {
   int hist_blocks = 0;
   int splits = 1;        // K splits of the down projection in moe_forward
   bool mfma = false;
+  bool fused = false;    // both expert GEMMs in one persistent launch
   size_t hist = 0, stat = 0, wsplit = 0, h = 0, yperm = 0, idx = 0, w = 0, slot = 0, rowtok = 0, counts = 0, kept = 0,
-         offsets = 0, total = 0;
+         offsets = 0, sched = 0, total = 0;
 };
 
 bool use_mfma(const moe_cfg* c) { return c->act == MOE_BF16 && c->F % 8 == 0; }
@@ -87,7 +88,8 @@ Layout layout(const moe_cfg* c) {
   L.hist_tokens = moe::router_tokens_per_block(c->N, c->noisy, c->act == MOE_BF16);
   L.hist_blocks = static_cast<int>((T + L.hist_tokens - 1) / L.hist_tokens);
   L.mfma = use_mfma(c);
-  if (L.mfma) {
+  L.fused = L.mfma && moe::gemm_fused_supported(L.A_max, c->N, c->H, c->F);
+  if (L.mfma && !L.fused) {
     // the down projection splits K when there are too few output tiles to
     // occupy 256 compute units
     int bm, bn;
@@ -119,6 +121,7 @@ Layout layout(const moe_cfg* c) {
   L.counts = take(static_cast<size_t>(c->N) * 4);
   L.kept = take(static_cast<size_t>(c->N) * 4);
   L.offsets = take(static_cast<size_t>(c->N + 1) * 4);
+  L.sched = take(L.fused ? static_cast<size_t>(moe::fused_sched_ints(L.A_max, c->N)) * 4 : 0);
   L.total = o;
   return L;
 }
@@ -196,7 +199,14 @@ moe_status run_gemms(const moe_cfg* c, const Layout& L, const void* a, const int
   g2.a_rows = L.A_max;
   g2.splits = splits;
   g2.swiglu = 0;
-  if (L.mfma) {
+  if (L.fused) {
+    g2.splits = 1;
+    int32_t* sched = at<int32_t>(ws, L.sched);
+    hipError_t e = moe::launch_fill_i32(sched, moe::fused_sched_ints(L.A_max, c->N), 0, s);
+    if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "fill launch failed: %s", hipGetErrorString(e));
+    moe::FusedParams fp{g1, g2, sched};
+    MOE_LAUNCH(MOE_KERNEL_EXPERTS, s, moe::launch_experts_fused(fp, s));
+  } else if (L.mfma) {
     MOE_LAUNCH(MOE_KERNEL_GEMM1, s, moe::launch_gemm_bf16_mfma(g1, s));
     MOE_LAUNCH(MOE_KERNEL_GEMM2, s, moe::launch_gemm_bf16_mfma(g2, s));
   } else {
