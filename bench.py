@@ -30,7 +30,7 @@ METRIC = "MoE-layer tokens/sec and % of bf16 MFMA peak, LLaMA-MoE-3.5B 2/8 shape
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_FP32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
-COUNTERS_FILE = os.path.join(ROOT, "profiles", "gemm1_swiglu_C2_counters.txt")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "experts_fused_C2_counters.txt")
 GEMM_SOURCE = os.path.join(ROOT, "sparse_mixture_experts_05_amd", "csrc", "gemm_mfma.hip")
 
 
