@@ -34,6 +34,10 @@ SMALL = {
     "one_token": lambda: synth.make_independent("t1", 32, 1, 256, 64, 8, 2),
     "capacity_zero": lambda: synth.make_independent("c0", 33, 50, 128, 32, 8, 2, capacity=0),
     "n64_k8": lambda: synth.make_independent("n64", 34, 200, 256, 64, 64, 8),
+    # prefill-sized, with three quarters of the tokens steered to expert 0: one
+    # expert owns many row blocks of the persistent expert kernel
+    "prefill_skewed": lambda: synth.apply_skew(synth.make_independent("pskew", 36, 2048, 512, 256, 8, 2),
+                                               n_pref=1536),
 }
 
 
@@ -72,6 +76,19 @@ def test_forward_empty_batch():
 
 def test_forward_is_deterministic():
     w = SMALL["split_noisy_stats"]()
+    d = upload(w)
+    a = run_forward(w, d=d)
+    b = run_forward(w, d=d)
+    for key in a:
+        assert np.array_equal(a[key], b[key]), key
+
+
+def test_full_C2_is_deterministic():
+    """The expert GEMMs run as one persistent launch whose workgroups take
+    tiles from a queue in whatever order they arrive; every output element is
+    still computed by one tile in a fixed K order, so two runs agree bit for
+    bit."""
+    w = synth.c2()
     d = upload(w)
     a = run_forward(w, d=d)
     b = run_forward(w, d=d)
