@@ -70,6 +70,8 @@ struct ScatterParams {
   int32_t* offsets;         // [N+1]
   int32_t* slot;            // [T,k]
   int32_t* row_token;       // [T*k]
+  int32_t* zero;            // [zero_n] set to 0 by block 0 (the expert kernel's queue counters), or null
+  int zero_n;
 };
 hipError_t launch_scatter(const ScatterParams& p, hipStream_t s);
 

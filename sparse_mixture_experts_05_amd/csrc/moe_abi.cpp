@@ -160,9 +160,11 @@ moe_status zero_expert_outputs(const moe_cfg* c, int32_t* a, int32_t* b, int32_t
   return MOE_OK;
 }
 
+// sched_zeroed: the fused kernel's queue counters were already zeroed on the
+// stream (by the scatter in moe_forward).
 moe_status run_gemms(const moe_cfg* c, const Layout& L, const void* a, const int32_t* row_token,
                      const int32_t* offsets, const void* Wgate, const void* Wup, const void* Wdown, float* y_perm,
-                     int splits, void* ws, hipStream_t s) {
+                     int splits, void* ws, bool sched_zeroed, hipStream_t s) {
   const int bf16 = c->act == MOE_BF16;
   moe::GemmParams g1{};
   g1.A = a;
@@ -202,8 +204,10 @@ moe_status run_gemms(const moe_cfg* c, const Layout& L, const void* a, const int
   if (L.fused) {
     g2.splits = 1;
     int32_t* sched = at<int32_t>(ws, L.sched);
-    hipError_t e = moe::launch_fill_i32(sched, moe::fused_sched_ints(L.A_max, c->N), 0, s);
-    if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "fill launch failed: %s", hipGetErrorString(e));
+    if (!sched_zeroed) {
+      hipError_t e = moe::launch_fill_i32(sched, moe::fused_sched_ints(L.A_max, c->N), 0, s);
+      if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "fill launch failed: %s", hipGetErrorString(e));
+    }
     moe::FusedParams fp{g1, g2, sched};
     MOE_LAUNCH(MOE_KERNEL_EXPERTS, s, moe::launch_experts_fused(fp, s));
   } else if (L.mfma) {
@@ -342,7 +346,7 @@ moe_status moe_grouped_swiglu(const moe_cfg* c, const void* a, const int32_t* ro
   st = check_ws(c, ws, ws_bytes);
   if (st != MOE_OK) return st;
   const Layout L = layout(c);
-  return run_gemms(c, L, a, row_token_opt, offsets, Wgate, Wup, Wdown, y_perm, 1, ws, s);
+  return run_gemms(c, L, a, row_token_opt, offsets, Wgate, Wup, Wdown, y_perm, 1, ws, false, s);
 }
 
 moe_status moe_combine(const moe_cfg* c, const float* y_perm, const int32_t* slot, const float* topk_w, void* y,
@@ -407,10 +411,11 @@ moe_status moe_forward(const moe_cfg* c, const void* x, const float* Wg, const f
   }
   moe::ScatterParams sc{topk_idx, at<int32_t>(ws, L.hist), L.hist_tokens, c->T, c->N, c->k, c->capacity,
                         (!stats && load_opt) ? load_opt : at<int32_t>(ws, L.counts), kept_opt, offsets, slot,
-                        row_token};
+                        row_token, L.fused ? at<int32_t>(ws, L.sched) : nullptr,
+                        L.fused ? moe::fused_sched_ints(L.A_max, c->N) : 0};
   MOE_LAUNCH(MOE_KERNEL_SCATTER, s, moe::launch_scatter(sc, s));
   float* y_perm = at<float>(ws, L.yperm);
-  st = run_gemms(c, L, x, row_token, offsets, Wgate, Wup, Wdown, y_perm, L.splits, ws, s);
+  st = run_gemms(c, L, x, row_token, offsets, Wgate, Wup, Wdown, y_perm, L.splits, ws, true, s);
   if (st != MOE_OK) return st;
   moe::CombineParams cp{y_perm, L.A_max * static_cast<int64_t>(c->H), L.splits, slot, topk_w, y,
                         c->out == MOE_BF16, c->T, c->H, c->k, c->out_scale};

@@ -78,6 +78,8 @@ __global__ __launch_bounds__(kScatterThreads) void k_scatter(ScatterParams p) {
   }
   __syncthreads();
   if (blockIdx.x == 0 && tid <= N) p.offsets[tid] = s_off[tid];
+  if (blockIdx.x == 0 && p.zero)
+    for (int i = tid; i < p.zero_n; i += kScatterThreads) p.zero[i] = 0;
 
   // this thread's token
   const int64_t t = tb0 + tid;
