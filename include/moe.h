@@ -168,10 +168,13 @@ const char* moe_last_error(void); /* thread-local text of the last failure, "" i
 
 /* Kernel timing for benchmarks. moe_profile_select(id) makes the library
  * bracket every later launch of kernel `id` (MOE_KERNEL_*) with a pair of HIP
- * events on the launch stream; -1 turns it off. moe_profile_read() waits for
- * the recorded events, returns the summed duration in ms and the number of
- * launches, and clears the record. Host only; not thread-safe against
- * concurrent launches of the selected kernel from other threads. */
+ * events on the launch stream; -1 turns it off. The first call with id >= 0
+ * creates a pool of 4096 event pairs (the only HIP objects the library
+ * creates; they live until the process ends), so a timed launch costs two
+ * hipEventRecord calls; launches past the pool's size before the next read
+ * are not timed. moe_profile_read() waits for the recorded events, returns
+ * the summed duration in ms and the number of launches timed, and clears the
+ * record. Host only. */
 enum {
   MOE_KERNEL_ROUTER = 0,
   MOE_KERNEL_HIST = 1,

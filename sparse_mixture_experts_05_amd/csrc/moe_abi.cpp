@@ -27,29 +27,31 @@ moe_status fail(moe_status s, const char* fmt, ...) {
 }
 
 // ---- kernel timing -----------------------------------------------------------
+// moe_profile_select creates a pool of event pairs once; a timed launch
+// records into the next free pair, so the timed region pays two
+// hipEventRecord calls per launch and no event creation.
 std::mutex g_prof_mu;
 int g_prof_kernel = -1;
-std::vector<std::pair<hipEvent_t, hipEvent_t>> g_prof_events;
+constexpr size_t kProfPairs = 4096;
+std::vector<std::pair<hipEvent_t, hipEvent_t>> g_prof_pool;
+size_t g_prof_used = 0;
 
 class ProfScope {
  public:
   ProfScope(int kernel, hipStream_t s) : s_(s) {
     std::lock_guard<std::mutex> lk(g_prof_mu);
-    if (kernel != g_prof_kernel) return;
-    if (hipEventCreate(&a_) != hipSuccess || hipEventCreate(&b_) != hipSuccess) return;
-    hipEventRecord(a_, s_);
+    if (kernel != g_prof_kernel || g_prof_used >= g_prof_pool.size()) return;
+    pair_ = g_prof_pool[g_prof_used++];
+    hipEventRecord(pair_.first, s_);
     on_ = true;
   }
   ~ProfScope() {
-    if (!on_) return;
-    hipEventRecord(b_, s_);
-    std::lock_guard<std::mutex> lk(g_prof_mu);
-    g_prof_events.emplace_back(a_, b_);
+    if (on_) hipEventRecord(pair_.second, s_);
   }
 
  private:
   hipStream_t s_;
-  hipEvent_t a_ = nullptr, b_ = nullptr;
+  std::pair<hipEvent_t, hipEvent_t> pair_{nullptr, nullptr};
   bool on_ = false;
 };
 
@@ -439,28 +441,32 @@ const char* moe_last_error(void) { return g_err.c_str(); }
 moe_status moe_profile_select(int32_t kernel_id) {
   if (kernel_id < -1 || kernel_id >= MOE_KERNEL_COUNT) return fail(MOE_ERR_INVALID, "unknown kernel id %d", kernel_id);
   std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (kernel_id >= 0 && g_prof_pool.empty()) {
+    for (size_t i = 0; i < kProfPairs; ++i) {
+      hipEvent_t a = nullptr, b = nullptr;
+      if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess)
+        return fail(MOE_ERR_DEVICE, "hipEventCreate failed");
+      g_prof_pool.emplace_back(a, b);
+    }
+  }
   g_prof_kernel = kernel_id;
   return MOE_OK;
 }
 
 moe_status moe_profile_read(double* total_ms, int64_t* launches) {
-  std::vector<std::pair<hipEvent_t, hipEvent_t>> ev;
-  {
-    std::lock_guard<std::mutex> lk(g_prof_mu);
-    ev.swap(g_prof_events);
-  }
+  std::lock_guard<std::mutex> lk(g_prof_mu);
   double tot = 0.0;
   moe_status st = MOE_OK;
-  for (auto& p : ev) {
+  for (size_t i = 0; i < g_prof_used; ++i) {
     float ms = 0.0f;
-    if (hipEventSynchronize(p.second) != hipSuccess || hipEventElapsedTime(&ms, p.first, p.second) != hipSuccess)
+    if (hipEventSynchronize(g_prof_pool[i].second) != hipSuccess ||
+        hipEventElapsedTime(&ms, g_prof_pool[i].first, g_prof_pool[i].second) != hipSuccess)
       st = fail(MOE_ERR_DEVICE, "event timing failed");
     tot += ms;
-    hipEventDestroy(p.first);
-    hipEventDestroy(p.second);
   }
   if (total_ms) *total_ms = tot;
-  if (launches) *launches = static_cast<int64_t>(ev.size());
+  if (launches) *launches = static_cast<int64_t>(g_prof_used);
+  g_prof_used = 0;
   return st;
 }
 
