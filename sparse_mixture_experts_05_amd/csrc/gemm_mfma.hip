@@ -29,6 +29,8 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <type_traits>
+
 namespace moe {
 
 namespace {
@@ -139,24 +141,29 @@ __device__ __forceinline__ void frag_rows(int wm, int wn, int lane, int (&arow)[
   }
 }
 
-// One BK step of MFMAs from an LDS stage.
-template <int MB, int NB, int BK>
+// One BK step of MFMAs from an LDS stage. PARTIAL: only the wave's first
+// `live` 32-row blocks hold rows of the expert (wave-uniform), and the rest of
+// an expert's last, partly filled tile is skipped, MFMAs and operand reads
+// alike; full tiles take the branch-free copy.
+template <int MB, int NB, int BK, bool PARTIAL = false>
 __device__ __forceinline__ void mma_stage(const uint16_t* __restrict__ a, const uint16_t* __restrict__ b,
                                           const int (&arow)[MB], const int (&brow)[NB], int khalf,
-                                          f32x16_t (&acc)[MB][NB]) {
+                                          f32x16_t (&acc)[MB][NB], int live = MB) {
 #pragma unroll
   for (int ks = 0; ks < BK / 16; ++ks) {
     const int chunk = ks * 2 + khalf;
     bf16x8_t af[MB], bfr[NB];
 #pragma unroll
-    for (int i = 0; i < MB; ++i) af[i] = *reinterpret_cast<const bf16x8_t*>(&a[swz<BK>(arow[i], chunk)]);
+    for (int i = 0; i < MB; ++i)
+      if (!PARTIAL || i < live) af[i] = *reinterpret_cast<const bf16x8_t*>(&a[swz<BK>(arow[i], chunk)]);
 #pragma unroll
     for (int j = 0; j < NB; ++j) bfr[j] = *reinterpret_cast<const bf16x8_t*>(&b[swz<BK>(brow[j], chunk)]);
 #pragma unroll
     for (int i = 0; i < MB; ++i)
+      if (!PARTIAL || i < live)
 #pragma unroll
-      for (int j = 0; j < NB; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < NB; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
   }
 }
 
@@ -253,13 +260,13 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 // two stages are disjoint, so it does not hold the current stage's LDS reads
 // until the just-issued loads land (the explicit waits and barrier at the top
 // of each step order the stages).
-template <int MB, int NB, int BK, class Issue>
+template <int MB, int NB, int BK, bool PARTIAL, class Issue>
 __device__ __forceinline__ void dma_step(Issue& issue, bool do_issue, int kt_next, const uint16_t* __restrict__ a_cur,
                                          const uint16_t* __restrict__ b_cur, uint16_t* __restrict__ a_nxt,
                                          uint16_t* __restrict__ b_nxt, const int (&arow)[MB], const int (&brow)[NB],
-                                         int khalf, f32x16_t (&acc)[MB][NB]) {
+                                         int khalf, f32x16_t (&acc)[MB][NB], int live) {
   if (do_issue) issue(a_nxt, b_nxt, kt_next);
-  mma_stage<MB, NB, BK>(a_cur, b_cur, arow, brow, khalf, acc);
+  mma_stage<MB, NB, BK, PARTIAL>(a_cur, b_cur, arow, brow, khalf, acc, live);
 }
 
 // LDS elements of one workgroup's operand stages.
@@ -352,18 +359,28 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const TilePos& tp
   int arow[MB], brow[NB];
   frag_rows<WM, WN, MB, NB, BN, SWIGLU>(wm, wn, lane, arow, brow);
   const int khalf = lane >> 5;
+  // 32-row blocks of this wave that hold rows of the tile
+  const int live = __builtin_amdgcn_readfirstlane(max(0, min(MB, (tp.ti.rows - wm * WM + 31) / 32)));
 
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s)
     if (s < tp.KT) issue(sA(s), sB(s), s);
-  for (int kt = 0; kt < tp.KT; ++kt) {
-    const int later = min(STAGES - 2, tp.KT - 1 - kt);
-    wait_stage<LPS, STAGES - 2>(later);
-    lds_barrier();  // stage kt is complete for every wave; stage kt-1 is free
-    const int st = kt % STAGES, nx = (kt + STAGES - 1) % STAGES;
-    dma_step<MB, NB, BK>(issue, kt + STAGES - 1 < tp.KT, kt + STAGES - 1, sA(st), sB(st), sA(nx), sB(nx), arow, brow,
-                     khalf, acc);
-  }
+  // the K loop, in a branch-free copy for full tiles and one that skips a
+  // partly filled tile's empty row blocks
+  auto kloop = [&](auto partial) {
+    for (int kt = 0; kt < tp.KT; ++kt) {
+      const int later = min(STAGES - 2, tp.KT - 1 - kt);
+      wait_stage<LPS, STAGES - 2>(later);
+      lds_barrier();  // stage kt is complete for every wave; stage kt-1 is free
+      const int st = kt % STAGES, nx = (kt + STAGES - 1) % STAGES;
+      dma_step<MB, NB, BK, decltype(partial)::value>(issue, kt + STAGES - 1 < tp.KT, kt + STAGES - 1, sA(st), sB(st),
+                                                     sA(nx), sB(nx), arow, brow, khalf, acc, live);
+    }
+  };
+  if (live == MB)
+    kloop(std::false_type{});
+  else
+    kloop(std::true_type{});
   epilogue<WM, WN, MB, NB, SWIGLU>(p, tp, wm, wn, lane, NO, acc);
 }
 
