@@ -42,11 +42,10 @@ class ProfScope {
     std::lock_guard<std::mutex> lk(g_prof_mu);
     if (kernel != g_prof_kernel || g_prof_used >= g_prof_pool.size()) return;
     pair_ = g_prof_pool[g_prof_used++];
-    hipEventRecord(pair_.first, s_);
-    on_ = true;
+    on_ = hipEventRecord(pair_.first, s_) == hipSuccess;
   }
   ~ProfScope() {
-    if (on_) hipEventRecord(pair_.second, s_);
+    if (on_) (void)hipEventRecord(pair_.second, s_);
   }
 
  private:

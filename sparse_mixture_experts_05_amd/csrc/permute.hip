@@ -52,7 +52,6 @@ __global__ __launch_bounds__(kScatterThreads) void k_scatter(ScatterParams p) {
   {
     const int64_t nel = nhb * N;
     const int64_t split = hb0 * N;  // elements before this block's first histogram row
-#pragma unroll 8
     for (int64_t i = tid; i < nel; i += kScatterThreads) {
       const int v = p.hist[i];
       const int n = static_cast<int>(i % N);
@@ -106,15 +105,16 @@ __global__ __launch_bounds__(kScatterThreads) void k_scatter(ScatterParams p) {
   if (tv) {
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) {
-      if (j >= k) break;
-      const int e = idx[j];
-      int woff = 0;
-      for (int w = 0; w < wave; ++w) woff += s_wcnt[w][e];
-      const int rank = s_base[e] + woff + pre[j];
-      const bool keep = p.capacity < 0 || rank < p.capacity;
-      const int row = keep ? s_off[e] + rank : -1;
-      p.slot[t * k + j] = row;
-      if (keep) p.row_token[row] = static_cast<int32_t>(t);
+      if (j < k) {
+        const int e = idx[j];
+        int woff = 0;
+        for (int w = 0; w < wave; ++w) woff += s_wcnt[w][e];
+        const int rank = s_base[e] + woff + pre[j];
+        const bool keep = p.capacity < 0 || rank < p.capacity;
+        const int row = keep ? s_off[e] + rank : -1;
+        p.slot[t * k + j] = row;
+        if (keep) p.row_token[row] = static_cast<int32_t>(t);
+      }
     }
   }
   // rows past the last kept one
