@@ -34,6 +34,10 @@ SMALL = {
     "one_token": lambda: synth.make_independent("t1", 32, 1, 256, 64, 8, 2),
     "capacity_zero": lambda: synth.make_independent("c0", 33, 50, 128, 32, 8, 2, capacity=0),
     "n64_k8": lambda: synth.make_independent("n64", 34, 200, 256, 64, 64, 8),
+    # the persistent expert kernel at the edges of its per-lane expert scans:
+    # 64 experts (one per lane) and a single expert
+    "fused_n64_k4": lambda: synth.make_independent("fn64", 37, 1024, 256, 64, 64, 4),
+    "fused_n1": lambda: synth.make_independent("fn1", 38, 600, 256, 136, 1, 1),
     # prefill-sized, with three quarters of the tokens steered to expert 0: one
     # expert owns many row blocks of the persistent expert kernel
     "prefill_skewed": lambda: synth.apply_skew(synth.make_independent("pskew", 36, 2048, 512, 256, 8, 2),
