@@ -149,59 +149,105 @@ template <int MB, int NB, int BK, bool PARTIAL = false>
 __device__ __forceinline__ void mma_stage(const uint16_t* __restrict__ a, const uint16_t* __restrict__ b,
                                           const int (&arow)[MB], const int (&brow)[NB], int khalf,
                                           f32x16_t (&acc)[MB][NB], int live = MB) {
-#pragma unroll
-  for (int ks = 0; ks < BK / 16; ++ks) {
+  // two fragment sets: the LDS reads of K slice ks + 1 are issued before the
+  // MFMAs of slice ks, so they land while those run
+  constexpr int KS = BK / 16;
+  bf16x8_t af[2][MB], bfr[2][NB];
+  auto load = [&](int ks, int buf) {
     const int chunk = ks * 2 + khalf;
-    bf16x8_t af[MB], bfr[NB];
 #pragma unroll
     for (int i = 0; i < MB; ++i)
-      if (!PARTIAL || i < live) af[i] = *reinterpret_cast<const bf16x8_t*>(&a[swz<BK>(arow[i], chunk)]);
+      if (!PARTIAL || i < live) af[buf][i] = *reinterpret_cast<const bf16x8_t*>(&a[swz<BK>(arow[i], chunk)]);
 #pragma unroll
-    for (int j = 0; j < NB; ++j) bfr[j] = *reinterpret_cast<const bf16x8_t*>(&b[swz<BK>(brow[j], chunk)]);
+    for (int j = 0; j < NB; ++j) bfr[buf][j] = *reinterpret_cast<const bf16x8_t*>(&b[swz<BK>(brow[j], chunk)]);
+  };
+  load(0, 0);
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const int cur = ks & 1;
+    if (ks + 1 < KS) load(ks + 1, cur ^ 1);
+    __builtin_amdgcn_sched_barrier(0);  // keep those reads ahead of the MFMAs below
 #pragma unroll
     for (int i = 0; i < MB; ++i)
       if (!PARTIAL || i < live)
 #pragma unroll
         for (int j = 0; j < NB; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][i], bfr[cur][j], acc[i][j], 0, 0, 0);
   }
+}
+
+// A wave-uniform buffer descriptor: the base address passes through
+// readfirstlane so the descriptor lives in scalar registers (a descriptor in
+// vector registers makes every load a per-lane loop).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* base, int64_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
+  void* p = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
+  const int num = __builtin_amdgcn_readfirstlane(static_cast<int>(bytes < 0x7FFFFFF0 ? bytes : 0x7FFFFFF0));
+  return __builtin_amdgcn_make_buffer_rsrc(p, 0, num, kBufferFlags);
 }
 
 // Accumulator layout of a 32x32 block: lane holds column (lane & 31) and rows
 // 8*(r/4) + 4*(lane/32) + r%4 for r = 0..15.
+//
+// The stores go through a buffer descriptor that spans exactly the tile's
+// valid rows, so the range check drops rows past the expert's end without a
+// branch; a column past Nout gets a byte offset of at least kStoreOOB, beyond
+// every descriptor (tile offsets stay far below 2^31, so the sum cannot wrap).
+constexpr uint32_t kStoreOOB = 0x80000000u;
+
+// SiLU(z) = z * sigmoid(z) with the hardware exp2 and reciprocal, each within
+// about one ulp of fp32, far below the bf16 rounding of h that follows.
+__device__ __forceinline__ float silu_fast(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z * -1.4426950408889634f));
+}
+
 template <int WM, int WN, int MB, int NB, bool SWIGLU>
 __device__ __forceinline__ void epilogue(const GemmParams& p, const TilePos& tp, int wm, int wn, int lane, int NO,
                                          f32x16_t (&acc)[MB][NB]) {
   const int col_l = lane & 31, khalf = lane >> 5;
+  const int row_l = wm * WM + khalf * 4;  // this lane's first row in the tile
   if (SWIGLU) {
-    uint16_t* __restrict__ C = static_cast<uint16_t*>(p.C);
+    const uint16_t* base = static_cast<const uint16_t*>(p.C) + static_cast<int64_t>(tp.ti.row0) * p.ldc;
+    const __amdgpu_buffer_rsrc_t rc = uniform_rsrc(base, static_cast<int64_t>(tp.ti.rows) * p.ldc * 2);
+    const uint32_t ld = static_cast<uint32_t>(p.ldc) * 2u;  // bytes per row
 #pragma unroll
     for (int i = 0; i < MB; ++i)
 #pragma unroll
       for (int j = 0; j < NB / 2; ++j) {
         const int f = tp.nt * NO + wn * (WN / 2) + j * 32 + col_l;
-        if (f >= p.Nout) continue;
+        const uint32_t cb = f < p.Nout ? static_cast<uint32_t>(row_l * p.ldc + f) * 2u : kStoreOOB;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int tr = wm * WM + i * 32 + (r >> 2) * 8 + khalf * 4 + (r & 3);
-          if (tr < tp.ti.rows) {
-            const float g = acc[i][j][r], u = acc[i][j + NB / 2][r];
-            C[static_cast<int64_t>(tp.ti.row0 + tr) * p.ldc + f] = f32_to_bf16(silu(g) * u);
-          }
+        for (int r = 0; r < 16; r += 2) {
+          // rows r and r + 1 are adjacent: one packed conversion, two stores
+          typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+          const bf16x2_t hv = {(__bf16)(silu_fast(acc[i][j][r]) * acc[i][j + NB / 2][r]),
+                               (__bf16)(silu_fast(acc[i][j][r + 1]) * acc[i][j + NB / 2][r + 1])};
+          const uint32_t bits = __builtin_bit_cast(uint32_t, hv);
+          const uint32_t off = cb + static_cast<uint32_t>(i * 32 + (r >> 2) * 8 + (r & 3)) * ld;
+          __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(bits), rc, off, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(bits >> 16), rc, off + ld, 0, 0);
         }
       }
   } else {
-    float* __restrict__ C = static_cast<float*>(p.C) + tp.split * p.c_split_stride;
+    const float* base = static_cast<const float*>(p.C) + tp.split * p.c_split_stride +
+                        static_cast<int64_t>(tp.ti.row0) * p.ldc;
+    const __amdgpu_buffer_rsrc_t rc = uniform_rsrc(base, static_cast<int64_t>(tp.ti.rows) * p.ldc * 4);
+    const uint32_t ld = static_cast<uint32_t>(p.ldc) * 4u;
 #pragma unroll
     for (int i = 0; i < MB; ++i)
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
         const int n = tp.nt * NO + wn * WN + j * 32 + col_l;
-        if (n >= p.Nout) continue;
+        const uint32_t cb = n < p.Nout ? static_cast<uint32_t>(row_l * p.ldc + n) * 4u : kStoreOOB;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int tr = wm * WM + i * 32 + (r >> 2) * 8 + khalf * 4 + (r & 3);
-          if (tr < tp.ti.rows) C[static_cast<int64_t>(tp.ti.row0 + tr) * p.ldc + n] = acc[i][j][r];
+          // the element goes through a scalar first: a bit_cast straight from
+          // the vector subscript is compiled as element 0 for every r
+          const float v = acc[i][j][r];
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rc,
+                                                cb + static_cast<uint32_t>(i * 32 + (r >> 2) * 8 + (r & 3)) * ld, 0, 0);
         }
       }
   }
@@ -240,18 +286,6 @@ __device__ __forceinline__ void wait_stage(int later) {
 }
 
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
-// A wave-uniform buffer descriptor: the base address passes through
-// readfirstlane so the descriptor lives in scalar registers (a descriptor in
-// vector registers makes every load a per-lane loop).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* base, int64_t bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
-  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
-  void* p = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
-  const int num = __builtin_amdgcn_readfirstlane(static_cast<int>(bytes < 0x7FFFFFF0 ? bytes : 0x7FFFFFF0));
-  return __builtin_amdgcn_make_buffer_rsrc(p, 0, num, kBufferFlags);
-}
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
