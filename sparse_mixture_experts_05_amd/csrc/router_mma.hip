@@ -85,33 +85,43 @@ __global__ __launch_bounds__(router_waves<NB16>() * 64) void k_router_mma(Router
 #pragma unroll
     for (int r = 0; r < 4; ++r) acc_hi[c][r] = acc_lo[c][r] = 0.0f;
 
-  constexpr int U = NB16 <= 1 ? 4 : (NB16 <= 2 ? 2 : 1);  // K steps whose loads are issued together
-  for (int s = s0; s < s1; s += U) {
-    bf16x8_t a[U], b[U][NB16][3];
+  // The x loads of XU K steps go out together (one memory round trip for
+  // the block's whole share of x at H = 4096); the weight parts, which stay
+  // in L2, are loaded one step ahead of their MFMAs.
+  constexpr int XU = NB16 == 2 ? 4 : 8;  // within 128 registers at 16 waves
+  for (int s = s0; s < s1; s += XU) {
+    bf16x8_t a[XU];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
+    for (int u = 0; u < XU; ++u) {
+      const int kk = (s + u) * 32 + kg * 8;
+      u32x4_t v = {0u, 0u, 0u, 0u};
+      if ((s + u) < s1 && kk < H && tok_ok) v = *reinterpret_cast<const u32x4_t*>(xrow + kk);
+      a[u] = __builtin_bit_cast(bf16x8_t, v);
+    }
+    bf16x8_t b[2][NB16][3];
+    auto load_w = [&](int u, int buf) {
       const int kk = (s + u) * 32 + kg * 8;
       const bool kin = (s + u) < s1 && kk < H;
-      u32x4_t v = {0u, 0u, 0u, 0u};
-      if (kin && tok_ok) v = *reinterpret_cast<const u32x4_t*>(xrow + kk);
-      a[u] = __builtin_bit_cast(bf16x8_t, v);
 #pragma unroll
       for (int c = 0; c < NB16; ++c)
 #pragma unroll
         for (int q = 0; q < 3; ++q) {
           u32x4_t wv = {0u, 0u, 0u, 0u};
           if (kin && c * 16 + row < n2) wv = *reinterpret_cast<const u32x4_t*>(Ws + q * part + static_cast<int64_t>(c * 16 + row) * H + kk);
-          b[u][c][q] = __builtin_bit_cast(bf16x8_t, wv);
+          b[buf][c][q] = __builtin_bit_cast(bf16x8_t, wv);
         }
-    }
+    };
+    load_w(0, 0);
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+    for (int u = 0; u < XU; ++u) {
+      if (u + 1 < XU) load_w(u + 1, (u + 1) & 1);
 #pragma unroll
       for (int c = 0; c < NB16; ++c) {
-        acc_hi[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], b[u][c][0], acc_hi[c], 0, 0, 0);
-        acc_lo[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], b[u][c][1], acc_lo[c], 0, 0, 0);
-        acc_lo[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], b[u][c][2], acc_lo[c], 0, 0, 0);
+        acc_hi[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], b[u & 1][c][0], acc_hi[c], 0, 0, 0);
+        acc_lo[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], b[u & 1][c][1], acc_lo[c], 0, 0, 0);
+        acc_lo[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], b[u & 1][c][2], acc_lo[c], 0, 0, 0);
       }
+    }
   }
   // lane holds column (lane & 15) and token rows 4*(lane/16) + r
 #pragma unroll
