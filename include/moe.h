@@ -108,9 +108,8 @@ size_t moe_workspace_bytes(const moe_cfg* cfg);
  *   P_opt [N] fp32 mean over tokens of softmax(logits);
  *   balance_opt [1] fp32 sum_i f_i P_i with f_i = load_i / (T k)
  *   (the coefficient lambda is left to the caller).
- *   ws: a workspace of moe_workspace_bytes(cfg) is required when cfg->act is
- *   MOE_BF16 (it holds the bf16 split of the router weights for the matrix
- *   cores) or when statistics are requested; otherwise it may be NULL.
+ *   ws: a workspace of moe_workspace_bytes(cfg) is required when statistics
+ *   are requested; otherwise it may be NULL.
  *   Returns MOE_ERR_WORKSPACE when it is too small. */
 moe_status moe_route(const moe_cfg* cfg, const void* x, const float* Wg, const float* Wn, const float* eps,
                      float* logits_opt, int32_t* topk_idx, float* topk_w, int32_t* load_opt,

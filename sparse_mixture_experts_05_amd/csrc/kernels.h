@@ -20,13 +20,11 @@ struct RouterParams {
   float* topk_w;          // [T,k]
   int32_t* hist;          // [blocks,N] assignments per expert per block, or null
   float* stat_part;       // [blocks,2N] importance and sum of softmax(logits), or null
-  uint16_t* wsplit;       // workspace: bf16 split of the router weights (bf16 activations)
 };
 // Tokens handled by one router block; the permutation scatter reads the
 // per-block histogram with this granularity.
 int router_tokens_per_block(int N, int noisy, int act_bf16);
 int router_blocks(int64_t T, int N, int noisy, int act_bf16);
-size_t router_wsplit_bytes(int H, int N, int noisy);
 hipError_t launch_router(const RouterParams& p, hipStream_t s);
 hipError_t launch_router_mma(const RouterParams& p, hipStream_t s);
 

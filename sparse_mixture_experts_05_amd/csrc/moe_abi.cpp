@@ -76,7 +76,7 @@ struct Layout {
   int splits = 1;        // K splits of the down projection in moe_forward
   bool mfma = false;
   bool fused = false;    // both expert GEMMs in one persistent launch
-  size_t hist = 0, stat = 0, wsplit = 0, h = 0, yperm = 0, idx = 0, w = 0, slot = 0, rowtok = 0, counts = 0, kept = 0,
+  size_t hist = 0, stat = 0, h = 0, yperm = 0, idx = 0, w = 0, slot = 0, rowtok = 0, counts = 0, kept = 0,
          offsets = 0, sched = 0, total = 0;
 };
 
@@ -112,7 +112,6 @@ Layout layout(const moe_cfg* c) {
   };
   L.hist = take(static_cast<size_t>(L.hist_blocks) * c->N * 4);
   L.stat = take(static_cast<size_t>(L.hist_blocks) * c->N * 2 * 4);
-  L.wsplit = take(c->act == MOE_BF16 ? moe::router_wsplit_bytes(c->H, c->N, c->noisy) : 0);
   L.h = take(static_cast<size_t>(L.A_max) * c->F * act);
   L.yperm = take(static_cast<size_t>(L.splits) * L.A_max * c->H * 4);
   L.idx = take(static_cast<size_t>(Tk) * 4);
@@ -279,7 +278,7 @@ moe_status moe_route(const moe_cfg* c, const void* x, const float* Wg, const flo
   MOE_REQUIRE(x && Wg && topk_idx && topk_w, "x, Wg, topk_idx and topk_w are required");
   MOE_REQUIRE(!c->noisy || (Wn && eps), "noisy routing needs Wn and eps");
   MOE_REQUIRE(aligned(x, 16) && aligned(Wg, 16) && (!Wn || aligned(Wn, 16)), "x, Wg and Wn must be 16-byte aligned");
-  if (stats || c->act == MOE_BF16) {
+  if (stats) {
     st = check_ws(c, ws, ws_bytes);
     if (st != MOE_OK) return st;
   }
@@ -301,7 +300,6 @@ moe_status moe_route(const moe_cfg* c, const void* x, const float* Wg, const flo
   rp.topk_w = topk_w;
   rp.hist = stats ? at<int32_t>(ws, L.hist) : nullptr;
   rp.stat_part = stats ? at<float>(ws, L.stat) : nullptr;
-  rp.wsplit = ws ? at<uint16_t>(ws, L.wsplit) : nullptr;
   MOE_LAUNCH(MOE_KERNEL_ROUTER, s, moe::launch_router(rp, s));
   if (stats) {
     moe::StatsParams sp{at<int32_t>(ws, L.hist), at<float>(ws, L.stat), L.hist_blocks, c->T, c->N, c->k,
@@ -403,7 +401,6 @@ moe_status moe_forward(const moe_cfg* c, const void* x, const float* Wg, const f
   rp.topk_w = topk_w;
   rp.hist = at<int32_t>(ws, L.hist);
   rp.stat_part = stats ? at<float>(ws, L.stat) : nullptr;
-  rp.wsplit = at<uint16_t>(ws, L.wsplit);
   MOE_LAUNCH(MOE_KERNEL_ROUTER, s, moe::launch_router(rp, s));
   if (stats) {
     moe::StatsParams sp{at<int32_t>(ws, L.hist), at<float>(ws, L.stat), L.hist_blocks, c->T, c->N, c->k,

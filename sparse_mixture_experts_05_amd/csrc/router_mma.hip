@@ -1,15 +1,19 @@
 // Router on the matrix cores for bf16 activations.
 //
 // The router product x.W_g (and x.W_noise) is a skinny GEMM: T x H times
-// H x N with N <= 64. The fp32 router weights are split exactly into three
-// bf16 parts, W = W1 + W2 + W3 (each part holds the next 8 significant bits),
+// H x N with N <= 64. Each fp32 router weight is split exactly into three
+// bf16 parts, W = W1 + W2 + W3 (each part holds the next 8 significant bits;
+// round-to-nearest-even leaves a remainder that the next part holds exactly),
 // so every product x * W_i of a bf16 activation is exact in fp32 and
 // v_mfma_f32_16x16x32_bf16 forms x.W with fp32 accumulation. The hi part and
-// the two lower parts go to separate accumulators and the four waves of a
-// block each cover a quarter of H, which keeps the accumulated rounding error
-// near that of a plain fp32 dot product.
+// the two lower parts go to separate accumulators and the waves of a block
+// each cover a share of H, which keeps the accumulated rounding error near
+// that of a plain fp32 dot product.
 //
-// A block owns 16 tokens. After the product, one wave per token applies the
+// A block owns 16 tokens. It walks H in chunks: the chunk's fp32 weight rows
+// are copied into LDS with coalesced loads (issued together with the x loads),
+// and each lane reads its eight operand values per K step from LDS and splits
+// them in registers. After the product, one wave per token applies the
 // noise term, KeepTopK by k rounds of a wave-wide argmax (ties to the lower
 // expert index; "Llama 3 Meets MoE" review, section 3) and the gate of the
 // chosen order (Mixtral: softmax over the kept scores; ST: softmax over all
@@ -34,32 +38,49 @@ constexpr int kTok = 16;    // tokens per block (M of the MFMA)
 template <int NB16>
 constexpr int router_waves() { return NB16 <= 2 ? 16 : (NB16 <= 4 ? 8 : 4); }
 
-// Ws[p][c][h], p = 0..2, c < N2p (columns: W_g, then W_noise, then zero
-// padding), K-contiguous bf16 bits.
-__global__ __launch_bounds__(256) void k_router_wsplit(const float* __restrict__ Wg, const float* __restrict__ Wn,
-                                                       int H, int N, int noisy, int N2p, uint16_t* __restrict__ Ws) {
-  const int total = N2p * H;
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < total; i += gridDim.x * blockDim.x) {
-    const int c = i / H, h = i - c * H;
-    float w = 0.0f;
-    if (c < N) w = Wg[static_cast<int64_t>(h) * N + c];
-    else if (noisy && c < 2 * N) w = Wn[static_cast<int64_t>(h) * N + (c - N)];
-    const uint16_t w1 = f32_to_bf16(w);
-    const float r1 = w - bf16_to_f32(w1);
-    const uint16_t w2 = f32_to_bf16(r1);
-    const float r2 = r1 - bf16_to_f32(w2);
-    const uint16_t w3 = f32_to_bf16(r2);
-    Ws[i] = w1;
-    Ws[total + i] = w2;
-    Ws[2 * total + i] = w3;
+constexpr int kWFloats = 32 * 1024;  // LDS for one chunk of fp32 weight rows (128 KB)
+// most K steps of one wave in one chunk (their x loads stay in registers)
+template <int NB16>
+constexpr int router_xu() { return NB16 == 2 ? 4 : 8; }
+
+// Rows of H per chunk: a multiple of 32 * waves (whole K steps for every
+// wave), at most kXU steps per wave, and within kWFloats for all n2 columns.
+constexpr int kWPad = 4;             // floats of padding per LDS column
+
+template <int NB16>
+int router_chunk_rows(int H, int n2) {
+  const int unit = 32 * router_waves<NB16>();
+  int rows = kWFloats / n2 / unit * unit;
+  rows = std::min(rows, router_xu<NB16>() * unit);
+  rows = std::max(rows, unit);
+  return std::min(rows, (H + unit - 1) / unit * unit);
+}
+
+// Exact three-way bf16 split of eight fp32 values.
+__device__ __forceinline__ void split3(const float (&w)[8], bf16x8_t& p1, bf16x8_t& p2, bf16x8_t& p3) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const __bf16 b1 = static_cast<__bf16>(w[i]);
+    const float r1 = w[i] - static_cast<float>(b1);
+    const __bf16 b2 = static_cast<__bf16>(r1);
+    const float r2 = r1 - static_cast<float>(b2);
+    p1[i] = b1;
+    p2[i] = b2;
+    p3[i] = static_cast<__bf16>(r2);
   }
 }
 
 template <int NB16>
-__global__ __launch_bounds__(router_waves<NB16>() * 64) void k_router_mma(RouterParams p, int N2p) {
+__global__ __launch_bounds__(router_waves<NB16>() * 64) void k_router_mma(RouterParams p, int hc) {
   constexpr int kWaves = router_waves<NB16>();
+  constexpr int kThreads = kWaves * 64;
   constexpr int NC = NB16 * 16;
-  __shared__ float s_part[kWaves][kTok][NC];
+  constexpr int kXU = router_xu<NB16>();
+  // the weight chunk; after the product, the per-wave partial sums
+  // (n2 <= 128 padded columns of at most kWFloats / n2 rows)
+  __shared__ __attribute__((aligned(16))) float s_w[kWFloats + kWPad * 128];
+  static_assert(kWaves * kTok * NC <= kWFloats, "partials fit in the weight buffer");
+  float (*s_part)[kTok][NC] = reinterpret_cast<float (*)[kTok][NC]>(s_w);
   __shared__ float s_log[kTok][NC];       // clean logits, then noise logits
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -67,17 +88,13 @@ __global__ __launch_bounds__(router_waves<NB16>() * 64) void k_router_mma(Router
   const int64_t T = p.T;
   const int64_t tok0 = static_cast<int64_t>(blockIdx.x) * kTok;
   const uint16_t* __restrict__ x = static_cast<const uint16_t*>(p.x);
-  const uint16_t* __restrict__ Ws = p.wsplit;
-  const int64_t part = static_cast<int64_t>(N2p) * H;
-  const int n2 = N * (p.noisy ? 2 : 1);  // real columns; the padding stays zero without loads
+  const int n2 = N * (p.noisy ? 2 : 1);  // real columns; the padding stays zero
 
-  // this wave's K range, in steps of 32
-  const int steps = (H + 31) / 32;
-  const int s0 = wave * steps / kWaves, s1 = (wave + 1) * steps / kWaves;
   const int row = lane & 15, kg = lane >> 4;  // A: token row; B: column; kg selects 8 of the 32 K
   const int64_t tok = tok0 + row;
   const bool tok_ok = tok < T;
   const uint16_t* xrow = x + (tok_ok ? tok : 0) * H;
+  const int wsteps = hc / 32 / kWaves;  // this wave's K steps per chunk
 
   f32x4_mma_t acc_hi[NB16], acc_lo[NB16];
 #pragma unroll
@@ -85,43 +102,86 @@ __global__ __launch_bounds__(router_waves<NB16>() * 64) void k_router_mma(Router
 #pragma unroll
     for (int r = 0; r < 4; ++r) acc_hi[c][r] = acc_lo[c][r] = 0.0f;
 
-  // The x loads of XU K steps go out together (one memory round trip for
-  // the block's whole share of x at H = 4096); the weight parts, which stay
-  // in L2, are loaded one step ahead of their MFMAs.
-  constexpr int XU = NB16 == 2 ? 4 : 8;  // within 128 registers at 16 waves
-  for (int s = s0; s < s1; s += XU) {
-    bf16x8_t a[XU];
+  // 16-byte weight loads need aligned pointers and whole rows per piece
+  const bool vec = (reinterpret_cast<uintptr_t>(p.Wg) & 15) == 0 &&
+                   (!p.noisy || (reinterpret_cast<uintptr_t>(p.Wn) & 15) == 0) && N % 4 == 0;
+  const int hcp = hc + kWPad;  // LDS column stride: column j of the chunk holds its rows k contiguous
+  for (int h0 = 0; h0 < H; h0 += hc) {
+    const int hn = min(hc, H - h0);  // weight rows in this chunk
+    // the chunk's weight rows go to LDS transposed, W_g as columns [0, N) and
+    // W_noise as columns [N, 2N): 16-byte pieces, all of a thread's loads out
+    // before any store
+    const int cnt = hn * N, c4 = vec ? cnt / 4 : 0, np = (p.noisy ? 2 : 1) * c4;
+    constexpr int kP = kWFloats / 4 / kThreads;  // most pieces per thread
+    f32x4_t wbuf[kP];
 #pragma unroll
-    for (int u = 0; u < XU; ++u) {
-      const int kk = (s + u) * 32 + kg * 8;
-      u32x4_t v = {0u, 0u, 0u, 0u};
-      if ((s + u) < s1 && kk < H && tok_ok) v = *reinterpret_cast<const u32x4_t*>(xrow + kk);
-      a[u] = __builtin_bit_cast(bf16x8_t, v);
-    }
-    bf16x8_t b[2][NB16][3];
-    auto load_w = [&](int u, int buf) {
-      const int kk = (s + u) * 32 + kg * 8;
-      const bool kin = (s + u) < s1 && kk < H;
-#pragma unroll
-      for (int c = 0; c < NB16; ++c)
-#pragma unroll
-        for (int q = 0; q < 3; ++q) {
-          u32x4_t wv = {0u, 0u, 0u, 0u};
-          if (kin && c * 16 + row < n2) wv = *reinterpret_cast<const u32x4_t*>(Ws + q * part + static_cast<int64_t>(c * 16 + row) * H + kk);
-          b[buf][c][q] = __builtin_bit_cast(bf16x8_t, wv);
-        }
-    };
-    load_w(0, 0);
-#pragma unroll
-    for (int u = 0; u < XU; ++u) {
-      if (u + 1 < XU) load_w(u + 1, (u + 1) & 1);
-#pragma unroll
-      for (int c = 0; c < NB16; ++c) {
-        acc_hi[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], b[u & 1][c][0], acc_hi[c], 0, 0, 0);
-        acc_lo[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], b[u & 1][c][1], acc_lo[c], 0, 0, 0);
-        acc_lo[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], b[u & 1][c][2], acc_lo[c], 0, 0, 0);
+    for (int j = 0; j < kP; ++j) {
+      const int i = threadIdx.x + j * kThreads;
+      if (i < np) {
+        const int m = i < c4 ? 0 : 1, q = i - m * c4;
+        wbuf[j] = *reinterpret_cast<const f32x4_t*>((m == 0 ? p.Wg : p.Wn) + static_cast<int64_t>(h0) * N + 4 * q);
       }
     }
+    // x of this wave's steps in the chunk
+    bf16x8_t a[kXU];
+#pragma unroll
+    for (int u = 0; u < kXU; ++u) {
+      const int kk = h0 + (wave * wsteps + u) * 32 + kg * 8;
+      u32x4_t v = {0u, 0u, 0u, 0u};
+      if (u < wsteps && kk < H && tok_ok) v = *reinterpret_cast<const u32x4_t*>(xrow + kk);
+      a[u] = __builtin_bit_cast(bf16x8_t, v);
+    }
+#pragma unroll
+    for (int j = 0; j < kP; ++j) {
+      const int i = threadIdx.x + j * kThreads;
+      if (i < np) {
+        const int m = i < c4 ? 0 : 1, q = i - m * c4;
+        const int f = 4 * q, r = f / N, n = f - r * N + m * N;  // row and first column of the piece
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s_w[(n + e) * hcp + r] = wbuf[j][e];
+      }
+    }
+    // what the pieces do not cover (an unaligned pointer, N % 4 != 0)
+    for (int m = 0; m < (p.noisy ? 2 : 1); ++m) {
+      const float* src = (m == 0 ? p.Wg : p.Wn) + static_cast<int64_t>(h0) * N;
+      for (int i = 4 * c4 + threadIdx.x; i < cnt; i += kThreads) {
+        const int r = i / N;
+        s_w[(i - r * N + m * N) * hcp + r] = src[i];
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kXU; ++u) {
+      if (u < wsteps) {
+        const int kl = (wave * wsteps + u) * 32 + kg * 8;  // K within the chunk
+#pragma unroll
+        for (int c = 0; c < NB16; ++c) {
+          const int col = c * 16 + row;
+          float wv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+          if (col < n2) {
+            const f32x4_t lo = *reinterpret_cast<const f32x4_t*>(s_w + col * hcp + kl);
+            const f32x4_t hi = *reinterpret_cast<const f32x4_t*>(s_w + col * hcp + kl + 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              wv[e] = lo[e];
+              wv[4 + e] = hi[e];
+            }
+            if (hn < hc) {  // rows past the chunk's end hold stale values
+#pragma unroll
+              for (int e = 0; e < 8; ++e)
+                if (kl + e >= hn) wv[e] = 0.0f;
+            }
+          }
+          bf16x8_t w1, w2, w3;
+          split3(wv, w1, w2, w3);
+          acc_hi[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], w1, acc_hi[c], 0, 0, 0);
+          acc_lo[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], w2, acc_lo[c], 0, 0, 0);
+          acc_lo[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], w3, acc_lo[c], 0, 0, 0);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);  // one step's operands live at a time
+    }
+    __syncthreads();  // the chunk buffer is free again
   }
   // lane holds column (lane & 15) and token rows 4*(lane/16) + r
 #pragma unroll
@@ -219,28 +279,12 @@ __global__ __launch_bounds__(router_waves<NB16>() * 64) void k_router_mma(Router
 
 }  // namespace
 
-int router_mma_columns(int N, int noisy) {
-  const int n2 = N * (noisy ? 2 : 1);
-  return (n2 + 15) / 16 * 16;
-}
-
-size_t router_wsplit_bytes(int H, int N, int noisy) {
-  return static_cast<size_t>(3) * router_mma_columns(N, noisy) * H * sizeof(uint16_t);
-}
-
 hipError_t launch_router_mma(const RouterParams& p, hipStream_t s) {
-  const int N2p = router_mma_columns(p.N, p.noisy);
-  {
-    const int64_t total = static_cast<int64_t>(N2p) * p.H;
-    const int blocks = static_cast<int>(std::min<int64_t>((total + 255) / 256, 2048));
-    hipLaunchKernelGGL(k_router_wsplit, dim3(blocks), dim3(256), 0, s, p.Wg, p.Wn, p.H, p.N, p.noisy, N2p, p.wsplit);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
+  const int n2 = p.N * (p.noisy ? 2 : 1);
   const dim3 grid(static_cast<unsigned>((p.T + kTok - 1) / kTok));
 #define MOE_ROUTER_MMA(NB) \
-  hipLaunchKernelGGL(k_router_mma<NB>, grid, dim3(router_waves<NB>() * 64), 0, s, p, N2p)
-  switch (N2p / 16) {
+  hipLaunchKernelGGL(k_router_mma<NB>, grid, dim3(router_waves<NB>() * 64), 0, s, p, router_chunk_rows<NB>(p.H, n2))
+  switch ((n2 + 15) / 16) {
     case 1: MOE_ROUTER_MMA(1); break;
     case 2: MOE_ROUTER_MMA(2); break;
     case 3: MOE_ROUTER_MMA(3); break;
