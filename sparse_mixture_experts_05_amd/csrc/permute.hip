@@ -41,6 +41,17 @@ __global__ __launch_bounds__(kScatterThreads) void k_scatter(ScatterParams p) {
   const int64_t nhb = (T + p.hist_tokens - 1) / p.hist_tokens;
   const int64_t hb0 = tb0 / p.hist_tokens;
 
+  // this thread's token; its expert list is loaded first so that the load
+  // overlaps the histogram reads below
+  const int64_t t = tb0 + tid;
+  const bool tv = t < T;
+  int idx[KMAX], pre[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    idx[j] = (tv && j < k) ? p.topk_idx[t * k + j] : -1;
+    pre[j] = 0;
+  }
+
   // per-expert totals and the count before this block: every thread reads
   // its share of the histogram at once and adds it into LDS (integer sums,
   // so the order of the adds does not matter)
@@ -52,12 +63,22 @@ __global__ __launch_bounds__(kScatterThreads) void k_scatter(ScatterParams p) {
   {
     const int64_t nel = nhb * N;
     const int64_t split = hb0 * N;  // elements before this block's first histogram row
-    for (int64_t i = tid; i < nel; i += kScatterThreads) {
-      const int v = p.hist[i];
-      const int n = static_cast<int>(i % N);
-      if (v) {
-        atomicAdd(&s_tot[n], v);
-        if (i < split) atomicAdd(&s_base[n], v);
+    constexpr int U = 8;  // loads in flight per thread before their adds
+    for (int64_t i0 = tid; i0 < nel; i0 += U * kScatterThreads) {
+      int v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t i = i0 + u * kScatterThreads;
+        v[u] = i < nel ? p.hist[i] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t i = i0 + u * kScatterThreads;
+        const int n = static_cast<int>(i % N);
+        if (v[u]) {
+          atomicAdd(&s_tot[n], v[u]);
+          if (i < split) atomicAdd(&s_base[n], v[u]);
+        }
       }
     }
   }
@@ -80,15 +101,6 @@ __global__ __launch_bounds__(kScatterThreads) void k_scatter(ScatterParams p) {
   if (blockIdx.x == 0 && p.zero)
     for (int i = tid; i < p.zero_n; i += kScatterThreads) p.zero[i] = 0;
 
-  // this thread's token
-  const int64_t t = tb0 + tid;
-  const bool tv = t < T;
-  int idx[KMAX], pre[KMAX];
-#pragma unroll
-  for (int j = 0; j < KMAX; ++j) {
-    idx[j] = (tv && j < k) ? p.topk_idx[t * k + j] : -1;
-    pre[j] = 0;
-  }
   // rank among earlier lanes of the wave, per expert, by ballot
   for (int e = 0; e < N; ++e) {
     bool has = false;
