@@ -307,76 +307,81 @@ __device__ __forceinline__ void dma_step(Issue& issue, bool do_issue, int kt_nex
 template <int BM, int BN, int STAGES, int BK>
 constexpr int dma_lds_elems() { return STAGES * (BM + BN) * BK; }
 
-// One output tile with buffer loads straight into LDS: the operand stages
-// live in `smem` (dma_lds_elems elements, one LDS object). The caller makes
-// sure no wave still reads `smem` from an earlier tile.
-template <int BM, int BN, int WGM, int WGN, int STAGES, int BK, bool SWIGLU, bool GATHER>
-__device__ __forceinline__ void gemm_tile(const GemmParams& p, const TilePos& tp, uint16_t* smem) {
-  constexpr int NW = WGM * WGN;
-  constexpr int WM = BM / WGM, WN = BN / WGN;
-  constexpr int MB = WM / 32, NB = WN / 32;
-  constexpr int CPR = BK / 8;                          // 16-byte chunks per LDS row
-  constexpr int RPS = 64 / CPR;                        // rows per 1-KB segment (one load per wave)
-  constexpr int IA = BM / RPS / NW, IB = BN / RPS / NW;  // segments a wave fills per stage
-  constexpr int LPS = IA + IB;
-  constexpr int NO = SWIGLU ? BN / 2 : BN;
-  static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be a multiple of 32");
-  static_assert(!SWIGLU || NB % 2 == 0, "swiglu needs gate/up block pairs");
-  static_assert(IA * NW * RPS == BM && IB * NW * RPS == BN, "segments must divide among waves");
-  static_assert(STAGES >= 2 && STAGES <= 5 && (STAGES - 2) * LPS <= 63, "stage count");
-
-  auto sA = [&](int st) { return smem + st * (BM + BN) * BK; };
-  auto sB = [&](int st) { return smem + st * (BM + BN) * BK + BM * BK; };
-
-  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = wave / WGN, wn = wave % WGN;
-
-  // lane q of 1-KB segment s holds row RPS*s + q/CPR at physical chunk q%CPR,
-  // which stores logical chunk (q%CPR) ^ key(row) (the swizzle is an XOR, so
-  // the same map in both directions). The key reads row bits 1..3, and every
-  // segment this wave fills starts at a row congruent to wave*RPS modulo 16,
-  // so one chunk per lane serves all of its loads.
-  static_assert((NW * RPS) % 16 == 0 && (BN / 2) % 16 == 0, "segment rows must keep the swizzle key");
-  const int lrow = lane / CPR;
-  const int lchunk = (lane % CPR) ^ swz_key<BK>(wave * RPS + lrow);
-  uint32_t aoff[IA];
-#pragma unroll
-  for (int i = 0; i < IA; ++i) {
-    const int r = (i * NW + wave) * RPS + lrow;
-    const bool v = r < tp.ti.rows;
-    int src = tp.ti.row0 + r;
-    if (GATHER) src = v ? p.row_token[src] : 0;
-    aoff[i] = v ? static_cast<uint32_t>(src) * static_cast<uint32_t>(p.lda) * 2u + lchunk * 16u : kOOB;
-  }
+// The loads of one output tile: per-lane byte offsets of the tile's A and B
+// rows and the wave-uniform buffer descriptors, and one K step's loads
+// straight into an LDS stage.
+//
+// Lane q of 1-KB segment s holds row RPS*s + q/CPR at physical chunk q%CPR,
+// which stores logical chunk (q%CPR) ^ key(row) (the swizzle is an XOR, so
+// the same map in both directions). The key reads row bits 1..3, and every
+// segment a wave fills starts at a row congruent to wave*RPS modulo 16, so
+// one chunk per lane serves all of its loads.
+template <int BM, int BN, int WGM, int WGN, int BK, bool SWIGLU, bool GATHER>
+struct TileLoader {
+  static constexpr int NW = WGM * WGN;
+  static constexpr int CPR = BK / 8;                          // 16-byte chunks per LDS row
+  static constexpr int RPS = 64 / CPR;                        // rows per 1-KB segment (one load per wave)
+  static constexpr int IA = BM / RPS / NW, IB = BN / RPS / NW;  // segments a wave fills per stage
+  static constexpr int LPS = IA + IB;
+  static constexpr int NO = SWIGLU ? BN / 2 : BN;
   // B segment of load i: for swiglu the first IB/2 loads of every wave fill
   // gate rows [0, BN/2) and the rest the matching up rows, so the weight
   // matrix of each load is known at compile time
-  constexpr int IBH = SWIGLU ? IB / 2 : IB;
+  static constexpr int IBH = SWIGLU ? IB / 2 : IB;
+  static_assert(IA * NW * RPS == BM && IB * NW * RPS == BN, "segments must divide among waves");
+  static_assert((NW * RPS) % 16 == 0 && (BN / 2) % 16 == 0, "segment rows must keep the swizzle key");
   static_assert(!SWIGLU || IB % 2 == 0, "swiglu splits the B loads in halves");
-  uint32_t boff[IB];
-#pragma unroll
-  for (int i = 0; i < IB; ++i) {
-    const int r = ((i % IBH) * NW + wave) * RPS + lrow;  // row within the gate (or plain) block
-    const int f = tp.nt * NO + r;
-    boff[i] = f < p.Nout ? static_cast<uint32_t>(f) * static_cast<uint32_t>(p.ldb) * 2u + lchunk * 16u : kOOB;
-  }
-  const int64_t b_bytes = static_cast<int64_t>(p.Nout) * p.ldb * 2;
-  const __amdgpu_buffer_rsrc_t ra = uniform_rsrc(p.A, p.a_rows * p.lda * 2);
-  const uint16_t* b0 = static_cast<const uint16_t*>(p.B0) + tp.ti.expert * p.b_expert_stride;
-  const uint16_t* b1 = SWIGLU ? static_cast<const uint16_t*>(p.B1) + tp.ti.expert * p.b_expert_stride : b0;
-  const __amdgpu_buffer_rsrc_t rb0 = uniform_rsrc(b0, b_bytes);
-  const __amdgpu_buffer_rsrc_t rb1 = uniform_rsrc(b1, b_bytes);
 
-  // One K step of loads into the LDS stage at (a_dst, b_dst).
-  auto issue = [&](uint16_t* a_dst, uint16_t* b_dst, int kt) {
-    const int kb = tp.kb0 + kt * BK;
-    const bool kval = kb + lchunk * 8 < tp.kb1;
+  uint32_t aoff[IA], boff[IB];
+  __amdgpu_buffer_rsrc_t ra, rb0, rb1;
+  int wave, lchunk, kb0, kb1;
+
+  __device__ __forceinline__ void init(const GemmParams& p, const TilePos& tp) {
+    const int lane = threadIdx.x & 63;
+    wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lrow = lane / CPR;
+    lchunk = (lane % CPR) ^ swz_key<BK>(wave * RPS + lrow);
+    kb0 = tp.kb0;
+    kb1 = tp.kb1;
+#pragma unroll
+    for (int i = 0; i < IA; ++i) {
+      const int r = (i * NW + wave) * RPS + lrow;
+      const bool v = r < tp.ti.rows;
+      int src = tp.ti.row0 + r;
+      if (GATHER) src = v ? p.row_token[src] : 0;
+      aoff[i] = v ? static_cast<uint32_t>(src) * static_cast<uint32_t>(p.lda) * 2u + lchunk * 16u : kOOB;
+    }
+#pragma unroll
+    for (int i = 0; i < IB; ++i) {
+      const int r = ((i % IBH) * NW + wave) * RPS + lrow;  // row within the gate (or plain) block
+      const int f = tp.nt * NO + r;
+      boff[i] = f < p.Nout ? static_cast<uint32_t>(f) * static_cast<uint32_t>(p.ldb) * 2u + lchunk * 16u : kOOB;
+    }
+    const int64_t b_bytes = static_cast<int64_t>(p.Nout) * p.ldb * 2;
+    ra = uniform_rsrc(p.A, p.a_rows * p.lda * 2);
+    const uint16_t* b0 = static_cast<const uint16_t*>(p.B0) + tp.ti.expert * p.b_expert_stride;
+    const uint16_t* b1 = SWIGLU ? static_cast<const uint16_t*>(p.B1) + tp.ti.expert * p.b_expert_stride : b0;
+    rb0 = uniform_rsrc(b0, b_bytes);
+    rb1 = uniform_rsrc(b1, b_bytes);
+  }
+
+  // K step kt's A rows into the LDS stage at a_dst
+  __device__ __forceinline__ void issue_a(uint16_t* a_dst, int kt) const {
+    const int kb = kb0 + kt * BK;
+    const bool kval = kb + lchunk * 8 < kb1;
     const uint32_t kbyte = static_cast<uint32_t>(kb) * 2u;
 #pragma unroll
     for (int i = 0; i < IA; ++i) {
       const uint32_t vo = (kval && aoff[i] != kOOB) ? aoff[i] + kbyte : kOOB;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(a_dst + (i * NW + wave) * 512), 16, vo, 0, 0, 0);
     }
+  }
+
+  // K step kt's B rows into the LDS stage at b_dst
+  __device__ __forceinline__ void issue_b(uint16_t* b_dst, int kt) const {
+    const int kb = kb0 + kt * BK;
+    const bool kval = kb + lchunk * 8 < kb1;
+    const uint32_t kbyte = static_cast<uint32_t>(kb) * 2u;
 #pragma unroll
     for (int i = 0; i < IB; ++i) {
       const uint32_t vo = (kval && boff[i] != kOOB) ? boff[i] + kbyte : kOOB;
@@ -386,6 +391,57 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const TilePos& tp
       else
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rb1, (lds_ptr_t)(b_dst + seg * 512), 16, vo, 0, 0, 0);
     }
+  }
+};
+
+// LDS stage addresses of the operand stages in `smem`.
+template <int BM, int BN, int BK>
+__device__ __forceinline__ uint16_t* stage_a(uint16_t* smem, int st) { return smem + st * (BM + BN) * BK; }
+template <int BM, int BN, int BK>
+__device__ __forceinline__ uint16_t* stage_b(uint16_t* smem, int st) { return smem + st * (BM + BN) * BK + BM * BK; }
+
+// Nothing to do during or after the K loop.
+struct NoHook {
+  __device__ __forceinline__ void operator()(uint16_t*, uint16_t*, int) const {}
+};
+struct NoReserve {
+  __device__ __forceinline__ void operator()() const {}
+};
+
+// One output tile with buffer loads straight into LDS: the operand stages
+// live in `smem` (dma_lds_elems elements, one LDS object). The caller makes
+// sure no wave still reads `smem` from an earlier tile.
+//
+// K step kt uses stage buffer (sbase + kt) % STAGES. pre says how much of
+// step 0 an earlier call already issued into buffer sbase: 0 nothing, 1 the B
+// rows, 2 A and B. reserve() runs three K steps before the end (at step 0 of
+// a shorter tile); after the MFMAs of the last K step are issued, hook(a, b,
+// buf) may issue loads into stage buffer buf (at a, b), which no wave reads
+// any more; the epilogue follows.
+template <int BM, int BN, int WGM, int WGN, int STAGES, int BK, bool SWIGLU, bool GATHER, class Hook = NoHook,
+          class Reserve = NoReserve>
+__device__ __forceinline__ void gemm_tile(const GemmParams& p, const TilePos& tp, uint16_t* smem, int sbase = 0,
+                                          int pre = 0, Hook&& hook = Hook{}, Reserve&& reserve = Reserve{}) {
+  using Loader = TileLoader<BM, BN, WGM, WGN, BK, SWIGLU, GATHER>;
+  constexpr int WM = BM / WGM, WN = BN / WGN;
+  constexpr int MB = WM / 32, NB = WN / 32;
+  constexpr int LPS = Loader::LPS;
+  constexpr int NO = Loader::NO;
+  static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be a multiple of 32");
+  static_assert(!SWIGLU || NB % 2 == 0, "swiglu needs gate/up block pairs");
+  static_assert(STAGES >= 2 && STAGES <= 5 && (STAGES - 2) * LPS <= 63, "stage count");
+
+  auto sA = [&](int st) { return stage_a<BM, BN, BK>(smem, st); };
+  auto sB = [&](int st) { return stage_b<BM, BN, BK>(smem, st); };
+
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave / WGN, wn = wave % WGN;
+
+  Loader ld;
+  ld.init(p, tp);
+  auto issue = [&](uint16_t* a_dst, uint16_t* b_dst, int kt) {
+    ld.issue_a(a_dst, kt);
+    ld.issue_b(b_dst, kt);
   };
 
   f32x16_t acc[MB][NB];
@@ -396,17 +452,23 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const TilePos& tp
   // 32-row blocks of this wave that hold rows of the tile
   const int live = __builtin_amdgcn_readfirstlane(max(0, min(MB, (tp.ti.rows - wm * WM + 31) / 32)));
 
+  if (tp.KT > 0) {
+    if (pre < 2) ld.issue_a(sA(sbase), 0);
+    if (pre < 1) ld.issue_b(sB(sbase), 0);
+  }
 #pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s)
-    if (s < tp.KT) issue(sA(s), sB(s), s);
+  for (int s = 1; s < STAGES - 1; ++s)
+    if (s < tp.KT) issue(sA((sbase + s) % STAGES), sB((sbase + s) % STAGES), s);
   // the K loop, in a branch-free copy for full tiles and one that skips a
   // partly filled tile's empty row blocks
+  const int kt_reserve = max(0, tp.KT - 3);
   auto kloop = [&](auto partial) {
     for (int kt = 0; kt < tp.KT; ++kt) {
       const int later = min(STAGES - 2, tp.KT - 1 - kt);
       wait_stage<LPS, STAGES - 2>(later);
       lds_barrier();  // stage kt is complete for every wave; stage kt-1 is free
-      const int st = kt % STAGES, nx = (kt + STAGES - 1) % STAGES;
+      if (kt == kt_reserve) reserve();
+      const int st = (sbase + kt) % STAGES, nx = (sbase + kt + STAGES - 1) % STAGES;
       dma_step<MB, NB, BK, decltype(partial)::value>(issue, kt + STAGES - 1 < tp.KT, kt + STAGES - 1, sA(st), sB(st),
                                                      sA(nx), sB(nx), arow, brow, khalf, acc, live);
     }
@@ -415,6 +477,8 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const TilePos& tp
     kloop(std::false_type{});
   else
     kloop(std::true_type{});
+  const int fb = (sbase + tp.KT) % STAGES;
+  hook(sA(fb), sB(fb), fb);
   epilogue<WM, WN, MB, NB, SWIGLU>(p, tp, wm, wn, lane, NO, acc);
 }
 
@@ -509,24 +573,75 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_experts_fused(FusedParams fp
   const int G = gridDim.x;
   const int S = min(n1, G);  // tickets below S are remapped XCD-aware
 
-  for (;;) {
-    __syncthreads();  // every wave is done with the LDS stages and the last item
-    if (threadIdx.x == 0) *s_item = atomicAdd(&fp.sched[kSchedTicket], 1);
-    __syncthreads();
-    const int ticket = __builtin_amdgcn_readfirstlane(*s_item);
-    if (ticket >= ntot) break;
-    const int it = ticket < S ? xcd_remap(ticket, S) : ticket;
-    TilePos tp{};
+  // tile of ticket t: gate/up (returns true) or down, its row block and position
+  auto decode = [&](int t, TilePos& tp, int& rb) {
+    const int it = t < S ? xcd_remap(t, S) : t;
+    tp = TilePos{};
     if (it < n1) {
       const int g = it / (GM * NT1);
       const int gm = min(GM, RB - g * GM);
       const int r_in = it - g * GM * NT1;
-      const int rb = g * GM + r_in % gm;
+      rb = g * GM + r_in % gm;
       tp.nt = r_in / gm;
       tp.ti = row_block<BM>(rb, eoff, ecnt, etl, incl);
       tp.kb1 = g1.K;
       tp.KT = (g1.K + BK - 1) / BK;
-      gemm_tile<BM, BN, WGM, WGN, STAGES, BK, true, GATHER>(g1, tp, smem);
+      return true;
+    }
+    const int j = it - n1;
+    rb = j / NT2;
+    tp.nt = j % NT2;
+    tp.ti = row_block<BM>(rb, eoff, ecnt, etl, incl);
+    tp.kb1 = g2.K;
+    tp.KT = (g2.K + BK - 1) / BK;
+    return false;
+  };
+
+  if (threadIdx.x == 0) *s_item = atomicAdd(&fp.sched[kSchedTicket], 1);
+  __syncthreads();
+  int ticket = __builtin_amdgcn_readfirstlane(*s_item);
+  int sbase = 0, pre = 0;  // stage buffer of K step 0, and how much of it is already loading
+  while (ticket < ntot) {
+    // The next ticket is reserved three K steps before this tile ends (late
+    // enough that the queue still balances the tail, early enough that the
+    // atomic's latency hides); it reaches the workgroup after the K loop,
+    // where the hook issues the next tile's first stage into the free stage
+    // buffer: all of it for a gate/up tile, only the weights for a down tile,
+    // whose h rows may not be ready. A reserved ticket is larger than the
+    // running one, so a workgroup that waits in a down tile holds only down
+    // tickets: every gate/up ticket still runs in or is reserved by a
+    // workgroup that waits on nothing.
+    int reserved = ntot;  // "none" unless reserve() runs
+    auto reserve = [&]() {
+      if (threadIdx.x == 0) reserved = atomicAdd(&fp.sched[kSchedTicket], 1);
+    };
+    int next = ntot, nsbase = 0, npre = 0;
+    auto hook = [&](uint16_t* a_free, uint16_t* b_free, int fb) {
+      if (threadIdx.x == 0) *s_item = reserved;
+      __syncthreads();
+      next = __builtin_amdgcn_readfirstlane(*s_item);
+      if (next < ntot) {
+        TilePos tq;
+        int rq;
+        if (decode(next, tq, rq)) {
+          TileLoader<BM, BN, WGM, WGN, BK, true, GATHER> lq;
+          lq.init(g1, tq);
+          lq.issue_a(a_free, 0);
+          lq.issue_b(b_free, 0);
+          npre = 2;
+        } else {
+          TileLoader<BM, BN, WGM, WGN, BK, false, false> lq;
+          lq.init(g2, tq);
+          lq.issue_b(b_free, 0);
+          npre = 1;
+        }
+        nsbase = fb;
+      }
+    };
+    TilePos tp;
+    int rb;
+    if (decode(ticket, tp, rb)) {
+      gemm_tile<BM, BN, WGM, WGN, STAGES, BK, true, GATHER>(g1, tp, smem, sbase, pre, hook, reserve);
       // publish: every wave's h stores complete, then one device-scope
       // release (a single write-back) before the count
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
@@ -536,19 +651,16 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_experts_fused(FusedParams fp
         __hip_atomic_fetch_add(&fp.sched[kSchedDone + rb], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     } else {
-      const int j = it - n1;
-      const int rb = j / NT2;
-      tp.nt = j % NT2;
       if (threadIdx.x == 0) {
         wait_count(&fp.sched[kSchedDone + rb], NT1, &fp.sched[kSchedError]);
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       }
       __syncthreads();
-      tp.ti = row_block<BM>(rb, eoff, ecnt, etl, incl);
-      tp.kb1 = g2.K;
-      tp.KT = (g2.K + BK - 1) / BK;
-      gemm_tile<BM, BN, WGM, WGN, STAGES, BK, false, false>(g2, tp, smem);
+      gemm_tile<BM, BN, WGM, WGN, STAGES, BK, false, false>(g2, tp, smem, sbase, pre, hook, reserve);
     }
+    ticket = next;
+    sbase = nsbase;
+    pre = npre;
   }
 }
 
