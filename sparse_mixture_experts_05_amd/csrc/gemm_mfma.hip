@@ -435,7 +435,10 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const TilePos& tp
   auto sB = [&](int st) { return stage_b<BM, BN, BK>(smem, st); };
 
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = wave / WGN, wn = wave % WGN;
+  // wave w takes row group w % WGM and column group w / WGM: the waves that
+  // share a SIMD (w and w + 4) cover different column groups, so a tile whose
+  // last columns lie past Nout still gives every SIMD the same MFMA work
+  const int wm = wave % WGM, wn = wave / WGM;
 
   Loader ld;
   ld.init(p, tp);
@@ -449,8 +452,11 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const TilePos& tp
   int arow[MB], brow[NB];
   frag_rows<WM, WN, MB, NB, BN, SWIGLU>(wm, wn, lane, arow, brow);
   const int khalf = lane >> 5;
-  // 32-row blocks of this wave that hold rows of the tile
-  const int live = __builtin_amdgcn_readfirstlane(max(0, min(MB, (tp.ti.rows - wm * WM + 31) / 32)));
+  // 32-row blocks of this wave that hold rows of the tile; none when all of
+  // the wave's output columns lie past Nout (an expert's last column tile)
+  const bool cols_dead = tp.nt * NO + wn * (SWIGLU ? WN / 2 : WN) >= p.Nout;
+  const int live =
+      cols_dead ? 0 : __builtin_amdgcn_readfirstlane(max(0, min(MB, (tp.ti.rows - wm * WM + 31) / 32)));
 
   if (tp.KT > 0) {
     if (pre < 2) ld.issue_a(sA(sbase), 0);
