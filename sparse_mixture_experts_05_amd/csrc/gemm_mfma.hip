@@ -554,7 +554,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_experts_fused(FusedParams fp
   // the operand stages and, after them, the broadcast work item: one LDS object
   __shared__ __attribute__((aligned(16))) uint16_t smem[kElems + 8];
   int* s_item = reinterpret_cast<int*>(smem + kElems);
-  constexpr int GM = 4;  // row blocks per group of gate/up tiles
+  constexpr int GM = 8;  // most row blocks per group of gate/up tiles
   const GemmParams& g1 = fp.g1;
   const GemmParams& g2 = fp.g2;
   const int lane = threadIdx.x & 63;
@@ -584,11 +584,23 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_experts_fused(FusedParams fp
     const int it = t < S ? xcd_remap(t, S) : t;
     tp = TilePos{};
     if (it < n1) {
-      const int g = it / (GM * NT1);
-      const int gm = min(GM, RB - g * GM);
-      const int r_in = it - g * GM * NT1;
-      rb = g * GM + r_in % gm;
-      tp.nt = r_in / gm;
+      // gate/up tiles go expert by expert, in groups of at most GM of the
+      // expert's row blocks (split evenly), column tile by column tile with the
+      // row block fastest: the tiles of a group share their weight panels, and
+      // an expert's last, partly filled row block rides along with the others
+      const int e = __popcll(__ballot(incl * NT1 <= it));  // expert of the tile
+      const int rb0 = __builtin_amdgcn_readfirstlane(__shfl(incl - etl, e, 64));
+      const int R = __builtin_amdgcn_readfirstlane(__shfl(etl, e, 64));
+      const int ng = (R + GM - 1) / GM, base = R / ng, extra = R % ng;
+      int q = it - rb0 * NT1;  // tile within the expert
+      int g0 = 0, gm = base + (extra > 0 ? 1 : 0);
+      for (int g = 0; q >= gm * NT1; ++g) {  // find the group (ng is small)
+        q -= gm * NT1;
+        g0 += gm;
+        gm = base + (g + 1 < extra ? 1 : 0);
+      }
+      rb = rb0 + g0 + q % gm;
+      tp.nt = q / gm;
       tp.ti = row_block<BM>(rb, eoff, ecnt, etl, incl);
       tp.kb1 = g1.K;
       tp.KT = (g1.K + BK - 1) / BK;
