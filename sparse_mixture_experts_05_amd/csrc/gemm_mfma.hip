@@ -506,16 +506,17 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm_dma(GemmParams p) {
 // projection is NT2 tiles, and those read every column of the row block's h,
 // so they may start only once all NT1 gate/up tiles of that row block are
 // done. Workgroups stay resident and take work items from one queue in
-// ticket order: first every gate/up tile (grouped GM row blocks at a time, as
-// in the separate launch), then the down tiles in row-block order, so the
-// down tiles of the first row blocks fill the compute units that the last
+// ticket order: first every gate/up tile (expert by expert, a group of the
+// expert's row blocks at a time), then the down tiles in row-block order, so
+// the down tiles of the first row blocks fill the compute units that the last
 // round of gate/up tiles leaves idle. The first tickets are remapped as the
 // separate launch remaps blockIdx: workgroups start in dispatch order, dealt
 // round-robin to the 8 XCDs, so the first round's tiles that share weight
 // panels land on one XCD and its L2. A down tile waits, with a bounded spin,
 // on its row block's count of finished gate/up tiles; all gate/up tickets
-// come before any down ticket, so every tile it waits on is already held by
-// a running workgroup that waits on nothing, and the wait always ends.
+// come before any down ticket, so every tile it waits on is already running
+// in, or reserved by, a workgroup that waits on nothing, and the wait always
+// ends.
 
 constexpr int kSchedTicket = 0;     // sched[kSchedTicket]: next ticket
 constexpr int kSchedError = 8;      // sched[kSchedError] = 1 if a wait gave up
