@@ -27,6 +27,7 @@
 //                through the buffer's range check, without branches.
 //   k_gemm_reg : global loads into registers, then LDS stores, two buffers.
 #include "common.h"
+#include "stats.h"
 #include "kernels.h"
 
 #include <type_traits>
@@ -681,6 +682,9 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_experts_fused(FusedParams fp
     sbase = nsbase;
     pre = npre;
   }
+  // the workgroup that drew the first ticket past the end reduces the router
+  // statistics, in LDS that no tile uses any more
+  if (fp.stats && ticket == ntot) stats_reduce(fp.st, smem);
 }
 
 // ---- register-staged loads -------------------------------------------------------

@@ -119,6 +119,8 @@ hipError_t launch_gemm_simple(const GemmParams& p, int bf16, hipStream_t s);
 struct FusedParams {
   GemmParams g1, g2;
   int32_t* sched;
+  StatsParams st;  // router statistics, reduced once the queue is empty
+  int stats;       // 1: reduce them (in the workgroup that draws the first ticket past the end)
 };
 int fused_sched_ints(int64_t rows_max, int N);
 bool gemm_fused_supported(int64_t rows_max, int N, int K1, int F);

@@ -161,10 +161,12 @@ moe_status zero_expert_outputs(const moe_cfg* c, int32_t* a, int32_t* b, int32_t
 }
 
 // sched_zeroed: the fused kernel's queue counters were already zeroed on the
-// stream (by the scatter in moe_forward).
+// stream (by the scatter in moe_forward). stats_tail: router statistics for
+// the fused kernel to reduce once its queue is empty (only when L.fused).
 moe_status run_gemms(const moe_cfg* c, const Layout& L, const void* a, const int32_t* row_token,
                      const int32_t* offsets, const void* Wgate, const void* Wup, const void* Wdown, float* y_perm,
-                     int splits, void* ws, bool sched_zeroed, hipStream_t s) {
+                     int splits, void* ws, bool sched_zeroed, hipStream_t s,
+                     const moe::StatsParams* stats_tail = nullptr) {
   const int bf16 = c->act == MOE_BF16;
   moe::GemmParams g1{};
   g1.A = a;
@@ -208,7 +210,7 @@ moe_status run_gemms(const moe_cfg* c, const Layout& L, const void* a, const int
       hipError_t e = moe::launch_fill_i32(sched, moe::fused_sched_ints(L.A_max, c->N), 0, s);
       if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "fill launch failed: %s", hipGetErrorString(e));
     }
-    moe::FusedParams fp{g1, g2, sched};
+    moe::FusedParams fp{g1, g2, sched, stats_tail ? *stats_tail : moe::StatsParams{}, stats_tail ? 1 : 0};
     MOE_LAUNCH(MOE_KERNEL_EXPERTS, s, moe::launch_experts_fused(fp, s));
   } else if (L.mfma) {
     MOE_LAUNCH(MOE_KERNEL_GEMM1, s, moe::launch_gemm_bf16_mfma(g1, s));
@@ -402,18 +404,19 @@ moe_status moe_forward(const moe_cfg* c, const void* x, const float* Wg, const f
   rp.hist = at<int32_t>(ws, L.hist);
   rp.stat_part = stats ? at<float>(ws, L.stat) : nullptr;
   MOE_LAUNCH(MOE_KERNEL_ROUTER, s, moe::launch_router(rp, s));
-  if (stats) {
-    moe::StatsParams sp{at<int32_t>(ws, L.hist), at<float>(ws, L.stat), L.hist_blocks, c->T, c->N, c->k,
-                        load_opt, importance_opt, P_opt, balance_opt};
-    MOE_LAUNCH(MOE_KERNEL_STATS, s, moe::launch_stats(sp, s));
-  }
+  // statistics: reduced by the persistent expert kernel once its queue is
+  // empty when that kernel runs, else by a launch of their own
+  const moe::StatsParams sp{at<int32_t>(ws, L.hist), at<float>(ws, L.stat), L.hist_blocks, c->T, c->N, c->k,
+                            load_opt, importance_opt, P_opt, balance_opt};
+  if (stats && !L.fused) MOE_LAUNCH(MOE_KERNEL_STATS, s, moe::launch_stats(sp, s));
   moe::ScatterParams sc{topk_idx, at<int32_t>(ws, L.hist), L.hist_tokens, c->T, c->N, c->k, c->capacity,
                         (!stats && load_opt) ? load_opt : at<int32_t>(ws, L.counts), kept_opt, offsets, slot,
                         row_token, L.fused ? at<int32_t>(ws, L.sched) : nullptr,
                         L.fused ? moe::fused_sched_ints(L.A_max, c->N) : 0};
   MOE_LAUNCH(MOE_KERNEL_SCATTER, s, moe::launch_scatter(sc, s));
   float* y_perm = at<float>(ws, L.yperm);
-  st = run_gemms(c, L, x, row_token, offsets, Wgate, Wup, Wdown, y_perm, L.splits, ws, true, s);
+  st = run_gemms(c, L, x, row_token, offsets, Wgate, Wup, Wdown, y_perm, L.splits, ws, true, s,
+                 stats && L.fused ? &sp : nullptr);
   if (st != MOE_OK) return st;
   moe::CombineParams cp{y_perm, L.A_max * static_cast<int64_t>(c->H), L.splits, slot, topk_w, y,
                         c->out == MOE_BF16, c->T, c->H, c->k, c->out_scale};

@@ -12,6 +12,7 @@
 // sums are written for the permutation and the balance statistics.
 #include "common.h"
 #include "kernels.h"
+#include "stats.h"
 
 namespace moe {
 
@@ -245,75 +246,10 @@ hipError_t launch_router_n(const RouterParams& p, hipStream_t s) {
 
 int nmax_for(int N) { return N <= 8 ? 8 : N <= 16 ? 16 : N <= 32 ? 32 : 64; }
 
-// Fixed-order reduction of the per-block statistics. Group g of kStatGroups
-// (one wave each) sums a contiguous range of router blocks in block order,
-// lane n holding expert n; wave 0 then adds the group partials in group
-// order. The order depends only on the block count, so the result is the same
-// on every run.
-constexpr int kStatGroups = 16;
-
+// The fixed-order statistics reduction (stats.h) in a workgroup of its own.
 __global__ __launch_bounds__(kStatGroups * 64) void k_stats(StatsParams p) {
-  const int n = threadIdx.x & 63, g = threadIdx.x >> 6;
-  const bool valid = n < p.N;
-  const int b0 = static_cast<int>(static_cast<int64_t>(p.blocks) * g / kStatGroups);
-  const int b1 = static_cast<int>(static_cast<int64_t>(p.blocks) * (g + 1) / kStatGroups);
-  __shared__ int64_t s_cnt[kStatGroups][64];
-  __shared__ float s_imp[kStatGroups][64], s_ps[kStatGroups][64];
-  int64_t c = 0;
-  float imp = 0.0f, ps = 0.0f;
-  if (valid) {
-    constexpr int U = 8;  // loads issued together before the in-order adds
-    for (int b = b0; b < b1; b += U) {
-      int hv[U];
-      float iv[U], pv[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int bb = b + u < b1 ? b + u : b;
-        hv[u] = p.hist[static_cast<int64_t>(bb) * p.N + n];
-        iv[u] = p.stat_part[static_cast<int64_t>(bb) * 2 * p.N + 2 * n];
-        pv[u] = p.stat_part[static_cast<int64_t>(bb) * 2 * p.N + 2 * n + 1];
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-        if (b + u < b1) {
-          c += hv[u];
-          imp += iv[u];
-          ps += pv[u];
-        }
-    }
-  }
-  s_cnt[g][n] = c;
-  s_imp[g][n] = imp;
-  s_ps[g][n] = ps;
-  __syncthreads();
-  if (g != 0) return;
-  c = 0;
-  imp = 0.0f;
-  ps = 0.0f;
-#pragma unroll
-  for (int q = 0; q < kStatGroups; ++q) {
-    c += s_cnt[q][n];
-    imp += s_imp[q][n];
-    ps += s_ps[q][n];
-  }
-  const float load = static_cast<float>(c);
-  if (valid && p.load) p.load[n] = static_cast<int32_t>(c);
-  const float Pn = p.T > 0 ? ps / static_cast<float>(p.T) : 0.0f;
-  const float fn = p.T > 0 ? load / (static_cast<float>(p.T) * static_cast<float>(p.k)) : 0.0f;
-  // balance = sum_i f_i P_i, summed in expert order by lane 0
-  __shared__ float fp[64];
-  fp[n] = valid ? fn * Pn : 0.0f;
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  if (valid) {
-    if (p.importance) p.importance[n] = imp;
-    if (p.P) p.P[n] = Pn;
-  }
-  if (n == 0 && p.balance) {
-    float b = 0.0f;
-    for (int i = 0; i < p.N; ++i) b += fp[i];
-    p.balance[0] = b;
-  }
+  __shared__ __attribute__((aligned(16))) char s_lds[kStatLdsBytes];
+  stats_reduce(p, s_lds);
 }
 
 __global__ void k_fill_i32(int32_t* p, int64_t n, int32_t v) {
