@@ -26,6 +26,8 @@
 //                the expert's segment and K past the range read as zero
 //                through the buffer's range check, without branches.
 //   k_gemm_reg : global loads into registers, then LDS stores, two buffers.
+// and k_experts_fused runs both projections of every expert in one persistent
+// launch on the k_gemm_dma tile (see the scheduling comment above it).
 #include "common.h"
 #include "stats.h"
 #include "kernels.h"
