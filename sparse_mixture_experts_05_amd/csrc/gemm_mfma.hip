@@ -20,14 +20,13 @@
 // row (see swz), which keeps both the row-wise global->LDS writes and the
 // column-wise MFMA operand reads free of bank conflicts.
 //
-// Two load paths share the tile order and the epilogue:
-//   k_gemm_dma : buffer loads straight into LDS (no register staging), STAGES
-//                deep, so several K steps of loads stay in flight; rows past
-//                the expert's segment and K past the range read as zero
-//                through the buffer's range check, without branches.
-//   k_gemm_reg : global loads into registers, then LDS stores, two buffers.
-// and k_experts_fused runs both projections of every expert in one persistent
-// launch on the k_gemm_dma tile (see the scheduling comment above it).
+// Loads go straight from buffer loads into LDS (no register staging), STAGES
+// deep, so several K steps of loads stay in flight; rows past the expert's
+// segment and K past the range read as zero through the buffer's range check,
+// without branches. k_gemm_dma runs one tile per workgroup (the decode-shaped
+// 32 x 256 tile with four stages, or 256 x 256 with two), and k_experts_fused
+// runs both projections of every expert in one persistent launch on the same
+// tile code (see the scheduling comment above it).
 #include "common.h"
 #include "stats.h"
 #include "kernels.h"
@@ -38,7 +37,6 @@ namespace moe {
 
 namespace {
 
-constexpr int kBKReg = 64;                   // K step of the register-staged kernel
 constexpr uint32_t kOOB = 0xFFFFFFF0u;       // byte offset past any buffer: loads return zero
 constexpr int kBufferFlags = 0x00020000;     // raw buffer, 32-bit data
 
@@ -691,121 +689,11 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_experts_fused(FusedParams fp
 
 // ---- register-staged loads -------------------------------------------------------
 
-template <int BM, int BN, int WGM, int WGN, bool SWIGLU, bool GATHER>
-__global__ __launch_bounds__(WGM * WGN * 64) void k_gemm_reg(GemmParams p) {
-  constexpr int NT = WGM * WGN * 64;
-  constexpr int WM = BM / WGM, WN = BN / WGN;
-  constexpr int MB = WM / 32, NB = WN / 32;
-  constexpr int CA = BM * 8 / NT, CB = BN * 8 / NT;  // 16-byte chunks per thread per K step
-  constexpr int NO = SWIGLU ? BN / 2 : BN;
-  static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be a multiple of 32");
-  static_assert(!SWIGLU || NB % 2 == 0, "swiglu needs gate/up block pairs");
-  static_assert(CA >= 1 && CB >= 1 && (BM * 8) % NT == 0 && (BN * 8) % NT == 0, "load split");
-
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * kBKReg];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[2][BN * kBKReg];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave / WGN, wn = wave % WGN;
-  TilePos tp;
-  if (!decode_tile<BM, NO, kBKReg>(p, tp)) return;
-
-  const uint16_t* __restrict__ Ab = static_cast<const uint16_t*>(p.A);
-  int aoff[CA], achunk[CA];
-  bool aval[CA];
-#pragma unroll
-  for (int i = 0; i < CA; ++i) {
-    const int ci = tid + i * NT;
-    const int r = ci >> 3;
-    achunk[i] = ci & 7;
-    aval[i] = r < tp.ti.rows;
-    int src = tp.ti.row0 + r;
-    if (GATHER) src = aval[i] ? p.row_token[src] : 0;
-    aoff[i] = (aval[i] ? src : 0) * static_cast<int>(p.lda) + achunk[i] * 8;
-  }
-  const uint16_t* __restrict__ B0 = static_cast<const uint16_t*>(p.B0) + tp.ti.expert * p.b_expert_stride;
-  const uint16_t* __restrict__ B1 =
-      SWIGLU ? static_cast<const uint16_t*>(p.B1) + tp.ti.expert * p.b_expert_stride : nullptr;
-  int boff[CB], bchunk[CB];
-  bool bval[CB], bup[CB];
-#pragma unroll
-  for (int i = 0; i < CB; ++i) {
-    const int ci = tid + i * NT;
-    const int r = ci >> 3;
-    bchunk[i] = ci & 7;
-    bup[i] = SWIGLU && r >= BN / 2;
-    const int f = tp.nt * NO + (bup[i] ? r - BN / 2 : r);
-    bval[i] = f < p.Nout;
-    boff[i] = (bval[i] ? f : 0) * static_cast<int>(p.ldb) + bchunk[i] * 8;
-  }
-
-  u32x4_t ra[CA], rb[CB];
-  auto gload = [&](int kt) {
-    const int kb = tp.kb0 + kt * kBKReg;
-#pragma unroll
-    for (int i = 0; i < CA; ++i) {
-      const int kk = kb + achunk[i] * 8;
-      if (aval[i] && kk < tp.kb1) ra[i] = *reinterpret_cast<const u32x4_t*>(Ab + aoff[i] + kb);
-      else ra[i] = u32x4_t{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int i = 0; i < CB; ++i) {
-      const int kk = kb + bchunk[i] * 8;
-      const uint16_t* bb = bup[i] ? B1 : B0;
-      if (bval[i] && kk < tp.kb1) rb[i] = *reinterpret_cast<const u32x4_t*>(bb + boff[i] + kb);
-      else rb[i] = u32x4_t{0u, 0u, 0u, 0u};
-    }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < CA; ++i)
-      *reinterpret_cast<u32x4_t*>(&sA[buf][swz<kBKReg>((tid + i * NT) >> 3, achunk[i])]) = ra[i];
-#pragma unroll
-    for (int i = 0; i < CB; ++i)
-      *reinterpret_cast<u32x4_t*>(&sB[buf][swz<kBKReg>((tid + i * NT) >> 3, bchunk[i])]) = rb[i];
-  };
-
-  f32x16_t acc[MB][NB];
-  zero_acc(acc);
-  int arow[MB], brow[NB];
-  frag_rows<WM, WN, MB, NB, BN, SWIGLU>(wm, wn, lane, arow, brow);
-  const int khalf = lane >> 5;
-
-  if (tp.KT > 0) {
-    gload(0);
-    lstore(0);
-  }
-  __syncthreads();
-  for (int kt = 0; kt < tp.KT; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < tp.KT) gload(kt + 1);
-    mma_stage<MB, NB, kBKReg>(sA[cur], sB[cur], arow, brow, khalf, acc);
-    if (kt + 1 < tp.KT) lstore(cur ^ 1);
-    __syncthreads();
-  }
-  epilogue<WM, WN, MB, NB, SWIGLU>(p, tp, wm, wn, lane, NO, acc);
-}
-
 int64_t grid_blocks(const GemmParams& p, int BM, int BN) {
   const int NO = p.swiglu ? BN / 2 : BN;
   const int64_t ntiles = (p.Nout + NO - 1) / NO;
   const int64_t mtiles = (p.rows_max + BM - 1) / BM + p.N;
   return ntiles * mtiles * p.splits;
-}
-
-template <int BM, int BN, int WGM, int WGN>
-hipError_t launch_reg(const GemmParams& p, hipStream_t s) {
-  const int64_t blocks = grid_blocks(p, BM, BN);
-  if (blocks <= 0) return hipSuccess;
-  const dim3 grid(static_cast<unsigned>(blocks)), block(WGM * WGN * 64);
-  if (p.swiglu) {
-    if (p.row_token) hipLaunchKernelGGL((k_gemm_reg<BM, BN, WGM, WGN, true, true>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((k_gemm_reg<BM, BN, WGM, WGN, true, false>), grid, block, 0, s, p);
-  } else {
-    if (p.row_token) hipLaunchKernelGGL((k_gemm_reg<BM, BN, WGM, WGN, false, true>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((k_gemm_reg<BM, BN, WGM, WGN, false, false>), grid, block, 0, s, p);
-  }
-  return hipGetLastError();
 }
 
 template <int BM, int BN, int WGM, int WGN, int STAGES, int BK>
@@ -868,7 +756,7 @@ hipError_t launch_experts_fused(const FusedParams& fp, hipStream_t s) {
 hipError_t launch_gemm_bf16_mfma(const GemmParams& p, hipStream_t s) {
   int bm, bn;
   gemm_bf16_mfma_tile(p.rows_max, p.N, &bm, &bn);
-  if (bm == 32) return launch_reg<32, 256, 1, 4>(p, s);
+  if (bm == 32) return launch_dma<32, 256, 1, 4, 4, 64>(p, s);
   return launch_dma<256, 256, 4, 2, 2, 64>(p, s);
 }
 
