@@ -57,6 +57,21 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
   return lane == 0 ? 0ull : (~0ull >> (64 - lane));
 }
 
+constexpr uint32_t kOOB = 0xFFFFFFF0u;    // byte offset past any buffer: loads return zero
+constexpr int kBufferFlags = 0x00020000;  // raw buffer, 32-bit data
+
+// A wave-uniform buffer descriptor: the base address passes through
+// readfirstlane so the descriptor lives in scalar registers (a descriptor in
+// vector registers makes every load a per-lane loop).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* base, int64_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
+  void* p = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
+  const int num = __builtin_amdgcn_readfirstlane(static_cast<int>(bytes < 0x7FFFFFF0 ? bytes : 0x7FFFFFF0));
+  return __builtin_amdgcn_make_buffer_rsrc(p, 0, num, kBufferFlags);
+}
+
 struct TileInfo {
   int expert;
   int row0;   // first permuted row of the tile

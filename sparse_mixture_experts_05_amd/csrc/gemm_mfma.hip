@@ -37,8 +37,6 @@ namespace moe {
 
 namespace {
 
-constexpr uint32_t kOOB = 0xFFFFFFF0u;       // byte offset past any buffer: loads return zero
-constexpr int kBufferFlags = 0x00020000;     // raw buffer, 32-bit data
 
 // Element offset of 16-byte chunk `chunk` of LDS row `row`. The LDS serves a
 // 16-byte read (ds_read_b128) for 16 lanes at a time over 64 four-byte banks
@@ -175,18 +173,6 @@ __device__ __forceinline__ void mma_stage(const uint16_t* __restrict__ a, const 
         for (int j = 0; j < NB; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][i], bfr[cur][j], acc[i][j], 0, 0, 0);
   }
-}
-
-// A wave-uniform buffer descriptor: the base address passes through
-// readfirstlane so the descriptor lives in scalar registers (a descriptor in
-// vector registers makes every load a per-lane loop).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* base, int64_t bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
-  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
-  void* p = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
-  const int num = __builtin_amdgcn_readfirstlane(static_cast<int>(bytes < 0x7FFFFFF0 ? bytes : 0x7FFFFFF0));
-  return __builtin_amdgcn_make_buffer_rsrc(p, 0, num, kBufferFlags);
 }
 
 // Accumulator layout of a 32x32 block: lane holds column (lane & 31) and rows

@@ -10,78 +10,110 @@
 // each cover a share of H, which keeps the accumulated rounding error near
 // that of a plain fp32 dot product.
 //
-// A block owns 16 tokens. It walks H in chunks: the chunk's fp32 weight rows
-// are copied into LDS with coalesced loads (issued together with the x loads),
-// and each lane reads its eight operand values per K step from LDS and splits
-// them in registers. After the product, one wave per token applies the
-// noise term, KeepTopK by k rounds of a wave-wide argmax (ties to the lower
-// expert index; "Llama 3 Meets MoE" review, section 3) and the gate of the
-// chosen order (Mixtral: softmax over the kept scores; ST: softmax over all
-// scores, section 5); threads of the block then sum the per-expert counts,
-// gate weights and softmax(logit) values over the block's tokens in token
-// order for the permutation and the balance statistics.
+// A block owns 16 tokens and walks H in chunks through two LDS buffers: while
+// the waves split and multiply chunk c, the fp32 weight rows and x of chunk
+// c + 1 are in flight, and they are written to the other buffer (transposed,
+// so that a lane reads its eight operand values of one column with two
+// 16-byte reads) before the barrier that ends the chunk.
+//
+// With at most 8 router columns, half the 16 columns of the MFMA B operand
+// would be zero, so they are "folded": columns 8..15 carry the same 8 router
+// columns for the next 32 rows of H, and the A rows 8..15 carry the same 8
+// tokens at those rows. The diagonal 8 x 8 blocks of the product are the two
+// halves of the dot products; the off-diagonal blocks are not used. Every
+// lane then splits weight values that are used, which halves the splitting
+// work per row of H.
+//
+// After the product, one wave per token applies the noise term, KeepTopK and
+// the gate of the chosen order: a lane's rank is the number of experts with a
+// larger score, or an equal score and a lower index ("Llama 3 Meets MoE"
+// review, section 3: ties to the lower expert index), and the experts of rank
+// < k are kept in rank order (Mixtral: softmax over the kept scores; ST:
+// softmax over all scores, section 5). Threads of the block then sum the
+// per-expert counts, gate weights and softmax(logit) values over the block's
+// tokens in token order for the permutation and the balance statistics.
 #include "common.h"
 #include "kernels.h"
 
 #include <algorithm>
 
 typedef float f32x4_mma_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 namespace moe {
 
 namespace {
 
-constexpr int kTok = 16;    // tokens per block (M of the MFMA)
-// waves per block, each over 1/W of H: more waves for fewer output columns
-// (shorter dependent load chains per wave), fewer when the partial sums of
-// every wave would not fit in LDS
+constexpr int kTok = 16;  // tokens per block (M of the MFMA)
+// waves per block, each over 1/W of a chunk's rows: more waves for fewer
+// output columns, fewer when the partial sums of every wave would not fit
 template <int NB16>
 constexpr int router_waves() { return NB16 <= 2 ? 16 : (NB16 <= 4 ? 8 : 4); }
 
-constexpr int kWFloats = 32 * 1024;  // LDS for one chunk of fp32 weight rows (128 KB)
-// most K steps of one wave in one chunk (their x loads stay in registers)
-template <int NB16>
-constexpr int router_xu() { return NB16 == 2 ? 4 : 8; }
-
-// Rows of H per chunk: a multiple of 32 * waves (whole K steps for every
-// wave), at most kXU steps per wave, and within kWFloats for all n2 columns.
+constexpr int kWFloats = 16 * 1024;  // fp32 weights of one chunk (64 KB); two buffers
 constexpr int kWPad = 4;             // floats of padding per LDS column
+constexpr int kWBuf = kWFloats + kWPad * 128;  // one buffer, up to 128 padded columns
 
+// 16-byte x loads per lane per chunk (kept in registers for two chunks)
 template <int NB16>
+constexpr int router_xl() { return NB16 <= 2 ? 4 : 8; }
+
+// Rows of H one MFMA step covers: 32, or 64 when the columns are folded.
+template <bool FOLD>
+constexpr int unit_rows() { return FOLD ? 64 : 32; }
+
+// Rows of H per chunk: whole steps for every wave, within one buffer for all
+// n2 columns and within the lanes' x registers.
+template <int NB16, bool FOLD>
 int router_chunk_rows(int H, int n2) {
-  const int unit = 32 * router_waves<NB16>();
+  const int unit = unit_rows<FOLD>() * router_waves<NB16>();
+  const int max_units = FOLD ? router_xl<NB16>() / 2 : router_xl<NB16>();
   int rows = kWFloats / n2 / unit * unit;
-  rows = std::min(rows, router_xu<NB16>() * unit);
+  rows = std::min(rows, max_units * unit);
   rows = std::max(rows, unit);
   return std::min(rows, (H + unit - 1) / unit * unit);
 }
 
-// Exact three-way bf16 split of eight fp32 values.
+// Exact three-way bf16 split of eight fp32 values, two at a time: the
+// converts round to nearest even, and each remainder is exact in fp32.
 __device__ __forceinline__ void split3(const float (&w)[8], bf16x8_t& p1, bf16x8_t& p2, bf16x8_t& p3) {
+  u32x4_t q1, q2, q3;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const __bf16 b1 = static_cast<__bf16>(w[i]);
-    const float r1 = w[i] - static_cast<float>(b1);
-    const __bf16 b2 = static_cast<__bf16>(r1);
-    const float r2 = r1 - static_cast<float>(b2);
-    p1[i] = b1;
-    p2[i] = b2;
-    p3[i] = static_cast<__bf16>(r2);
+  for (int i = 0; i < 4; ++i) {
+    const f32x2_t v = {w[2 * i], w[2 * i + 1]};
+    const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+    const f32x2_t r1 = v - f32x2_t{__uint_as_float(h << 16), __uint_as_float(h & 0xffff0000u)};
+    const uint32_t m = __builtin_bit_cast(uint32_t, __builtin_convertvector(r1, bf16x2_t));
+    const f32x2_t r2 = r1 - f32x2_t{__uint_as_float(m << 16), __uint_as_float(m & 0xffff0000u)};
+    q1[i] = h;
+    q2[i] = m;
+    q3[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(r2, bf16x2_t));
   }
+  p1 = __builtin_bit_cast(bf16x8_t, q1);
+  p2 = __builtin_bit_cast(bf16x8_t, q2);
+  p3 = __builtin_bit_cast(bf16x8_t, q3);
 }
 
-template <int NB16>
+__device__ __forceinline__ float lane_value(float v, int m) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), m));
+}
+
+template <int NB16, bool FOLD>
 __global__ __launch_bounds__(router_waves<NB16>() * 64) void k_router_mma(RouterParams p, int hc) {
   constexpr int kWaves = router_waves<NB16>();
   constexpr int kThreads = kWaves * 64;
   constexpr int NC = NB16 * 16;
-  constexpr int kXU = router_xu<NB16>();
-  // the weight chunk; after the product, the per-wave partial sums
-  // (n2 <= 128 padded columns of at most kWFloats / n2 rows)
-  __shared__ __attribute__((aligned(16))) float s_w[kWFloats + kWPad * 128];
-  static_assert(kWaves * kTok * NC <= kWFloats, "partials fit in the weight buffer");
-  float (*s_part)[kTok][NC] = reinterpret_cast<float (*)[kTok][NC]>(s_w);
-  __shared__ float s_log[kTok][NC];       // clean logits, then noise logits
+  constexpr int kXL = router_xl<NB16>();
+  constexpr int UR = unit_rows<FOLD>();
+  constexpr int AF = FOLD ? 2 : 1;        // A fragments per step (token halves when folded)
+  constexpr int kU = kXL / AF;            // most steps of one wave in one chunk
+  constexpr int kP = kWFloats / 4 / kThreads;  // most 16-byte weight pieces per thread per chunk
+  static_assert(!FOLD || NB16 == 1, "folding is for at most 8 columns");
+  // the weight chunks; after the product, the per-wave partial sums
+  __shared__ __attribute__((aligned(16))) float s_w[2 * kWBuf];
+  static_assert(kWaves * kTok * NC <= 2 * kWBuf, "partials fit in the weight buffers");
+  __shared__ float s_log[kTok][NC];  // clean logits, then noise logits
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int N = p.N, H = p.H, k = p.k;
@@ -90,83 +122,112 @@ __global__ __launch_bounds__(router_waves<NB16>() * 64) void k_router_mma(Router
   const uint16_t* __restrict__ x = static_cast<const uint16_t*>(p.x);
   const int n2 = N * (p.noisy ? 2 : 1);  // real columns; the padding stays zero
 
-  const int row = lane & 15, kg = lane >> 4;  // A: token row; B: column; kg selects 8 of the 32 K
-  const int64_t tok = tok0 + row;
-  const bool tok_ok = tok < T;
-  const uint16_t* xrow = x + (tok_ok ? tok : 0) * H;
-  const int wsteps = hc / 32 / kWaves;  // this wave's K steps per chunk
+  // MFMA roles: A row / B column `row`, K group `kg` (8 of the step's rows).
+  // Folded, row bit 3 selects the upper 32 rows of the 64-row step on both
+  // sides, and A row r of token half th is token 8 * th + (r & 7).
+  const int row = lane & 15, kg = lane >> 4;
+  const int koff = FOLD ? 32 * (row >> 3) + 8 * kg : 8 * kg;
+  const int bcol = FOLD ? (row & 7) : row;
+  // x rows of this block through a buffer descriptor: a load past the rows
+  // or past H (offset kOOB) returns zeros, so every lane issues the same loads
+  // in every chunk and the waits for them are exact
+  const int tv = static_cast<int>(T - tok0 < kTok ? T - tok0 : kTok);  // tokens of this block
+  const __amdgpu_buffer_rsrc_t rx = uniform_rsrc(x + tok0 * H, static_cast<int64_t>(tv) * H * 2);
+  int trow[AF];
+#pragma unroll
+  for (int th = 0; th < AF; ++th) trow[th] = FOLD ? 8 * th + (row & 7) : row;
+  const int wu = hc / UR / kWaves;  // this wave's steps per chunk
+  const int hcp = hc + kWPad;       // LDS column stride: column j holds the chunk's rows contiguous
 
-  f32x4_mma_t acc_hi[NB16], acc_lo[NB16];
+  f32x4_mma_t acc_hi[NB16][AF], acc_lo[NB16][AF];
 #pragma unroll
   for (int c = 0; c < NB16; ++c)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) acc_hi[c][r] = acc_lo[c][r] = 0.0f;
+    for (int th = 0; th < AF; ++th)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc_hi[c][th][r] = acc_lo[c][th][r] = 0.0f;
 
   // 16-byte weight loads need aligned pointers and whole rows per piece
   const bool vec = (reinterpret_cast<uintptr_t>(p.Wg) & 15) == 0 &&
                    (!p.noisy || (reinterpret_cast<uintptr_t>(p.Wn) & 15) == 0) && N % 4 == 0;
-  const int hcp = hc + kWPad;  // LDS column stride: column j of the chunk holds its rows k contiguous
-  for (int h0 = 0; h0 < H; h0 += hc) {
-    const int hn = min(hc, H - h0);  // weight rows in this chunk
-    // the chunk's weight rows go to LDS transposed, W_g as columns [0, N) and
-    // W_noise as columns [N, 2N): 16-byte pieces, all of a thread's loads out
-    // before any store
-    const int cnt = hn * N, c4 = vec ? cnt / 4 : 0, np = (p.noisy ? 2 : 1) * c4;
-    constexpr int kP = kWFloats / 4 / kThreads;  // most pieces per thread
-    f32x4_t wbuf[kP];
+  const int64_t w_bytes = static_cast<int64_t>(H) * N * 4;
+  const __amdgpu_buffer_rsrc_t rw[2] = {uniform_rsrc(p.Wg, w_bytes), uniform_rsrc(p.noisy ? p.Wn : p.Wg, w_bytes)};
+  // weight piece j of this thread: matrix (W_g, or W_noise for the upper half
+  // of the pieces when noisy) and 16-byte piece index within the chunk
+  auto piece = [&](int j, int& m, int& q) {
+    m = (p.noisy && j >= kP / 2) ? 1 : 0;
+    q = threadIdx.x + (j - m * (kP / 2)) * kThreads;
+  };
+
+  f32x4_t wbuf[kP];
+  bf16x8_t a_cur[kXL], a_nxt[kXL];
+  // a chunk's weight rows, W_g as columns [0, N) and W_noise as [N, 2N), in
+  // 16-byte pieces
+  auto load_w = [&](int h0) {
+    const int hn = min(hc, H - h0);
+    const int c4 = vec ? hn * N / 4 : 0;
 #pragma unroll
     for (int j = 0; j < kP; ++j) {
-      const int i = threadIdx.x + j * kThreads;
-      if (i < np) {
-        const int m = i < c4 ? 0 : 1, q = i - m * c4;
-        wbuf[j] = *reinterpret_cast<const f32x4_t*>((m == 0 ? p.Wg : p.Wn) + static_cast<int64_t>(h0) * N + 4 * q);
+      int m, q;
+      piece(j, m, q);
+      const uint32_t off = q < c4 ? static_cast<uint32_t>(h0 * N + 4 * q) * 4u : kOOB;
+      wbuf[j] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw[m], off, 0, 0));
+    }
+  };
+  auto load_x = [&](int h0, bf16x8_t (&a)[kXL]) {
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+#pragma unroll
+      for (int th = 0; th < AF; ++th) {
+        const int kk = h0 + (wave * wu + u) * UR + koff;
+        const bool ok = u < wu && kk < H && trow[th] < tv;
+        const uint32_t off = ok ? static_cast<uint32_t>(trow[th] * H + kk) * 2u : kOOB;
+        a[u * AF + th] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0));
       }
-    }
-    // x of this wave's steps in the chunk
-    bf16x8_t a[kXU];
-#pragma unroll
-    for (int u = 0; u < kXU; ++u) {
-      const int kk = h0 + (wave * wsteps + u) * 32 + kg * 8;
-      u32x4_t v = {0u, 0u, 0u, 0u};
-      if (u < wsteps && kk < H && tok_ok) v = *reinterpret_cast<const u32x4_t*>(xrow + kk);
-      a[u] = __builtin_bit_cast(bf16x8_t, v);
-    }
+  };
+  // transposed stores of the pieces, and what they do not cover (an
+  // unaligned pointer, N % 4 != 0) straight from global memory
+  auto store_w = [&](int h0, float* sb) {
+    const int hn = min(hc, H - h0);
+    const int cnt = hn * N, c4 = vec ? cnt / 4 : 0;
 #pragma unroll
     for (int j = 0; j < kP; ++j) {
-      const int i = threadIdx.x + j * kThreads;
-      if (i < np) {
-        const int m = i < c4 ? 0 : 1, q = i - m * c4;
+      int m, q;
+      piece(j, m, q);
+      if (q < c4) {
         const int f = 4 * q, r = f / N, n = f - r * N + m * N;  // row and first column of the piece
 #pragma unroll
-        for (int e = 0; e < 4; ++e) s_w[(n + e) * hcp + r] = wbuf[j][e];
+        for (int e = 0; e < 4; ++e) sb[(n + e) * hcp + r] = wbuf[j][e];
       }
     }
-    // what the pieces do not cover (an unaligned pointer, N % 4 != 0)
     for (int m = 0; m < (p.noisy ? 2 : 1); ++m) {
       const float* src = (m == 0 ? p.Wg : p.Wn) + static_cast<int64_t>(h0) * N;
       for (int i = 4 * c4 + threadIdx.x; i < cnt; i += kThreads) {
         const int r = i / N;
-        s_w[(i - r * N + m * N) * hcp + r] = src[i];
+        sb[(i - r * N + m * N) * hcp + r] = src[i];
       }
     }
-    __syncthreads();
+  };
+  auto compute = [&](int h0, const float* sb) {
+    const int hn = min(hc, H - h0);  // weight rows in this chunk; the rest hold stale values
 #pragma unroll
-    for (int u = 0; u < kXU; ++u) {
-      if (u < wsteps) {
-        const int kl = (wave * wsteps + u) * 32 + kg * 8;  // K within the chunk
+    for (int u = 0; u < kU; ++u) {
+      if (u < wu) {
+        const int kl = (wave * wu + u) * UR + koff;  // row within the chunk
 #pragma unroll
         for (int c = 0; c < NB16; ++c) {
-          const int col = c * 16 + row;
+          const int col = c * 16 + bcol;
           float wv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
           if (col < n2) {
-            const f32x4_t lo = *reinterpret_cast<const f32x4_t*>(s_w + col * hcp + kl);
-            const f32x4_t hi = *reinterpret_cast<const f32x4_t*>(s_w + col * hcp + kl + 4);
+            // col * hcp + kl is a multiple of 4 floats
+            const f32x4_t* src = reinterpret_cast<const f32x4_t*>(sb) + ((col * hcp + kl) >> 2);
+            const f32x4_t lo = src[0], hi = src[1];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               wv[e] = lo[e];
               wv[4 + e] = hi[e];
             }
-            if (hn < hc) {  // rows past the chunk's end hold stale values
+            if (hn < hc) {
 #pragma unroll
               for (int e = 0; e < 8; ++e)
                 if (kl + e >= hn) wv[e] = 0.0f;
@@ -174,27 +235,75 @@ __global__ __launch_bounds__(router_waves<NB16>() * 64) void k_router_mma(Router
           }
           bf16x8_t w1, w2, w3;
           split3(wv, w1, w2, w3);
-          acc_hi[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], w1, acc_hi[c], 0, 0, 0);
-          acc_lo[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], w2, acc_lo[c], 0, 0, 0);
-          acc_lo[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], w3, acc_lo[c], 0, 0, 0);
+#pragma unroll
+          for (int th = 0; th < AF; ++th) {
+            const bf16x8_t a = a_cur[u * AF + th];
+            acc_hi[c][th] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, w1, acc_hi[c][th], 0, 0, 0);
+            acc_lo[c][th] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, w2, acc_lo[c][th], 0, 0, 0);
+            acc_lo[c][th] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, w3, acc_lo[c][th], 0, 0, 0);
+          }
         }
       }
       __builtin_amdgcn_sched_barrier(0);  // one step's operands live at a time
     }
-    __syncthreads();  // the chunk buffer is free again
-  }
-  // lane holds column (lane & 15) and token rows 4*(lane/16) + r
-#pragma unroll
-  for (int c = 0; c < NB16; ++c)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) s_part[wave][kg * 4 + r][c * 16 + row] = acc_hi[c][r] + acc_lo[c][r];
+  };
+
+  // software pipeline over the chunks: chunk c + 1 loads while chunk c computes
+  load_w(0);
+  load_x(0, a_cur);
+  store_w(0, s_w);
+  // chunk 0's x has landed too: no load is pending where the loop starts, so
+  // the waits inside it count only the next chunk's loads
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  for (int i = threadIdx.x; i < kTok * NC; i += kWaves * 64) {
-    const int t = i / NC, c = i % NC;
-    float v = s_part[0][t][c];
+  for (int h0 = 0, c = 0; h0 < H; h0 += hc, ++c) {
+    const bool more = h0 + hc < H;
+    if (more) {
+      load_w(h0 + hc);
+      load_x(h0 + hc, a_nxt);
+    }
+    compute(h0, s_w + (c & 1) * kWBuf);
+    if (more) store_w(h0 + hc, s_w + ((c + 1) & 1) * kWBuf);
+    __syncthreads();
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) v += s_part[w][t][c];
-    s_log[t][c] = v;
+    for (int i = 0; i < kXL; ++i) a_cur[i] = a_nxt[i];
+  }
+
+  // lane holds output rows 4 * kg + r and column `row` of each product
+  if constexpr (FOLD) {
+    // the diagonal blocks: rows 0..7 x columns 0..7 (lower 32 rows of each
+    // step) and rows 8..15 x columns 8..15 (upper 32 rows)
+    float (*s_part)[2][kTok][8] = reinterpret_cast<float (*)[2][kTok][8]>(s_w);
+    const int half = kg >> 1;
+    if (half == (row >> 3)) {
+#pragma unroll
+      for (int th = 0; th < AF; ++th)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          s_part[wave][half][8 * th + ((4 * kg + r) & 7)][row & 7] = acc_hi[0][th][r] + acc_lo[0][th][r];
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < kTok * 8; i += kThreads) {
+      const int t = i / 8, c = i % 8;
+      float v = s_part[0][0][t][c] + s_part[0][1][t][c];
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) v += s_part[w][0][t][c] + s_part[w][1][t][c];
+      s_log[t][c] = v;
+    }
+  } else {
+    float (*s_part)[kTok][NC] = reinterpret_cast<float (*)[kTok][NC]>(s_w);
+#pragma unroll
+    for (int c = 0; c < NB16; ++c)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s_part[wave][kg * 4 + r][c * 16 + row] = acc_hi[c][0][r] + acc_lo[c][0][r];
+    __syncthreads();
+    for (int i = threadIdx.x; i < kTok * NC; i += kThreads) {
+      const int t = i / NC, c = i % NC;
+      float v = s_part[0][t][c];
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) v += s_part[w][t][c];
+      s_log[t][c] = v;
+    }
   }
   __syncthreads();
 
@@ -212,48 +321,33 @@ __global__ __launch_bounds__(router_waves<NB16>() * 64) void k_router_mma(Router
     // normal draw being the input eps[t, i]
     if (p.noisy && valid) hv = fmaf(p.eps[g * N + lane], softplus(s_log[t][N + lane]), lv);
     if (p.logits && valid) p.logits[g * N + lane] = lv;
-    // KeepTopK: k rounds of a wave-wide (score desc, index asc) argmax
-    float cur = valid ? hv : -INFINITY;
-    int curi = valid ? lane : 4096 + lane;
-    bool taken = false;
-    float my_v = 0.0f;
-    int my_i = 0;
-    for (int jj = 0; jj < k; ++jj) {
-      float bv = cur;
-      int bi = curi;
-#pragma unroll
-      for (int m = 32; m >= 1; m >>= 1) {
-        const float ov = __shfl_xor(bv, m, 64);
-        const int oi = __shfl_xor(bi, m, 64);
-        if (ov > bv || (ov == bv && oi < bi)) {
-          bv = ov;
-          bi = oi;
-        }
-      }
-      if (lane == jj) {
-        my_v = bv;
-        my_i = bi;
-      }
-      if (curi == bi) {
-        taken = true;
-        cur = -INFINITY;
-        curi = 8192 + lane;
-      }
+    // rank: experts with a larger score, or an equal one at a lower index
+    int rank = 0;
+    for (int m = 0; m < N; ++m) {
+      const float sm = lane_value(hv, m);
+      rank += (sm > hv || (sm == hv && m < lane)) ? 1 : 0;
     }
-    const float hmax = __shfl(my_v, 0, 64);
-    // Mixtral order: softmax over the kept scores; ST: over all N scores
-    const float den = p.order == 0 ? wave_sum(lane < k ? expf(my_v - hmax) : 0.0f)
-                                   : wave_sum(valid ? expf(hv - hmax) : 0.0f);
-    if (lane < k) {
-      p.topk_idx[g * k + lane] = my_i;
-      p.topk_w[g * k + lane] = expf(my_v - hmax) / den;
+    const bool kept = valid && rank < k;
+    const float hmax = lane_value(hv, static_cast<int>(__builtin_ctzll(__ballot(valid && rank == 0))));
+    // Mixtral order: softmax over the kept scores; ST: over all N scores.
+    // The denominator adds the terms in expert order.
+    const float ex = (p.order == 0 ? kept : valid) ? expf(hv - hmax) : 0.0f;
+    float den = 0.0f;
+    for (int m = 0; m < N; ++m) den += lane_value(ex, m);
+    const float wgt = kept ? ex / den : 0.0f;
+    if (kept) {
+      p.topk_idx[g * k + rank] = lane;
+      p.topk_w[g * k + rank] = wgt;
     }
-    s_take[t][lane] = taken ? 1 : 0;
-    s_sel[t][lane] = taken ? expf(hv - hmax) / den : 0.0f;  // the value written for this expert
+    s_take[t][lane] = kept ? 1 : 0;
+    s_sel[t][lane] = wgt;
     if (p.stat_part) {
-      const float lmax = wave_max(lv);
+      float lmax = -INFINITY;
+      for (int m = 0; m < N; ++m) lmax = fmaxf(lmax, lane_value(lv, m));
       const float el = valid ? expf(lv - lmax) : 0.0f;
-      s_p[t][lane] = el / wave_sum(el);
+      float ls = 0.0f;
+      for (int m = 0; m < N; ++m) ls += lane_value(el, m);
+      s_p[t][lane] = el / ls;
     }
   }
   __syncthreads();
@@ -263,11 +357,12 @@ __global__ __launch_bounds__(router_waves<NB16>() * 64) void k_router_mma(Router
     const int n = threadIdx.x;
     int cnt = 0;
     float imp = 0.0f, ps = 0.0f;
+#pragma unroll
     for (int t = 0; t < kTok; ++t) {
-      if (tok0 + t >= T) break;
-      cnt += s_take[t][n];
-      imp += s_sel[t][n];
-      if (p.stat_part) ps += s_p[t][n];
+      const bool ok = t < tv;
+      cnt += ok ? s_take[t][n] : 0;
+      imp += ok ? s_sel[t][n] : 0.0f;
+      ps += ok ? s_p[t][n] : 0.0f;
     }
     p.hist[static_cast<int64_t>(blockIdx.x) * N + n] = cnt;
     if (p.stat_part) {
@@ -282,17 +377,21 @@ __global__ __launch_bounds__(router_waves<NB16>() * 64) void k_router_mma(Router
 hipError_t launch_router_mma(const RouterParams& p, hipStream_t s) {
   const int n2 = p.N * (p.noisy ? 2 : 1);
   const dim3 grid(static_cast<unsigned>((p.T + kTok - 1) / kTok));
-#define MOE_ROUTER_MMA(NB) \
-  hipLaunchKernelGGL(k_router_mma<NB>, grid, dim3(router_waves<NB>() * 64), 0, s, p, router_chunk_rows<NB>(p.H, n2))
+#define MOE_ROUTER_MMA(NB, FOLD)                                                              \
+  hipLaunchKernelGGL((k_router_mma<NB, FOLD>), grid, dim3(router_waves<NB>() * 64), 0, s, p, \
+                     router_chunk_rows<NB, FOLD>(p.H, n2))
   switch ((n2 + 15) / 16) {
-    case 1: MOE_ROUTER_MMA(1); break;
-    case 2: MOE_ROUTER_MMA(2); break;
-    case 3: MOE_ROUTER_MMA(3); break;
-    case 4: MOE_ROUTER_MMA(4); break;
-    case 5: MOE_ROUTER_MMA(5); break;
-    case 6: MOE_ROUTER_MMA(6); break;
-    case 7: MOE_ROUTER_MMA(7); break;
-    default: MOE_ROUTER_MMA(8); break;
+    case 1:
+      if (n2 <= 8) MOE_ROUTER_MMA(1, true);
+      else MOE_ROUTER_MMA(1, false);
+      break;
+    case 2: MOE_ROUTER_MMA(2, false); break;
+    case 3: MOE_ROUTER_MMA(3, false); break;
+    case 4: MOE_ROUTER_MMA(4, false); break;
+    case 5: MOE_ROUTER_MMA(5, false); break;
+    case 6: MOE_ROUTER_MMA(6, false); break;
+    case 7: MOE_ROUTER_MMA(7, false); break;
+    default: MOE_ROUTER_MMA(8, false); break;
   }
 #undef MOE_ROUTER_MMA
   return hipGetLastError();
