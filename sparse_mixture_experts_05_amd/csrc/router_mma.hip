@@ -55,9 +55,11 @@ constexpr int kWFloats = 16 * 1024;  // fp32 weights of one chunk (64 KB); two b
 constexpr int kWPad = 4;             // floats of padding per LDS column
 constexpr int kWBuf = kWFloats + kWPad * 128;  // one buffer, up to 128 padded columns
 
-// 16-byte x loads per lane per chunk (kept in registers for two chunks)
-template <int NB16>
-constexpr int router_xl() { return NB16 <= 2 ? 4 : 8; }
+// 16-byte x loads per lane per chunk (two chunks stay in registers): folded
+// chunks give a wave two steps of two A fragments; otherwise the buffer holds
+// at most two steps per wave
+template <bool FOLD>
+constexpr int router_xl() { return FOLD ? 4 : 2; }
 
 // Rows of H one MFMA step covers: 32, or 64 when the columns are folded.
 template <bool FOLD>
@@ -68,7 +70,7 @@ constexpr int unit_rows() { return FOLD ? 64 : 32; }
 template <int NB16, bool FOLD>
 int router_chunk_rows(int H, int n2) {
   const int unit = unit_rows<FOLD>() * router_waves<NB16>();
-  const int max_units = FOLD ? router_xl<NB16>() / 2 : router_xl<NB16>();
+  const int max_units = FOLD ? router_xl<FOLD>() / 2 : router_xl<FOLD>();
   int rows = kWFloats / n2 / unit * unit;
   rows = std::min(rows, max_units * unit);
   rows = std::max(rows, unit);
@@ -99,12 +101,14 @@ __device__ __forceinline__ float lane_value(float v, int m) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), m));
 }
 
-template <int NB16, bool FOLD>
+// SHORT: H fits in the two buffers; the weights are staged first, then all
+// of x is requested at once.
+template <int NB16, bool FOLD, bool SHORT>
 __global__ __launch_bounds__(router_waves<NB16>() * 64) void k_router_mma(RouterParams p, int hc) {
   constexpr int kWaves = router_waves<NB16>();
   constexpr int kThreads = kWaves * 64;
   constexpr int NC = NB16 * 16;
-  constexpr int kXL = router_xl<NB16>();
+  constexpr int kXL = router_xl<FOLD>();
   constexpr int UR = unit_rows<FOLD>();
   constexpr int AF = FOLD ? 2 : 1;        // A fragments per step (token halves when folded)
   constexpr int kU = kXL / AF;            // most steps of one wave in one chunk
@@ -159,11 +163,11 @@ __global__ __launch_bounds__(router_waves<NB16>() * 64) void k_router_mma(Router
     q = threadIdx.x + (j - m * (kP / 2)) * kThreads;
   };
 
-  f32x4_t wbuf[kP];
-  bf16x8_t a_cur[kXL], a_nxt[kXL];
+  f32x4_t wbuf[kP], wbuf2[kP];
+  bf16x8_t a_cur[kXL], a_nxt[kXL];  // x of this chunk and of the next
   // a chunk's weight rows, W_g as columns [0, N) and W_noise as [N, 2N), in
   // 16-byte pieces
-  auto load_w = [&](int h0) {
+  auto load_w = [&](int h0, f32x4_t (&wb)[kP]) {
     const int hn = min(hc, H - h0);
     const int c4 = vec ? hn * N / 4 : 0;
 #pragma unroll
@@ -171,7 +175,7 @@ __global__ __launch_bounds__(router_waves<NB16>() * 64) void k_router_mma(Router
       int m, q;
       piece(j, m, q);
       const uint32_t off = q < c4 ? static_cast<uint32_t>(h0 * N + 4 * q) * 4u : kOOB;
-      wbuf[j] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw[m], off, 0, 0));
+      wb[j] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw[m], off, 0, 0));
     }
   };
   auto load_x = [&](int h0, bf16x8_t (&a)[kXL]) {
@@ -187,7 +191,7 @@ __global__ __launch_bounds__(router_waves<NB16>() * 64) void k_router_mma(Router
   };
   // transposed stores of the pieces, and what they do not cover (an
   // unaligned pointer, N % 4 != 0) straight from global memory
-  auto store_w = [&](int h0, float* sb) {
+  auto store_w = [&](int h0, float* sb, const f32x4_t (&wb)[kP]) {
     const int hn = min(hc, H - h0);
     const int cnt = hn * N, c4 = vec ? cnt / 4 : 0;
 #pragma unroll
@@ -197,7 +201,7 @@ __global__ __launch_bounds__(router_waves<NB16>() * 64) void k_router_mma(Router
       if (q < c4) {
         const int f = 4 * q, r = f / N, n = f - r * N + m * N;  // row and first column of the piece
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sb[(n + e) * hcp + r] = wbuf[j][e];
+        for (int e = 0; e < 4; ++e) sb[(n + e) * hcp + r] = wb[j][e];
       }
     }
     for (int m = 0; m < (p.noisy ? 2 : 1); ++m) {
@@ -208,7 +212,7 @@ __global__ __launch_bounds__(router_waves<NB16>() * 64) void k_router_mma(Router
       }
     }
   };
-  auto compute = [&](int h0, const float* sb) {
+  auto compute = [&](int h0, const float* sb, const bf16x8_t (&a)[kXL]) {
     const int hn = min(hc, H - h0);  // weight rows in this chunk; the rest hold stale values
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
@@ -237,10 +241,10 @@ __global__ __launch_bounds__(router_waves<NB16>() * 64) void k_router_mma(Router
           split3(wv, w1, w2, w3);
 #pragma unroll
           for (int th = 0; th < AF; ++th) {
-            const bf16x8_t a = a_cur[u * AF + th];
-            acc_hi[c][th] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, w1, acc_hi[c][th], 0, 0, 0);
-            acc_lo[c][th] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, w2, acc_lo[c][th], 0, 0, 0);
-            acc_lo[c][th] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, w3, acc_lo[c][th], 0, 0, 0);
+            const bf16x8_t af = a[u * AF + th];
+            acc_hi[c][th] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, w1, acc_hi[c][th], 0, 0, 0);
+            acc_lo[c][th] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, w2, acc_lo[c][th], 0, 0, 0);
+            acc_lo[c][th] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, w3, acc_lo[c][th], 0, 0, 0);
           }
         }
       }
@@ -248,25 +252,43 @@ __global__ __launch_bounds__(router_waves<NB16>() * 64) void k_router_mma(Router
     }
   };
 
-  // software pipeline over the chunks: chunk c + 1 loads while chunk c computes
-  load_w(0);
-  load_x(0, a_cur);
-  store_w(0, s_w);
-  // chunk 0's x has landed too: no load is pending where the loop starts, so
-  // the waits inside it count only the next chunk's loads
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  for (int h0 = 0, c = 0; h0 < H; h0 += hc, ++c) {
-    const bool more = h0 + hc < H;
-    if (more) {
-      load_w(h0 + hc);
-      load_x(h0 + hc, a_nxt);
-    }
-    compute(h0, s_w + (c & 1) * kWBuf);
-    if (more) store_w(h0 + hc, s_w + ((c + 1) & 1) * kWBuf);
+  if constexpr (SHORT) {
+    // Both chunks' weights are requested first and stored; x follows. Every
+    // block reads the same weights, and their first reads from memory would
+    // otherwise queue behind the whole of x.
+    load_w(0, wbuf);
+    load_w(hc, wbuf2);
+    store_w(0, s_w, wbuf);
+    store_w(hc, s_w + kWBuf, wbuf2);
     __syncthreads();
+    load_x(0, a_cur);
+    load_x(hc, a_nxt);
+    compute(0, s_w, a_cur);
+    if (hc < H) compute(hc, s_w + kWBuf, a_nxt);
+    __syncthreads();
+  } else {
+    // software pipeline over the chunks: chunk c + 1 loads while chunk c
+    // computes, and is stored to the other buffer before the barrier that
+    // ends chunk c
+    load_w(0, wbuf);
+    load_x(0, a_cur);
+    store_w(0, s_w, wbuf);
+    // chunk 0's x has landed too: no load is pending where the loop starts,
+    // so the waits inside it count only the next chunk's loads
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int h0 = 0, c = 0; h0 < H; h0 += hc, ++c) {
+      const bool more = h0 + hc < H;
+      if (more) {
+        load_w(h0 + hc, wbuf);
+        load_x(h0 + hc, a_nxt);
+      }
+      compute(h0, s_w + (c & 1) * kWBuf, a_cur);
+      if (more) store_w(h0 + hc, s_w + ((c + 1) & 1) * kWBuf, wbuf);
+      __syncthreads();
 #pragma unroll
-    for (int i = 0; i < kXL; ++i) a_cur[i] = a_nxt[i];
+      for (int i = 0; i < kXL; ++i) a_cur[i] = a_nxt[i];
+    }
   }
 
   // lane holds output rows 4 * kg + r and column `row` of each product
@@ -377,21 +399,26 @@ __global__ __launch_bounds__(router_waves<NB16>() * 64) void k_router_mma(Router
 hipError_t launch_router_mma(const RouterParams& p, hipStream_t s) {
   const int n2 = p.N * (p.noisy ? 2 : 1);
   const dim3 grid(static_cast<unsigned>((p.T + kTok - 1) / kTok));
-#define MOE_ROUTER_MMA(NB, FOLD)                                                              \
-  hipLaunchKernelGGL((k_router_mma<NB, FOLD>), grid, dim3(router_waves<NB>() * 64), 0, s, p, \
-                     router_chunk_rows<NB, FOLD>(p.H, n2))
+#define MOE_ROUTER_MMA(NB, FOLD, SHORT)                                                                \
+  do {                                                                                                 \
+    const int hc = router_chunk_rows<NB, FOLD>(p.H, n2);                                               \
+    if (SHORT && 2 * hc >= p.H)                                                                        \
+      hipLaunchKernelGGL((k_router_mma<NB, FOLD, SHORT>), grid, dim3(router_waves<NB>() * 64), 0, s, p, hc); \
+    else                                                                                               \
+      hipLaunchKernelGGL((k_router_mma<NB, FOLD, false>), grid, dim3(router_waves<NB>() * 64), 0, s, p, hc); \
+  } while (0)
   switch ((n2 + 15) / 16) {
     case 1:
-      if (n2 <= 8) MOE_ROUTER_MMA(1, true);
-      else MOE_ROUTER_MMA(1, false);
+      if (n2 <= 8) MOE_ROUTER_MMA(1, true, true);
+      else MOE_ROUTER_MMA(1, false, true);
       break;
-    case 2: MOE_ROUTER_MMA(2, false); break;
-    case 3: MOE_ROUTER_MMA(3, false); break;
-    case 4: MOE_ROUTER_MMA(4, false); break;
-    case 5: MOE_ROUTER_MMA(5, false); break;
-    case 6: MOE_ROUTER_MMA(6, false); break;
-    case 7: MOE_ROUTER_MMA(7, false); break;
-    default: MOE_ROUTER_MMA(8, false); break;
+    case 2: MOE_ROUTER_MMA(2, false, true); break;
+    case 3: MOE_ROUTER_MMA(3, false, false); break;
+    case 4: MOE_ROUTER_MMA(4, false, false); break;
+    case 5: MOE_ROUTER_MMA(5, false, false); break;
+    case 6: MOE_ROUTER_MMA(6, false, false); break;
+    case 7: MOE_ROUTER_MMA(7, false, false); break;
+    default: MOE_ROUTER_MMA(8, false, false); break;
   }
 #undef MOE_ROUTER_MMA
   return hipGetLastError();
