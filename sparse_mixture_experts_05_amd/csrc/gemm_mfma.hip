@@ -23,10 +23,10 @@
 // Loads go straight from buffer loads into LDS (no register staging), STAGES
 // deep, so several K steps of loads stay in flight; rows past the expert's
 // segment and K past the range read as zero through the buffer's range check,
-// without branches. k_gemm_dma runs one tile per workgroup (the decode-shaped
-// 32 x 256 tile with four stages, or 256 x 256 with two), and k_experts_fused
-// runs both projections of every expert in one persistent launch on the same
-// tile code (see the scheduling comment above it).
+// without branches. k_gemm_dma runs one 256 x 256 tile per workgroup,
+// k_experts_fused runs both projections of every expert in one persistent
+// launch on the same tile code (see the scheduling comment above it), and
+// k_gemm_decode serves experts with few rows (see the comment above it).
 #include "common.h"
 #include "stats.h"
 #include "kernels.h"
@@ -486,6 +486,147 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm_dma(GemmParams p) {
   gemm_tile<BM, BN, WGM, WGN, STAGES, BK, SWIGLU, GATHER>(p, tp, smem);
 }
 
+// ---- decode-shaped tiles: a long K step per weight row -----------------------
+//
+// When experts get few rows, the GEMMs stream the expert weights from HBM
+// once and the matrix cores are nearly idle, so the tile is shaped for the
+// memory system: 32 rows of A, 64 rows of B (32 gate and 32 up rows for
+// swiglu) and a K step of BK = 128 bf16, 256 contiguous bytes of every weight
+// row per step, in three stages of 24 KB, so that two workgroups share a
+// compute unit and one's barrier wait overlaps the other's loads. The NW
+// waves split each step's K slices; their partial sums meet in LDS after the
+// K loop and wave 0 runs the epilogue.
+//
+// LDS rows hold BK bf16 (16 or 32 chunks of 16 bytes); chunk c of row r sits
+// at physical chunk c ^ (r & 15), so the 16 rows an MFMA operand read covers
+// at one chunk land in 16 distinct groups of four banks.
+constexpr int kDecBM = 32, kDecBN = 64;
+
+template <int BK>
+__device__ __forceinline__ int dec_swz(int row, int chunk) {
+  return row * BK + ((chunk ^ (row & 15)) << 3);
+}
+
+template <int BK, int STAGES, int NW, bool SWIGLU, bool GATHER>
+__global__ __launch_bounds__(NW * 64) void k_gemm_decode(GemmParams p) {
+  constexpr int BM = kDecBM, BN = kDecBN;
+  constexpr int NO = SWIGLU ? BN / 2 : BN;
+  constexpr int CPR = BK / 8;              // 16-byte chunks per LDS row
+  constexpr int RPS = 64 / CPR;            // rows per 1-KB load segment (one load per wave)
+  constexpr int IA = BM / RPS / NW, IB = BN / RPS / NW;  // segments a wave fills per stage
+  constexpr int LPS = IA + IB;
+  constexpr int KS = BK / 16;              // MFMA K slices per step
+  constexpr int KSW = KS / NW;             // slices per wave
+  static_assert(CPR >= 16 && IA * RPS * NW == BM && IB * RPS * NW == BN && KSW * NW == KS, "decode tile shape");
+  static_assert(STAGES >= 2 && (STAGES - 2) * LPS <= 63, "stage count");
+  static_assert(STAGES * (BM + BN) * BK >= NW * 2 * 16 * 64 * 2, "partials fit in the stages");
+  __shared__ __attribute__((aligned(16))) uint16_t smem[STAGES * (BM + BN) * BK];
+
+  TilePos tp;
+  if (!decode_tile<BM, NO, BK>(p, tp)) return;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+  // per-load lane offsets: segment i * NW + wave, row RPS * segment + lane / CPR,
+  // physical chunk lane % CPR holding logical chunk (lane % CPR) ^ (row & 15)
+  const int prow = lane / CPR, pchunk = lane % CPR;
+  uint32_t aoff[IA], boff[IB];
+  int alc[IA], blc[IB];
+#pragma unroll
+  for (int i = 0; i < IA; ++i) {
+    const int r = (i * NW + wave) * RPS + prow;
+    alc[i] = pchunk ^ (r & 15);
+    const bool v = r < tp.ti.rows;
+    int src = tp.ti.row0 + r;
+    if (GATHER) src = v ? p.row_token[src] : 0;
+    aoff[i] = v ? static_cast<uint32_t>(src) * static_cast<uint32_t>(p.lda) * 2u + alc[i] * 16u : kOOB;
+  }
+#pragma unroll
+  for (int i = 0; i < IB; ++i) {
+    const int r = (i * NW + wave) * RPS + prow;  // B row of the tile
+    blc[i] = pchunk ^ (r & 15);
+    const int f = tp.nt * NO + (SWIGLU && r >= BN / 2 ? r - BN / 2 : r);
+    boff[i] = f < p.Nout ? static_cast<uint32_t>(f) * static_cast<uint32_t>(p.ldb) * 2u + blc[i] * 16u : kOOB;
+  }
+  const int64_t b_bytes = static_cast<int64_t>(p.Nout) * p.ldb * 2;
+  const __amdgpu_buffer_rsrc_t ra = uniform_rsrc(p.A, p.a_rows * p.lda * 2);
+  const uint16_t* b0 = static_cast<const uint16_t*>(p.B0) + tp.ti.expert * p.b_expert_stride;
+  const uint16_t* b1 = SWIGLU ? static_cast<const uint16_t*>(p.B1) + tp.ti.expert * p.b_expert_stride : b0;
+  const __amdgpu_buffer_rsrc_t rb0 = uniform_rsrc(b0, b_bytes), rb1 = uniform_rsrc(b1, b_bytes);
+
+  auto sA = [&](int st) { return smem + st * (BM + BN) * BK; };
+  auto sB = [&](int st) { return smem + st * (BM + BN) * BK + BM * BK; };
+  auto issue = [&](int st, int kt) {
+    const int kb = tp.kb0 + kt * BK;
+    const uint32_t kbyte = static_cast<uint32_t>(kb) * 2u;
+#pragma unroll
+    for (int i = 0; i < IA; ++i) {
+      const bool kval = kb + alc[i] * 8 < tp.kb1;
+      const uint32_t vo = (kval && aoff[i] != kOOB) ? aoff[i] + kbyte : kOOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(sA(st) + (i * NW + wave) * 512), 16, vo, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < IB; ++i) {
+      const int r0 = (i * NW + wave) * RPS;  // first row of the segment (wave-uniform)
+      const bool kval = kb + blc[i] * 8 < tp.kb1;
+      const uint32_t vo = (kval && boff[i] != kOOB) ? boff[i] + kbyte : kOOB;
+      if (!SWIGLU || r0 < BN / 2)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb0, (lds_ptr_t)(sB(st) + (i * NW + wave) * 512), 16, vo, 0, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb1, (lds_ptr_t)(sB(st) + (i * NW + wave) * 512), 16, vo, 0, 0, 0);
+    }
+  };
+
+  f32x16_t acc[1][2];
+  zero_acc(acc);
+  const int frow = lane & 31, khalf = lane >> 5;
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s)
+    if (s < tp.KT) issue(s, s);
+  for (int kt = 0; kt < tp.KT; ++kt) {
+    wait_stage<LPS, STAGES - 2>(min(STAGES - 2, tp.KT - 1 - kt));
+    lds_barrier();  // stage kt is complete for every wave; stage kt-1 is free
+    if (kt + STAGES - 1 < tp.KT) issue((kt + STAGES - 1) % STAGES, kt + STAGES - 1);
+    const uint16_t* a = sA(kt % STAGES);
+    const uint16_t* b = sB(kt % STAGES);
+    bf16x8_t af[KSW], bf0[KSW], bf1[KSW];
+#pragma unroll
+    for (int q = 0; q < KSW; ++q) {
+      const int chunk = (wave * KSW + q) * 2 + khalf;
+      af[q] = *reinterpret_cast<const bf16x8_t*>(&a[dec_swz<BK>(frow, chunk)]);
+      bf0[q] = *reinterpret_cast<const bf16x8_t*>(&b[dec_swz<BK>(frow, chunk)]);
+      bf1[q] = *reinterpret_cast<const bf16x8_t*>(&b[dec_swz<BK>(32 + frow, chunk)]);
+    }
+#pragma unroll
+    for (int q = 0; q < KSW; ++q) {
+      acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[q], bf0[q], acc[0][0], 0, 0, 0);
+      acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[q], bf1[q], acc[0][1], 0, 0, 0);
+    }
+  }
+
+  // partial sums of the four waves, added in wave order by wave 0
+  lds_barrier();
+  float* red = reinterpret_cast<float*>(smem);  // [wave][j][r][lane]
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float v = acc[0][j][r];
+      red[((wave * 2 + j) * 16 + r) * 64 + lane] = v;
+    }
+  lds_barrier();
+  if (wave != 0) return;
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float v = red[(j * 16 + r) * 64 + lane];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) v += red[((w * 2 + j) * 16 + r) * 64 + lane];
+      acc[0][j][r] = v;
+    }
+  epilogue<BM, BN, 1, 2, SWIGLU>(p, tp, 0, 0, lane, NO, acc);
+}
+
 // ---- both expert GEMMs in one persistent launch ---------------------------------
 //
 // A row block is BM consecutive permuted rows of one expert. The gate/up
@@ -697,6 +838,21 @@ hipError_t launch_dma(const GemmParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int BK, int STAGES, int NW>
+hipError_t launch_decode(const GemmParams& p, hipStream_t s) {
+  const int64_t blocks = grid_blocks(p, kDecBM, kDecBN);
+  if (blocks <= 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>(blocks)), block(NW * 64);
+  if (p.swiglu) {
+    if (p.row_token) hipLaunchKernelGGL((k_gemm_decode<BK, STAGES, NW, true, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((k_gemm_decode<BK, STAGES, NW, true, false>), grid, block, 0, s, p);
+  } else {
+    if (p.row_token) hipLaunchKernelGGL((k_gemm_decode<BK, STAGES, NW, false, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((k_gemm_decode<BK, STAGES, NW, false, false>), grid, block, 0, s, p);
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
 
 bool gemm_bf16_mfma_supported(int K, int Nout) { return K % 8 == 0 && K > 0 && Nout > 0; }
@@ -706,8 +862,8 @@ bool gemm_bf16_mfma_supported(int K, int Nout) { return K % 8 == 0 && K > 0 && N
 void gemm_bf16_mfma_tile(int64_t rows_max, int N, int* bm, int* bn) {
   const int64_t avg_rows = rows_max / (N > 0 ? N : 1);
   if (avg_rows <= 48) {
-    *bm = 32;
-    *bn = 256;
+    *bm = kDecBM;
+    *bn = kDecBN;
   } else {
     *bm = 256;
     *bn = 256;
@@ -742,7 +898,7 @@ hipError_t launch_experts_fused(const FusedParams& fp, hipStream_t s) {
 hipError_t launch_gemm_bf16_mfma(const GemmParams& p, hipStream_t s) {
   int bm, bn;
   gemm_bf16_mfma_tile(p.rows_max, p.N, &bm, &bn);
-  if (bm == 32) return launch_dma<32, 256, 1, 4, 4, 64>(p, s);
+  if (bm == kDecBM) return launch_decode<128, 3, 4>(p, s);
   return launch_dma<256, 256, 4, 2, 2, 64>(p, s);
 }
 

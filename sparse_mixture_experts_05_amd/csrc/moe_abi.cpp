@@ -92,12 +92,13 @@ Layout layout(const moe_cfg* c) {
   L.fused = L.mfma && moe::gemm_fused_supported(L.A_max, c->N, c->H, c->F);
   if (L.mfma && !L.fused) {
     // the down projection splits K when there are too few output tiles to
-    // occupy 256 compute units
+    // spread evenly over 256 compute units (the grid bound below counts a
+    // partial row tile per expert, so it overstates the real tiles)
     int bm, bn;
     moe::gemm_bf16_mfma_tile(L.A_max, c->N, &bm, &bn);
     const int64_t tiles = ((L.A_max + bm - 1) / bm + std::min<int64_t>(c->N, L.A_max)) * ((c->H + bn - 1) / bn);
-    if (tiles > 0 && tiles < 512) {
-      int64_t s = (1024 + tiles - 1) / tiles;
+    if (tiles > 0 && tiles < 2048) {
+      int64_t s = (2048 + tiles - 1) / tiles;
       s = std::min<int64_t>(s, 8);
       s = std::min<int64_t>(s, std::max<int64_t>(1, c->F / 512));
       L.splits = static_cast<int>(std::max<int64_t>(1, s));

@@ -26,6 +26,9 @@ SMALL = {
                                                 capacity=synth.capacity_from_cf(512, 8, 2, 4.0)),
     "upcycled_dropless": lambda: synth.make_upcycled("up_dl", 25, 300, 256, 192, 8, 2),
     "decode_skewed": lambda: synth.apply_skew(synth.make_independent("dec", 26, 64, 512, 1024, 8, 2), n_pref=32),
+    # decode-shaped tiles with K tails inside a K step in both GEMMs (H 1032,
+    # F 1376), a ragged last column tile, and the down projection split over K
+    "decode_k_tails": lambda: synth.make_independent("deck", 39, 30, 1032, 1376, 8, 2),
     "fp32_split": lambda: synth.make_split("fp32", 27, 200, 128, 8 * 40, 8, 2, act="f32", wt="f32"),
     "st_order": lambda: synth.make_split("st", 28, 150, 256, 8 * 32, 8, 2, order=synth.ST),
     "bf16_f_not_mult8": lambda: synth.make_independent("f86", 29, 100, 256, 86, 8, 2, out_scale=4.0),

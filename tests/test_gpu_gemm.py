@@ -21,6 +21,7 @@ CASES = {
     "mfma_k_tail_688": (260, 768, 688, 16, 4, "bf16", -1),
     "mfma_capacity": (400, 256, 136, 8, 2, "bf16", 37),
     "mfma_small_m": (20, 512, 384, 8, 2, "bf16", -1),
+    "mfma_decode_k_tails": (24, 1032, 1376, 8, 2, "bf16", -1),
     "mfma_one_expert": (130, 256, 64, 1, 1, "bf16", -1),
     "vector_bf16_f86": (150, 256, 86, 8, 2, "bf16", -1),
     "vector_f32": (256, 256, 86, 8, 2, "f32", -1),
