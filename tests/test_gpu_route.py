@@ -31,6 +31,12 @@ CASES = {
     "n1k1": lambda: synth.make_independent("n1", 19, 33, 64, 8, 1, 1),
     "n64k8_noisy": lambda: synth.make_independent("n64", 20, 40, 256, 8, 64, 8, noisy=True, want_stats=True),
     "exact_ties": _ties,
+    # the matrix-core router's code paths: folded B operand with the noise
+    # columns (N <= 4), folded with H past two LDS chunks (the chunk loop,
+    # with a partial last chunk), and unfolded at 9..16 columns
+    "fold_noisy_n4k2": lambda: synth.make_independent("fn4", 21, 100, 256, 8, 4, 2, noisy=True, want_stats=True),
+    "fold_long_h": lambda: synth.make_independent("flh", 22, 50, 4360, 8, 8, 2),
+    "n12k3": lambda: synth.make_independent("n12", 23, 120, 512, 8, 12, 3),
     "C1_full": synth.c1,
     "C2_full_routing": lambda: synth.make_split("C2_routing", 1002, 4096, 4096, 8 * 8, 8, 2, out_scale=4.0),
     "C3_full_routing": lambda: synth.make_split("C3_routing", 1003, 4096, 4096, 16 * 8, 16, 4, noisy=True,
