@@ -183,6 +183,8 @@ __device__ __forceinline__ void mma_stage(const uint16_t* __restrict__ a, const 
 // branch; a column past Nout gets a byte offset of at least kStoreOOB, beyond
 // every descriptor (tile offsets stay far below 2^31, so the sum cannot wrap).
 constexpr uint32_t kStoreOOB = 0x80000000u;
+// cache-policy bits of the epilogue stores (h, and y_perm or its split partials)
+constexpr int kHStorePolicy = 0, kYStorePolicy = 0;
 
 // SiLU(z) = z * sigmoid(z) with the hardware exp2 and reciprocal, each within
 // about one ulp of fp32, far below the bf16 rounding of h that follows.
@@ -213,8 +215,8 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, const TilePos& tp,
                                (__bf16)(silu_fast(acc[i][j][r + 1]) * acc[i][j + NB / 2][r + 1])};
           const uint32_t bits = __builtin_bit_cast(uint32_t, hv);
           const uint32_t off = cb + static_cast<uint32_t>(i * 32 + (r >> 2) * 8 + (r & 3)) * ld;
-          __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(bits), rc, off, 0, 0);
-          __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(bits >> 16), rc, off + ld, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(bits), rc, off, 0, kHStorePolicy);
+          __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(bits >> 16), rc, off + ld, 0, kHStorePolicy);
         }
       }
   } else {
@@ -234,7 +236,8 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, const TilePos& tp,
           // the vector subscript is compiled as element 0 for every r
           const float v = acc[i][j][r];
           __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rc,
-                                                cb + static_cast<uint32_t>(i * 32 + (r >> 2) * 8 + (r & 3)) * ld, 0, 0);
+                                                cb + static_cast<uint32_t>(i * 32 + (r >> 2) * 8 + (r & 3)) * ld, 0,
+                                                kYStorePolicy);
         }
       }
   }
