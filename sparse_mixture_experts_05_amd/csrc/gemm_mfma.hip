@@ -510,9 +510,9 @@ __device__ __forceinline__ int dec_swz(int row, int chunk) {
   return row * BK + ((chunk ^ (row & 15)) << 3);
 }
 
-template <int BK, int STAGES, int NW, bool SWIGLU, bool GATHER>
+template <int BM, int BK, int STAGES, int NW, bool SWIGLU, bool GATHER>
 __global__ __launch_bounds__(NW * 64) void k_gemm_decode(GemmParams p) {
-  constexpr int BM = kDecBM, BN = kDecBN;
+  constexpr int BN = kDecBN, MB = BM / 32;
   constexpr int NO = SWIGLU ? BN / 2 : BN;
   constexpr int CPR = BK / 8;              // 16-byte chunks per LDS row
   constexpr int RPS = 64 / CPR;            // rows per 1-KB load segment (one load per wave)
@@ -522,7 +522,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_decode(GemmParams p) {
   constexpr int KSW = KS / NW;             // slices per wave
   static_assert(CPR >= 16 && IA * RPS * NW == BM && IB * RPS * NW == BN && KSW * NW == KS, "decode tile shape");
   static_assert(STAGES >= 2 && (STAGES - 2) * LPS <= 63, "stage count");
-  static_assert(STAGES * (BM + BN) * BK >= NW * 2 * 16 * 64 * 2, "partials fit in the stages");
+  static_assert(STAGES * (BM + BN) * BK >= NW * MB * 2 * 16 * 64 * 2, "partials fit in the stages");
   __shared__ __attribute__((aligned(16))) uint16_t smem[STAGES * (BM + BN) * BK];
 
   TilePos tp;
@@ -579,7 +579,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_decode(GemmParams p) {
     }
   };
 
-  f32x16_t acc[1][2];
+  f32x16_t acc[MB][2];
   zero_acc(acc);
   const int frow = lane & 31, khalf = lane >> 5;
 #pragma unroll
@@ -591,43 +591,50 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_decode(GemmParams p) {
     if (kt + STAGES - 1 < tp.KT) issue((kt + STAGES - 1) % STAGES, kt + STAGES - 1);
     const uint16_t* a = sA(kt % STAGES);
     const uint16_t* b = sB(kt % STAGES);
-    bf16x8_t af[KSW], bf0[KSW], bf1[KSW];
+    bf16x8_t af[KSW][MB], bf0[KSW], bf1[KSW];
 #pragma unroll
     for (int q = 0; q < KSW; ++q) {
       const int chunk = (wave * KSW + q) * 2 + khalf;
-      af[q] = *reinterpret_cast<const bf16x8_t*>(&a[dec_swz<BK>(frow, chunk)]);
+#pragma unroll
+      for (int i = 0; i < MB; ++i) af[q][i] = *reinterpret_cast<const bf16x8_t*>(&a[dec_swz<BK>(i * 32 + frow, chunk)]);
       bf0[q] = *reinterpret_cast<const bf16x8_t*>(&b[dec_swz<BK>(frow, chunk)]);
       bf1[q] = *reinterpret_cast<const bf16x8_t*>(&b[dec_swz<BK>(32 + frow, chunk)]);
     }
 #pragma unroll
-    for (int q = 0; q < KSW; ++q) {
-      acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[q], bf0[q], acc[0][0], 0, 0, 0);
-      acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[q], bf1[q], acc[0][1], 0, 0, 0);
-    }
+    for (int q = 0; q < KSW; ++q)
+#pragma unroll
+      for (int i = 0; i < MB; ++i) {
+        acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[q][i], bf0[q], acc[i][0], 0, 0, 0);
+        acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[q][i], bf1[q], acc[i][1], 0, 0, 0);
+      }
   }
 
   // partial sums of the four waves, added in wave order by wave 0
   lds_barrier();
-  float* red = reinterpret_cast<float*>(smem);  // [wave][j][r][lane]
+  float* red = reinterpret_cast<float*>(smem);  // [wave][i][j][r][lane]
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+  for (int i = 0; i < MB; ++i)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float v = acc[0][j][r];
-      red[((wave * 2 + j) * 16 + r) * 64 + lane] = v;
-    }
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float v = acc[i][j][r];
+        red[(((wave * MB + i) * 2 + j) * 16 + r) * 64 + lane] = v;
+      }
   lds_barrier();
   if (wave != 0) return;
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+  for (int i = 0; i < MB; ++i)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float v = red[(j * 16 + r) * 64 + lane];
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int w = 1; w < NW; ++w) v += red[((w * 2 + j) * 16 + r) * 64 + lane];
-      acc[0][j][r] = v;
-    }
-  epilogue<BM, BN, 1, 2, SWIGLU>(p, tp, 0, 0, lane, NO, acc);
+      for (int r = 0; r < 16; ++r) {
+        float v = red[((i * 2 + j) * 16 + r) * 64 + lane];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) v += red[(((w * MB + i) * 2 + j) * 16 + r) * 64 + lane];
+        acc[i][j][r] = v;
+      }
+  epilogue<BM, BN, MB, 2, SWIGLU>(p, tp, 0, 0, lane, NO, acc);
 }
 
 // ---- both expert GEMMs in one persistent launch ---------------------------------
@@ -841,17 +848,17 @@ hipError_t launch_dma(const GemmParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int BK, int STAGES, int NW>
+template <int BM, int BK, int STAGES, int NW>
 hipError_t launch_decode(const GemmParams& p, hipStream_t s) {
-  const int64_t blocks = grid_blocks(p, kDecBM, kDecBN);
+  const int64_t blocks = grid_blocks(p, BM, kDecBN);
   if (blocks <= 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>(blocks)), block(NW * 64);
   if (p.swiglu) {
-    if (p.row_token) hipLaunchKernelGGL((k_gemm_decode<BK, STAGES, NW, true, true>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((k_gemm_decode<BK, STAGES, NW, true, false>), grid, block, 0, s, p);
+    if (p.row_token) hipLaunchKernelGGL((k_gemm_decode<BM, BK, STAGES, NW, true, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((k_gemm_decode<BM, BK, STAGES, NW, true, false>), grid, block, 0, s, p);
   } else {
-    if (p.row_token) hipLaunchKernelGGL((k_gemm_decode<BK, STAGES, NW, false, true>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((k_gemm_decode<BK, STAGES, NW, false, false>), grid, block, 0, s, p);
+    if (p.row_token) hipLaunchKernelGGL((k_gemm_decode<BM, BK, STAGES, NW, false, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((k_gemm_decode<BM, BK, STAGES, NW, false, false>), grid, block, 0, s, p);
   }
   return hipGetLastError();
 }
@@ -901,7 +908,7 @@ hipError_t launch_experts_fused(const FusedParams& fp, hipStream_t s) {
 hipError_t launch_gemm_bf16_mfma(const GemmParams& p, hipStream_t s) {
   int bm, bn;
   gemm_bf16_mfma_tile(p.rows_max, p.N, &bm, &bn);
-  if (bm == kDecBM) return launch_decode<128, 3, 4>(p, s);
+  if (bm == kDecBM) return launch_decode<kDecBM, 128, 3, 4>(p, s);
   return launch_dma<256, 256, 4, 2, 2, 64>(p, s);
 }
 
