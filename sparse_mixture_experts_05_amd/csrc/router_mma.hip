@@ -140,6 +140,20 @@ __global__ __launch_bounds__(router_waves<NB16>() * 64) void k_router_mma(Router
   int trow[AF];
 #pragma unroll
   for (int th = 0; th < AF; ++th) trow[th] = FOLD ? 8 * th + (row & 7) : row;
+  // f / N for the weight pieces' rows: a multiply-high by ceil(2^32 / N),
+  // exact for f < 2^32 / N (f stays below a chunk's hc * N floats); N = 1,
+  // whose multiplier does not fit 32 bits, is the identity
+  const uint32_t n_inv = N > 1 ? 0xFFFFFFFFu / static_cast<uint32_t>(N) + 1u : 0u;
+  auto div_n = [&](int f) { return N > 1 ? static_cast<int>(__umulhi(static_cast<uint32_t>(f), n_inv)) : f; };
+  // the noise draws of this wave's tokens, requested now so that their
+  // latency hides behind the product
+  constexpr int kTW = (kTok + kWaves - 1) / kWaves;  // tokens per wave in the gate step
+  float eps_pre[kTW];
+#pragma unroll
+  for (int i = 0; i < kTW; ++i) {
+    const int t = wave + i * kWaves;
+    eps_pre[i] = (p.noisy && lane < N && t < kTok && tok0 + t < T) ? p.eps[(tok0 + t) * N + lane] : 0.0f;
+  }
   const int wu = hc / UR / kWaves;  // this wave's steps per chunk
   const int hcp = hc + kWPad;       // LDS column stride: column j holds the chunk's rows contiguous
 
@@ -199,7 +213,7 @@ __global__ __launch_bounds__(router_waves<NB16>() * 64) void k_router_mma(Router
       int m, q;
       piece(j, m, q);
       if (q < c4) {
-        const int f = 4 * q, r = f / N, n = f - r * N + m * N;  // row and first column of the piece
+        const int f = 4 * q, r = div_n(f), n = f - r * N + m * N;  // row and first column of the piece
 #pragma unroll
         for (int e = 0; e < 4; ++e) sb[(n + e) * hcp + r] = wb[j][e];
       }
@@ -207,7 +221,7 @@ __global__ __launch_bounds__(router_waves<NB16>() * 64) void k_router_mma(Router
     for (int m = 0; m < (p.noisy ? 2 : 1); ++m) {
       const float* src = (m == 0 ? p.Wg : p.Wn) + static_cast<int64_t>(h0) * N;
       for (int i = 4 * c4 + threadIdx.x; i < cnt; i += kThreads) {
-        const int r = i / N;
+        const int r = div_n(i);
         sb[(i - r * N + m * N) * hcp + r] = src[i];
       }
     }
@@ -334,14 +348,16 @@ __global__ __launch_bounds__(router_waves<NB16>() * 64) void k_router_mma(Router
   __shared__ int s_take[kTok][64];   // 1 if expert n is among the token's top k
   __shared__ float s_p[kTok][64];    // softmax of the clean logits
   const bool valid = lane < N;
-  for (int t = wave; t < kTok; t += kWaves) {
+#pragma unroll
+  for (int i = 0; i < kTW; ++i) {
+    const int t = wave + i * kWaves;
     const int64_t g = tok0 + t;
-    if (g >= T) break;  // wave-uniform
+    if (t >= kTok || g >= T) break;  // wave-uniform
     const float lv = valid ? s_log[t][lane] : -INFINITY;
     float hv = lv;
     // H_i = (x W_g)_i + StandardNormal() * Softplus((x W_noise)_i), the
     // normal draw being the input eps[t, i]
-    if (p.noisy && valid) hv = fmaf(p.eps[g * N + lane], softplus(s_log[t][N + lane]), lv);
+    if (p.noisy && valid) hv = fmaf(eps_pre[i], softplus(s_log[t][N + lane]), lv);
     if (p.logits && valid) p.logits[g * N + lane] = lv;
     // rank: experts with a larger score, or an equal one at a lower index
     int rank = 0;
