@@ -824,7 +824,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_experts_fused(FusedParams fp
   if (fp.stats && ticket == ntot) stats_reduce(fp.st, smem);
 }
 
-// ---- register-staged loads -------------------------------------------------------
+// ---- launches --------------------------------------------------------------------
 
 int64_t grid_blocks(const GemmParams& p, int BM, int BN) {
   const int NO = p.swiglu ? BN / 2 : BN;
