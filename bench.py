@@ -91,7 +91,7 @@ WORKLOADS = {
 def main():
     args = parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build runs the MoE layer on a single MI355X and has no "
+        print(f"bench.py measures one GPU: the MoE layer runs on a single MI355X and there is no "
               f"multi-GPU path (asked for --gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
     if args.config not in WORKLOADS:
