@@ -309,9 +309,16 @@ def cpu_baseline(w, target_s: float):
     t1 = time.perf_counter()
     oracle.forward(sample(S), nthreads=cores)
     dt = time.perf_counter() - t1
+    # the same oracle on one thread, on a sample a core count smaller
+    S1 = max(1, S // cores)
+    t2 = time.perf_counter()
+    oracle.forward(sample(S1), nthreads=1)
+    dt1 = time.perf_counter() - t2
     return {"value": round(S / dt, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"first {S} of {w.T} tokens of the same layer (routing, capacity and experts of those "
-                      f"tokens), fp64 accumulation, {dt:.1f} s"}
+                      f"tokens), fp64 accumulation, {dt:.1f} s",
+            "single_thread": {"value": round(S1 / dt1, 2), "unit": "tokens/s", "cores": 1,
+                              "sample": f"first {S1} tokens, {dt1:.1f} s"}}
 
 
 if __name__ == "__main__":
