@@ -140,40 +140,64 @@ __device__ __forceinline__ void frag_rows(int wm, int wn, int lane, int (&arow)[
   }
 }
 
-// One BK step of MFMAs from an LDS stage. PARTIAL: only the wave's first
-// `live` 32-row blocks hold rows of the expert (wave-uniform), and the rest of
-// an expert's last, partly filled tile is skipped, MFMAs and operand reads
-// alike; full tiles take the branch-free copy.
-template <int MB, int NB, int BK, bool PARTIAL = false>
-__device__ __forceinline__ void mma_stage(const uint16_t* __restrict__ a, const uint16_t* __restrict__ b,
-                                          const int (&arow)[MB], const int (&brow)[NB], int khalf,
-                                          f32x16_t (&acc)[MB][NB], int live = MB) {
-  // two fragment sets: the LDS reads of K slice ks + 1 are issued before the
-  // MFMAs of slice ks, so they land while those run
-  constexpr int KS = BK / 16;
+// A wave's operand fragments for the K loop, in two register sets: the LDS
+// reads of one K slice are in flight while the MFMAs of the previous slice
+// run. A stage's last slice lands in set 1 and its MFMAs wait for the next
+// step, after the barrier, so that step's first reads overlap them instead of
+// leaving the matrix cores idle. PARTIAL: only the wave's first `live` 32-row
+// blocks hold rows of the expert (wave-uniform), and the rest of an expert's
+// last, partly filled tile is skipped, MFMAs and operand reads alike; full
+// tiles take the branch-free copy.
+template <int MB, int NB, int BK, bool PARTIAL>
+struct FragPipe {
+  static constexpr int KS = BK / 16;
+  static_assert(KS % 2 == 0, "a stage's last slice must land in set 1");
   bf16x8_t af[2][MB], bfr[2][NB];
-  auto load = [&](int ks, int buf) {
+
+  // set 1 starts as zeros, so the carried MFMAs of the first step add exact zeros
+  __device__ __forceinline__ void init() {
+#pragma unroll
+    for (int i = 0; i < MB; ++i) af[1][i] = bf16x8_t{};
+#pragma unroll
+    for (int j = 0; j < NB; ++j) bfr[1][j] = bf16x8_t{};
+  }
+
+  __device__ __forceinline__ void load(const uint16_t* __restrict__ a, const uint16_t* __restrict__ b,
+                                       const int (&arow)[MB], const int (&brow)[NB], int khalf, int ks, int buf,
+                                       int live) {
     const int chunk = ks * 2 + khalf;
 #pragma unroll
     for (int i = 0; i < MB; ++i)
       if (!PARTIAL || i < live) af[buf][i] = *reinterpret_cast<const bf16x8_t*>(&a[swz<BK>(arow[i], chunk)]);
 #pragma unroll
     for (int j = 0; j < NB; ++j) bfr[buf][j] = *reinterpret_cast<const bf16x8_t*>(&b[swz<BK>(brow[j], chunk)]);
-  };
-  load(0, 0);
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    const int cur = ks & 1;
-    if (ks + 1 < KS) load(ks + 1, cur ^ 1);
-    __builtin_amdgcn_sched_barrier(0);  // keep those reads ahead of the MFMAs below
+  }
+
+  __device__ __forceinline__ void mma(int buf, f32x16_t (&acc)[MB][NB], int live) {
 #pragma unroll
     for (int i = 0; i < MB; ++i)
       if (!PARTIAL || i < live)
 #pragma unroll
         for (int j = 0; j < NB; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][i], bfr[cur][j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[buf][i], bfr[buf][j], acc[i][j], 0, 0, 0);
   }
-}
+
+  // one stage: slice 0's reads, then the previous stage's last slice, then
+  // slices 0 .. KS-2 each behind the next slice's reads; slice KS-1 stays in set 1
+  __device__ __forceinline__ void stage(const uint16_t* __restrict__ a, const uint16_t* __restrict__ b,
+                                        const int (&arow)[MB], const int (&brow)[NB], int khalf,
+                                        f32x16_t (&acc)[MB][NB], int live) {
+    load(a, b, arow, brow, khalf, 0, 0, live);
+    __builtin_amdgcn_sched_barrier(0);  // keep those reads ahead of the MFMAs below
+    mma(1, acc, live);
+#pragma unroll
+    for (int ks = 0; ks + 1 < KS; ++ks) {
+      load(a, b, arow, brow, khalf, ks + 1, (ks + 1) & 1, live);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(ks & 1, acc, live);
+    }
+  }
+};
 
 // Accumulator layout of a 32x32 block: lane holds column (lane & 31) and rows
 // 8*(r/4) + 4*(lane/32) + r%4 for r = 0..15.
@@ -275,7 +299,16 @@ __device__ __forceinline__ void wait_stage(int later) {
   wait_vm<0>();
 }
 
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+// LDS operations complete, then a workgroup barrier. The wait is the builtin
+// (lgkmcnt 0, the other counters at their maximum) rather than inline asm, so
+// the compiler's own wait insertion knows that every earlier LDS read has
+// landed; the empty asm statements keep memory operations on their side.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -288,9 +321,10 @@ template <int MB, int NB, int BK, bool PARTIAL, class Issue>
 __device__ __forceinline__ void dma_step(Issue& issue, bool do_issue, int kt_next, const uint16_t* __restrict__ a_cur,
                                          const uint16_t* __restrict__ b_cur, uint16_t* __restrict__ a_nxt,
                                          uint16_t* __restrict__ b_nxt, const int (&arow)[MB], const int (&brow)[NB],
-                                         int khalf, f32x16_t (&acc)[MB][NB], int live) {
+                                         int khalf, f32x16_t (&acc)[MB][NB], int live,
+                                         FragPipe<MB, NB, BK, PARTIAL>& fp) {
   if (do_issue) issue(a_nxt, b_nxt, kt_next);
-  mma_stage<MB, NB, BK, PARTIAL>(a_cur, b_cur, arow, brow, khalf, acc, live);
+  fp.stage(a_cur, b_cur, arow, brow, khalf, acc, live);
 }
 
 // LDS elements of one workgroup's operand stages.
@@ -459,6 +493,8 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const TilePos& tp
   // partly filled tile's empty row blocks
   const int kt_reserve = max(0, tp.KT - 3);
   auto kloop = [&](auto partial) {
+    FragPipe<MB, NB, BK, decltype(partial)::value> fp;
+    fp.init();
     for (int kt = 0; kt < tp.KT; ++kt) {
       const int later = min(STAGES - 2, tp.KT - 1 - kt);
       wait_stage<LPS, STAGES - 2>(later);
@@ -466,8 +502,9 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const TilePos& tp
       if (kt == kt_reserve) reserve();
       const int st = (sbase + kt) % STAGES, nx = (sbase + kt + STAGES - 1) % STAGES;
       dma_step<MB, NB, BK, decltype(partial)::value>(issue, kt + STAGES - 1 < tp.KT, kt + STAGES - 1, sA(st), sB(st),
-                                                     sA(nx), sB(nx), arow, brow, khalf, acc, live);
+                                                     sA(nx), sB(nx), arow, brow, khalf, acc, live, fp);
     }
+    fp.mma(1, acc, live);  // the last stage's last slice
   };
   if (live == MB)
     kloop(std::false_type{});
