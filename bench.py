@@ -254,6 +254,15 @@ def main():
         torch.cuda.synchronize()
         warm_ms = (time.perf_counter() - t1) * 1e3 / args.steps
         g2 = per_kernel.get("gemm2_down")
+        # per-step HBM rates of the data-movement steps from their own bytes:
+        # the combine reads every kept fp32 y_perm row and the routing and
+        # writes fp32 y; the scatter reads topk_idx and the per-block
+        # histogram and writes slot and row_token (the x rows are gathered
+        # inside the gate/up GEMM, so no x_perm is written)
+        comb_b = A * H * 4 + T * k * 8 + T * H * 4
+        scat_b = T * k * 4 + ((T + 15) // 16) * N * 4 + T * k * 4 + A * 4
+        step_gbs = {name: round(b / (per_kernel[name] * 1e-6) / 1e9, 1)
+                    for name, b in (("combine", comb_b), ("permute_scatter", scat_b)) if per_kernel.get(name)}
         detail = dict(device=dev_name, kept_rows=A, active_experts=active, kept_per_expert=kept_h.tolist(),
                       kernel_avg_us=per_kernel, layer_us=round(t_layer * 1e6, 2),
                       layer_tflops=round((f_expert + f_router) / t_layer / 1e12, 1),
@@ -261,6 +270,7 @@ def main():
                       layer_roofline_us=round(t_roof * 1e6, 2), layer_bound="hbm" if t_mem > t_compute else "compute",
                       layer_frac_of_roofline=round(t_roof / t_layer, 4),
                       gemm2_tflops=round(2.0 * A * F * H / (g2 * 1e-6) / 1e12, 1) if g2 else None,
+                      step_bytes={"combine": comb_b, "permute_scatter": scat_b}, step_gbs=step_gbs,
                       same_inputs_every_step_ms=round(warm_ms, 4), input_copies=len(copies))
 
     cpu = None
