@@ -64,20 +64,41 @@ __global__ __launch_bounds__(kScatterThreads) void k_scatter(ScatterParams p) {
     const int64_t nel = nhb * N;
     const int64_t split = hb0 * N;  // elements before this block's first histogram row
     constexpr int U = 8;  // loads in flight per thread before their adds
-    for (int64_t i0 = tid; i0 < nel; i0 += U * kScatterThreads) {
-      int v[U];
+    if (kScatterThreads % N == 0) {
+      // every element this thread reads is a count of expert tid % N: sum in
+      // registers, then one LDS add per counter instead of one per element
+      int tot = 0, base = 0;
+      for (int64_t i0 = tid; i0 < nel; i0 += U * kScatterThreads) {
+        int v[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int64_t i = i0 + u * kScatterThreads;
-        v[u] = i < nel ? p.hist[i] : 0;
+        for (int u = 0; u < U; ++u) {
+          const int64_t i = i0 + u * kScatterThreads;
+          v[u] = i < nel ? p.hist[i] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          tot += v[u];
+          if (i0 + u * kScatterThreads < split) base += v[u];
+        }
       }
+      if (tot) atomicAdd(&s_tot[tid % N], tot);
+      if (base) atomicAdd(&s_base[tid % N], base);
+    } else {
+      for (int64_t i0 = tid; i0 < nel; i0 += U * kScatterThreads) {
+        int v[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int64_t i = i0 + u * kScatterThreads;
-        const int n = static_cast<int>(i % N);
-        if (v[u]) {
-          atomicAdd(&s_tot[n], v[u]);
-          if (i < split) atomicAdd(&s_base[n], v[u]);
+        for (int u = 0; u < U; ++u) {
+          const int64_t i = i0 + u * kScatterThreads;
+          v[u] = i < nel ? p.hist[i] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int64_t i = i0 + u * kScatterThreads;
+          const int n = static_cast<int>(i % N);
+          if (v[u]) {
+            atomicAdd(&s_tot[n], v[u]);
+            if (i < split) atomicAdd(&s_base[n], v[u]);
+          }
         }
       }
     }
