@@ -90,6 +90,28 @@ def test_forward_is_deterministic():
         assert np.array_equal(a[key], b[key]), key
 
 
+def test_forward_follows_the_callers_stream():
+    """Every launch goes to the stream the caller makes current: on a side
+    stream whose x is written only after a long matmul, the layer must read
+    the new x (a launch on another stream would race ahead and see zeros)."""
+    w = synth.make_split("strm", 41, 1200, 1024, 8 * 96, 8, 2, out_scale=4.0, want_stats=True)
+    d = upload(w)
+    ref = run_forward(w, d=d)
+    side = torch.cuda.Stream()  # default priority
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        x2 = torch.zeros_like(d["x"])
+        m = torch.randn(4096, 4096, device="cuda")
+        for _ in range(8):
+            m = torch.mm(m, m) * 1e-3  # keeps the side stream busy for a while
+        x2.copy_(d["x"])
+        got = run_forward(w, d=dict(d, x=x2))
+    side.synchronize()
+    for key in ref:
+        assert np.array_equal(ref[key], got[key]), key
+    del m
+
+
 def test_full_C2_is_deterministic():
     """The expert GEMMs run as one persistent launch whose workgroups take
     tiles from a queue in whatever order they arrive; every output element is
