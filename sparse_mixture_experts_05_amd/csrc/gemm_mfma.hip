@@ -207,8 +207,12 @@ struct FragPipe {
 // branch; a column past Nout gets a byte offset of at least kStoreOOB, beyond
 // every descriptor (tile offsets stay far below 2^31, so the sum cannot wrap).
 constexpr uint32_t kStoreOOB = 0x80000000u;
-// cache-policy bits of the epilogue stores (h, and y_perm or its split partials)
-constexpr int kHStorePolicy = 0, kYStorePolicy = 0;
+// Cache-policy bits of the epilogue stores. h is stored at device scope (sc1,
+// bit 4 of the policy): such a store is coherent across the XCDs' L2s once it
+// has completed, so the persistent kernel publishes a finished h tile by
+// waiting for its stores instead of writing back the whole L2. y_perm (or its
+// split partials) is read only by a later launch and uses the default policy.
+constexpr int kHStorePolicy = 16, kYStorePolicy = 0;
 
 // SiLU(z) = z * sigmoid(z) with the hardware exp2 and reciprocal, each within
 // about one ulp of fp32, far below the bf16 rounding of h that follows.
@@ -836,14 +840,15 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_experts_fused(FusedParams fp
     int rb;
     if (decode(ticket, tp, rb)) {
       gemm_tile<BM, BN, WGM, WGN, STAGES, BK, true, GATHER>(g1, tp, smem, sbase, pre, hook, reserve);
-      // publish: every wave's h stores complete, then one device-scope
-      // release (a single write-back) before the count
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      // publish: every wave waits until its device-scope h stores have
+      // completed (the wait also covers the next tile's first loads, issued
+      // before the epilogue and needed next anyway), then one count. No L2
+      // write-back: the h lines were written through at device scope.
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0); the other counters at their maximum
       __syncthreads();
-      if (threadIdx.x == 0) {
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      if (threadIdx.x == 0)
         __hip_atomic_fetch_add(&fp.sched[kSchedDone + rb], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
     } else {
       if (threadIdx.x == 0) {
         wait_count(&fp.sched[kSchedDone + rb], NT1, &fp.sched[kSchedError]);
