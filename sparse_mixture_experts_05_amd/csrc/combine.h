@@ -14,6 +14,14 @@
 namespace moe {
 namespace cmb {
 
+// Every y_perm element is read once and every y element written once, so
+// both go through non-temporal accesses (same values; at the 2/8 and 4/16
+// LLaMA-MoE shapes the layer runs 1.4% and 2.4% faster than with the default
+// cache policy).
+__device__ __forceinline__ f32x4_t ld_nt(const float* src) {
+  return __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(src));
+}
+
 // Sum of one 4-column group over the token's kept slots, in slot order; the
 // split-K partials of a row are added in split order first.
 template <int KMAX>
@@ -26,8 +34,8 @@ __device__ __forceinline__ f32x4_t gather_sum(const CombineParams& p, const int 
     v[j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     if (sl[j] >= 0) {
       const float* src = p.y_perm + static_cast<int64_t>(sl[j]) * p.H + c * 4;
-      v[j] = *reinterpret_cast<const f32x4_t*>(src);
-      for (int s = 1; s < p.splits; ++s) v[j] += *reinterpret_cast<const f32x4_t*>(src + s * p.split_stride);
+      v[j] = ld_nt(src);
+      for (int s = 1; s < p.splits; ++s) v[j] += ld_nt(src + s * p.split_stride);
     }
   }
 #pragma unroll
@@ -47,9 +55,10 @@ __device__ __forceinline__ void store4(const CombineParams& p, int64_t t, int64_
     uint16_t* y = static_cast<uint16_t*>(p.y) + t * p.H + c * 4;
     const uint32_t lo = static_cast<uint32_t>(f32_to_bf16(acc[0])) | (static_cast<uint32_t>(f32_to_bf16(acc[1])) << 16);
     const uint32_t hi = static_cast<uint32_t>(f32_to_bf16(acc[2])) | (static_cast<uint32_t>(f32_to_bf16(acc[3])) << 16);
-    *reinterpret_cast<uint2*>(y) = make_uint2(lo, hi);
+    typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+    __builtin_nontemporal_store(u32x2_t{lo, hi}, reinterpret_cast<u32x2_t*>(y));
   } else {
-    *(reinterpret_cast<f32x4_t*>(static_cast<float*>(p.y) + t * p.H) + c) = acc;
+    __builtin_nontemporal_store(acc, reinterpret_cast<f32x4_t*>(static_cast<float*>(p.y) + t * p.H) + c);
   }
 }
 
@@ -66,8 +75,8 @@ __device__ __forceinline__ void token_any(const CombineParams& p, int64_t t, int
       if (sl < 0) continue;
       const float w = p.topk_w[t * k + j];
       const float* src = p.y_perm + static_cast<int64_t>(sl) * p.H + c * 4;
-      f32x4_t v = *reinterpret_cast<const f32x4_t*>(src);
-      for (int s = 1; s < p.splits; ++s) v += *reinterpret_cast<const f32x4_t*>(src + s * p.split_stride);
+      f32x4_t v = ld_nt(src);
+      for (int s = 1; s < p.splits; ++s) v += ld_nt(src + s * p.split_stride);
 #pragma unroll
       for (int q = 0; q < 4; ++q) acc[q] = fmaf(w, v[q], acc[q]);
     }
