@@ -142,6 +142,9 @@ int oracle_route(const oracle_cfg* c, const void* x, const float* Wg, const floa
        * draw is the input eps[t,i] */
       double hv = lg[i];
       if (c->noisy) hv += static_cast<double>(eps[t * N + i]) * oracle_softplus(nz[i]);
+      /* the pages leave non-numbers open; a NaN score is read as -inf: it
+       * never outranks a number and adds 0 to every softmax denominator */
+      if (std::isnan(hv)) hv = -std::numeric_limits<double>::infinity();
       Hrow[i] = static_cast<float>(hv);
     }
     /* KeepTopK ([UP] section 3): the k largest scores, ties to the lower index */

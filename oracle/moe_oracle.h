@@ -58,7 +58,8 @@ typedef struct {
 /* Router + KeepTopK + gate weights for every token.
  * x [T,H] (x_dtype), Wg [H,N] fp32, Wn [H,N] fp32 and eps [T,N] fp32 (used iff noisy).
  * Out: logits [T,N] fp32 = fl32(x.Wg) (clean), Hv [T,N] fp32 = selection scores,
- *      topk_idx [T,k] (sorted by Hv descending, ties to the lower index),
+ *      topk_idx [T,k] (sorted by Hv descending, ties to the lower index;
+ *      a NaN score is stored and ranked as -inf),
  *      topk_w [T,k] double, min_gap [T] double (smallest gap between adjacent
  *      sorted scores among the first min(k+1, N); +inf when N == 1). */
 int oracle_route(const oracle_cfg* c, const void* x, const float* Wg, const float* Wn, const float* eps,

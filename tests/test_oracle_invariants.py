@@ -13,6 +13,8 @@ I8  stats closed form at a zero router.
 I9  k = 1 Mixtral gives w = 1; all-equal scores give w = 1/k on 0..k-1.
 I10 dropless outputs are equivariant under token permutation.
 I11 relabelling the experts leaves y unchanged (no score ties).
+I12 a NaN router score ranks as -inf: the layer equals the same layer
+    without that expert (reading of the pages' silence on non-numbers).
 """
 import numpy as np
 import torch
@@ -156,6 +158,26 @@ def test_I8_stats_closed_form_at_zero_router():
         assert abs(st["balance"] - 1.0 / N) < 1e-15
         assert st["load"].sum() == w.T * k
         assert abs(st["importance"].sum() - w.T) < 1e-12
+        # the code example's variant: importance shares (1/k on the first k)
+        # times the uniform P, times N, with its 1e-6 guard on the total
+        assert abs(st["balance_code"] - w.T / (w.T + 1e-6)) < 1e-14
+
+
+def test_I8b_code_balance_hand_case():
+    """One token, two experts, ST order, top-1, logits (l, 0) with
+    l = fl32(ln 3): softmax = (p, 1 - p), p = 1 / (1 + e^-l), so expert 0 is
+    kept with weight p; importance = (p, 0), P = (p, 1 - p), f = (1, 0).
+    balance = p; the code example's variant = N * (p / (p + 1e-6)) * p."""
+    l = float(np.float32(np.log(3.0)))
+    w = synth.Workload("bal", 1, 1, 1, 2, 1, -1, synth.ST, False, True, 1.0, "f32", "f32",
+                       x=np.ones((1, 1), np.float32), Wg=np.array([[l, 0.0]], np.float32))
+    r = oracle.route(w)
+    st = oracle.stats(w, r)
+    p = 1.0 / (1.0 + np.exp(-l))
+    assert r["topk_idx"].tolist() == [[0]]
+    assert abs(r["topk_w"][0, 0] - p) < 1e-15
+    assert abs(st["balance"] - p) < 1e-15
+    assert abs(st["balance_code"] - 2.0 * (p / (p + 1e-6)) * p) < 1e-15
 
 
 def test_I9_k1_and_equal_scores():
@@ -198,3 +220,31 @@ def test_empty_batch():
     out = oracle.forward(w)
     assert out["y"].shape == (0, w.H)
     assert np.all(out["counts"] == 0) and np.all(out["offsets"] == 0)
+
+
+def test_I12_nan_score_ranks_below_every_number():
+    """A NaN router column (expert 2) is never chosen while k < N, and the
+    routing and output equal those of the same layer without expert 2, in
+    both orders; with k = N it is kept last, with weight 0."""
+    for order in (synth.MIXTRAL, synth.ST):
+        w = f32_split(15, T=20, N=5, k=2, Ftot=5 * 8, order=order)
+        drop = 2
+        keep = [e for e in range(w.N) if e != drop]
+        v = synth.Workload("nan_ref", w.T, w.H, w.F, w.N - 1, w.k, -1, order, False, False, 1.0, "f32", "f32",
+                           x=w.x, Wg=np.ascontiguousarray(w.Wg[:, keep]),
+                           Wgate=np.ascontiguousarray(w.Wgate[keep]), Wup=np.ascontiguousarray(w.Wup[keep]),
+                           Wdown=np.ascontiguousarray(w.Wdown[keep]))
+        w.Wg = w.Wg.copy()
+        w.Wg[:, drop] = np.nan
+        a = oracle.forward(w)
+        b = oracle.forward(v)
+        assert np.array_equal(np.array(keep)[b["topk_idx"]], a["topk_idx"])
+        np.testing.assert_array_equal(a["topk_w"], b["topk_w"])
+        np.testing.assert_array_equal(a["y64"], b["y64"])
+        assert np.all(np.isneginf(a["H"][:, drop]))
+    w = f32_split(16, T=10, N=3, k=3, Ftot=3 * 8)
+    w.Wg = w.Wg.copy()
+    w.Wg[:, 1] = np.nan
+    a = oracle.route(w)
+    assert np.all(a["topk_idx"][:, 2] == 1) and np.all(a["topk_w"][:, 2] == 0.0)
+    np.testing.assert_allclose(a["topk_w"].sum(axis=1), 1.0, rtol=1e-15)

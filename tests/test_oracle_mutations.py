@@ -55,6 +55,14 @@ MUTANTS = [
      "for (int64_t j = 0; j < 1; ++j) {\n      if (slot[t * k + j] < 0) continue;"),
     ("logit_reads_wrong_column", "a += xd[h] * static_cast<double>(Wg[h * N + i]);",
      "a += xd[h] * static_cast<double>(Wg[h * N + (N - 1 - i)]);"),
+    ("code_balance_uses_load", "pm_dot_freq += (importance[i] / (tot_imp + 1e-6)) * P[i];",
+     "pm_dot_freq += (static_cast<double>(load[i]) / (T * k + 1e-6)) * P[i];"),
+    ("code_balance_drops_times_n", "*balance_code = pm_dot_freq * static_cast<double>(N);",
+     "*balance_code = pm_dot_freq;"),
+    ("code_balance_drops_guard", "pm_dot_freq += (importance[i] / (tot_imp + 1e-6)) * P[i];",
+     "pm_dot_freq += (importance[i] / tot_imp) * P[i];"),
+    ("nan_score_not_ranked_last",
+     "if (std::isnan(hv)) hv = -std::numeric_limits<double>::infinity();", "(void)0;"),
 ]
 
 PIN_FILES = ["tests/test_golden.py", "tests/test_oracle_pins.py", "tests/test_oracle_invariants.py",
