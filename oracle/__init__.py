@@ -48,9 +48,10 @@ def load(path: str = None):
     lib.oracle_capacity.argtypes = [cfgp] + [vp] * 6
     lib.oracle_expert_rows.argtypes = [cfgp, vp, vp, vp, vp, i32, vp, i64, i32, vp, vp]
     lib.oracle_combine_tokens.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, vp, vp]
+    lib.oracle_combine_rows.argtypes = [cfgp, vp, vp, vp, i64, vp, vp, vp]
     lib.brute_layer.argtypes = [cfgp] + [vp] * 17
     for f in ("oracle_route", "oracle_stats", "oracle_capacity", "oracle_expert_rows",
-              "oracle_combine_tokens", "brute_layer"):
+              "oracle_combine_tokens", "oracle_combine_rows", "brute_layer"):
         getattr(lib, f).restype = ctypes.c_int
     for f in ("oracle_round_bf16", "oracle_round_f32", "oracle_silu", "oracle_softplus", "brute_round_bf16"):
         getattr(lib, f).argtypes = [ctypes.c_double]
@@ -153,6 +154,37 @@ def combine_tokens(w, topk_idx, topk_w, slot, tokens, nthreads=1, h_round=None, 
                                      _p(np.ascontiguousarray(topk_w, np.float64)),
                                      _p(np.ascontiguousarray(slot, np.int64)), _p(tokens), n, int(nthreads),
                                      _p(y64), _p(y32)), "oracle_combine_tokens")
+    return y64, y32
+
+
+def assignment_outputs(w, topk_idx, tokens=None, nthreads=1, h_round=None, lib=None):
+    """E [n,k,H]: the output of expert topk_idx[t,j] for token t, for every
+    slot j of the listed tokens (all when None), whether or not a capacity
+    keeps it. Each expert runs once over the tokens that chose it."""
+    tokens = np.arange(w.T, dtype=np.int64) if tokens is None else np.asarray(tokens, np.int64)
+    idx = np.asarray(topk_idx)[tokens]
+    E = np.zeros((tokens.size, w.k, w.H))
+    for e in range(w.N):
+        ii, jj = np.nonzero(idx == e)
+        if ii.size:
+            E[ii, jj] = expert_rows(w, e, tokens[ii], nthreads=nthreads, h_round=h_round, lib=lib)
+    return E
+
+
+def combine_rows(w, topk_w, slot, E, tokens=None, h_round=None, lib=None):
+    """The layer output of the listed tokens from expert outputs E [n,k,H]
+    (see assignment_outputs) and a capacity setting's slots."""
+    lib = lib or load()
+    c = cfg(w, h_round)
+    tokens = np.arange(w.T, dtype=np.int64) if tokens is None else np.ascontiguousarray(tokens, np.int64)
+    n = tokens.size
+    E = np.ascontiguousarray(E, np.float64)
+    assert E.shape == (n, w.k, w.H)
+    y64 = np.zeros((n, w.H))
+    y32 = np.zeros((n, w.H), np.float32)
+    _check(lib.oracle_combine_rows(ctypes.byref(c), _p(np.ascontiguousarray(topk_w, np.float64)),
+                                   _p(np.ascontiguousarray(slot, np.int64)), _p(tokens), n, _p(E), _p(y64),
+                                   _p(y32)), "oracle_combine_rows")
     return y64, y32
 
 

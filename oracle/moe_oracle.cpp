@@ -298,4 +298,31 @@ int oracle_combine_tokens(const oracle_cfg* c, const void* x, const void* Wgate,
   return 0;
 }
 
+int oracle_combine_rows(const oracle_cfg* c, const double* topk_w, const int64_t* slot, const int64_t* tokens,
+                        int64_t n, const double* E, double* y64, float* y32) {
+  if (!cfg_ok(c)) return -1;
+  if (n > 0 && (!topk_w || !slot || !tokens || !E)) return -2;
+  const int64_t H = c->H, k = c->k;
+  std::vector<double> acc(H);
+  for (int64_t i = 0; i < n; ++i) {
+    const int64_t t = tokens[i];
+    std::fill(acc.begin(), acc.end(), 0.0);
+    /* [UP] section 3: y = sum_i G(x)_i E_i(x) over the kept experts, in the
+     * token's top-k order; an overflowed slot adds 0 */
+    for (int64_t j = 0; j < k; ++j) {
+      if (slot[t * k + j] < 0) continue;
+      const double w = topk_w[t * k + j];
+      const double* Ej = E + (i * k + j) * H;
+      for (int64_t h = 0; h < H; ++h) acc[h] += w * Ej[h];
+    }
+    /* [V2] rescaling section: y = s * sum G_i E_i */
+    for (int64_t h = 0; h < H; ++h) {
+      const double y = c->out_scale * acc[h];
+      if (y64) y64[i * H + h] = y;
+      if (y32) y32[i * H + h] = static_cast<float>(y);
+    }
+  }
+  return 0;
+}
+
 }  // extern "C"

@@ -94,6 +94,14 @@ int oracle_combine_tokens(const oracle_cfg* c, const void* x, const void* Wgate,
                           const int64_t* slot, const int64_t* tokens, int64_t n, int32_t nthreads,
                           double* y64, float* y32);
 
+/* The same combine as oracle_combine_tokens, from expert outputs computed
+ * beforehand: E [n,k,H] holds E_{idx_j}(x_t) for the listed tokens (row j of
+ * token i; rows of dropped slots are not read). One expert pass then serves
+ * several capacity settings of the same routing.
+ * y64 [n,H] double (may be NULL), y32 [n,H] = fl32(y64) (may be NULL). */
+int oracle_combine_rows(const oracle_cfg* c, const double* topk_w, const int64_t* slot, const int64_t* tokens,
+                        int64_t n, const double* E, double* y64, float* y32);
+
 /* Scalar pieces, exported so tests can pin them against library routines. */
 double oracle_round_bf16(double v);   /* round to nearest bf16, ties to even */
 double oracle_round_f32(double v);    /* round to nearest fp32, ties to even */

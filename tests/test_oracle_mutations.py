@@ -61,6 +61,9 @@ MUTANTS = [
      "*balance_code = pm_dot_freq;"),
     ("code_balance_drops_guard", "pm_dot_freq += (importance[i] / (tot_imp + 1e-6)) * P[i];",
      "pm_dot_freq += (importance[i] / tot_imp) * P[i];"),
+    ("combine_rows_drops_scale", "const double y = c->out_scale * acc[h];\n      if (y64) y64[i * H + h] = y;\n      if (y32) y32[i * H + h] = static_cast<float>(y);\n    }\n  }\n  return 0;",
+     "const double y = acc[h];\n      if (y64) y64[i * H + h] = y;\n      if (y32) y32[i * H + h] = static_cast<float>(y);\n    }\n  }\n  return 0;"),
+    ("combine_rows_reads_wrong_slot", "const double* Ej = E + (i * k + j) * H;", "const double* Ej = E + (i * k) * H;"),
     ("nan_score_not_ranked_last",
      "if (std::isnan(hv)) hv = -std::numeric_limits<double>::infinity();", "(void)0;"),
 ]

@@ -125,3 +125,21 @@ def test_h_rounding_modes():
     lib = oracle.load()
     assert np.array_equal(hb, np.vectorize(lib.brute_round_bf16)(hx))
     assert np.abs(hb - hx).max() <= np.abs(hx).max() * 2 ** -8
+
+
+def test_combine_rows_equals_combine_tokens():
+    """The two-step combine (expert outputs of every slot first, then the
+    gate-weighted sum for one capacity setting) gives the same bits as the
+    one-step combine, with and without drops, in both orders."""
+    for order, cap in ((synth.MIXTRAL, -1), (synth.MIXTRAL, 3), (synth.ST, 2), (synth.MIXTRAL, 0)):
+        w = synth.make_independent("rows", 40 + cap, 24, 32, 16, 6, 3, act="f32", wt="f32", order=order,
+                                   capacity=cap, out_scale=2.0)
+        r = oracle.route(w)
+        cap_ = oracle.capacity(w, r["topk_idx"])
+        toks = np.array([0, 3, 5, 11, 23], np.int64)
+        E = oracle.assignment_outputs(w, r["topk_idx"], toks)
+        a64, a32 = oracle.combine_tokens(w, r["topk_idx"], r["topk_w"], cap_["slot"], toks)
+        b64, b32 = oracle.combine_rows(w, r["topk_w"], cap_["slot"], E, toks)
+        assert np.array_equal(a64, b64) and np.array_equal(a32, b32)
+        if cap == 0:
+            assert np.all(b64 == 0.0)
