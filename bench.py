@@ -177,16 +177,22 @@ def main():
         step(i)
 
     # timed region; the dominant kernel bracketed by HIP events on the launch stream
+    # (per-step durations from events recorded between the steps on the
+    # launch stream, for the median and the 10th/90th percentiles)
     abi.moe_profile_select(dom_id)
     abi.moe_profile_read()
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    marks[0].record(stream)
     for i in range(args.steps):
         step(i)
+        marks[i + 1].record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     abi.moe_profile_select(-1)
     dom_ms, dom_n = abi.moe_profile_read()
+    step_ms = np.array([marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)])
 
     ms_per_step = elapsed * 1e3 / args.steps
     tokens_per_s = T * args.steps / elapsed
@@ -280,6 +286,8 @@ def main():
     out = {
         "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "step_ms": {"median": round(float(np.median(step_ms)), 4), "p10": round(float(np.percentile(step_ms, 10)), 4),
+                    "p90": round(float(np.percentile(step_ms, 90)), 4)},
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if bf16 else "f32",
         "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights; no checkpoint)",
         "config": {"workload": desc, "T": T, "H": H, "F": F, "N": N, "k": k, "capacity": w.capacity,
@@ -299,11 +307,14 @@ def cpu_baseline(w, target_s: float):
     import oracle
     import synth
 
+    # threads: this process's CPU share (its affinity mask), at most 16, the
+    # share of one GPU on a shared host; the host's own count is reported too
+    host_cpus = os.cpu_count() or 1
     try:
-        cores = len(os.sched_getaffinity(0))
+        share = len(os.sched_getaffinity(0))
     except AttributeError:
-        cores = os.cpu_count() or 1
-    cores = max(1, min(16, cores))
+        share = host_cpus
+    cores = max(1, min(16, share))
 
     def sample(S):
         return synth.Workload(w.name, S, w.H, w.F, w.N, w.k, w.capacity, w.order, w.noisy, False, w.out_scale,
@@ -325,6 +336,7 @@ def cpu_baseline(w, target_s: float):
     oracle.forward(sample(S1), nthreads=1)
     dt1 = time.perf_counter() - t2
     return {"value": round(S / dt, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "host_cpus": host_cpus, "affinity_cpus": share,
             "sample": f"first {S} of {w.T} tokens of the same layer (routing, capacity and experts of those "
                       f"tokens), fp64 accumulation, {dt:.1f} s",
             "single_thread": {"value": round(S1 / dt1, 2), "unit": "tokens/s", "cores": 1,

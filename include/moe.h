@@ -97,7 +97,9 @@ size_t moe_workspace_bytes(const moe_cfg* cfg);
  *   normal draws, one per token and expert) are read only when cfg->noisy.
  *   logits_opt [T,N] fp32: clean router logits x.W_g.
  *   topk_idx [T,k] int32: the k highest scores per token, in descending
- *   order, ties to the lower expert index.
+ *   order, ties to the lower expert index. A NaN score (from NaN or Inf in x
+ *   or the router weights) counts as -inf: it ranks below every number and
+ *   adds 0 to the softmax denominators, so exactly k experts are kept.
  *   topk_w [T,k] fp32: Mixtral: softmax over the k kept scores; ST: softmax
  *   over all N scores taken at the kept experts (not renormalised).
  *   Statistics, written when cfg->want_stats and the pointer is non-NULL
@@ -156,7 +158,14 @@ moe_status moe_combine(const moe_cfg* cfg, const float* y_perm, const int32_t* s
  * and moe_combine on one stream without host synchronisation. Optional
  * outputs: topk_idx_opt [T,k], topk_w_opt [T,k], kept_opt [N] (after
  * capacity), load_opt [N] (before capacity), and the statistics as in
- * moe_route. */
+ * moe_route.
+ *   Device-side failure: in the persistent expert kernel (bf16 prefill
+ *   shapes) a down-projection tile waits, with a bounded number of polls, for
+ *   the gate/up tiles of its rows. If a wait ever gives up, that tile writes
+ *   NaN over its y_perm rows and the combine writes every element of y as
+ *   NaN, so the failure cannot pass as a result (moe_grouped_swiglu alone
+ *   leaves the NaN rows in y_perm). The call still returns MOE_OK, since no
+ *   call synchronises the host. */
 moe_status moe_forward(const moe_cfg* cfg, const void* x, const float* Wg, const float* Wn, const float* eps,
                        const void* Wgate, const void* Wup, const void* Wdown, void* y, int32_t* topk_idx_opt,
                        float* topk_w_opt, int32_t* kept_opt, int32_t* load_opt, float* importance_opt,
@@ -188,6 +197,15 @@ enum {
 };
 moe_status moe_profile_select(int32_t kernel_id);
 moe_status moe_profile_read(double* total_ms, int64_t* launches);
+
+/* Test hook for the expert kernel's bounded wait (see moe_forward). Later
+ * launches poll at most spin_limit times (<= 0: the default, about a second)
+ * and wait for wait_extra more finished gate/up tiles than exist, so with
+ * wait_extra > 0 every wait gives up after spin_limit polls and the failure
+ * path runs while every kernel still ends normally. moe_debug_set_wait(0, 0)
+ * restores normal operation. Process-wide, host only; MOE_ERR_INVALID for
+ * wait_extra < 0. */
+moe_status moe_debug_set_wait(int32_t spin_limit, int32_t wait_extra);
 
 #ifdef __cplusplus
 }

@@ -25,7 +25,7 @@ MOE_TOPK_THEN_SOFTMAX, MOE_SOFTMAX_THEN_TOPK = 0, 1
 
 EXPORTED = ["moe_capacity", "moe_check", "moe_workspace_bytes", "moe_route", "moe_permute",
             "moe_grouped_swiglu", "moe_combine", "moe_forward", "moe_status_str", "moe_last_error",
-            "moe_profile_select", "moe_profile_read"]
+            "moe_profile_select", "moe_profile_read", "moe_debug_set_wait"]
 
 
 class moe_cfg(ctypes.Structure):
@@ -80,6 +80,8 @@ def load_library(path: Optional[str] = None):
     lib.moe_profile_select.restype = i32
     lib.moe_profile_read.argtypes = [ctypes.POINTER(f64), ctypes.POINTER(i64)]
     lib.moe_profile_read.restype = i32
+    lib.moe_debug_set_wait.argtypes = [i32, i32]
+    lib.moe_debug_set_wait.restype = i32
     if path is None:
         _lib = lib
     return lib
@@ -204,3 +206,7 @@ def moe_profile_read():
     n = ctypes.c_int64()
     _check(load_library().moe_profile_read(ctypes.byref(ms), ctypes.byref(n)), "moe_profile_read")
     return ms.value, n.value
+
+
+def moe_debug_set_wait(spin_limit: int, wait_extra: int):
+    _check(load_library().moe_debug_set_wait(int(spin_limit), int(wait_extra)), "moe_debug_set_wait")

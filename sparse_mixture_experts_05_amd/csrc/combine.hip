@@ -6,11 +6,25 @@ namespace moe {
 
 namespace {
 
+// When an earlier kernel of the layer reported a failure (a bounded wait that
+// gave up), the whole output is NaN, so the failure cannot pass as a result.
+template <bool OUT_BF16>
+__device__ __forceinline__ bool poisoned(const CombineParams& p, int64_t t) {
+  if (!p.error || *p.error == 0) return false;
+  const f32x4_t nan4 = {__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+  for (int64_t c = threadIdx.x; c < p.H / 4; c += blockDim.x) {
+    const f32x4_t v = nan4;
+    cmb::store4<OUT_BF16>(p, t, c, v);
+  }
+  return true;
+}
+
 template <bool OUT_BF16, int KMAX>
 __global__ __launch_bounds__(256) void k_combine(CombineParams p) {
   const int64_t t = blockIdx.x;
   const int k = p.k, H = p.H;
   const int64_t H4 = H / 4;
+  if (poisoned<OUT_BF16>(p, t)) return;
   int sl[KMAX];
   float w[KMAX];
 #pragma unroll
@@ -25,6 +39,7 @@ __global__ __launch_bounds__(256) void k_combine(CombineParams p) {
 // Any k: the same sums with the slots read inside the loop.
 template <bool OUT_BF16>
 __global__ __launch_bounds__(256) void k_combine_any(CombineParams p) {
+  if (poisoned<OUT_BF16>(p, blockIdx.x)) return;
   cmb::token_any<OUT_BF16>(p, blockIdx.x, threadIdx.x, 256);
 }
 

@@ -72,6 +72,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* base,
   return __builtin_amdgcn_make_buffer_rsrc(p, 0, num, kBufferFlags);
 }
 
+// Expert e's segment of the permuted rows, [off, off + cnt), from the
+// device-side offsets, clamped to [0, rows_max): offsets that a caller
+// passes in (or that disagree with the row bound the workspace was sized
+// for) can then never move a tile's loads or stores past its buffers.
+__device__ __forceinline__ void expert_segment(const int32_t* __restrict__ offsets, int e, int rows_max, int& off,
+                                               int& cnt) {
+  const int a = min(max(offsets[e], 0), rows_max);
+  const int b = min(max(offsets[e + 1], a), rows_max);
+  off = a;
+  cnt = b - a;
+}
+
 struct TileInfo {
   int expert;
   int row0;   // first permuted row of the tile
@@ -82,13 +94,11 @@ struct TileInfo {
 // expert e's row count; a lane-wise inclusive scan of the per-expert tile
 // counts locates the expert. Returns false past the last tile.
 template <int BM>
-__device__ __forceinline__ bool find_tile(const int32_t* __restrict__ offsets, int N, int mt, TileInfo& ti) {
+__device__ __forceinline__ bool find_tile(const int32_t* __restrict__ offsets, int N, int rows_max, int mt,
+                                          TileInfo& ti) {
   const int lane = threadIdx.x & 63;
   int off = 0, cnt = 0;
-  if (lane < N) {
-    off = offsets[lane];
-    cnt = offsets[lane + 1] - off;
-  }
+  if (lane < N) expert_segment(offsets, lane, rows_max, off, cnt);
   const int tl = (cnt + BM - 1) / BM;
   int incl = tl;
 #pragma unroll

@@ -23,10 +23,10 @@
 // Loads go straight from buffer loads into LDS (no register staging), STAGES
 // deep, so several K steps of loads stay in flight; rows past the expert's
 // segment and K past the range read as zero through the buffer's range check,
-// without branches. k_gemm_dma runs one 256 x 256 tile per workgroup,
-// k_experts_fused runs both projections of every expert in one persistent
-// launch on the same tile code (see the scheduling comment above it), and
-// k_gemm_decode serves experts with few rows (see the comment above it).
+// without branches. k_experts_fused runs both projections of every expert in
+// one persistent launch of 256 x 256 tiles (see the scheduling comment above
+// it), and k_gemm_decode serves experts with few rows (see the comment above
+// it).
 #include "common.h"
 #include "stats.h"
 #include "kernels.h"
@@ -83,10 +83,7 @@ __device__ __forceinline__ bool decode_tile(const GemmParams& p, TilePos& tp) {
   const int ntiles = (p.Nout + NO - 1) / NO;
   // per-expert m-tile counts (lane e = expert e), inclusive scan over lanes
   int eoff = 0, ecnt = 0;
-  if (lane < p.N) {
-    eoff = p.offsets[lane];
-    ecnt = p.offsets[lane + 1] - eoff;
-  }
+  if (lane < p.N) expert_segment(p.offsets, lane, static_cast<int>(p.rows_max), eoff, ecnt);
   const int etl = (ecnt + BM - 1) / BM;
   int incl = etl;
 #pragma unroll
@@ -449,7 +446,8 @@ struct NoReserve {
 template <int BM, int BN, int WGM, int WGN, int STAGES, int BK, bool SWIGLU, bool GATHER, class Hook = NoHook,
           class Reserve = NoReserve>
 __device__ __forceinline__ void gemm_tile(const GemmParams& p, const TilePos& tp, uint16_t* smem, int sbase = 0,
-                                          int pre = 0, Hook&& hook = Hook{}, Reserve&& reserve = Reserve{}) {
+                                          int pre = 0, Hook&& hook = Hook{}, Reserve&& reserve = Reserve{},
+                                          bool poison = false) {
   using Loader = TileLoader<BM, BN, WGM, WGN, BK, SWIGLU, GATHER>;
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int MB = WM / 32, NB = WN / 32;
@@ -516,18 +514,15 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const TilePos& tp
     kloop(std::true_type{});
   const int fb = (sbase + tp.KT) % STAGES;
   hook(sA(fb), sB(fb), fb);
+  if (poison) {
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = __builtin_nanf("");
+  }
   epilogue<WM, WN, MB, NB, SWIGLU>(p, tp, wm, wn, lane, NO, acc);
-}
-
-template <int BM, int BN, int WGM, int WGN, int STAGES, int BK, bool SWIGLU, bool GATHER>
-__global__ __launch_bounds__(WGM * WGN * 64) void k_gemm_dma(GemmParams p) {
-  // one LDS object for every stage of A and B: with a single object the
-  // compiler's alias scopes can tell the stages apart
-  __shared__ __attribute__((aligned(16))) uint16_t smem[dma_lds_elems<BM, BN, STAGES, BK>()];
-  constexpr int NO = SWIGLU ? BN / 2 : BN;
-  TilePos tp;
-  if (!decode_tile<BM, NO, BK>(p, tp)) return;
-  gemm_tile<BM, BN, WGM, WGN, STAGES, BK, SWIGLU, GATHER>(p, tp, smem);
 }
 
 // ---- decode-shaped tiles: a long K step per weight row -----------------------
@@ -715,17 +710,19 @@ __device__ __forceinline__ TileInfo row_block(int rb, int eoff, int ecnt, int et
   return ti;
 }
 
-// Spin until *ctr reaches target. The loads are relaxed: an acquire load
-// invalidates the caches every time round the loop, under the tiles that run
-// beside it; the caller issues one acquire fence after the wait.
-__device__ __forceinline__ void wait_count(int32_t* ctr, int target, int32_t* err) {
+// Spin until *ctr reaches target, at most `limit` polls; returns false (and
+// raises the error word) when it gives up. The loads are relaxed: an acquire
+// load invalidates the caches every time round the loop, under the tiles that
+// run beside it; the caller issues one acquire fence after the wait.
+__device__ __forceinline__ bool wait_count(int32_t* ctr, int target, int32_t* err, int limit) {
   for (int it = 0; __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target; ++it) {
-    if (it >= (1 << 22)) {  // about a second: never reached unless a producer failed
+    if (it >= limit) {
       __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      break;
+      return false;
     }
     __builtin_amdgcn_s_sleep(8);
   }
+  return true;
 }
 
 template <int BM, int BN, int WGM, int WGN, int STAGES, int BK, bool GATHER>
@@ -733,18 +730,17 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_experts_fused(FusedParams fp
   constexpr int kElems = dma_lds_elems<BM, BN, STAGES, BK>();
   // the operand stages and, after them, the broadcast work item: one LDS object
   __shared__ __attribute__((aligned(16))) uint16_t smem[kElems + 8];
-  int* s_item = reinterpret_cast<int*>(smem + kElems);
+  int* s_item = reinterpret_cast<int*>(smem + kElems);  // [0] next ticket, [1] a down tile's wait gave up
   constexpr int GM = 8;  // most row blocks per group of gate/up tiles
   const GemmParams& g1 = fp.g1;
   const GemmParams& g2 = fp.g2;
   const int lane = threadIdx.x & 63;
 
   // per-expert row blocks (lane e = expert e), inclusive scan over lanes
+  // (clamped to the rows the workspace holds, so RB never exceeds the row
+  // blocks the queue counters were sized for)
   int eoff = 0, ecnt = 0;
-  if (lane < g1.N) {
-    eoff = g1.offsets[lane];
-    ecnt = g1.offsets[lane + 1] - eoff;
-  }
+  if (lane < g1.N) expert_segment(g1.offsets, lane, static_cast<int>(g1.rows_max), eoff, ecnt);
   const int etl = (ecnt + BM - 1) / BM;
   int incl = etl;
 #pragma unroll
@@ -850,12 +846,17 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_experts_fused(FusedParams fp
       if (threadIdx.x == 0)
         __hip_atomic_fetch_add(&fp.sched[kSchedDone + rb], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     } else {
+      // a wait that gives up leaves the error word raised and writes NaN over
+      // this tile's outputs instead of sums of h rows that may be unpublished
       if (threadIdx.x == 0) {
-        wait_count(&fp.sched[kSchedDone + rb], NT1, &fp.sched[kSchedError]);
+        const bool ok = wait_count(&fp.sched[kSchedDone + rb], NT1 + fp.wait_extra, &fp.sched[kSchedError],
+                                   fp.spin_limit);
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        s_item[1] = ok ? 0 : 1;
       }
       __syncthreads();
-      gemm_tile<BM, BN, WGM, WGN, STAGES, BK, false, false>(g2, tp, smem, sbase, pre, hook, reserve);
+      const bool poison = __builtin_amdgcn_readfirstlane(s_item[1]) != 0;
+      gemm_tile<BM, BN, WGM, WGN, STAGES, BK, false, false>(g2, tp, smem, sbase, pre, hook, reserve, poison);
     }
     ticket = next;
     sbase = nsbase;
@@ -873,21 +874,6 @@ int64_t grid_blocks(const GemmParams& p, int BM, int BN) {
   const int64_t ntiles = (p.Nout + NO - 1) / NO;
   const int64_t mtiles = (p.rows_max + BM - 1) / BM + p.N;
   return ntiles * mtiles * p.splits;
-}
-
-template <int BM, int BN, int WGM, int WGN, int STAGES, int BK>
-hipError_t launch_dma(const GemmParams& p, hipStream_t s) {
-  const int64_t blocks = grid_blocks(p, BM, BN);
-  if (blocks <= 0) return hipSuccess;
-  const dim3 grid(static_cast<unsigned>(blocks)), block(WGM * WGN * 64);
-  if (p.swiglu) {
-    if (p.row_token) hipLaunchKernelGGL((k_gemm_dma<BM, BN, WGM, WGN, STAGES, BK, true, true>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((k_gemm_dma<BM, BN, WGM, WGN, STAGES, BK, true, false>), grid, block, 0, s, p);
-  } else {
-    if (p.row_token) hipLaunchKernelGGL((k_gemm_dma<BM, BN, WGM, WGN, STAGES, BK, false, true>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((k_gemm_dma<BM, BN, WGM, WGN, STAGES, BK, false, false>), grid, block, 0, s, p);
-  }
-  return hipGetLastError();
 }
 
 template <int BM, int BK, int STAGES, int NW>
@@ -909,27 +895,23 @@ hipError_t launch_decode(const GemmParams& p, hipStream_t s) {
 
 bool gemm_bf16_mfma_supported(int K, int Nout) { return K % 8 == 0 && K > 0 && Nout > 0; }
 
-// Tile shape by the average rows per expert: short, wide tiles when experts
-// get few rows (decode), large square tiles otherwise.
-void gemm_bf16_mfma_tile(int64_t rows_max, int N, int* bm, int* bn) {
-  const int64_t avg_rows = rows_max / (N > 0 ? N : 1);
-  if (avg_rows <= 48) {
-    *bm = kDecBM;
-    *bn = kDecBN;
-  } else {
-    *bm = 256;
-    *bn = 256;
-  }
+// Experts with few rows on average (decode shapes) take the decode tile in two
+// launches; the others the persistent kernel's 256 x 256 tiles.
+bool gemm_decode_shape(int64_t rows_max, int N) { return rows_max / (N > 0 ? N : 1) <= 48; }
+
+void gemm_decode_tile(int* bm, int* bn) {
+  *bm = kDecBM;
+  *bn = kDecBN;
 }
+
+int fused_error_index() { return kSchedError; }
 
 int fused_sched_ints(int64_t rows_max, int N) {
   return kSchedDone + static_cast<int>((rows_max + kFusedBM - 1) / kFusedBM) + N + 1;
 }
 
 bool gemm_fused_supported(int64_t rows_max, int N, int K1, int F) {
-  int bm, bn;
-  gemm_bf16_mfma_tile(rows_max, N, &bm, &bn);
-  return bm == kFusedBM && bn == kFusedBN && gemm_bf16_mfma_supported(K1, F);
+  return !gemm_decode_shape(rows_max, N) && gemm_bf16_mfma_supported(K1, F);
 }
 
 hipError_t launch_experts_fused(const FusedParams& fp, hipStream_t s) {
@@ -947,11 +929,6 @@ hipError_t launch_experts_fused(const FusedParams& fp, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_bf16_mfma(const GemmParams& p, hipStream_t s) {
-  int bm, bn;
-  gemm_bf16_mfma_tile(p.rows_max, p.N, &bm, &bn);
-  if (bm == kDecBM) return launch_decode<kDecBM, 128, 3, 4>(p, s);
-  return launch_dma<256, 256, 4, 2, 2, 64>(p, s);
-}
+hipError_t launch_gemm_decode(const GemmParams& p, hipStream_t s) { return launch_decode<kDecBM, 128, 3, 4>(p, s); }
 
 }  // namespace moe

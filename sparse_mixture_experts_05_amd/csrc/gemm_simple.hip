@@ -30,7 +30,7 @@ __global__ __launch_bounds__(256) void k_gemm_simple(GemmParams p) {
   const int mt = bid % mtiles;
   const int split = bid / mtiles;
   TileInfo ti;
-  if (!find_tile<TM>(p.offsets, p.N, mt, ti)) return;
+  if (!find_tile<TM>(p.offsets, p.N, static_cast<int>(p.rows_max), mt, ti)) return;
 
   const int kper = (p.K + p.splits - 1) / p.splits;
   const int kb0 = split * kper;
@@ -51,7 +51,10 @@ __global__ __launch_bounds__(256) void k_gemm_simple(GemmParams p) {
     const int r = e / TK;
     aval[i] = r < ti.rows;
     int64_t src = ti.row0 + r;
-    if (GATHER) src = aval[i] ? p.row_token[src] : 0;
+    if (GATHER) {
+      src = aval[i] ? p.row_token[src] : 0;
+      aval[i] = aval[i] && src >= 0 && src < p.a_rows;  // a row_token entry outside x reads zeros
+    }
     arow[i] = aval[i] ? src * p.lda : 0;
     const int f = nt * TN + r;
     bval[i] = f < p.Nout;

@@ -80,6 +80,7 @@ struct GatherParams {
   const int32_t* offsets;
   int64_t rows_max;       // T*k
   int H, N, elem_bytes;
+  int64_t T;              // rows of x
 };
 hipError_t launch_gather(const GatherParams& p, hipStream_t s);
 
@@ -108,20 +109,30 @@ struct GemmParams {
   int64_t a_rows;             // rows of A (bounds of the gathered or permuted operand)
   int swiglu;
 };
-hipError_t launch_gemm_bf16_mfma(const GemmParams& p, hipStream_t s);
+// Decode-shaped tiles (few rows per expert), one launch per GEMM.
+hipError_t launch_gemm_decode(const GemmParams& p, hipStream_t s);
 bool gemm_bf16_mfma_supported(int K, int Nout);
-void gemm_bf16_mfma_tile(int64_t rows_max, int N, int* bm, int* bn);
+bool gemm_decode_shape(int64_t rows_max, int N);
+void gemm_decode_tile(int* bm, int* bn);
 hipError_t launch_gemm_simple(const GemmParams& p, int bf16, hipStream_t s);
 
 // Both expert GEMMs in one persistent launch: g1 is the gate/up GEMM with the
 // SwiGLU epilogue (writing h), g2 the down projection reading h (no K split).
 // sched: fused_sched_ints(rows_max, N) int32 of workspace, zero on entry.
+// A down tile waits for its row block's gate/up tiles at most spin_limit
+// polls; if it gives up it raises sched[fused_error_index()] and writes NaN
+// over its outputs. wait_extra raises the awaited count (0 in use; a test
+// sets it so that every wait gives up).
 struct FusedParams {
   GemmParams g1, g2;
   int32_t* sched;
   StatsParams st;  // router statistics, reduced once the queue is empty
   int stats;       // 1: reduce them (in the workgroup that draws the first ticket past the end)
+  int spin_limit;
+  int wait_extra;
 };
+constexpr int kDefaultSpinLimit = 1 << 22;  // about a second of polling
+int fused_error_index();
 int fused_sched_ints(int64_t rows_max, int N);
 bool gemm_fused_supported(int64_t rows_max, int N, int K1, int F);
 hipError_t launch_experts_fused(const FusedParams& fp, hipStream_t s);
@@ -138,6 +149,7 @@ struct CombineParams {
   int64_t T;
   int H, k;
   float scale;
+  const int32_t* error;      // *error != 0: an earlier kernel failed, and y is written as all NaN. May be null.
 };
 hipError_t launch_combine(const CombineParams& p, hipStream_t s);
 

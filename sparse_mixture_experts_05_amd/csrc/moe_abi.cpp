@@ -65,6 +65,11 @@ class ProfScope {
       return fail(MOE_ERR_DEVICE, "%s launch failed: %s", #KID, hipGetErrorString(e_)); \
   } while (0)
 
+// ---- the expert kernel's bounded wait (test hook) -----------------------------
+std::mutex g_wait_mu;
+int g_wait_spin = 0;   // <= 0: the default limit
+int g_wait_extra = 0;
+
 // ---- configuration -----------------------------------------------------------
 constexpr size_t kAlign = 256;
 size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
@@ -91,11 +96,12 @@ Layout layout(const moe_cfg* c) {
   L.mfma = use_mfma(c);
   L.fused = L.mfma && moe::gemm_fused_supported(L.A_max, c->N, c->H, c->F);
   if (L.mfma && !L.fused) {
-    // the down projection splits K when there are too few output tiles to
-    // spread evenly over 256 compute units (the grid bound below counts a
-    // partial row tile per expert, so it overstates the real tiles)
+    // decode-shaped tiles: the down projection splits K when there are too
+    // few output tiles to spread evenly over 256 compute units (the grid
+    // bound below counts a partial row tile per expert, so it overstates the
+    // real tiles)
     int bm, bn;
-    moe::gemm_bf16_mfma_tile(L.A_max, c->N, &bm, &bn);
+    moe::gemm_decode_tile(&bm, &bn);
     const int64_t tiles = ((L.A_max + bm - 1) / bm + std::min<int64_t>(c->N, L.A_max)) * ((c->H + bn - 1) / bn);
     if (tiles > 0 && tiles < 2048) {
       int64_t s = (2048 + tiles - 1) / tiles;
@@ -211,11 +217,17 @@ moe_status run_gemms(const moe_cfg* c, const Layout& L, const void* a, const int
       hipError_t e = moe::launch_fill_i32(sched, moe::fused_sched_ints(L.A_max, c->N), 0, s);
       if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "fill launch failed: %s", hipGetErrorString(e));
     }
-    moe::FusedParams fp{g1, g2, sched, stats_tail ? *stats_tail : moe::StatsParams{}, stats_tail ? 1 : 0};
+    int spin = moe::kDefaultSpinLimit, extra = 0;
+    {
+      std::lock_guard<std::mutex> lk(g_wait_mu);
+      if (g_wait_spin > 0) spin = g_wait_spin;
+      extra = g_wait_extra;
+    }
+    moe::FusedParams fp{g1, g2, sched, stats_tail ? *stats_tail : moe::StatsParams{}, stats_tail ? 1 : 0, spin, extra};
     MOE_LAUNCH(MOE_KERNEL_EXPERTS, s, moe::launch_experts_fused(fp, s));
   } else if (L.mfma) {
-    MOE_LAUNCH(MOE_KERNEL_GEMM1, s, moe::launch_gemm_bf16_mfma(g1, s));
-    MOE_LAUNCH(MOE_KERNEL_GEMM2, s, moe::launch_gemm_bf16_mfma(g2, s));
+    MOE_LAUNCH(MOE_KERNEL_GEMM1, s, moe::launch_gemm_decode(g1, s));
+    MOE_LAUNCH(MOE_KERNEL_GEMM2, s, moe::launch_gemm_decode(g2, s));
   } else {
     MOE_LAUNCH(MOE_KERNEL_GEMM1, s, moe::launch_gemm_simple(g1, bf16, s));
     MOE_LAUNCH(MOE_KERNEL_GEMM2, s, moe::launch_gemm_simple(g2, bf16, s));
@@ -330,7 +342,7 @@ moe_status moe_permute(const moe_cfg* c, const void* x, const int32_t* topk_idx,
                         counts, nullptr, offsets, slot, row_token};
   MOE_LAUNCH(MOE_KERNEL_SCATTER, s, moe::launch_scatter(sp, s));
   if (x_perm) {
-    moe::GatherParams gp{x, x_perm, row_token, offsets, c->T * c->k, c->H, c->N, c->act == MOE_BF16 ? 2 : 4};
+    moe::GatherParams gp{x, x_perm, row_token, offsets, c->T * c->k, c->H, c->N, c->act == MOE_BF16 ? 2 : 4, c->T};
     MOE_LAUNCH(MOE_KERNEL_GATHER, s, moe::launch_gather(gp, s));
   }
   return MOE_OK;
@@ -358,7 +370,7 @@ moe_status moe_combine(const moe_cfg* c, const float* y_perm, const int32_t* slo
   if (c->T == 0) return MOE_OK;
   MOE_REQUIRE(y_perm && slot && topk_w && y, "y_perm, slot, topk_w and y are required");
   MOE_REQUIRE(aligned(y_perm, 16) && aligned(y, 16), "y_perm and y must be 16-byte aligned");
-  moe::CombineParams cp{y_perm, 0, 1, slot, topk_w, y, c->out == MOE_BF16, c->T, c->H, c->k, c->out_scale};
+  moe::CombineParams cp{y_perm, 0, 1, slot, topk_w, y, c->out == MOE_BF16, c->T, c->H, c->k, c->out_scale, nullptr};
   MOE_LAUNCH(MOE_KERNEL_COMBINE, s, moe::launch_combine(cp, s));
   return MOE_OK;
 }
@@ -420,7 +432,8 @@ moe_status moe_forward(const moe_cfg* c, const void* x, const float* Wg, const f
                  stats && L.fused ? &sp : nullptr);
   if (st != MOE_OK) return st;
   moe::CombineParams cp{y_perm, L.A_max * static_cast<int64_t>(c->H), L.splits, slot, topk_w, y,
-                        c->out == MOE_BF16, c->T, c->H, c->k, c->out_scale};
+                        c->out == MOE_BF16, c->T, c->H, c->k, c->out_scale,
+                        L.fused ? at<int32_t>(ws, L.sched) + moe::fused_error_index() : nullptr};
   MOE_LAUNCH(MOE_KERNEL_COMBINE, s, moe::launch_combine(cp, s));
   return MOE_OK;
 }
@@ -437,6 +450,14 @@ const char* moe_status_str(moe_status s) {
 }
 
 const char* moe_last_error(void) { return g_err.c_str(); }
+
+moe_status moe_debug_set_wait(int32_t spin_limit, int32_t wait_extra) {
+  if (wait_extra < 0) return fail(MOE_ERR_INVALID, "wait_extra = %d < 0", wait_extra);
+  std::lock_guard<std::mutex> lk(g_wait_mu);
+  g_wait_spin = spin_limit;
+  g_wait_extra = wait_extra;
+  return MOE_OK;
+}
 
 moe_status moe_profile_select(int32_t kernel_id) {
   if (kernel_id < -1 || kernel_id >= MOE_KERNEL_COUNT) return fail(MOE_ERR_INVALID, "unknown kernel id %d", kernel_id);

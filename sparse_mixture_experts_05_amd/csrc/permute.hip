@@ -122,36 +122,51 @@ __global__ __launch_bounds__(kScatterThreads) void k_scatter(ScatterParams p) {
   if (blockIdx.x == 0 && p.zero)
     for (int i = tid; i < p.zero_n; i += kScatterThreads) p.zero[i] = 0;
 
-  // rank among earlier lanes of the wave, per expert, by ballot
+  // rank among the wave's earlier assignments, per expert, by ballot: every
+  // slot of earlier lanes, then the earlier slots of the same token (a row of
+  // topk_idx from a caller may name one expert twice; each entry is its own
+  // assignment, in (token, slot) order)
   for (int e = 0; e < N; ++e) {
-    bool has = false;
+    int before = 0, total = 0;
 #pragma unroll
-    for (int j = 0; j < KMAX; ++j) has = has || (idx[j] == e);
-    const uint64_t m = __ballot(has);
-    if (lane == 0) s_wcnt[wave][e] = __popcll(m);
-    const int before = __popcll(m & lanemask_lt());
+    for (int j = 0; j < KMAX; ++j) {
+      if (j < k) {  // uniform over the wave
+        const uint64_t m = __ballot(idx[j] == e);
+        total += __popcll(m);
+        before += __popcll(m & lanemask_lt());
+      }
+    }
+    if (lane == 0) s_wcnt[wave][e] = total;
+    int same = 0;
 #pragma unroll
     for (int j = 0; j < KMAX; ++j)
-      if (idx[j] == e) pre[j] = before;
+      if (idx[j] == e) pre[j] = before + same++;
   }
   __syncthreads();
   if (tv) {
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) {
       if (j < k) {
+        // an expert index outside [0, N) (possible only in a caller's
+        // topk_idx) is dropped; the row bound guards against a histogram
+        // that disagrees with topk_idx
         const int e = idx[j];
-        int woff = 0;
-        for (int w = 0; w < wave; ++w) woff += s_wcnt[w][e];
-        const int rank = s_base[e] + woff + pre[j];
-        const bool keep = p.capacity < 0 || rank < p.capacity;
-        const int row = keep ? s_off[e] + rank : -1;
-        p.slot[t * k + j] = row;
+        const bool ve = e >= 0 && e < N;
+        int rank = 0;
+        if (ve) {
+          int woff = 0;
+          for (int w = 0; w < wave; ++w) woff += s_wcnt[w][e];
+          rank = s_base[e] + woff + pre[j];
+        }
+        const int64_t row = ve ? static_cast<int64_t>(s_off[e]) + rank : -1;
+        const bool keep = ve && (p.capacity < 0 || rank < p.capacity) && row < T * k;
+        p.slot[t * k + j] = keep ? static_cast<int32_t>(row) : -1;
         if (keep) p.row_token[row] = static_cast<int32_t>(t);
       }
     }
   }
   // rows past the last kept one
-  const int64_t A = s_off[N];
+  const int64_t A = min(static_cast<int64_t>(s_off[N]), T * k);
   for (int64_t r = A + tb0 + tid; r < T * k; r += static_cast<int64_t>(gridDim.x) * kScatterThreads)
     p.row_token[r] = -1;
 }
@@ -160,12 +175,16 @@ __global__ __launch_bounds__(kScatterThreads) void k_scatter(ScatterParams p) {
 __global__ __launch_bounds__(256) void k_gather(GatherParams p) {
   const int lane = threadIdx.x & 63;
   const int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  const int64_t A = p.offsets[p.N];
+  const int64_t A = min(static_cast<int64_t>(p.offsets[p.N]), p.rows_max);
   if (r >= A) return;
   const int64_t src = p.row_token[r];
   const int64_t row_bytes = static_cast<int64_t>(p.H) * p.elem_bytes;
-  const char* s = static_cast<const char*>(p.x) + src * row_bytes;
   char* d = static_cast<char*>(p.x_perm) + r * row_bytes;
+  if (src < 0 || src >= p.T) {  // never from the scatter; a guard against a row index outside x
+    for (int64_t o = lane * 16; o < row_bytes; o += 64 * 16) *reinterpret_cast<u32x4_t*>(d + o) = u32x4_t{0, 0, 0, 0};
+    return;
+  }
+  const char* s = static_cast<const char*>(p.x) + src * row_bytes;
   for (int64_t o = lane * 16; o < row_bytes; o += 64 * 16)
     *reinterpret_cast<u32x4_t*>(d + o) = *reinterpret_cast<const u32x4_t*>(s + o);
 }
@@ -182,10 +201,11 @@ hipError_t launch_hist(const HistParams& p, hipStream_t s) {
 hipError_t launch_scatter(const ScatterParams& p, hipStream_t s) {
   const int64_t blocks = (p.T + kScatterThreads - 1) / kScatterThreads;
   if (blocks <= 0) return hipSuccess;
-  if (p.k <= 8)
-    hipLaunchKernelGGL(k_scatter<8>, dim3(static_cast<unsigned>(blocks)), dim3(kScatterThreads), 0, s, p);
-  else
-    hipLaunchKernelGGL(k_scatter<64>, dim3(static_cast<unsigned>(blocks)), dim3(kScatterThreads), 0, s, p);
+  const dim3 grid(static_cast<unsigned>(blocks)), block(kScatterThreads);
+  if (p.k <= 2) hipLaunchKernelGGL(k_scatter<2>, grid, block, 0, s, p);
+  else if (p.k <= 4) hipLaunchKernelGGL(k_scatter<4>, grid, block, 0, s, p);
+  else if (p.k <= 8) hipLaunchKernelGGL(k_scatter<8>, grid, block, 0, s, p);
+  else hipLaunchKernelGGL(k_scatter<64>, grid, block, 0, s, p);
   return hipGetLastError();
 }
 

@@ -141,6 +141,9 @@ __global__ __launch_bounds__(kRouterWaves * kWave) void k_router(RouterParams p)
       // normal draw is the input eps[t, i]
       if (valid) hv = fmaf(p.eps[tok * N + lane], softplus(nz), lv);
     }
+    // a NaN score counts as -inf in KeepTopK and the gates: the argmax below
+    // then compares a strict total order, so every lane agrees on the winner
+    if (hv != hv) hv = -INFINITY;
     if (p.logits && valid) p.logits[tok * N + lane] = lv;
 
     // KeepTopK: k rounds of a wave-wide argmax, ties to the lower index

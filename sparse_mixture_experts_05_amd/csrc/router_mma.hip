@@ -27,9 +27,9 @@
 // After the product, one wave per token applies the noise term, KeepTopK and
 // the gate of the chosen order: a lane's rank is the number of experts with a
 // larger score, or an equal score and a lower index ("Llama 3 Meets MoE"
-// review, section 3: ties to the lower expert index), and the experts of rank
-// < k are kept in rank order (Mixtral: softmax over the kept scores; ST:
-// softmax over all scores, section 5). Threads of the block then sum the
+// review, section 3: ties to the lower expert index; a NaN score counts as
+// -inf), and the experts of rank < k are kept in rank order (Mixtral:
+// softmax over the kept scores; ST: softmax over all scores, section 5). Threads of the block then sum the
 // per-expert counts, gate weights and softmax(logit) values over the block's
 // tokens in token order for the permutation and the balance statistics.
 #include "common.h"
@@ -358,6 +358,9 @@ __global__ __launch_bounds__(router_waves<NB16>() * 64) void k_router_mma(Router
     // H_i = (x W_g)_i + StandardNormal() * Softplus((x W_noise)_i), the
     // normal draw being the input eps[t, i]
     if (p.noisy && valid) hv = fmaf(eps_pre[i], softplus(s_log[t][N + lane]), lv);
+    // a NaN score counts as -inf in KeepTopK and the gates, so the rank below
+    // is a strict total order and exactly k experts are kept
+    if (hv != hv) hv = -INFINITY;
     if (p.logits && valid) p.logits[g * N + lane] = lv;
     // rank: experts with a larger score, or an equal one at a lower index
     int rank = 0;

@@ -26,3 +26,13 @@ def _host_libs():
     if not os.path.exists(os.path.join(ROOT, "oracle", "liboracle.so")):
         oracle.build.build()
     yield
+
+
+@pytest.fixture(autouse=True)
+def _guard_bands():
+    """After a GPU test, check the guard bands around the buffers it
+    allocated through gpu_util (a kernel writing past a buffer fails it)."""
+    yield
+    gu = sys.modules.get("gpu_util")
+    if gu is not None:
+        gu.check_guards()

@@ -8,6 +8,7 @@ gap among the top k+1 is <= 1e-6: such flips are reported, not failed.
 """
 from __future__ import annotations
 
+import os
 import sys
 
 import numpy as np
@@ -19,9 +20,50 @@ from sparse_mixture_experts_05_amd import abi
 
 TIE_GAP = 1e-6
 
+# Guard bands: every workspace and layer output a test allocates through this
+# module sits between two 4 KiB bands of a known byte; after each GPU test the
+# bands are checked, so a kernel that writes past its buffer fails the test
+# that ran it.
+GUARD_BYTES = 4096
+GUARD_BYTE = 0x5A
+_guarded = []
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def oracle_threads() -> int:
+    """Threads for the oracle's token loop: this host's CPU share, at most 16."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def guarded_empty(shape, dtype=torch.float32) -> torch.Tensor:
+    """An uninitialised device tensor with guard bands on both sides."""
+    numel = int(np.prod(shape)) if len(shape) else 1
+    nbytes = numel * torch.empty((), dtype=dtype).element_size()
+    buf = torch.full((nbytes + 2 * GUARD_BYTES,), GUARD_BYTE, dtype=torch.uint8, device="cuda")
+    _guarded.append((buf, nbytes))
+    return buf[GUARD_BYTES:GUARD_BYTES + nbytes].view(dtype).view(*shape)
+
+
+def check_guards():
+    """Fail if any kernel wrote into a guard band since the last check."""
+    if not _guarded:
+        return
+    torch.cuda.synchronize()
+    bad = []
+    for buf, n in _guarded:
+        lo = buf[:GUARD_BYTES]
+        hi = buf[GUARD_BYTES + n:]
+        if not (bool(torch.all(lo == GUARD_BYTE)) and bool(torch.all(hi == GUARD_BYTE))):
+            bad.append(n)
+    _guarded.clear()
+    assert not bad, f"a kernel wrote past a buffer of {bad[0]} bytes (guard band changed)"
 
 
 def dev(a: np.ndarray | None):
@@ -82,7 +124,8 @@ def routing_flips(gpu_idx: np.ndarray, ora: dict, what: str) -> np.ndarray:
 
 
 def workspace(cfg: abi.MoEConfig) -> torch.Tensor:
-    return abi.workspace(cfg)
+    """moe_workspace_bytes(cfg) bytes (at least 256), 256-byte aligned, between guard bands."""
+    return guarded_empty((max(256, abi.moe_workspace_bytes(cfg)),), torch.uint8)
 
 
 def run_route(w, want_logits=True):
@@ -105,7 +148,7 @@ def run_forward(w, out="f32", d=None, extras=True):
     cfg = cfg_of(w, out)
     d = d or upload(w)
     T, N, k = w.T, w.N, w.k
-    y = torch.empty(T, w.H, dtype=torch.float32 if out == "f32" else torch.bfloat16, device="cuda")
+    y = guarded_empty((T, w.H), torch.float32 if out == "f32" else torch.bfloat16)
     o = dict(topk_idx=torch.empty(T, k, dtype=torch.int32, device="cuda"), topk_w=torch.empty(T, k, device="cuda"),
              kept=torch.empty(N, dtype=torch.int32, device="cuda"), load=torch.empty(N, dtype=torch.int32, device="cuda"),
              importance=torch.empty(N, device="cuda"), P=torch.empty(N, device="cuda"),
@@ -121,21 +164,16 @@ def run_forward(w, out="f32", d=None, extras=True):
     return res
 
 
-def sample_tokens(w, n: int, extra=()) -> np.ndarray:
-    rng = np.random.default_rng(w.T * 31 + w.N)
-    pick = set(rng.choice(w.T, size=min(n, w.T), replace=False).tolist())
-    pick.update([0, w.T - 1])
-    pick.update(int(t) for t in extra if 0 <= t < w.T)
-    return np.array(sorted(pick), dtype=np.int64)
-
-
-def check_forward(w, tokens=None, nthreads=16, out="f32", d=None):
-    """moe_forward against the oracle on `tokens` (all when None). Returns
-    the GPU outputs and the oracle result."""
+def check_forward(w, tokens=None, nthreads=None, out="f32", d=None, ora=None, E=None):
+    """moe_forward against the oracle on `tokens` (all when None). ora: the
+    oracle's routing of w, if already computed; E: the oracle's expert
+    outputs of every slot of every token (oracle.assignment_outputs), if
+    already computed. Returns the GPU outputs and the oracle result."""
     log(f"[forward] {w.name} T={w.T} H={w.H} F={w.F} N={w.N} k={w.k} cap={w.capacity} "
         f"order={w.order} noisy={w.noisy} out={out}")
+    nthreads = nthreads or oracle_threads()
     g = run_forward(w, out=out, d=d)
-    ora = oracle.route(w)
+    ora = ora if ora is not None else oracle.route(w)
     cap = oracle.capacity(w, ora["topk_idx"])
     flips = routing_flips(g["topk_idx"], ora, w.name)
     # downstream comparison only where the routing (and so every later rank)
@@ -149,7 +187,10 @@ def check_forward(w, tokens=None, nthreads=16, out="f32", d=None):
         assert np.array_equal(g["kept"], cap["kept"]), (g["kept"], cap["kept"])
         assert np.array_equal(g["load"], cap["counts"])
     np.testing.assert_allclose(g["topk_w"][~flips], ora["topk_w"][~flips], rtol=2e-6, atol=1e-7)
-    _, y_ref = oracle.combine_tokens(w, ora["topk_idx"], ora["topk_w"], cap["slot"], tokens, nthreads=nthreads)
+    if E is not None:
+        _, y_ref = oracle.combine_rows(w, ora["topk_w"], cap["slot"], E[tokens], tokens)
+    else:
+        _, y_ref = oracle.combine_tokens(w, ora["topk_idx"], ora["topk_w"], cap["slot"], tokens, nthreads=nthreads)
     assert_close(g["y"][tokens], y_ref, w, f"{w.name} y[{len(tokens)} tokens]")
     dropped_all = np.all(cap["slot"][tokens] < 0, axis=1)
     if dropped_all.any():

@@ -140,3 +140,9 @@ def test_missing_library_fails_loudly(tmp_path):
     from sparse_mixture_experts_05_amd import abi as a
     with pytest.raises(RuntimeError, match="missing"):
         a.load_library(str(tmp_path / "nope.so"))
+
+
+def test_debug_wait_hook_validates_on_the_host(abi):
+    with pytest.raises(abi.MoEError):
+        abi.moe_debug_set_wait(10, -1)
+    abi.moe_debug_set_wait(0, 0)
