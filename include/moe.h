@@ -171,6 +171,28 @@ moe_status moe_forward(const moe_cfg* cfg, const void* x, const float* Wg, const
                        float* topk_w_opt, int32_t* kept_opt, int32_t* load_opt, float* importance_opt,
                        float* P_opt, float* balance_opt, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* moe_forward without a caller workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). Same arguments, outputs and results as
+ * moe_forward, minus ws and ws_bytes; it allocates nothing and makes no
+ * allocating call.
+ *   The workspace is a static device array of moe_noalloc_scratch_bytes()
+ *   bytes (320 MiB) that each GPU the library runs on holds until the
+ *   process ends; its device address is looked up on a device's first call.
+ *   It covers the LLaMA-MoE-3.5B layers (4096 tokens: 2/8 needs 157 MB, 4/16
+ *   with top-4 291 MB); a layer whose moe_workspace_bytes(cfg) exceeds it is
+ *   rejected with MOE_ERR_WORKSPACE before any launch.
+ *   Every call on one GPU shares that GPU's array and leaves its contents
+ *   behind; each call re-initialises what it needs (the expert kernel's queue
+ *   counters are cleared on the stream). Calls that overlap on one GPU (on
+ *   different streams, or from several threads without ordering) race on the
+ *   array and give undefined results. */
+moe_status moe_forward_noalloc(const moe_cfg* cfg, const void* x, const float* Wg, const float* Wn, const float* eps,
+                               const void* Wgate, const void* Wup, const void* Wdown, void* y, int32_t* topk_idx_opt,
+                               float* topk_w_opt, int32_t* kept_opt, int32_t* load_opt, float* importance_opt,
+                               float* P_opt, float* balance_opt, hipStream_t stream);
+size_t moe_noalloc_scratch_bytes(void);
+
 const char* moe_status_str(moe_status s);
 const char* moe_last_error(void); /* thread-local text of the last failure, "" if none */
 

@@ -25,7 +25,8 @@ MOE_TOPK_THEN_SOFTMAX, MOE_SOFTMAX_THEN_TOPK = 0, 1
 
 EXPORTED = ["moe_capacity", "moe_check", "moe_workspace_bytes", "moe_route", "moe_permute",
             "moe_grouped_swiglu", "moe_combine", "moe_forward", "moe_status_str", "moe_last_error",
-            "moe_profile_select", "moe_profile_read", "moe_debug_set_wait"]
+            "moe_profile_select", "moe_profile_read", "moe_debug_set_wait", "moe_forward_noalloc",
+            "moe_noalloc_scratch_bytes"]
 
 
 class moe_cfg(ctypes.Structure):
@@ -80,6 +81,10 @@ def load_library(path: Optional[str] = None):
     lib.moe_profile_select.restype = i32
     lib.moe_profile_read.argtypes = [ctypes.POINTER(f64), ctypes.POINTER(i64)]
     lib.moe_profile_read.restype = i32
+    lib.moe_forward_noalloc.argtypes = [cfgp] + [vp] * 15 + [vp]
+    lib.moe_forward_noalloc.restype = i32
+    lib.moe_noalloc_scratch_bytes.argtypes = []
+    lib.moe_noalloc_scratch_bytes.restype = sz
     lib.moe_debug_set_wait.argtypes = [i32, i32]
     lib.moe_debug_set_wait.restype = i32
     if path is None:
@@ -195,6 +200,18 @@ def moe_forward(cfg, x, Wg, Wn, eps, Wgate, Wup, Wdown, y, topk_idx=None, topk_w
                                       _p(Wdown), _p(y), _p(topk_idx), _p(topk_w), _p(kept), _p(load),
                                       _p(importance), _p(P), _p(balance), _p(ws),
                                       0 if ws is None else ws.numel(), _s(stream)), "moe_forward")
+
+
+def moe_forward_noalloc(cfg, x, Wg, Wn, eps, Wgate, Wup, Wdown, y, topk_idx=None, topk_w=None, kept=None,
+                        load=None, importance=None, P=None, balance=None, stream=None):
+    c = cfg.c()
+    _check(load_library().moe_forward_noalloc(ctypes.byref(c), _p(x), _p(Wg), _p(Wn), _p(eps), _p(Wgate), _p(Wup),
+                                              _p(Wdown), _p(y), _p(topk_idx), _p(topk_w), _p(kept), _p(load),
+                                              _p(importance), _p(P), _p(balance), _s(stream)), "moe_forward_noalloc")
+
+
+def moe_noalloc_scratch_bytes() -> int:
+    return int(load_library().moe_noalloc_scratch_bytes())
 
 
 def moe_profile_select(kernel_id: int):

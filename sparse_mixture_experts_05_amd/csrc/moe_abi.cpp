@@ -9,6 +9,7 @@
 #include <utility>
 #include <vector>
 
+#include "abi_internal.h"
 #include "kernels.h"
 #include "moe.h"
 
@@ -236,6 +237,20 @@ moe_status run_gemms(const moe_cfg* c, const Layout& L, const void* a, const int
 }
 
 }  // namespace
+
+namespace moe {
+
+moe_status set_error(moe_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+}  // namespace moe
 
 extern "C" {
 

@@ -146,3 +146,22 @@ def test_debug_wait_hook_validates_on_the_host(abi):
     with pytest.raises(abi.MoEError):
         abi.moe_debug_set_wait(10, -1)
     abi.moe_debug_set_wait(0, 0)
+
+
+def test_noalloc_entry_rejects_oversized_layers_on_the_host(abi):
+    """The allocation-free entry point's size check runs before any device
+    call: the 8192-token Llama-3 E8T2 layer needs more workspace than its
+    320 MiB scratch array and is rejected; a malformed cfg is rejected first."""
+    assert abi.moe_noalloc_scratch_bytes() == 320 << 20
+    big = abi.MoEConfig(T=8192, H=4096, F=14336, N=8, k=2)
+    assert abi.moe_workspace_bytes(big) > abi.moe_noalloc_scratch_bytes()
+    c2 = abi.MoEConfig(T=4096, H=4096, F=1376, N=8, k=2, out_scale=4.0)
+    c3 = abi.MoEConfig(T=4096, H=4096, F=688, N=16, k=4, noisy=True, want_stats=True, out_scale=4.0)
+    assert abi.moe_workspace_bytes(c2) <= abi.moe_noalloc_scratch_bytes()
+    assert abi.moe_workspace_bytes(c3) <= abi.moe_noalloc_scratch_bytes()
+    with pytest.raises(abi.MoEError) as ei:
+        abi.moe_forward_noalloc(big, 16, 16, None, None, 16, 16, 16, 16, stream=0)
+    assert ei.value.status == abi.MOE_ERR_WORKSPACE
+    with pytest.raises(abi.MoEError) as ei:
+        abi.moe_forward_noalloc(cfg(abi, k=9), 16, 16, None, None, 16, 16, 16, 16, stream=0)
+    assert ei.value.status == abi.MOE_ERR_INVALID
