@@ -49,9 +49,10 @@ def load(path: str = None):
     lib.oracle_expert_rows.argtypes = [cfgp, vp, vp, vp, vp, i32, vp, i64, i32, vp, vp]
     lib.oracle_combine_tokens.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, vp, vp]
     lib.oracle_combine_rows.argtypes = [cfgp, vp, vp, vp, i64, vp, vp, vp]
+    lib.oracle_smooth_load.argtypes = [cfgp] + [vp] * 5
     lib.brute_layer.argtypes = [cfgp] + [vp] * 17
     for f in ("oracle_route", "oracle_stats", "oracle_capacity", "oracle_expert_rows",
-              "oracle_combine_tokens", "oracle_combine_rows", "brute_layer"):
+              "oracle_combine_tokens", "oracle_combine_rows", "oracle_smooth_load", "brute_layer"):
         getattr(lib, f).restype = ctypes.c_int
     for f in ("oracle_round_bf16", "oracle_round_f32", "oracle_silu", "oracle_softplus", "brute_round_bf16"):
         getattr(lib, f).argtypes = [ctypes.c_double]
@@ -115,6 +116,16 @@ def stats(w, r, lib=None):
                             ctypes.byref(bal), ctypes.byref(balc)), "oracle_stats")
     out["balance"] = bal.value
     out["balance_code"] = balc.value
+    return out
+
+
+def smooth_load(w, lib=None):
+    """Smooth gate load [N] of the noisy top-k gate (see moe_oracle.h)."""
+    lib = lib or load()
+    c = cfg(w)
+    out = np.zeros(w.N)
+    _check(lib.oracle_smooth_load(ctypes.byref(c), _p(w.x), _p(w.Wg), _p(w.Wn), _p(w.eps), _p(out)),
+           "oracle_smooth_load")
     return out
 
 

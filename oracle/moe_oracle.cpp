@@ -219,6 +219,47 @@ int oracle_stats(const oracle_cfg* c, const float* logits, const int32_t* topk_i
   return 0;
 }
 
+int oracle_smooth_load(const oracle_cfg* c, const void* x, const float* Wg, const float* Wn, const float* eps,
+                       double* smooth_load) {
+  if (!cfg_ok(c) || !c->noisy) return -1;
+  if (!smooth_load) return -2;
+  if (c->T > 0 && (!x || !Wg || !Wn || !eps)) return -2;
+  const int64_t T = c->T, H = c->H, N = c->N, k = c->k;
+  std::vector<double> xd(H), lg(N), sp(N);
+  std::vector<float> hv(N), others;
+  for (int64_t i = 0; i < N; ++i) smooth_load[i] = 0.0;
+  for (int64_t t = 0; t < T; ++t) {
+    for (int64_t h = 0; h < H; ++h) xd[h] = load_val(x, c->x_dtype, t * H + h);
+    for (int64_t i = 0; i < N; ++i) {
+      double a = 0.0, b = 0.0;
+      for (int64_t h = 0; h < H; ++h) {
+        a += xd[h] * static_cast<double>(Wg[h * N + i]);
+        b += xd[h] * static_cast<double>(Wn[h * N + i]);
+      }
+      lg[i] = static_cast<double>(static_cast<float>(a)); /* the fp32 clean logit */
+      sp[i] = oracle_softplus(b);
+      /* the selection score H_i of [UP] section 3, as oracle_route stores it
+       * (fp32; a NaN read as -inf) */
+      double s = a + static_cast<double>(eps[t * N + i]) * sp[i];
+      if (std::isnan(s)) s = -std::numeric_limits<double>::infinity();
+      hv[i] = static_cast<float>(s);
+    }
+    for (int64_t i = 0; i < N; ++i) {
+      /* kth_excluding: the k-th highest score among the other experts */
+      others.clear();
+      for (int64_t j = 0; j < N; ++j)
+        if (j != i) others.push_back(hv[j]);
+      std::sort(others.begin(), others.end(), [](float a, float b) { return a > b; });
+      const double thr = static_cast<int64_t>(others.size()) >= k ? static_cast<double>(others[k - 1])
+                                                                  : -std::numeric_limits<double>::infinity();
+      /* Phi(z) = erfc(-z / sqrt(2)) / 2 */
+      const double z = (lg[i] - thr) / sp[i];
+      smooth_load[i] += 0.5 * std::erfc(-z / std::sqrt(2.0));
+    }
+  }
+  return 0;
+}
+
 int oracle_capacity(const oracle_cfg* c, const int32_t* topk_idx, int64_t* counts, int64_t* kept,
                     int64_t* offsets, int64_t* slot, int64_t* row_token) {
   if (!cfg_ok(c)) return -1;

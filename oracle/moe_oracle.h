@@ -73,6 +73,17 @@ int oracle_stats(const oracle_cfg* c, const float* logits, const int32_t* topk_i
                  int64_t* load, double* importance, double* P, double* f, double* balance,
                  double* balance_code);
 
+/* Smooth gate load of the noisy top-k gate (the TopK Noisy Gate of Shazeer et
+ * al. 2017 that the LLaMA-MoE hub page names, with its Gate Load monitor):
+ *   smooth_load_i = sum_t P(x_t, i),
+ *   P(x, i) = Phi( (fl32((x.W_g)_i) - kth_excluding(H(x), k, i)) / Softplus((x.W_noise)_i) ),
+ * the probability that expert i is among the top k when only its own normal
+ * draw is taken again. kth_excluding(H, k, i) is the k-th highest of the
+ * other experts' scores H (fp32, as oracle_route stores them), or -inf when
+ * fewer than k others exist; Phi is the standard normal CDF. Needs noisy. */
+int oracle_smooth_load(const oracle_cfg* c, const void* x, const float* Wg, const float* Wn, const float* eps,
+                       double* smooth_load);
+
 /* Capacity clip and expert-contiguous permutation.
  * counts[N] (before capacity), kept[N] = min(counts, C), offsets[N+1] =
  * exclusive scan of kept, slot[T,k] = row of (t,j) or -1 when dropped,

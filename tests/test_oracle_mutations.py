@@ -64,6 +64,11 @@ MUTANTS = [
     ("combine_rows_drops_scale", "const double y = c->out_scale * acc[h];\n      if (y64) y64[i * H + h] = y;\n      if (y32) y32[i * H + h] = static_cast<float>(y);\n    }\n  }\n  return 0;",
      "const double y = acc[h];\n      if (y64) y64[i * H + h] = y;\n      if (y32) y32[i * H + h] = static_cast<float>(y);\n    }\n  }\n  return 0;"),
     ("combine_rows_reads_wrong_slot", "const double* Ej = E + (i * k + j) * H;", "const double* Ej = E + (i * k) * H;"),
+    ("smooth_uses_noisy_numerator", "const double z = (lg[i] - thr) / sp[i];",
+     "const double z = (static_cast<double>(hv[i]) - thr) / sp[i];"),
+    ("smooth_kth_includes_self", "if (j != i) others.push_back(hv[j]);", "others.push_back(hv[j]);"),
+    ("smooth_phi_sign", "0.5 * std::erfc(-z / std::sqrt(2.0))", "0.5 * std::erfc(z / std::sqrt(2.0))"),
+    ("smooth_no_sqrt2", "0.5 * std::erfc(-z / std::sqrt(2.0))", "0.5 * std::erfc(-z)"),
     ("nan_score_not_ranked_last",
      "if (std::isnan(hv)) hv = -std::numeric_limits<double>::infinity();", "(void)0;"),
 ]

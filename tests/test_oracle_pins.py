@@ -3,6 +3,7 @@ routines (torch, numpy) that are independent of the oracle's code."""
 import math
 
 import numpy as np
+import pytest
 import torch
 
 import oracle
@@ -143,3 +144,58 @@ def test_combine_rows_equals_combine_tokens():
         assert np.array_equal(a64, b64) and np.array_equal(a32, b32)
         if cap == 0:
             assert np.all(b64 == 0.0)
+
+
+def _token(w, t):
+    """Token t of w as a one-token workload (same weights and draws)."""
+    return synth.Workload(w.name, 1, w.H, w.F, w.N, w.k, w.capacity, w.order, w.noisy, False, w.out_scale, w.act,
+                          w.wt, np.ascontiguousarray(w.x[t:t + 1]), w.Wg, w.Wn,
+                          np.ascontiguousarray(w.eps[t:t + 1]), w.Wgate, w.Wup, w.Wdown)
+
+
+def test_smooth_load_against_monte_carlo():
+    """P(x, i) is the probability that expert i lands in the top k when only
+    its own normal draw is taken again (the other experts keep their scores):
+    estimated here by sampling that draw, with the rank taken over the whole
+    score vector, it must agree with the oracle within 5 standard errors."""
+    w = synth.make_independent("smooth", 70, 6, 64, 8, 6, 2, act="f32", wt="f32", noisy=True, wsig=0.3)
+    rng = np.random.default_rng(7)
+    M = 200_000
+    for t in range(w.T):
+        wt = _token(w, t)
+        r = oracle.route(wt)
+        P = oracle.smooth_load(wt)
+        n = torch.from_numpy(wt.x).double() @ torch.from_numpy(wt.Wn).double()
+        sp = torch.nn.functional.softplus(n)[0].numpy()
+        Hs = r["H"][0].astype(np.float64)
+        for i in range(w.N):
+            z = rng.standard_normal(M)
+            hi = float(r["logits"][0, i]) + z * sp[i]
+            others = np.delete(Hs, i)
+            rank = (others[None, :] > hi[:, None]).sum(axis=1)
+            frac = float(np.mean(rank < w.k))
+            se = np.sqrt(max(P[i] * (1 - P[i]), 1e-12) / M)
+            assert abs(frac - P[i]) <= 5 * se + 1e-9, (t, i, frac, P[i])
+
+
+def test_smooth_load_limits():
+    """k = N keeps every expert whatever its draw: each P = 1, load = T. With
+    the noise scale driven to ~0 (Softplus of a very negative noise logit),
+    P becomes the indicator that the clean logit beats the others' k-th
+    score, so the smooth load equals the hard load of the clean gate."""
+    w = synth.make_independent("smooth_kn", 71, 9, 32, 8, 4, 4, act="f32", wt="f32", noisy=True)
+    np.testing.assert_array_equal(oracle.smooth_load(w), np.full(4, 9.0))
+    w = synth.make_independent("smooth_lim", 72, 40, 32, 8, 6, 2, act="f32", wt="f32", noisy=True)
+    w.x = np.abs(w.x) + 0.5                       # every x.W_noise below -40 with W_noise = -1
+    w.Wn = np.full_like(w.Wn, -1.0)
+    w.Wg = synth.normal_f32(72, 99, w.Wg.shape, 1.0)
+    r = oracle.route(w)
+    assert np.all(r["min_gap"] > 1e-9)            # far above the noise scale of ~1e-18
+    hard = np.bincount(r["topk_idx"].ravel(), minlength=w.N).astype(np.float64)
+    np.testing.assert_allclose(oracle.smooth_load(w), hard, atol=1e-12)
+
+
+def test_smooth_load_needs_the_noisy_gate():
+    w = synth.make_independent("smooth_clean", 73, 4, 16, 8, 4, 2, act="f32", wt="f32")
+    with pytest.raises(ValueError):
+        oracle.smooth_load(w)
