@@ -109,14 +109,21 @@ size_t moe_workspace_bytes(const moe_cfg* cfg);
  *   importance_opt [N] fp32 sum of gate weights per expert;
  *   P_opt [N] fp32 mean over tokens of softmax(logits);
  *   balance_opt [1] fp32 sum_i f_i P_i with f_i = load_i / (T k)
- *   (the coefficient lambda is left to the caller).
+ *   (the coefficient lambda is left to the caller);
+ *   smooth_load_opt [N] fp32, noisy gate only (MOE_ERR_INVALID otherwise):
+ *   the smooth load estimate of the TopK Noisy Gate (Shazeer et al. 2017,
+ *   which the LLaMA-MoE hub page names), sum over tokens of
+ *   Phi(((x.W_g)_i - kth_excluding(H, k, i)) / Softplus((x.W_noise)_i)), the
+ *   chance that expert i stays in the top k when only its own normal draw
+ *   is taken again; kth_excluding is the k-th highest score of the other
+ *   experts (-inf when k = N).
  *   ws: a workspace of moe_workspace_bytes(cfg) is required when statistics
  *   are requested; otherwise it may be NULL.
  *   Returns MOE_ERR_WORKSPACE when it is too small. */
 moe_status moe_route(const moe_cfg* cfg, const void* x, const float* Wg, const float* Wn, const float* eps,
                      float* logits_opt, int32_t* topk_idx, float* topk_w, int32_t* load_opt,
-                     float* importance_opt, float* P_opt, float* balance_opt, void* ws, size_t ws_bytes,
-                     hipStream_t stream);
+                     float* importance_opt, float* P_opt, float* balance_opt, float* smooth_load_opt, void* ws,
+                     size_t ws_bytes, hipStream_t stream);
 
 /* Capacity clip and permutation into expert-contiguous order (review,
  * section 3, capacity factor: each expert keeps its first cfg->capacity
@@ -169,7 +176,8 @@ moe_status moe_combine(const moe_cfg* cfg, const float* y_perm, const int32_t* s
 moe_status moe_forward(const moe_cfg* cfg, const void* x, const float* Wg, const float* Wn, const float* eps,
                        const void* Wgate, const void* Wup, const void* Wdown, void* y, int32_t* topk_idx_opt,
                        float* topk_w_opt, int32_t* kept_opt, int32_t* load_opt, float* importance_opt,
-                       float* P_opt, float* balance_opt, void* ws, size_t ws_bytes, hipStream_t stream);
+                       float* P_opt, float* balance_opt, float* smooth_load_opt, void* ws, size_t ws_bytes,
+                       hipStream_t stream);
 
 /* moe_forward without a caller workspace, for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops,
@@ -190,7 +198,7 @@ moe_status moe_forward(const moe_cfg* cfg, const void* x, const float* Wg, const
 moe_status moe_forward_noalloc(const moe_cfg* cfg, const void* x, const float* Wg, const float* Wn, const float* eps,
                                const void* Wgate, const void* Wup, const void* Wdown, void* y, int32_t* topk_idx_opt,
                                float* topk_w_opt, int32_t* kept_opt, int32_t* load_opt, float* importance_opt,
-                               float* P_opt, float* balance_opt, hipStream_t stream);
+                               float* P_opt, float* balance_opt, float* smooth_load_opt, hipStream_t stream);
 size_t moe_noalloc_scratch_bytes(void);
 
 const char* moe_status_str(moe_status s);

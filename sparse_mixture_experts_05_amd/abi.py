@@ -63,7 +63,7 @@ def load_library(path: Optional[str] = None):
     lib.moe_check.restype = i32
     lib.moe_workspace_bytes.argtypes = [cfgp]
     lib.moe_workspace_bytes.restype = sz
-    lib.moe_route.argtypes = [cfgp] + [vp] * 11 + [vp, sz, vp]
+    lib.moe_route.argtypes = [cfgp] + [vp] * 12 + [vp, sz, vp]
     lib.moe_route.restype = i32
     lib.moe_permute.argtypes = [cfgp] + [vp] * 7 + [vp, sz, vp]
     lib.moe_permute.restype = i32
@@ -71,7 +71,7 @@ def load_library(path: Optional[str] = None):
     lib.moe_grouped_swiglu.restype = i32
     lib.moe_combine.argtypes = [cfgp] + [vp] * 4 + [vp]
     lib.moe_combine.restype = i32
-    lib.moe_forward.argtypes = [cfgp] + [vp] * 15 + [vp, sz, vp]
+    lib.moe_forward.argtypes = [cfgp] + [vp] * 16 + [vp, sz, vp]
     lib.moe_forward.restype = i32
     lib.moe_status_str.argtypes = [i32]
     lib.moe_status_str.restype = ctypes.c_char_p
@@ -81,7 +81,7 @@ def load_library(path: Optional[str] = None):
     lib.moe_profile_select.restype = i32
     lib.moe_profile_read.argtypes = [ctypes.POINTER(f64), ctypes.POINTER(i64)]
     lib.moe_profile_read.restype = i32
-    lib.moe_forward_noalloc.argtypes = [cfgp] + [vp] * 15 + [vp]
+    lib.moe_forward_noalloc.argtypes = [cfgp] + [vp] * 16 + [vp]
     lib.moe_forward_noalloc.restype = i32
     lib.moe_noalloc_scratch_bytes.argtypes = []
     lib.moe_noalloc_scratch_bytes.restype = sz
@@ -166,10 +166,11 @@ def workspace(cfg: MoEConfig, device="cuda") -> torch.Tensor:
 
 
 def moe_route(cfg, x, Wg, Wn, eps, logits, topk_idx, topk_w, load=None, importance=None, P=None, balance=None,
-              ws=None, stream=None):
+              ws=None, stream=None, smooth_load=None):
     c = cfg.c()
     _check(load_library().moe_route(ctypes.byref(c), _p(x), _p(Wg), _p(Wn), _p(eps), _p(logits), _p(topk_idx),
-                                    _p(topk_w), _p(load), _p(importance), _p(P), _p(balance), _p(ws),
+                                    _p(topk_w), _p(load), _p(importance), _p(P), _p(balance), _p(smooth_load),
+                                    _p(ws),
                                     0 if ws is None else ws.numel(), _s(stream)), "moe_route")
 
 
@@ -194,20 +195,21 @@ def moe_combine(cfg, y_perm, slot, topk_w, y, stream=None):
 
 
 def moe_forward(cfg, x, Wg, Wn, eps, Wgate, Wup, Wdown, y, topk_idx=None, topk_w=None, kept=None, load=None,
-                importance=None, P=None, balance=None, ws=None, stream=None):
+                importance=None, P=None, balance=None, ws=None, stream=None, smooth_load=None):
     c = cfg.c()
     _check(load_library().moe_forward(ctypes.byref(c), _p(x), _p(Wg), _p(Wn), _p(eps), _p(Wgate), _p(Wup),
                                       _p(Wdown), _p(y), _p(topk_idx), _p(topk_w), _p(kept), _p(load),
-                                      _p(importance), _p(P), _p(balance), _p(ws),
+                                      _p(importance), _p(P), _p(balance), _p(smooth_load), _p(ws),
                                       0 if ws is None else ws.numel(), _s(stream)), "moe_forward")
 
 
 def moe_forward_noalloc(cfg, x, Wg, Wn, eps, Wgate, Wup, Wdown, y, topk_idx=None, topk_w=None, kept=None,
-                        load=None, importance=None, P=None, balance=None, stream=None):
+                        load=None, importance=None, P=None, balance=None, stream=None, smooth_load=None):
     c = cfg.c()
     _check(load_library().moe_forward_noalloc(ctypes.byref(c), _p(x), _p(Wg), _p(Wn), _p(eps), _p(Wgate), _p(Wup),
                                               _p(Wdown), _p(y), _p(topk_idx), _p(topk_w), _p(kept), _p(load),
-                                              _p(importance), _p(P), _p(balance), _s(stream)), "moe_forward_noalloc")
+                                              _p(importance), _p(P), _p(balance), _p(smooth_load), _s(stream)),
+           "moe_forward_noalloc")
 
 
 def moe_noalloc_scratch_bytes() -> int:

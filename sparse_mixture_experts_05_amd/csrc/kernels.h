@@ -19,8 +19,10 @@ struct RouterParams {
   int32_t* topk_idx;      // [T,k]
   float* topk_w;          // [T,k]
   int32_t* hist;          // [blocks,N] assignments per expert per block, or null
-  float* stat_part;       // [blocks,2N] importance and sum of softmax(logits), or null
+  float* stat_part;       // [blocks,3N] importance, sum of softmax(logits), smooth load; or null
+  int smooth;             // 1: fill the smooth-load partials (noisy gate only)
 };
+constexpr int kStatsPerExpert = 3;  // importance, softmax(logits) sum, smooth load
 // Tokens handled by one router block; the permutation scatter reads the
 // per-block histogram with this granularity.
 int router_tokens_per_block(int N, int noisy, int act_bf16);
@@ -39,6 +41,7 @@ struct StatsParams {
   float* importance;      // [N] or null
   float* P;               // [N] or null
   float* balance;         // [1] or null
+  float* smooth_load;     // [N] or null (needs the router's smooth partials)
 };
 hipError_t launch_stats(const StatsParams& p, hipStream_t s);
 

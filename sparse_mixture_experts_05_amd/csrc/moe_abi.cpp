@@ -119,7 +119,7 @@ Layout layout(const moe_cfg* c) {
     return at;
   };
   L.hist = take(static_cast<size_t>(L.hist_blocks) * c->N * 4);
-  L.stat = take(static_cast<size_t>(L.hist_blocks) * c->N * 2 * 4);
+  L.stat = take(static_cast<size_t>(L.hist_blocks) * c->N * moe::kStatsPerExpert * 4);
   L.h = take(static_cast<size_t>(L.A_max) * c->F * act);
   L.yperm = take(static_cast<size_t>(L.splits) * L.A_max * c->H * 4);
   L.idx = take(static_cast<size_t>(Tk) * 4);
@@ -296,13 +296,19 @@ size_t moe_workspace_bytes(const moe_cfg* c) {
 
 moe_status moe_route(const moe_cfg* c, const void* x, const float* Wg, const float* Wn, const float* eps,
                      float* logits_opt, int32_t* topk_idx, float* topk_w, int32_t* load_opt,
-                     float* importance_opt, float* P_opt, float* balance_opt, void* ws, size_t ws_bytes,
-                     hipStream_t s) {
+                     float* importance_opt, float* P_opt, float* balance_opt, float* smooth_load_opt, void* ws,
+                     size_t ws_bytes, hipStream_t s) {
   moe_status st = moe_check(c);
   if (st != MOE_OK) return st;
-  const bool stats = c->want_stats && (load_opt || importance_opt || P_opt || balance_opt);
+  MOE_REQUIRE(!smooth_load_opt || c->noisy, "the smooth load needs the noisy gate (cfg->noisy = 1)");
+  const bool stats = c->want_stats && (load_opt || importance_opt || P_opt || balance_opt || smooth_load_opt);
   if (c->T == 0) {
-    if (stats) return zero_expert_outputs(c, load_opt, nullptr, nullptr, importance_opt, P_opt, balance_opt, s);
+    if (stats) {
+      st = zero_expert_outputs(c, load_opt, nullptr, nullptr, importance_opt, P_opt, balance_opt, s);
+      if (st == MOE_OK && smooth_load_opt) st = zero_expert_outputs(c, nullptr, nullptr, nullptr, smooth_load_opt,
+                                                                     nullptr, nullptr, s);
+      return st;
+    }
     return MOE_OK;
   }
   MOE_REQUIRE(x && Wg && topk_idx && topk_w, "x, Wg, topk_idx and topk_w are required");
@@ -330,10 +336,11 @@ moe_status moe_route(const moe_cfg* c, const void* x, const float* Wg, const flo
   rp.topk_w = topk_w;
   rp.hist = stats ? at<int32_t>(ws, L.hist) : nullptr;
   rp.stat_part = stats ? at<float>(ws, L.stat) : nullptr;
+  rp.smooth = stats && smooth_load_opt ? 1 : 0;
   MOE_LAUNCH(MOE_KERNEL_ROUTER, s, moe::launch_router(rp, s));
   if (stats) {
     moe::StatsParams sp{at<int32_t>(ws, L.hist), at<float>(ws, L.stat), L.hist_blocks, c->T, c->N, c->k,
-                        load_opt, importance_opt, P_opt, balance_opt};
+                        load_opt, importance_opt, P_opt, balance_opt, smooth_load_opt};
     MOE_LAUNCH(MOE_KERNEL_STATS, s, moe::launch_stats(sp, s));
   }
   return MOE_OK;
@@ -393,13 +400,19 @@ moe_status moe_combine(const moe_cfg* c, const float* y_perm, const int32_t* slo
 moe_status moe_forward(const moe_cfg* c, const void* x, const float* Wg, const float* Wn, const float* eps,
                        const void* Wgate, const void* Wup, const void* Wdown, void* y, int32_t* topk_idx_opt,
                        float* topk_w_opt, int32_t* kept_opt, int32_t* load_opt, float* importance_opt,
-                       float* P_opt, float* balance_opt, void* ws, size_t ws_bytes, hipStream_t s) {
+                       float* P_opt, float* balance_opt, float* smooth_load_opt, void* ws, size_t ws_bytes,
+                       hipStream_t s) {
   moe_status st = moe_check(c);
   if (st != MOE_OK) return st;
-  const bool stats = c->want_stats && (load_opt || importance_opt || P_opt || balance_opt);
-  if (c->T == 0)
-    return zero_expert_outputs(c, kept_opt, load_opt, nullptr, stats ? importance_opt : nullptr,
-                               stats ? P_opt : nullptr, stats ? balance_opt : nullptr, s);
+  MOE_REQUIRE(!smooth_load_opt || c->noisy, "the smooth load needs the noisy gate (cfg->noisy = 1)");
+  const bool stats = c->want_stats && (load_opt || importance_opt || P_opt || balance_opt || smooth_load_opt);
+  if (c->T == 0) {
+    st = zero_expert_outputs(c, kept_opt, load_opt, nullptr, stats ? importance_opt : nullptr,
+                             stats ? P_opt : nullptr, stats ? balance_opt : nullptr, s);
+    if (st == MOE_OK && stats && smooth_load_opt)
+      st = zero_expert_outputs(c, nullptr, nullptr, nullptr, smooth_load_opt, nullptr, nullptr, s);
+    return st;
+  }
   MOE_REQUIRE(x && Wg && Wgate && Wup && Wdown && y, "x, Wg, expert weights and y are required");
   MOE_REQUIRE(!c->noisy || (Wn && eps), "noisy routing needs Wn and eps");
   MOE_REQUIRE(aligned(x, 16) && aligned(Wg, 16) && (!Wn || aligned(Wn, 16)) && aligned(Wgate, 16) &&
@@ -431,11 +444,12 @@ moe_status moe_forward(const moe_cfg* c, const void* x, const float* Wg, const f
   rp.topk_w = topk_w;
   rp.hist = at<int32_t>(ws, L.hist);
   rp.stat_part = stats ? at<float>(ws, L.stat) : nullptr;
+  rp.smooth = stats && smooth_load_opt ? 1 : 0;
   MOE_LAUNCH(MOE_KERNEL_ROUTER, s, moe::launch_router(rp, s));
   // statistics: reduced by the persistent expert kernel once its queue is
   // empty when that kernel runs, else by a launch of their own
   const moe::StatsParams sp{at<int32_t>(ws, L.hist), at<float>(ws, L.stat), L.hist_blocks, c->T, c->N, c->k,
-                            load_opt, importance_opt, P_opt, balance_opt};
+                            load_opt, importance_opt, P_opt, balance_opt, smooth_load_opt};
   if (stats && !L.fused) MOE_LAUNCH(MOE_KERNEL_STATS, s, moe::launch_stats(sp, s));
   moe::ScatterParams sc{topk_idx, at<int32_t>(ws, L.hist), L.hist_tokens, c->T, c->N, c->k, c->capacity,
                         (!stats && load_opt) ? load_opt : at<int32_t>(ws, L.counts), kept_opt, offsets, slot,

@@ -55,7 +55,7 @@ size_t moe_noalloc_scratch_bytes(void) { return kScratchBytes; }
 moe_status moe_forward_noalloc(const moe_cfg* c, const void* x, const float* Wg, const float* Wn, const float* eps,
                                const void* Wgate, const void* Wup, const void* Wdown, void* y, int32_t* topk_idx_opt,
                                float* topk_w_opt, int32_t* kept_opt, int32_t* load_opt, float* importance_opt,
-                               float* P_opt, float* balance_opt, hipStream_t stream) {
+                               float* P_opt, float* balance_opt, float* smooth_load_opt, hipStream_t stream) {
   moe_status st = moe_check(c);
   if (st != MOE_OK) return st;
   const size_t need = moe_workspace_bytes(c);
@@ -68,7 +68,7 @@ moe_status moe_forward_noalloc(const moe_cfg* c, const void* x, const float* Wg,
   st = scratch_ptr(&ws);
   if (st != MOE_OK) return st;
   return moe_forward(c, x, Wg, Wn, eps, Wgate, Wup, Wdown, y, topk_idx_opt, topk_w_opt, kept_opt, load_opt,
-                     importance_opt, P_opt, balance_opt, ws, kScratchBytes, stream);
+                     importance_opt, P_opt, balance_opt, smooth_load_opt, ws, kScratchBytes, stream);
 }
 
 }  // extern "C"

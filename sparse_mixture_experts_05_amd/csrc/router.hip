@@ -117,7 +117,7 @@ __global__ __launch_bounds__(kRouterWaves * kWave) void k_router(RouterParams p)
     if constexpr (NOISY) accumulate<NMAX, TPW, VEC4>(p.Wn, h, N, xv, nacc);
   }
 
-  float cnt = 0.0f, imp = 0.0f, psum = 0.0f;  // this lane's expert, summed over the wave's tokens
+  float cnt = 0.0f, imp = 0.0f, psum = 0.0f, slsum = 0.0f;  // this lane's expert, summed over the wave's tokens
   const bool valid = lane < N;
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
@@ -174,6 +174,26 @@ __global__ __launch_bounds__(kRouterWaves * kWave) void k_router(RouterParams p)
         curi = 4096 + lane;
       }
     }
+    // smooth load (Shazeer et al. 2017, the TopK Noisy Gate the LLaMA-MoE hub
+    // page names): Phi((clean logit - k-th highest other score) /
+    // Softplus(noise logit)); that score is the k-th highest overall for an
+    // expert not kept, the (k+1)-th (one more argmax round; -inf when k = N)
+    // for a kept one
+    float sl = 0.0f;
+    if constexpr (NOISY) {
+      if (p.smooth && p.stat_part) {
+        const float vk = __shfl(my_v, k - 1, kWave);
+        float vk1 = -INFINITY;
+        if (k < N) {
+          float bv = cur;
+#pragma unroll
+          for (int m = 32; m >= 1; m >>= 1) bv = fmaxf(bv, __shfl_xor(bv, m, kWave));
+          vk1 = bv;
+        }
+        const float z = (lv - (taken ? vk1 : vk)) / softplus(nz);
+        sl = valid ? 0.5f * erfcf(z * -0.70710678118654752f) : 0.0f;
+      }
+    }
     const float hmax = __shfl(my_v, 0, kWave);
     float den;
     if (p.order == 0) {
@@ -196,29 +216,34 @@ __global__ __launch_bounds__(kRouterWaves * kWave) void k_router(RouterParams p)
         const float el = valid ? expf(lv - lmax) : 0.0f;
         const float dl = wave_sum(el);
         psum += el / dl;
+        slsum += sl;
       }
     }
   }
 
   if (p.hist) {
-    __shared__ float red[kRouterWaves][3][64];
+    __shared__ float red[kRouterWaves][4][64];
     red[wave][0][lane] = cnt;
     red[wave][1][lane] = imp;
     red[wave][2][lane] = psum;
+    red[wave][3][lane] = slsum;
     __syncthreads();
     if (threadIdx.x < N) {
       const int n = threadIdx.x;
-      float c = 0.0f, s_imp = 0.0f, s_p = 0.0f;
+      float c = 0.0f, s_imp = 0.0f, s_p = 0.0f, s_sl = 0.0f;
 #pragma unroll
       for (int w = 0; w < kRouterWaves; ++w) {
         c += red[w][0][n];
         s_imp += red[w][1][n];
         s_p += red[w][2][n];
+        s_sl += red[w][3][n];
       }
       p.hist[static_cast<int64_t>(blockIdx.x) * N + n] = static_cast<int32_t>(c);
       if (p.stat_part) {
-        p.stat_part[static_cast<int64_t>(blockIdx.x) * 2 * N + 2 * n] = s_imp;
-        p.stat_part[static_cast<int64_t>(blockIdx.x) * 2 * N + 2 * n + 1] = s_p;
+        float* part = p.stat_part + (static_cast<int64_t>(blockIdx.x) * N + n) * kStatsPerExpert;
+        part[0] = s_imp;
+        part[1] = s_p;
+        part[2] = s_sl;
       }
     }
   }

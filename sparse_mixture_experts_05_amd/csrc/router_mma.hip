@@ -347,6 +347,7 @@ __global__ __launch_bounds__(router_waves<NB16>() * 64) void k_router_mma(Router
   __shared__ float s_sel[kTok][64];  // gate weight of expert n if kept, else 0
   __shared__ int s_take[kTok][64];   // 1 if expert n is among the token's top k
   __shared__ float s_p[kTok][64];    // softmax of the clean logits
+  __shared__ float s_sl[kTok][64];   // smooth-load probability of expert n
   const bool valid = lane < N;
 #pragma unroll
   for (int i = 0; i < kTW; ++i) {
@@ -357,7 +358,8 @@ __global__ __launch_bounds__(router_waves<NB16>() * 64) void k_router_mma(Router
     float hv = lv;
     // H_i = (x W_g)_i + StandardNormal() * Softplus((x W_noise)_i), the
     // normal draw being the input eps[t, i]
-    if (p.noisy && valid) hv = fmaf(eps_pre[i], softplus(s_log[t][N + lane]), lv);
+    const float sp = (p.noisy && valid) ? softplus(s_log[t][N + lane]) : 1.0f;
+    if (p.noisy && valid) hv = fmaf(eps_pre[i], sp, lv);
     // a NaN score counts as -inf in KeepTopK and the gates, so the rank below
     // is a strict total order and exactly k experts are kept
     if (hv != hv) hv = -INFINITY;
@@ -389,6 +391,19 @@ __global__ __launch_bounds__(router_waves<NB16>() * 64) void k_router_mma(Router
       float ls = 0.0f;
       for (int m = 0; m < N; ++m) ls += lane_value(el, m);
       s_p[t][lane] = el / ls;
+      if (p.smooth) {
+        // smooth load (Shazeer et al. 2017, the TopK Noisy Gate the LLaMA-MoE
+        // hub page names): the chance that expert i stays in the top k when
+        // only its own draw is taken again, Phi((clean logit - k-th highest
+        // other score) / Softplus(noise logit)); the k-th highest other score
+        // is the score of rank k for a kept expert, of rank k - 1 otherwise
+        // (-inf when no expert has rank k)
+        const uint64_t bk1 = __ballot(valid && rank == k - 1), bk = __ballot(valid && rank == k);
+        const float v1 = lane_value(hv, static_cast<int>(__builtin_ctzll(bk1)));
+        const float v2 = bk ? lane_value(hv, static_cast<int>(__builtin_ctzll(bk))) : -INFINITY;
+        const float z = (lv - (kept ? v2 : v1)) / sp;
+        s_sl[t][lane] = valid ? 0.5f * erfcf(z * -0.70710678118654752f) : 0.0f;
+      }
     }
   }
   __syncthreads();
@@ -397,18 +412,21 @@ __global__ __launch_bounds__(router_waves<NB16>() * 64) void k_router_mma(Router
   if (p.hist && threadIdx.x < N) {
     const int n = threadIdx.x;
     int cnt = 0;
-    float imp = 0.0f, ps = 0.0f;
+    float imp = 0.0f, ps = 0.0f, sl = 0.0f;
 #pragma unroll
     for (int t = 0; t < kTok; ++t) {
       const bool ok = t < tv;
       cnt += ok ? s_take[t][n] : 0;
       imp += ok ? s_sel[t][n] : 0.0f;
       ps += ok ? s_p[t][n] : 0.0f;
+      sl += (ok && p.smooth) ? s_sl[t][n] : 0.0f;
     }
     p.hist[static_cast<int64_t>(blockIdx.x) * N + n] = cnt;
     if (p.stat_part) {
-      p.stat_part[static_cast<int64_t>(blockIdx.x) * 2 * N + 2 * n] = imp;
-      p.stat_part[static_cast<int64_t>(blockIdx.x) * 2 * N + 2 * n + 1] = ps;
+      float* part = p.stat_part + (static_cast<int64_t>(blockIdx.x) * N + n) * kStatsPerExpert;
+      part[0] = imp;
+      part[1] = ps;
+      part[2] = sl;
     }
   }
 }

@@ -6,7 +6,8 @@
 // (balance loss) and the LLaMA-MoE monitoring list: load_i = assignments to
 // expert i before capacity, importance_i = sum of its gate weights,
 // P_i = mean over tokens of softmax(logits)_i, balance = sum_i f_i P_i with
-// f_i = load_i / (T k).
+// f_i = load_i / (T k). The smooth load is the sum over tokens of the
+// router's per-token probabilities (see the routers).
 #pragma once
 #include "common.h"
 #include "kernels.h"
@@ -15,7 +16,7 @@ namespace moe {
 
 constexpr int kStatGroups = 8;  // waves of the reducing workgroup, one group of router blocks each
 // LDS the reduction needs (8-byte aligned)
-constexpr int kStatLdsBytes = kStatGroups * 64 * (8 + 4 + 4) + 64 * 4;
+constexpr int kStatLdsBytes = kStatGroups * 64 * (8 + 4 + 4 + 4) + 64 * 4;
 
 // Run by every thread of a workgroup of at least kStatGroups * 64 threads
 // (threads past that take no part). Group g (one wave) sums a contiguous range
@@ -26,25 +27,29 @@ __device__ inline void stats_reduce(const StatsParams& p, void* lds) {
   int64_t* s_cnt = static_cast<int64_t*>(lds);                 // [kStatGroups][64]
   float* s_imp = reinterpret_cast<float*>(s_cnt + kStatGroups * 64);  // [kStatGroups][64]
   float* s_ps = s_imp + kStatGroups * 64;                         // [kStatGroups][64]
-  float* s_fp = s_ps + kStatGroups * 64;                          // [64]
+  float* s_sl = s_ps + kStatGroups * 64;                          // [kStatGroups][64]
+  float* s_fp = s_sl + kStatGroups * 64;                          // [64]
+  constexpr int S = kStatsPerExpert;
   const int n = threadIdx.x & 63, g = threadIdx.x >> 6;
   const bool part = g < kStatGroups;
   const bool valid = part && n < p.N;
   const int b0 = static_cast<int>(static_cast<int64_t>(p.blocks) * g / kStatGroups);
   const int b1 = static_cast<int>(static_cast<int64_t>(p.blocks) * (g + 1) / kStatGroups);
   int64_t c = 0;
-  float imp = 0.0f, ps = 0.0f;
+  float imp = 0.0f, ps = 0.0f, sl = 0.0f;
   if (valid) {
     constexpr int U = 8;  // loads issued together before the in-order adds
     for (int b = b0; b < b1; b += U) {
       int hv[U];
-      float iv[U], pv[U];
+      float iv[U], pv[U], sv[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int bb = b + u < b1 ? b + u : b;
+        const float* part = p.stat_part + (static_cast<int64_t>(bb) * p.N + n) * S;
         hv[u] = p.hist[static_cast<int64_t>(bb) * p.N + n];
-        iv[u] = p.stat_part[static_cast<int64_t>(bb) * 2 * p.N + 2 * n];
-        pv[u] = p.stat_part[static_cast<int64_t>(bb) * 2 * p.N + 2 * n + 1];
+        iv[u] = part[0];
+        pv[u] = part[1];
+        sv[u] = part[2];
       }
 #pragma unroll
       for (int u = 0; u < U; ++u)
@@ -52,6 +57,7 @@ __device__ inline void stats_reduce(const StatsParams& p, void* lds) {
           c += hv[u];
           imp += iv[u];
           ps += pv[u];
+          sl += sv[u];
         }
     }
   }
@@ -59,17 +65,20 @@ __device__ inline void stats_reduce(const StatsParams& p, void* lds) {
     s_cnt[g * 64 + n] = c;
     s_imp[g * 64 + n] = imp;
     s_ps[g * 64 + n] = ps;
+    s_sl[g * 64 + n] = sl;
   }
   __syncthreads();
   if (g != 0) return;
   c = 0;
   imp = 0.0f;
   ps = 0.0f;
+  sl = 0.0f;
 #pragma unroll
   for (int q = 0; q < kStatGroups; ++q) {
     c += s_cnt[q * 64 + n];
     imp += s_imp[q * 64 + n];
     ps += s_ps[q * 64 + n];
+    sl += s_sl[q * 64 + n];
   }
   const bool vn = n < p.N;
   const float load = static_cast<float>(c);
@@ -83,6 +92,7 @@ __device__ inline void stats_reduce(const StatsParams& p, void* lds) {
   if (vn) {
     if (p.importance) p.importance[n] = imp;
     if (p.P) p.P[n] = Pn;
+    if (p.smooth_load) p.smooth_load[n] = sl;
   }
   if (n == 0 && p.balance) {
     float b = 0.0f;

@@ -111,6 +111,17 @@ def assert_close(got: np.ndarray, want: np.ndarray, w, what: str):
     assert rel <= rel_tol, f"{what}: relative L2 error {rel:.3e} > {rel_tol}"
 
 
+def check_smooth_load(got: np.ndarray, w, what: str):
+    """The smooth gate load against the oracle. Each token adds a probability
+    in [0, 1] computed in fp32 (one erfc, about 1e-6 relative) and summed in
+    fp32 over at most a few thousand tokens, while the threshold scores agree
+    to fp32 rounding and the probability is continuous in them (no flips at
+    near ties): relative 1e-4 plus 1e-3 absolute is well above that."""
+    want = oracle.smooth_load(w)
+    log(f"  {what}: smooth load max |diff| {np.abs(got - want).max():.3e} (sum {want.sum():.3f})")
+    np.testing.assert_allclose(got, want, rtol=1e-4, atol=1e-3)
+
+
 def routing_flips(gpu_idx: np.ndarray, ora: dict, what: str) -> np.ndarray:
     """Tokens whose top-k list differs from the oracle's. Fails unless every
     such token is a near tie (oracle gap <= 1e-6); returns their mask."""
@@ -136,10 +147,11 @@ def run_route(w, want_logits=True):
                topk_idx=torch.empty(T, k, dtype=torch.int32, device="cuda"),
                topk_w=torch.empty(T, k, device="cuda"),
                load=torch.empty(N, dtype=torch.int32, device="cuda"), importance=torch.empty(N, device="cuda"),
-               P=torch.empty(N, device="cuda"), balance=torch.empty(1, device="cuda"))
+               P=torch.empty(N, device="cuda"), balance=torch.empty(1, device="cuda"),
+               smooth_load=torch.empty(N, device="cuda") if w.noisy else None)
     ws = workspace(cfg)
     abi.moe_route(cfg, d["x"], d["Wg"], d["Wn"], d["eps"], out["logits"], out["topk_idx"], out["topk_w"],
-                  out["load"], out["importance"], out["P"], out["balance"], ws=ws)
+                  out["load"], out["importance"], out["P"], out["balance"], ws=ws, smooth_load=out["smooth_load"])
     torch.cuda.synchronize()
     return {k_: (host(v) if v is not None else None) for k_, v in out.items()}
 
@@ -153,10 +165,12 @@ def run_forward(w, out="f32", d=None, extras=True):
              kept=torch.empty(N, dtype=torch.int32, device="cuda"), load=torch.empty(N, dtype=torch.int32, device="cuda"),
              importance=torch.empty(N, device="cuda"), P=torch.empty(N, device="cuda"),
              balance=torch.empty(1, device="cuda")) if extras else {}
+    if extras and w.noisy:
+        o["smooth_load"] = torch.empty(N, device="cuda")
     ws = workspace(cfg)
     abi.moe_forward(cfg, d["x"], d["Wg"], d["Wn"], d["eps"], d["Wgate"], d["Wup"], d["Wdown"], y,
                     o.get("topk_idx"), o.get("topk_w"), o.get("kept"), o.get("load"), o.get("importance"),
-                    o.get("P"), o.get("balance"), ws=ws)
+                    o.get("P"), o.get("balance"), ws=ws, smooth_load=o.get("smooth_load"))
     torch.cuda.synchronize()
     res = {k_: host(v) for k_, v in o.items()}
     yh = host(y)

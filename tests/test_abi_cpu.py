@@ -106,25 +106,29 @@ def test_entry_points_reject_bad_arguments_before_launch(abi):
     fake = ctypes.c_void_p(1 << 20)            # never dereferenced: validation fails first
     # missing required pointers
     assert lib.moe_route(ctypes.byref(c), null, fake, null, null, null, fake, fake, null, null, null, null,
-                         null, 0, null) == abi.MOE_ERR_INVALID
+                         null, null, 0, null) == abi.MOE_ERR_INVALID
     # noisy without W_noise / eps
     cn = cfg(abi, noisy=True).c()
     assert lib.moe_route(ctypes.byref(cn), fake, fake, null, null, null, fake, fake, null, null, null, null,
-                         null, 0, null) == abi.MOE_ERR_INVALID
+                         null, null, 0, null) == abi.MOE_ERR_INVALID
+    # the smooth load without the noisy gate
+    assert lib.moe_route(ctypes.byref(c), fake, fake, null, null, null, fake, fake, null, null, null, null,
+                         fake, null, 0, null) == abi.MOE_ERR_INVALID
+    assert b"noisy" in lib.moe_last_error()
     # misaligned x
     odd = ctypes.c_void_p((1 << 20) + 2)
     assert lib.moe_route(ctypes.byref(c), odd, fake, null, null, null, fake, fake, null, null, null, null,
-                         null, 0, null) == abi.MOE_ERR_INVALID
+                         null, null, 0, null) == abi.MOE_ERR_INVALID
     assert b"aligned" in lib.moe_last_error()
     # workspace too small
     assert lib.moe_permute(ctypes.byref(c), fake, fake, fake, fake, fake, fake, null, fake, 16,
                            null) == abi.MOE_ERR_WORKSPACE
     assert lib.moe_forward(ctypes.byref(c), fake, fake, null, null, fake, fake, fake, fake, null, null, null,
-                           null, null, null, null, fake, 16, null) == abi.MOE_ERR_WORKSPACE
+                           null, null, null, null, null, fake, 16, null) == abi.MOE_ERR_WORKSPACE
     # misaligned workspace
     big = abi.moe_workspace_bytes(cfg(abi))
     assert lib.moe_forward(ctypes.byref(c), fake, fake, null, null, fake, fake, fake, fake, null, null, null,
-                           null, null, null, null, ctypes.c_void_p((1 << 20) + 64), big,
+                           null, null, null, null, null, ctypes.c_void_p((1 << 20) + 64), big,
                            null) == abi.MOE_ERR_INVALID
     # invalid cfg is reported by every entry point
     bad = cfg(abi, k=20).c()

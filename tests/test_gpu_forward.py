@@ -14,7 +14,7 @@ import torch
 
 import oracle
 import synth
-from gpu_util import check_forward, log, oracle_threads, run_forward, upload
+from gpu_util import check_forward, check_smooth_load, log, oracle_threads, run_forward, upload
 
 pytestmark = pytest.mark.gpu
 
@@ -69,6 +69,8 @@ def test_forward_small(name):
         np.testing.assert_allclose(g["importance"], st["importance"], rtol=1e-5, atol=1e-4)
         np.testing.assert_allclose(g["P"], st["P"], rtol=1e-5, atol=1e-7)
         np.testing.assert_allclose(g["balance"][0], st["balance"], rtol=1e-5)
+        if w.noisy:
+            check_smooth_load(g["smooth_load"], w, name)
 
 
 def test_forward_bf16_output_within_one_ulp():
@@ -172,6 +174,7 @@ def test_full_C3():
     np.testing.assert_allclose(g["importance"], st["importance"], rtol=1e-5)
     np.testing.assert_allclose(g["P"], st["P"], rtol=1e-5)
     np.testing.assert_allclose(g["balance"][0], st["balance"], rtol=1e-5)
+    check_smooth_load(g["smooth_load"], w, "C3")
 
 
 @pytest.mark.timeout(900)

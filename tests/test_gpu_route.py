@@ -6,7 +6,7 @@ import pytest
 
 import oracle
 import synth
-from gpu_util import log, routing_flips, run_route
+from gpu_util import check_smooth_load, log, routing_flips, run_route
 
 pytestmark = pytest.mark.gpu
 
@@ -20,6 +20,10 @@ def _ties():
 
 CASES = {
     "f32_n8k2": lambda: synth.make_split("f32_n8k2", 11, 300, 256, 8 * 24, 8, 2, act="f32", wt="f32"),
+    "f32_noisy_n16k4_stats": lambda: synth.make_independent("f32_noisy", 24, 301, 256, 8, 16, 4, act="f32",
+                                                            wt="f32", noisy=True, want_stats=True),
+    "f32_noisy_keqn": lambda: synth.make_independent("f32_noisy_keqn", 25, 130, 128, 8, 4, 4, act="f32",
+                                                     wt="f32", noisy=True, want_stats=True),
     "bf16_n8k2": lambda: synth.make_split("bf16_n8k2", 12, 333, 512, 8 * 16, 8, 2),
     "noisy_n16k4_stats": lambda: synth.make_split("noisy", 13, 517, 1024, 16 * 8, 16, 4, noisy=True,
                                                    want_stats=True),
@@ -65,6 +69,8 @@ def test_route_matches_oracle(name):
         np.testing.assert_allclose(g["importance"], st["importance"], rtol=1e-5, atol=1e-4)
         np.testing.assert_allclose(g["P"], st["P"], rtol=1e-5, atol=1e-7)
         np.testing.assert_allclose(g["balance"][0], st["balance"], rtol=1e-5)
+        if w.noisy:
+            check_smooth_load(g["smooth_load"], w, name)
 
 
 def test_route_skewed_decode_prefers_expert_zero():
