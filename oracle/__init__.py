@@ -50,9 +50,11 @@ def load(path: str = None):
     lib.oracle_combine_tokens.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, vp, vp]
     lib.oracle_combine_rows.argtypes = [cfgp, vp, vp, vp, i64, vp, vp, vp]
     lib.oracle_smooth_load.argtypes = [cfgp] + [vp] * 5
+    lib.oracle_residual_combine_rows.argtypes = [cfgp, vp, vp, vp, i64, vp, vp, vp, vp]
     lib.brute_layer.argtypes = [cfgp] + [vp] * 17
     for f in ("oracle_route", "oracle_stats", "oracle_capacity", "oracle_expert_rows",
-              "oracle_combine_tokens", "oracle_combine_rows", "oracle_smooth_load", "brute_layer"):
+              "oracle_combine_tokens", "oracle_combine_rows", "oracle_smooth_load", "oracle_residual_combine_rows",
+              "brute_layer"):
         getattr(lib, f).restype = ctypes.c_int
     for f in ("oracle_round_bf16", "oracle_round_f32", "oracle_silu", "oracle_softplus", "brute_round_bf16"):
         getattr(lib, f).argtypes = [ctypes.c_double]
@@ -197,6 +199,40 @@ def combine_rows(w, topk_w, slot, E, tokens=None, h_round=None, lib=None):
                                    _p(np.ascontiguousarray(slot, np.int64)), _p(tokens), n, _p(E), _p(y64),
                                    _p(y32)), "oracle_combine_rows")
     return y64, y32
+
+
+def shared_slice(w):
+    """The residual layer's shared slice as a one-expert layer (its weights
+    [1,Fs,H], [1,Fs,H], [1,H,Fs]), for expert_rows."""
+    Sg, Su, Sd = w.shared
+    Fs = Sg.shape[0]
+    return type(w)(w.name + "_shared", w.T, w.H, Fs, 1, 1, -1, w.order, False, False, 1.0, w.act, w.wt, w.x,
+                   None, None, None, Sg[None], Su[None], Sd[None])
+
+
+def residual_forward(w, tokens=None, nthreads=1, h_round=None, lib=None, E=None, ora=None):
+    """The residual (shared-slice) layer: routing and capacity for every
+    token, y = shared(x) + s * sum_j w_j E_j(x) for `tokens` (all when None).
+    E: expert outputs of every slot of those tokens, if already computed."""
+    lib = lib or load()
+    r = ora if ora is not None else route(w, lib)
+    cap = capacity(w, r["topk_idx"], lib)
+    tokens = np.arange(w.T, dtype=np.int64) if tokens is None else np.ascontiguousarray(tokens, np.int64)
+    if E is None:
+        E = assignment_outputs(w, r["topk_idx"], tokens, nthreads=nthreads, h_round=h_round, lib=lib)
+    R = expert_rows(shared_slice(w), 0, tokens, nthreads=nthreads, h_round=h_round, lib=lib)
+    c = cfg(w, h_round)
+    n = tokens.size
+    y64 = np.zeros((n, w.H))
+    y32 = np.zeros((n, w.H), np.float32)
+    _check(lib.oracle_residual_combine_rows(ctypes.byref(c), _p(np.ascontiguousarray(r["topk_w"], np.float64)),
+                                            _p(np.ascontiguousarray(cap["slot"], np.int64)), _p(tokens), n,
+                                            _p(np.ascontiguousarray(E, np.float64)), _p(np.ascontiguousarray(R)),
+                                            _p(y64), _p(y32)), "oracle_residual_combine_rows")
+    out = dict(r)
+    out.update(cap)
+    out.update(tokens=tokens, y64=y64, y=y32, R=R)
+    return out
 
 
 def forward(w, tokens=None, nthreads=1, h_round=None, lib=None):

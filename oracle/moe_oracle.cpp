@@ -366,4 +366,33 @@ int oracle_combine_rows(const oracle_cfg* c, const double* topk_w, const int64_t
   return 0;
 }
 
+int oracle_residual_combine_rows(const oracle_cfg* c, const double* topk_w, const int64_t* slot,
+                                 const int64_t* tokens, int64_t n, const double* E, const double* R, double* y64,
+                                 float* y32) {
+  if (!cfg_ok(c)) return -1;
+  if (n > 0 && (!topk_w || !slot || !tokens || !E || !R)) return -2;
+  const int64_t H = c->H, k = c->k;
+  std::vector<double> acc(H);
+  for (int64_t i = 0; i < n; ++i) {
+    const int64_t t = tokens[i];
+    std::fill(acc.begin(), acc.end(), 0.0);
+    /* the routed part: sum of the kept experts' gate-weighted outputs, in the
+     * token's top-k order */
+    for (int64_t j = 0; j < k; ++j) {
+      if (slot[t * k + j] < 0) continue;
+      const double w = topk_w[t * k + j];
+      const double* Ej = E + (i * k + j) * H;
+      for (int64_t h = 0; h < H; ++h) acc[h] += w * Ej[h];
+    }
+    /* the shared slice is always active and is not rescaled; s applies to
+     * the routed sum */
+    for (int64_t h = 0; h < H; ++h) {
+      const double y = R[i * H + h] + c->out_scale * acc[h];
+      if (y64) y64[i * H + h] = y;
+      if (y32) y32[i * H + h] = static_cast<float>(y);
+    }
+  }
+  return 0;
+}
+
 }  // extern "C"

@@ -113,6 +113,17 @@ int oracle_combine_tokens(const oracle_cfg* c, const void* x, const void* Wgate,
 int oracle_combine_rows(const oracle_cfg* c, const double* topk_w, const int64_t* slot, const int64_t* tokens,
                         int64_t n, const double* E, double* y64, float* y32);
 
+/* The residual (shared-neuron, "Inter" mode) layer of the LLaMA-MoE hub
+ * page's construction list and the LLaMA-MoE v2 article's shared-neuron
+ * section: a slice of always-active neurons R(x) = FFN_shared(x) added to the
+ * routed experts,  y_t = R(x_t) + s * sum_j w_j E_{idx_j}(x_t)  (kept j, in
+ * j order). R [n,H] holds R(x_t) of the listed tokens (oracle_expert_rows of
+ * the shared slice as a one-expert layer); E [n,k,H] as in
+ * oracle_combine_rows. */
+int oracle_residual_combine_rows(const oracle_cfg* c, const double* topk_w, const int64_t* slot,
+                                 const int64_t* tokens, int64_t n, const double* E, const double* R, double* y64,
+                                 float* y32);
+
 /* Scalar pieces, exported so tests can pin them against library routines. */
 double oracle_round_bf16(double v);   /* round to nearest bf16, ties to even */
 double oracle_round_f32(double v);    /* round to nearest fp32, ties to even */

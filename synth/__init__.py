@@ -140,6 +140,7 @@ class Workload:
     Wup: Optional[np.ndarray] = None
     Wdown: Optional[np.ndarray] = None
     meta: dict = field(default_factory=dict)
+    shared: Optional[tuple] = None   # residual layer: (gate [Fs,H], up [Fs,H], down [H,Fs]) of the shared slice
 
     def f32(self, name: str) -> np.ndarray:
         """fp32 values of a tensor (exact upcast for bf16 storage)."""
@@ -193,6 +194,49 @@ def make_split(name, seed, T, H, Ftot, N, k, *, act="bf16", wt="bf16", order=MIX
     w = Workload(name, T, H, Ftot // N, N, k, capacity, order, noisy, want_stats, out_scale, act, wt,
                  x, Wg, Wn, eps, Wgate, Wup, Wdown)
     w.meta.update(kind="split", seed=seed, perm=perm, dense=(Wgate_d, Wup_d, Wdown_d))
+    return w
+
+
+def make_residual(name, seed, T, H, Ftot, Fs, N, k, *, act="bf16", wt="bf16", order=MIXTRAL, noisy=False,
+                  want_stats=False, out_scale=1.0, capacity=-1, wsig=0.02) -> Workload:
+    """A residual (shared-neuron, "Inter" mode) LLaMA-MoE layer: one dense FFN
+    whose neurons perm[:Fs] form an always-active shared slice and whose other
+    Ftot - Fs neurons are split into N experts (LLaMA-MoE hub page, Inter
+    mode; LLaMA-MoE v2 article, shared-neuron partitioning). The seeded
+    permutation stands in for the gradient-importance choice of the shared
+    neurons, which needs a trained model and data."""
+    x = _rand_w(seed, S_X, (T, H), 1.0, act)
+    Wgate_d = _rand_w(seed, S_WGATE, (Ftot, H), wsig, wt)
+    Wup_d = _rand_w(seed, S_WUP, (Ftot, H), wsig, wt)
+    Wdown_d = _rand_w(seed, S_WDOWN, (H, Ftot), wsig, wt)
+    perm = permutation(seed, S_PERM, Ftot)
+    sh, rest = perm[:Fs], perm[Fs:]
+    Wgate, Wup, Wdown = split_dense(Wgate_d[rest], Wup_d[rest], Wdown_d[:, rest], np.arange(Ftot - Fs), N)
+    shared = (np.ascontiguousarray(Wgate_d[sh]), np.ascontiguousarray(Wup_d[sh]),
+              np.ascontiguousarray(Wdown_d[:, sh]))
+    Wg = normal_f32(seed, S_WG, (H, N), wsig)
+    Wn = normal_f32(seed, S_WNOISE, (H, N), wsig) if noisy else None
+    eps = normal_f32(seed, S_EPS, (T, N), 1.0) if noisy else None
+    w = Workload(name, T, H, (Ftot - Fs) // N, N, k, capacity, order, noisy, want_stats, out_scale, act, wt,
+                 x, Wg, Wn, eps, Wgate, Wup, Wdown, shared=shared)
+    w.meta.update(kind="residual", seed=seed, perm=perm, dense=(Wgate_d, Wup_d, Wdown_d))
+    return w
+
+
+def make_inner_shared(name, seed, T, H, Ftot, Fs, N, k, *, act="bf16", wt="bf16", out_scale=1.0,
+                      capacity=-1, wsig=0.02) -> Workload:
+    """The "Inner" sharing mode: every expert holds the shared neurons
+    perm[:Fs] followed by its own share of the rest (experts of Fs +
+    (Ftot - Fs)/N neurons; the shared weights are repeated in each expert)."""
+    r = make_residual(name, seed, T, H, Ftot, Fs, N, k, act=act, wt=wt, out_scale=out_scale, capacity=capacity,
+                      wsig=wsig)
+    Sg, Su, Sd = r.shared
+    Wgate = np.ascontiguousarray(np.concatenate([np.broadcast_to(Sg, (N,) + Sg.shape), r.Wgate], axis=1))
+    Wup = np.ascontiguousarray(np.concatenate([np.broadcast_to(Su, (N,) + Su.shape), r.Wup], axis=1))
+    Wdown = np.ascontiguousarray(np.concatenate([np.broadcast_to(Sd, (N,) + Sd.shape), r.Wdown], axis=2))
+    w = Workload(name, T, H, Fs + r.F, N, k, capacity, MIXTRAL, False, False, out_scale, act, wt, r.x, r.Wg,
+                 None, None, Wgate, Wup, Wdown)
+    w.meta.update(kind="inner_shared", seed=seed, residual=r)
     return w
 
 

@@ -248,3 +248,49 @@ def test_I12_nan_score_ranks_below_every_number():
     a = oracle.route(w)
     assert np.all(a["topk_idx"][:, 2] == 1) and np.all(a["topk_w"][:, 2] == 0.0)
     np.testing.assert_allclose(a["topk_w"].sum(axis=1), 1.0, rtol=1e-15)
+
+
+def test_I13_residual_layer_reduces_to_the_dense_ffn():
+    """Shared slice + routed experts of one dense FFN (the Inter / residual
+    mode): with a zero router (every gate 1/N), k = N and s = N, the routed
+    experts sum to the rest of the FFN, so the layer is the dense FFN."""
+    w = synth.make_residual("res", 17, 12, 32, 8 * 6 + 16, 16, 6, 6, act="f32", wt="f32", out_scale=6.0)
+    w.Wg = np.zeros_like(w.Wg)
+    out = oracle.residual_forward(w, h_round=oracle.H_EXACT)
+    Wg_d, Wu_d, Wd_d = w.meta["dense"]
+    np.testing.assert_allclose(out["y64"], dense_ffn(w.x, Wg_d, Wu_d, Wd_d), rtol=1e-12, atol=1e-13)
+
+
+def test_I14_residual_layer_with_every_slot_dropped_is_the_shared_slice():
+    """Capacity 0 drops every routed slot: the output is exactly the shared
+    slice's FFN, which equals the dense FFN restricted to those neurons."""
+    w = synth.make_residual("res0", 18, 10, 32, 4 * 8 + 8, 8, 4, 2, act="f32", wt="f32", capacity=0, out_scale=2.0)
+    out = oracle.residual_forward(w, h_round=oracle.H_EXACT)
+    assert np.array_equal(out["y64"], out["R"])
+    Wg_d, Wu_d, Wd_d = w.meta["dense"]
+    sh = w.meta["perm"][:8]
+    np.testing.assert_allclose(out["y64"], dense_ffn(w.x, Wg_d[sh], Wu_d[sh], Wd_d[:, sh]), rtol=1e-12, atol=1e-13)
+
+
+def test_I15_residual_adds_the_shared_slice_to_the_plain_layer():
+    """The routed part is the plain layer of the same experts: y - R equals
+    the one-step oracle's output (same routing, slots and scale)."""
+    w = synth.make_residual("res_r", 19, 16, 32, 4 * 8 + 8, 8, 4, 2, act="f32", wt="f32", capacity=5,
+                            out_scale=2.0)
+    out = oracle.residual_forward(w)
+    plain = oracle.forward(w)
+    np.testing.assert_allclose(out["y64"] - out["R"], plain["y64"], rtol=1e-12, atol=1e-13)
+    assert np.any(out["slot"] < 0) and np.any(np.abs(out["R"]) > 0)
+
+
+def test_I16_inner_sharing_expert_is_shared_plus_own_neurons():
+    """Inner mode: an expert holding the shared neurons and its own is, in
+    exact arithmetic, the shared slice's FFN plus its own slice's FFN."""
+    w = synth.make_inner_shared("inner", 20, 8, 32, 4 * 8 + 8, 8, 4, 2, act="f32", wt="f32")
+    r = w.meta["residual"]
+    toks = np.arange(w.T)
+    for e in range(w.N):
+        got = oracle.expert_rows(w, e, toks, h_round=oracle.H_EXACT)
+        want = (oracle.expert_rows(oracle.shared_slice(r), 0, toks, h_round=oracle.H_EXACT)
+                + oracle.expert_rows(r, e, toks, h_round=oracle.H_EXACT))
+        np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-13)

@@ -69,6 +69,13 @@ MUTANTS = [
     ("smooth_kth_includes_self", "if (j != i) others.push_back(hv[j]);", "others.push_back(hv[j]);"),
     ("smooth_phi_sign", "0.5 * std::erfc(-z / std::sqrt(2.0))", "0.5 * std::erfc(z / std::sqrt(2.0))"),
     ("smooth_no_sqrt2", "0.5 * std::erfc(-z / std::sqrt(2.0))", "0.5 * std::erfc(-z)"),
+    ("residual_scaled_with_routed", "const double y = R[i * H + h] + c->out_scale * acc[h];",
+     "const double y = c->out_scale * (R[i * H + h] + acc[h]);"),
+    ("residual_dropped", "const double y = R[i * H + h] + c->out_scale * acc[h];",
+     "const double y = c->out_scale * acc[h];"),
+    ("residual_keeps_dropped_slots",
+     "      if (slot[t * k + j] < 0) continue;\n      const double w = topk_w[t * k + j];\n      const double* Ej = E + (i * k + j) * H;\n      for (int64_t h = 0; h < H; ++h) acc[h] += w * Ej[h];\n    }\n    /* the shared",
+     "      const double w = topk_w[t * k + j];\n      const double* Ej = E + (i * k + j) * H;\n      for (int64_t h = 0; h < H; ++h) acc[h] += w * Ej[h];\n    }\n    /* the shared"),
     ("nan_score_not_ranked_last",
      "if (std::isnan(hv)) hv = -std::numeric_limits<double>::infinity();", "(void)0;"),
 ]
