@@ -83,6 +83,9 @@ WORKLOADS = {
                    lambda synth: synth.c4("dropless")),
     "C4cf1_assign": ("Llama-3-8B upcycled E8T2 layer: T=8192, 8 experts of 14336, top-2, capacity factor 1 "
                      "counted per assignment (C=2048)", lambda synth: synth.c4("cf1_assign")),
+    "C2res": ("LLaMA-MoE-3.5B-shape residual (shared-neuron Inter mode) layer: T=4096, hidden 4096, 11008 neurons = "
+              "1376 shared + 7 routed experts of 1376, top-2 Mixtral, dropless, s=1",
+              lambda synth: synth.make_residual("C2res", 1007, 4096, 4096, 11008, 1376, 7, 2, out_scale=1.0)),
     "C5": ("decode-shaped E8T2 layer: T=64 tokens, hidden 4096, 8 experts of 14336, top-2, half the tokens "
            "steered to expert 0, dropless", lambda synth: synth.c5()),
 }
@@ -141,13 +144,23 @@ def main():
                  importance=torch.empty(N, dtype=torch.float32, device="cuda"),
                  P=torch.empty(N, dtype=torch.float32, device="cuda"),
                  balance=torch.empty(1, dtype=torch.float32, device="cuda")) if w.want_stats else {}
-    ws = abi.workspace(cfg)
+    Fs = w.shared[0].shape[0] if w.shared is not None else 0
+    if Fs:
+        shared = [tuple(dev(a) for a in w.shared) for _ in range(len(copies))]
+        ws = torch.empty(abi.moe_residual_workspace_bytes(cfg, Fs), dtype=torch.uint8, device="cuda")
+    else:
+        ws = abi.workspace(cfg)
     stream = torch.cuda.current_stream()
 
     def step(i, d=None):
-        d = d if d is not None else copies[i % len(copies)]
-        abi.moe_forward(cfg, d["x"], d["Wg"], d["Wn"], d["eps"], d["Wgate"], d["Wup"], d["Wdown"], y, kept=kept,
-                        ws=ws, stream=stream, **stats)
+        j = i % len(copies)
+        d = d if d is not None else copies[j]
+        if Fs:
+            abi.moe_forward_residual(cfg, Fs, d["x"], d["Wg"], d["Wn"], d["eps"], d["Wgate"], d["Wup"], d["Wdown"],
+                                     *shared[j], y, kept=kept, ws=ws, stream=stream, **stats)
+        else:
+            abi.moe_forward(cfg, d["x"], d["Wg"], d["Wn"], d["eps"], d["Wgate"], d["Wup"], d["Wdown"], y,
+                            kept=kept, ws=ws, stream=stream, **stats)
 
     # one step first: the kept counts, and whether the library runs the
     # expert GEMMs as one persistent launch (the dominant kernel) or as two
@@ -197,17 +210,19 @@ def main():
     ms_per_step = elapsed * 1e3 / args.steps
     tokens_per_s = T * args.steps / elapsed
     t_layer = elapsed / args.steps
-    dom_avg_s = dom_ms / 1e3 / max(1, dom_n)
+    # the residual layer launches the expert kernel twice a step (shared
+    # slice, then the routed experts): its roofline covers both launches
+    dom_avg_s = dom_ms / 1e3 / max(1, dom_n) * (2 if Fs else 1)
 
     # layer roofline over the kept assignments: expert flops on the matrix
     # cores plus the fp32 router, or the bytes of reading x, the router
     # weights, the active experts' weights once, the routing outputs, and
     # writing fp32 y once, whichever takes longer
     eb = 2 if bf16 else 4
-    f_expert = 6.0 * A * H * F
+    f_expert = 6.0 * A * H * F + 6.0 * T * H * Fs
     f_router = 2.0 * T * H * N * (2 if w.noisy else 1)
     b_alg = (T * H * eb + H * N * 4 * (2 if w.noisy else 1) + (T * N * 4 if w.noisy else 0)
-             + active * 3 * F * H * eb + T * k * 8 + T * H * 4)
+             + active * 3 * F * H * eb + 3 * Fs * H * eb + T * k * 8 + T * H * 4)
     peak_expert = PEAK_BF16_TFLOPS if bf16 else PEAK_FP32_TFLOPS
     t_compute = f_expert / (peak_expert * 1e12) + f_router / (PEAK_FP32_TFLOPS * 1e12)
     t_mem = b_alg / (PEAK_HBM_GBS * 1e9)
@@ -218,8 +233,8 @@ def main():
     # GEMM alone does 4*A*H*F and reads two of them
     if fused:
         dom_name = "experts_gate_up_swiglu_down"
-        dom_flops = 6.0 * A * H * F
-        dom_bytes = active * 3 * F * H * eb + A * H * eb + A * H * 4
+        dom_flops = 6.0 * A * H * F + 6.0 * T * H * Fs
+        dom_bytes = active * 3 * F * H * eb + A * H * eb + A * H * 4 + 3 * Fs * H * eb + T * H * eb + T * H * 4
     else:
         dom_name = "gemm1_gate_up_swiglu"
         dom_flops = 4.0 * A * H * F
@@ -319,21 +334,26 @@ def cpu_baseline(w, target_s: float):
     def sample(S):
         return synth.Workload(w.name, S, w.H, w.F, w.N, w.k, w.capacity, w.order, w.noisy, False, w.out_scale,
                               w.act, w.wt, w.x[:S].copy(), w.Wg, w.Wn, None if w.eps is None else w.eps[:S].copy(),
-                              w.Wgate, w.Wup, w.Wdown)
+                              w.Wgate, w.Wup, w.Wdown, shared=w.shared)
+
+    def run(v, nthreads):
+        if v.shared is not None:
+            return oracle.residual_forward(v, nthreads=nthreads)
+        return oracle.forward(v, nthreads=nthreads)
 
     S0 = max(cores, 16)
     t0 = time.perf_counter()
-    oracle.forward(sample(S0), nthreads=cores)
+    run(sample(S0), cores)
     dt0 = time.perf_counter() - t0
     S = int(min(w.T, max(S0, S0 * target_s / max(dt0, 1e-3))))
     S = max(cores, S // cores * cores)
     t1 = time.perf_counter()
-    oracle.forward(sample(S), nthreads=cores)
+    run(sample(S), cores)
     dt = time.perf_counter() - t1
     # the same oracle on one thread, on a sample a core count smaller
     S1 = max(1, S // cores)
     t2 = time.perf_counter()
-    oracle.forward(sample(S1), nthreads=1)
+    run(sample(S1), 1)
     dt1 = time.perf_counter() - t2
     return {"value": round(S / dt, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "host_cpus": host_cpus, "affinity_cpus": share,

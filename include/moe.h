@@ -179,6 +179,26 @@ moe_status moe_forward(const moe_cfg* cfg, const void* x, const float* Wg, const
                        float* P_opt, float* balance_opt, float* smooth_load_opt, void* ws, size_t ws_bytes,
                        hipStream_t stream);
 
+/* The residual (shared-neuron, "Inter" mode) layer: an always-active shared
+ * slice of F_shared SwiGLU neurons added to the routed experts (LLaMA-MoE
+ * hub page, shared-neuron partitioning, Inter mode; LLaMA-MoE v2 article,
+ * shared-neuron partitioning):
+ *   y[t] = FFN_shared(x[t]) + s * sum_{kept j} topk_w[t,j] * E_{idx[t,j]}(x[t])
+ * FFN_shared(x) = Ws_down . (SiLU(Ws_gate . x) * (Ws_up . x)), h rounded to
+ * act as in the experts; the rescale s applies to the routed sum only.
+ *   Ws_gate, Ws_up [F_shared,H] wt; Ws_down [H,F_shared] wt, 16-byte aligned.
+ *   Everything else as moe_forward. The workspace must hold
+ *   moe_residual_workspace_bytes(cfg, F_shared) bytes (0 if invalid).
+ *   The shared slice runs as a one-expert layer over all T rows through the
+ *   same expert kernels, then the routed layer; the combine adds the two. */
+size_t moe_residual_workspace_bytes(const moe_cfg* cfg, int32_t F_shared);
+moe_status moe_forward_residual(const moe_cfg* cfg, int32_t F_shared, const void* x, const float* Wg, const float* Wn,
+                                const float* eps, const void* Wgate, const void* Wup, const void* Wdown,
+                                const void* Ws_gate, const void* Ws_up, const void* Ws_down, void* y,
+                                int32_t* topk_idx_opt, float* topk_w_opt, int32_t* kept_opt, int32_t* load_opt,
+                                float* importance_opt, float* P_opt, float* balance_opt, float* smooth_load_opt,
+                                void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* moe_forward without a caller workspace, for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc). Same arguments, outputs and results as

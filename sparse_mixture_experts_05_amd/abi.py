@@ -26,7 +26,7 @@ MOE_TOPK_THEN_SOFTMAX, MOE_SOFTMAX_THEN_TOPK = 0, 1
 EXPORTED = ["moe_capacity", "moe_check", "moe_workspace_bytes", "moe_route", "moe_permute",
             "moe_grouped_swiglu", "moe_combine", "moe_forward", "moe_status_str", "moe_last_error",
             "moe_profile_select", "moe_profile_read", "moe_debug_set_wait", "moe_forward_noalloc",
-            "moe_noalloc_scratch_bytes"]
+            "moe_noalloc_scratch_bytes", "moe_forward_residual", "moe_residual_workspace_bytes"]
 
 
 class moe_cfg(ctypes.Structure):
@@ -83,6 +83,10 @@ def load_library(path: Optional[str] = None):
     lib.moe_profile_read.restype = i32
     lib.moe_forward_noalloc.argtypes = [cfgp] + [vp] * 16 + [vp]
     lib.moe_forward_noalloc.restype = i32
+    lib.moe_forward_residual.argtypes = [cfgp, i32] + [vp] * 19 + [vp, sz, vp]
+    lib.moe_forward_residual.restype = i32
+    lib.moe_residual_workspace_bytes.argtypes = [cfgp, i32]
+    lib.moe_residual_workspace_bytes.restype = sz
     lib.moe_noalloc_scratch_bytes.argtypes = []
     lib.moe_noalloc_scratch_bytes.restype = sz
     lib.moe_debug_set_wait.argtypes = [i32, i32]
@@ -210,6 +214,22 @@ def moe_forward_noalloc(cfg, x, Wg, Wn, eps, Wgate, Wup, Wdown, y, topk_idx=None
                                               _p(Wdown), _p(y), _p(topk_idx), _p(topk_w), _p(kept), _p(load),
                                               _p(importance), _p(P), _p(balance), _p(smooth_load), _s(stream)),
            "moe_forward_noalloc")
+
+
+def moe_residual_workspace_bytes(cfg: MoEConfig, F_shared: int) -> int:
+    c = cfg.c()
+    return int(load_library().moe_residual_workspace_bytes(ctypes.byref(c), int(F_shared)))
+
+
+def moe_forward_residual(cfg, F_shared, x, Wg, Wn, eps, Wgate, Wup, Wdown, Ws_gate, Ws_up, Ws_down, y, topk_idx=None,
+                         topk_w=None, kept=None, load=None, importance=None, P=None, balance=None, smooth_load=None,
+                         ws=None, stream=None):
+    c = cfg.c()
+    _check(load_library().moe_forward_residual(ctypes.byref(c), int(F_shared), _p(x), _p(Wg), _p(Wn), _p(eps),
+                                               _p(Wgate), _p(Wup), _p(Wdown), _p(Ws_gate), _p(Ws_up), _p(Ws_down),
+                                               _p(y), _p(topk_idx), _p(topk_w), _p(kept), _p(load), _p(importance),
+                                               _p(P), _p(balance), _p(smooth_load), _p(ws),
+                                               0 if ws is None else ws.numel(), _s(stream)), "moe_forward_residual")
 
 
 def moe_noalloc_scratch_bytes() -> int:

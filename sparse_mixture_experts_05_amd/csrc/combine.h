@@ -46,11 +46,20 @@ __device__ __forceinline__ f32x4_t gather_sum(const CombineParams& p, const int 
   return acc;
 }
 
-// y[t, 4c .. 4c+3] = s * acc
+// y[t, 4c .. 4c+3] = s * acc, or residual + s * acc for the residual layer
+// (its shared slice's partial rows added in split order first)
 template <bool OUT_BF16>
 __device__ __forceinline__ void store4(const CombineParams& p, int64_t t, int64_t c, f32x4_t acc) {
+  if (p.residual) {
+    const float* src = p.residual + t * p.H + c * 4;
+    f32x4_t r = ld_nt(src);
+    for (int s = 1; s < p.res_splits; ++s) r += ld_nt(src + s * p.res_split_stride);
 #pragma unroll
-  for (int q = 0; q < 4; ++q) acc[q] *= p.scale;
+    for (int q = 0; q < 4; ++q) acc[q] = fmaf(p.scale, acc[q], r[q]);
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[q] *= p.scale;
+  }
   if constexpr (OUT_BF16) {
     uint16_t* y = static_cast<uint16_t*>(p.y) + t * p.H + c * 4;
     const uint32_t lo = static_cast<uint32_t>(f32_to_bf16(acc[0])) | (static_cast<uint32_t>(f32_to_bf16(acc[1])) << 16);

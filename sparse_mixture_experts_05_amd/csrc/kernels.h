@@ -153,6 +153,9 @@ struct CombineParams {
   int H, k;
   float scale;
   const int32_t* error;      // *error != 0: an earlier kernel failed, and y is written as all NaN. May be null.
+  const float* residual;     // [res_splits][T][H]: added unscaled, y = residual + s * sum; or null
+  int64_t res_split_stride;  // elements
+  int res_splits;
 };
 hipError_t launch_combine(const CombineParams& p, hipStream_t s);
 

@@ -236,6 +236,68 @@ moe_status run_gemms(const moe_cfg* c, const Layout& L, const void* a, const int
   return MOE_OK;
 }
 
+// The routed layer's launches after validation: router (and statistics),
+// scatter, expert GEMMs and combine. res: the residual layer's shared-slice
+// output, added by the combine, or null.
+struct Residual {
+  const float* y;        // [splits][T][H] fp32 partial sums
+  int64_t split_stride;  // elements
+  int splits;
+};
+
+moe_status forward_launch(const moe_cfg* c, const void* x, const float* Wg, const float* Wn, const float* eps,
+                          const void* Wgate, const void* Wup, const void* Wdown, void* y, int32_t* topk_idx_opt,
+                          float* topk_w_opt, int32_t* kept_opt, int32_t* load_opt, float* importance_opt,
+                          float* P_opt, float* balance_opt, float* smooth_load_opt, bool stats, void* ws,
+                          const Residual* res, hipStream_t s) {
+  const Layout L = layout(c);
+  int32_t* topk_idx = topk_idx_opt ? topk_idx_opt : at<int32_t>(ws, L.idx);
+  float* topk_w = topk_w_opt ? topk_w_opt : at<float>(ws, L.w);
+  int32_t* slot = at<int32_t>(ws, L.slot);
+  int32_t* row_token = at<int32_t>(ws, L.rowtok);
+  int32_t* offsets = at<int32_t>(ws, L.offsets);
+
+  moe::RouterParams rp{};
+  rp.x = x;
+  rp.act_bf16 = c->act == MOE_BF16;
+  rp.Wg = Wg;
+  rp.Wn = Wn;
+  rp.eps = eps;
+  rp.T = c->T;
+  rp.H = c->H;
+  rp.N = c->N;
+  rp.k = c->k;
+  rp.order = c->order;
+  rp.noisy = c->noisy;
+  rp.logits = nullptr;
+  rp.topk_idx = topk_idx;
+  rp.topk_w = topk_w;
+  rp.hist = at<int32_t>(ws, L.hist);
+  rp.stat_part = stats ? at<float>(ws, L.stat) : nullptr;
+  rp.smooth = stats && smooth_load_opt ? 1 : 0;
+  MOE_LAUNCH(MOE_KERNEL_ROUTER, s, moe::launch_router(rp, s));
+  // statistics: reduced by the persistent expert kernel once its queue is
+  // empty when that kernel runs, else by a launch of their own
+  const moe::StatsParams sp{at<int32_t>(ws, L.hist), at<float>(ws, L.stat), L.hist_blocks, c->T, c->N, c->k,
+                            load_opt, importance_opt, P_opt, balance_opt, smooth_load_opt};
+  if (stats && !L.fused) MOE_LAUNCH(MOE_KERNEL_STATS, s, moe::launch_stats(sp, s));
+  moe::ScatterParams sc{topk_idx, at<int32_t>(ws, L.hist), L.hist_tokens, c->T, c->N, c->k, c->capacity,
+                        (!stats && load_opt) ? load_opt : at<int32_t>(ws, L.counts), kept_opt, offsets, slot,
+                        row_token, L.fused ? at<int32_t>(ws, L.sched) : nullptr,
+                        L.fused ? moe::fused_sched_ints(L.A_max, c->N) : 0};
+  MOE_LAUNCH(MOE_KERNEL_SCATTER, s, moe::launch_scatter(sc, s));
+  float* y_perm = at<float>(ws, L.yperm);
+  const moe_status st = run_gemms(c, L, x, row_token, offsets, Wgate, Wup, Wdown, y_perm, L.splits, ws, true, s,
+                                  stats && L.fused ? &sp : nullptr);
+  if (st != MOE_OK) return st;
+  moe::CombineParams cp{y_perm, L.A_max * static_cast<int64_t>(c->H), L.splits, slot, topk_w, y,
+                        c->out == MOE_BF16, c->T, c->H, c->k, c->out_scale,
+                        L.fused ? at<int32_t>(ws, L.sched) + moe::fused_error_index() : nullptr,
+                        res ? res->y : nullptr, res ? res->split_stride : 0, res ? res->splits : 0};
+  MOE_LAUNCH(MOE_KERNEL_COMBINE, s, moe::launch_combine(cp, s));
+  return MOE_OK;
+}
+
 }  // namespace
 
 namespace moe {
@@ -420,51 +482,77 @@ moe_status moe_forward(const moe_cfg* c, const void* x, const float* Wg, const f
               "x, router and expert weights and y must be 16-byte aligned");
   st = check_ws(c, ws, ws_bytes);
   if (st != MOE_OK) return st;
-  const Layout L = layout(c);
-  int32_t* topk_idx = topk_idx_opt ? topk_idx_opt : at<int32_t>(ws, L.idx);
-  float* topk_w = topk_w_opt ? topk_w_opt : at<float>(ws, L.w);
-  int32_t* slot = at<int32_t>(ws, L.slot);
-  int32_t* row_token = at<int32_t>(ws, L.rowtok);
-  int32_t* offsets = at<int32_t>(ws, L.offsets);
+  return forward_launch(c, x, Wg, Wn, eps, Wgate, Wup, Wdown, y, topk_idx_opt, topk_w_opt, kept_opt, load_opt,
+                        importance_opt, P_opt, balance_opt, smooth_load_opt, stats, ws, nullptr, s);
+}
 
-  moe::RouterParams rp{};
-  rp.x = x;
-  rp.act_bf16 = c->act == MOE_BF16;
-  rp.Wg = Wg;
-  rp.Wn = Wn;
-  rp.eps = eps;
-  rp.T = c->T;
-  rp.H = c->H;
-  rp.N = c->N;
-  rp.k = c->k;
-  rp.order = c->order;
-  rp.noisy = c->noisy;
-  rp.logits = nullptr;
-  rp.topk_idx = topk_idx;
-  rp.topk_w = topk_w;
-  rp.hist = at<int32_t>(ws, L.hist);
-  rp.stat_part = stats ? at<float>(ws, L.stat) : nullptr;
-  rp.smooth = stats && smooth_load_opt ? 1 : 0;
-  MOE_LAUNCH(MOE_KERNEL_ROUTER, s, moe::launch_router(rp, s));
-  // statistics: reduced by the persistent expert kernel once its queue is
-  // empty when that kernel runs, else by a launch of their own
-  const moe::StatsParams sp{at<int32_t>(ws, L.hist), at<float>(ws, L.stat), L.hist_blocks, c->T, c->N, c->k,
-                            load_opt, importance_opt, P_opt, balance_opt, smooth_load_opt};
-  if (stats && !L.fused) MOE_LAUNCH(MOE_KERNEL_STATS, s, moe::launch_stats(sp, s));
-  moe::ScatterParams sc{topk_idx, at<int32_t>(ws, L.hist), L.hist_tokens, c->T, c->N, c->k, c->capacity,
-                        (!stats && load_opt) ? load_opt : at<int32_t>(ws, L.counts), kept_opt, offsets, slot,
-                        row_token, L.fused ? at<int32_t>(ws, L.sched) : nullptr,
-                        L.fused ? moe::fused_sched_ints(L.A_max, c->N) : 0};
-  MOE_LAUNCH(MOE_KERNEL_SCATTER, s, moe::launch_scatter(sc, s));
-  float* y_perm = at<float>(ws, L.yperm);
-  st = run_gemms(c, L, x, row_token, offsets, Wgate, Wup, Wdown, y_perm, L.splits, ws, true, s,
-                 stats && L.fused ? &sp : nullptr);
+// The residual layer's shared slice: a one-expert layer over all T rows
+// (gate/up width F_shared), whose workspace follows the routed layer's.
+static moe_cfg shared_cfg(const moe_cfg* c, int32_t F_shared) {
+  moe_cfg sc = *c;
+  sc.F = F_shared;
+  sc.N = 1;
+  sc.k = 1;
+  sc.capacity = -1;
+  sc.order = MOE_TOPK_THEN_SOFTMAX;
+  sc.noisy = 0;
+  sc.want_stats = 0;
+  sc.out_scale = 1.0f;
+  return sc;
+}
+
+size_t moe_residual_workspace_bytes(const moe_cfg* c, int32_t F_shared) {
+  if (moe_check(c) != MOE_OK || F_shared < 1) return 0;
+  const moe_cfg sc = shared_cfg(c, F_shared);
+  if (moe_check(&sc) != MOE_OK) return 0;
+  return layout(c).total + layout(&sc).total;
+}
+
+moe_status moe_forward_residual(const moe_cfg* c, int32_t F_shared, const void* x, const float* Wg, const float* Wn,
+                                const float* eps, const void* Wgate, const void* Wup, const void* Wdown,
+                                const void* Ws_gate, const void* Ws_up, const void* Ws_down, void* y,
+                                int32_t* topk_idx_opt, float* topk_w_opt, int32_t* kept_opt, int32_t* load_opt,
+                                float* importance_opt, float* P_opt, float* balance_opt, float* smooth_load_opt,
+                                void* ws, size_t ws_bytes, hipStream_t s) {
+  moe_status st = moe_check(c);
   if (st != MOE_OK) return st;
-  moe::CombineParams cp{y_perm, L.A_max * static_cast<int64_t>(c->H), L.splits, slot, topk_w, y,
-                        c->out == MOE_BF16, c->T, c->H, c->k, c->out_scale,
-                        L.fused ? at<int32_t>(ws, L.sched) + moe::fused_error_index() : nullptr};
-  MOE_LAUNCH(MOE_KERNEL_COMBINE, s, moe::launch_combine(cp, s));
-  return MOE_OK;
+  MOE_REQUIRE(F_shared >= 1, "F_shared = %d: the shared slice needs at least one neuron", F_shared);
+  const moe_cfg sc = shared_cfg(c, F_shared);
+  st = moe_check(&sc);
+  if (st != MOE_OK) return st;
+  MOE_REQUIRE(!smooth_load_opt || c->noisy, "the smooth load needs the noisy gate (cfg->noisy = 1)");
+  const bool stats = c->want_stats && (load_opt || importance_opt || P_opt || balance_opt || smooth_load_opt);
+  if (c->T == 0) {
+    st = zero_expert_outputs(c, kept_opt, load_opt, nullptr, stats ? importance_opt : nullptr,
+                             stats ? P_opt : nullptr, stats ? balance_opt : nullptr, s);
+    if (st == MOE_OK && stats && smooth_load_opt)
+      st = zero_expert_outputs(c, nullptr, nullptr, nullptr, smooth_load_opt, nullptr, nullptr, s);
+    return st;
+  }
+  MOE_REQUIRE(x && Wg && Wgate && Wup && Wdown && Ws_gate && Ws_up && Ws_down && y,
+              "x, Wg, expert and shared-slice weights and y are required");
+  MOE_REQUIRE(!c->noisy || (Wn && eps), "noisy routing needs Wn and eps");
+  MOE_REQUIRE(aligned(x, 16) && aligned(Wg, 16) && (!Wn || aligned(Wn, 16)) && aligned(Wgate, 16) &&
+                  aligned(Wup, 16) && aligned(Wdown, 16) && aligned(Ws_gate, 16) && aligned(Ws_up, 16) &&
+                  aligned(Ws_down, 16) && aligned(y, 16),
+              "x, router, expert and shared-slice weights and y must be 16-byte aligned");
+  const size_t need = moe_residual_workspace_bytes(c, F_shared);
+  if (ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, need);
+  MOE_REQUIRE(ws && aligned(ws, 256), "the workspace must be non-NULL and 256-byte aligned");
+  // the shared slice first (it does not depend on the routing): rows 0..T-1
+  // of its one expert are the tokens themselves
+  const Layout L = layout(c), Ls = layout(&sc);
+  void* ws_s = static_cast<char*>(ws) + L.total;
+  int32_t* offsets_s = at<int32_t>(ws_s, Ls.offsets);
+  hipError_t e = moe::launch_fill_i32(offsets_s, 1, 0, s);
+  if (e == hipSuccess) e = moe::launch_fill_i32(offsets_s + 1, 1, static_cast<int32_t>(c->T), s);
+  if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "fill launch failed: %s", hipGetErrorString(e));
+  float* y_s = at<float>(ws_s, Ls.yperm);
+  st = run_gemms(&sc, Ls, x, nullptr, offsets_s, Ws_gate, Ws_up, Ws_down, y_s, Ls.splits, ws_s, false, s);
+  if (st != MOE_OK) return st;
+  const Residual res{y_s, Ls.A_max * static_cast<int64_t>(c->H), Ls.splits};
+  return forward_launch(c, x, Wg, Wn, eps, Wgate, Wup, Wdown, y, topk_idx_opt, topk_w_opt, kept_opt, load_opt,
+                        importance_opt, P_opt, balance_opt, smooth_load_opt, stats, ws, &res, s);
 }
 
 const char* moe_status_str(moe_status s) {
