@@ -51,10 +51,11 @@ def load(path: str = None):
     lib.oracle_combine_rows.argtypes = [cfgp, vp, vp, vp, i64, vp, vp, vp]
     lib.oracle_smooth_load.argtypes = [cfgp] + [vp] * 5
     lib.oracle_residual_combine_rows.argtypes = [cfgp, vp, vp, vp, i64, vp, vp, vp, vp]
+    lib.oracle_backward.argtypes = [cfgp] + [vp] * 8 + [ctypes.c_double] + [vp] * 6
     lib.brute_layer.argtypes = [cfgp] + [vp] * 17
     for f in ("oracle_route", "oracle_stats", "oracle_capacity", "oracle_expert_rows",
               "oracle_combine_tokens", "oracle_combine_rows", "oracle_smooth_load", "oracle_residual_combine_rows",
-              "brute_layer"):
+              "oracle_backward", "brute_layer"):
         getattr(lib, f).restype = ctypes.c_int
     for f in ("oracle_round_bf16", "oracle_round_f32", "oracle_silu", "oracle_softplus", "brute_round_bf16"):
         getattr(lib, f).argtypes = [ctypes.c_double]
@@ -233,6 +234,23 @@ def residual_forward(w, tokens=None, nthreads=1, h_round=None, lib=None, E=None,
     out.update(cap)
     out.update(tokens=tokens, y64=y64, y=y32, R=R)
     return out
+
+
+def backward(w, dy, d_balance=0.0, h_round=None, lib=None):
+    """Gradients of <dy, y> + d_balance * balance (see moe_oracle.h):
+    dict of dx, dWg, dWn, dWgate, dWup, dWdown (double)."""
+    lib = lib or load()
+    c = cfg(w, h_round)
+    T, H, F, N = w.T, w.H, w.F, w.N
+    o = dict(dx=np.zeros((T, H)), dWg=np.zeros((H, N)), dWn=np.zeros((H, N)), dWgate=np.zeros((N, F, H)),
+             dWup=np.zeros((N, F, H)), dWdown=np.zeros((N, H, F)))
+    Wn = w.Wn if w.noisy else None
+    eps = w.eps if w.noisy else None
+    _check(lib.oracle_backward(ctypes.byref(c), _p(w.x), _p(w.Wg), _p(Wn), _p(eps), _p(w.Wgate), _p(w.Wup),
+                               _p(w.Wdown), _p(np.ascontiguousarray(dy, np.float32)), float(d_balance), _p(o["dx"]),
+                               _p(o["dWg"]), _p(o["dWn"]), _p(o["dWgate"]), _p(o["dWup"]), _p(o["dWdown"])),
+           "oracle_backward")
+    return o
 
 
 def forward(w, tokens=None, nthreads=1, h_round=None, lib=None):

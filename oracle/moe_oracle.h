@@ -124,6 +124,27 @@ int oracle_residual_combine_rows(const oracle_cfg* c, const double* topk_w, cons
                                  const int64_t* tokens, int64_t n, const double* E, const double* R, double* y64,
                                  float* y32);
 
+/* Backward of the layer, for a training step (continual pre-training is the
+ * pages' main workload: LLaMA-MoE hub page and paper summary, continual
+ * pre-training; the balance loss of the LLaMA-MoE v2 article's gating
+ * section). Given the upstream gradient dy [T,H] of the layer output and
+ * d_balance, the upstream gradient of the balance statistic sum_i f_i P_i
+ * (lambda of the article; f_i is a count and carries no gradient), it
+ * returns the gradients of L = <dy, y> + d_balance * balance:
+ *   dx [T,H], dWg [H,N], dWn [H,N] (zeroed unless noisy),
+ *   dWgate, dWup [N,F,H], dWdown [N,H,F]   (all double).
+ * Routing (KeepTopK and the capacity clip) is piecewise constant: no
+ * gradient flows through the choice of experts or slots, only through the
+ * gate weights of the chosen ones. The forward is recomputed here in the
+ * same way as the oracle's forward (h rounded per h_round). With
+ * h_round = ORC_H_BF16 the backward rounds to bf16 where the bf16 layer
+ * feeds matrix cores: the expert-output gradient dE = s w dy and the SwiGLU
+ * gradients dg, du; otherwise nothing is rounded (exact mode, for finite
+ * differences). */
+int oracle_backward(const oracle_cfg* c, const void* x, const float* Wg, const float* Wn, const float* eps,
+                    const void* Wgate, const void* Wup, const void* Wdown, const float* dy, double d_balance,
+                    double* dx, double* dWg, double* dWn, double* dWgate, double* dWup, double* dWdown);
+
 /* Scalar pieces, exported so tests can pin them against library routines. */
 double oracle_round_bf16(double v);   /* round to nearest bf16, ties to even */
 double oracle_round_f32(double v);    /* round to nearest fp32, ties to even */

@@ -76,12 +76,31 @@ MUTANTS = [
     ("residual_keeps_dropped_slots",
      "      if (slot[t * k + j] < 0) continue;\n      const double w = topk_w[t * k + j];\n      const double* Ej = E + (i * k + j) * H;\n      for (int64_t h = 0; h < H; ++h) acc[h] += w * Ej[h];\n    }\n    /* the shared",
      "      const double w = topk_w[t * k + j];\n      const double* Ej = E + (i * k + j) * H;\n      for (int64_t h = 0; h < H; ++h) acc[h] += w * Ej[h];\n    }\n    /* the shared"),
+    ("bwd_silu_derivative_drops_term", "dg[f] = rnd(dh[f] * u[f] * sg * (1.0 + g[f] * (1.0 - sg)));",
+     "dg[f] = rnd(dh[f] * u[f] * sg);"),
+    ("bwd_mixtral_jacobian_drops_mean", "dH[idx[t * k + j]] += w[t * k + j] * (dw[j] - sdot);",
+     "dH[idx[t * k + j]] += w[t * k + j] * dw[j];"),
+    ("bwd_st_jacobian_drops_p", "for (int64_t i = 0; i < N; ++i) dH[i] = p[i] * (dp[i] - sdot);",
+     "for (int64_t i = 0; i < N; ++i) dH[i] = dp[i] - sdot;"),
+    ("bwd_balance_sign", "(static_cast<double>(counts[i]) / static_cast<double>(T * k) - fp);",
+     "(fp - static_cast<double>(counts[i]) / static_cast<double>(T * k));"),
+    ("bwd_noise_softplus_not_sigmoid", "dn[i] = dH[i] * static_cast<double>(eps[t * N + i]) / (1.0 + std::exp(-b));",
+     "dn[i] = dH[i] * static_cast<double>(eps[t * N + i]) * oracle_softplus(b);"),
+    ("bwd_dE_drops_scale", "dE[o] = rnd(c->out_scale * w[t * k + j] * static_cast<double>(dy[t * H + o]));",
+     "dE[o] = rnd(w[t * k + j] * static_cast<double>(dy[t * H + o]));"),
+    ("bwd_dw_drops_scale", "dw[j] = c->out_scale * d;", "dw[j] = d;"),
+    ("bwd_dWdown_transposed", "for (int64_t f = 0; f < F; ++f) dWdown[wb + o * F + f] += dE[o] * hh[f];",
+     "for (int64_t f = 0; f < F; ++f) dWdown[wb + f * H + o] += dE[o] * hh[f];"),
+    ("bwd_dropped_slot_gets_gradient", "      if (slot[t * k + j] < 0) continue;  /* a dropped slot adds nothing to y: no gradient */",
+     "      /* mistake: dropped slots handled like kept ones */"),
+    ("bwd_dx_misses_router_term", "        dx[t * H + h] += dlog[i] * static_cast<double>(Wg[h * N + i]);",
+     "        (void)0;"),
     ("nan_score_not_ranked_last",
      "if (std::isnan(hv)) hv = -std::numeric_limits<double>::infinity();", "(void)0;"),
 ]
 
 PIN_FILES = ["tests/test_golden.py", "tests/test_oracle_pins.py", "tests/test_oracle_invariants.py",
-             "tests/test_oracle_brute.py"]
+             "tests/test_oracle_brute.py", "tests/test_oracle_backward.py"]
 
 
 @pytest.mark.parametrize("name,orig,bad", MUTANTS, ids=[m[0] for m in MUTANTS])
