@@ -199,6 +199,38 @@ moe_status moe_forward_residual(const moe_cfg* cfg, int32_t F_shared, const void
                                 float* importance_opt, float* P_opt, float* balance_opt, float* smooth_load_opt,
                                 void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Training: a forward that keeps what the backward needs, and the backward
+ * of the layer (continual pre-training is the pages' main workload:
+ * LLaMA-MoE hub page and paper summary, continual pre-training; the balance
+ * loss is the LLaMA-MoE v2 article's gating section).
+ *   Shapes: bf16 activations and weights, F % 8 == 0, more than 48 rows per
+ *   expert on average (the persistent expert kernel's shapes); otherwise
+ *   MOE_ERR_UNSUPPORTED. ws holds moe_train_workspace_bytes(cfg) bytes.
+ *   moe_forward_train computes the same layer as moe_forward (same bits of
+ *   y and the statistics) and leaves in ws the routing, the router logits,
+ *   the gate/up pre-activations g and u (fp32), h and the expert outputs.
+ *   moe_backward must follow it on the same stream with the same cfg, inputs
+ *   and ws, untouched in between. It returns the gradients of
+ *   L = <dy, y> + d_balance * balance:
+ *     dy [T,H] fp32; dx [T,H] fp32; dWg [H,N] fp32; dWn_opt [H,N] fp32
+ *     (required when noisy); dWgate, dWup [N,F,H] fp32; dWdown [N,H,F] fp32.
+ *   KeepTopK and the capacity clip are piecewise constant: the router gets
+ *   gradient only through the chosen experts' gate weights (Mixtral: softmax
+ *   over the kept scores; ST: softmax over all), a dropped slot gets none,
+ *   and f_i of the balance is a count (no gradient); the noise path
+ *   differentiates Softplus to the sigmoid. Matrix-core operands are bf16
+ *   (dE = s w dy and the SwiGLU gradients dg, du, rounded to nearest even),
+ *   every sum is fp32. Results are bitwise reproducible. */
+size_t moe_train_workspace_bytes(const moe_cfg* cfg);
+moe_status moe_forward_train(const moe_cfg* cfg, const void* x, const float* Wg, const float* Wn, const float* eps,
+                             const void* Wgate, const void* Wup, const void* Wdown, void* y, int32_t* kept_opt,
+                             int32_t* load_opt, float* importance_opt, float* P_opt, float* balance_opt,
+                             float* smooth_load_opt, void* ws, size_t ws_bytes, hipStream_t stream);
+moe_status moe_backward(const moe_cfg* cfg, const void* x, const float* Wg, const float* Wn, const float* eps,
+                        const void* Wgate, const void* Wup, const void* Wdown, const float* dy, float d_balance,
+                        float* dx, float* dWg, float* dWn_opt, float* dWgate, float* dWup, float* dWdown, void* ws,
+                        size_t ws_bytes, hipStream_t stream);
+
 /* moe_forward without a caller workspace, for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc). Same arguments, outputs and results as
@@ -243,7 +275,13 @@ enum {
   MOE_KERNEL_COMBINE = 6,
   MOE_KERNEL_STATS = 7,
   MOE_KERNEL_EXPERTS = 8,  /* both expert GEMMs in one persistent launch (bf16, prefill shapes) */
-  MOE_KERNEL_COUNT = 9
+  MOE_KERNEL_BWD_GATE = 9,       /* backward: gate weights to the router, dE */
+  MOE_KERNEL_BWD_TRANSPOSE = 10, /* backward: the K-contiguous copies (every transpose of one call) */
+  MOE_KERNEL_BWD_DGRAD = 11,     /* backward: dh with the SwiGLU derivative, and dx of the experts */
+  MOE_KERNEL_BWD_DX = 12,        /* backward: dx gathered back to tokens, with the router terms */
+  MOE_KERNEL_BWD_WGRAD = 13,     /* backward: expert weight gradients */
+  MOE_KERNEL_BWD_ROUTER = 14,    /* backward: router and noise weight gradients */
+  MOE_KERNEL_COUNT = 15
 };
 moe_status moe_profile_select(int32_t kernel_id);
 moe_status moe_profile_read(double* total_ms, int64_t* launches);

@@ -21,12 +21,15 @@ MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_DEVICE 
 MOE_F32, MOE_BF16 = 0, 1
 MOE_TOPK_THEN_SOFTMAX, MOE_SOFTMAX_THEN_TOPK = 0, 1
 (MOE_KERNEL_ROUTER, MOE_KERNEL_HIST, MOE_KERNEL_SCATTER, MOE_KERNEL_GATHER, MOE_KERNEL_GEMM1,
- MOE_KERNEL_GEMM2, MOE_KERNEL_COMBINE, MOE_KERNEL_STATS, MOE_KERNEL_EXPERTS) = range(9)
+ MOE_KERNEL_GEMM2, MOE_KERNEL_COMBINE, MOE_KERNEL_STATS, MOE_KERNEL_EXPERTS, MOE_KERNEL_BWD_GATE,
+ MOE_KERNEL_BWD_TRANSPOSE, MOE_KERNEL_BWD_DGRAD, MOE_KERNEL_BWD_DX, MOE_KERNEL_BWD_WGRAD,
+ MOE_KERNEL_BWD_ROUTER) = range(15)
 
 EXPORTED = ["moe_capacity", "moe_check", "moe_workspace_bytes", "moe_route", "moe_permute",
             "moe_grouped_swiglu", "moe_combine", "moe_forward", "moe_status_str", "moe_last_error",
             "moe_profile_select", "moe_profile_read", "moe_debug_set_wait", "moe_forward_noalloc",
-            "moe_noalloc_scratch_bytes", "moe_forward_residual", "moe_residual_workspace_bytes"]
+            "moe_noalloc_scratch_bytes", "moe_forward_residual", "moe_residual_workspace_bytes",
+            "moe_train_workspace_bytes", "moe_forward_train", "moe_backward"]
 
 
 class moe_cfg(ctypes.Structure):
@@ -87,6 +90,12 @@ def load_library(path: Optional[str] = None):
     lib.moe_forward_residual.restype = i32
     lib.moe_residual_workspace_bytes.argtypes = [cfgp, i32]
     lib.moe_residual_workspace_bytes.restype = sz
+    lib.moe_train_workspace_bytes.argtypes = [cfgp]
+    lib.moe_train_workspace_bytes.restype = sz
+    lib.moe_forward_train.argtypes = [cfgp] + [vp] * 14 + [vp, sz, vp]
+    lib.moe_forward_train.restype = i32
+    lib.moe_backward.argtypes = [cfgp] + [vp] * 8 + [ctypes.c_float] + [vp] * 6 + [vp, sz, vp]
+    lib.moe_backward.restype = i32
     lib.moe_noalloc_scratch_bytes.argtypes = []
     lib.moe_noalloc_scratch_bytes.restype = sz
     lib.moe_debug_set_wait.argtypes = [i32, i32]
@@ -230,6 +239,29 @@ def moe_forward_residual(cfg, F_shared, x, Wg, Wn, eps, Wgate, Wup, Wdown, Ws_ga
                                                _p(y), _p(topk_idx), _p(topk_w), _p(kept), _p(load), _p(importance),
                                                _p(P), _p(balance), _p(smooth_load), _p(ws),
                                                0 if ws is None else ws.numel(), _s(stream)), "moe_forward_residual")
+
+
+def moe_train_workspace_bytes(cfg: MoEConfig) -> int:
+    c = cfg.c()
+    return int(load_library().moe_train_workspace_bytes(ctypes.byref(c)))
+
+
+def moe_forward_train(cfg, x, Wg, Wn, eps, Wgate, Wup, Wdown, y, kept=None, load=None, importance=None, P=None,
+                      balance=None, smooth_load=None, ws=None, stream=None):
+    c = cfg.c()
+    _check(load_library().moe_forward_train(ctypes.byref(c), _p(x), _p(Wg), _p(Wn), _p(eps), _p(Wgate), _p(Wup),
+                                            _p(Wdown), _p(y), _p(kept), _p(load), _p(importance), _p(P),
+                                            _p(balance), _p(smooth_load), _p(ws), 0 if ws is None else ws.numel(),
+                                            _s(stream)), "moe_forward_train")
+
+
+def moe_backward(cfg, x, Wg, Wn, eps, Wgate, Wup, Wdown, dy, d_balance, dx, dWg, dWn, dWgate, dWup, dWdown, ws=None,
+                 stream=None):
+    c = cfg.c()
+    _check(load_library().moe_backward(ctypes.byref(c), _p(x), _p(Wg), _p(Wn), _p(eps), _p(Wgate), _p(Wup),
+                                       _p(Wdown), _p(dy), float(d_balance), _p(dx), _p(dWg), _p(dWn), _p(dWgate),
+                                       _p(dWup), _p(dWdown), _p(ws), 0 if ws is None else ws.numel(), _s(stream)),
+           "moe_backward")
 
 
 def moe_noalloc_scratch_bytes() -> int:

@@ -1,0 +1,374 @@
+// Backward of the MoE layer on gfx950, for a training step (continual
+// pre-training is the pages' main workload: LLaMA-MoE hub page and paper
+// summary; the balance loss comes from the LLaMA-MoE v2 article's gating
+// section). Gradients of L = <dy, y> + d_balance * balance; KeepTopK and the
+// capacity clip are piecewise constant, so the router gets gradient only
+// through the chosen experts' gate weights.
+//
+// The kernels here move and reduce data; the four expert GEMMs of the
+// backward (dh = dE Wdown, dx = dg Wgate + du Wup, and the weight gradients)
+// run on the matrix-core tiles of gemm_mfma.hip, whose operands must be
+// K-contiguous: k_transpose writes the transposed copies they need, with each
+// expert's rows padded to a multiple of 64 columns for the weight gradients
+// (whose K runs over an expert's rows).
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+namespace {
+
+__device__ __forceinline__ float lane_value(float v, int m) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), m));
+}
+
+// Sum over the 256 threads of a block in a fixed order (each wave's butterfly,
+// then the four waves in order); every thread gets the result.
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  v = wave_sum(v);
+  const int wave = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[wave] = v;
+  __syncthreads();
+  return ((red[0] + red[1]) + red[2]) + red[3];
+}
+
+// One token per block: dw_j = s <dy_t, E_j> over the kept slots (E_j is the
+// y_perm row of slot j), dE_j = bf16(s w_j dy_t) into the slot's row, then one
+// wave takes the gate weights back to the scores and the router logits:
+//   Mixtral (softmax over the kept scores): dH = w_j (dw_j - sum w dw) at idx_j;
+//   ST (softmax over all scores): dH = p (dp - <p, dp>), dp = dw at idx_j;
+//   balance: dlogit += d_balance / T * p_clean (f - <f, p_clean>), f = load/(T k);
+//   noise: dn = dH * eps * sigmoid(noise logit).
+__global__ __launch_bounds__(256) void k_bwd_gate(BwdGateParams p) {
+  __shared__ float red[4];
+  __shared__ float s_dw[64];
+  const int64_t t = blockIdx.x;
+  const int H = p.H, k = p.k, N = p.N;
+  const float s = p.scale;
+  const float* dy = p.dy + t * H;
+  for (int j0 = 0; j0 < k; j0 += 8) {
+    int sl[8];
+    float wj[8], acc[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int j = j0 + q;
+      sl[q] = j < k ? p.slot[t * k + j] : -1;
+      wj[q] = j < k ? p.topk_w[t * k + j] : 0.0f;
+      acc[q] = 0.0f;
+    }
+    for (int c = threadIdx.x; c < H / 4; c += 256) {
+      const f32x4_t d = *reinterpret_cast<const f32x4_t*>(dy + c * 4);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        if (sl[q] < 0) continue;
+        const f32x4_t e = *reinterpret_cast<const f32x4_t*>(p.y_perm + static_cast<int64_t>(sl[q]) * H + c * 4);
+        acc[q] = fmaf(d[0], e[0], fmaf(d[1], e[1], fmaf(d[2], e[2], fmaf(d[3], e[3], acc[q]))));
+        const float sw = s * wj[q];
+        const uint32_t lo = f32_to_bf16(sw * d[0]) | (static_cast<uint32_t>(f32_to_bf16(sw * d[1])) << 16);
+        const uint32_t hi = f32_to_bf16(sw * d[2]) | (static_cast<uint32_t>(f32_to_bf16(sw * d[3])) << 16);
+        typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+        *reinterpret_cast<u32x2_t*>(p.dE + static_cast<int64_t>(sl[q]) * H + c * 4) = u32x2_t{lo, hi};
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      if (j0 + q >= k) break;
+      const float v = block_sum(acc[q], red);  // same value on every thread
+      if (threadIdx.x == 0) s_dw[j0 + q] = sl[q] >= 0 ? s * v : 0.0f;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x >= 64) return;
+  const int lane = threadIdx.x;
+  const bool valid = lane < N;
+  // this lane's expert among the token's top k (the slot index j), if any
+  int jj = -1;
+  for (int j = 0; j < k; ++j)
+    if (p.topk_idx[t * k + j] == lane) jj = j;
+  const float dw = jj >= 0 ? s_dw[jj] : 0.0f;
+  float dH = 0.0f;
+  const float lv = valid ? p.logits[t * N + lane] : -INFINITY;
+  float spv = 0.0f, nz = 0.0f, ev = 0.0f;
+  if (p.noisy && valid) {
+    nz = p.noise_logits[t * N + lane];
+    ev = p.eps[t * N + lane];
+    spv = softplus(nz);
+  }
+  if (p.order == 0) {
+    const float wv = jj >= 0 ? p.topk_w[t * k + jj] : 0.0f;
+    float sdot = 0.0f;
+    for (int j = 0; j < k; ++j) sdot += p.topk_w[t * k + j] * s_dw[j];
+    dH = jj >= 0 ? wv * (dw - sdot) : 0.0f;
+  } else {
+    // the router's scores and softmax, recomputed with the same operations
+    float hv = lv;
+    if (p.noisy && valid) hv = fmaf(ev, spv, lv);
+    if (hv != hv) hv = -INFINITY;
+    const float hmax = lane_value(hv, p.topk_idx[t * k]);
+    const float ex = valid ? expf(hv - hmax) : 0.0f;
+    float den = 0.0f;
+    for (int m = 0; m < N; ++m) den += lane_value(ex, m);
+    const float pv = ex / den;
+    float sdot = 0.0f;
+    const float pd = pv * dw;
+    for (int m = 0; m < N; ++m) sdot += lane_value(pd, m);
+    dH = valid ? pv * (dw - sdot) : 0.0f;
+  }
+  float dl = dH;
+  if (p.d_balance != 0.0f) {
+    float lmax = -INFINITY;
+    for (int m = 0; m < N; ++m) lmax = fmaxf(lmax, lane_value(lv, m));
+    const float el = valid ? expf(lv - lmax) : 0.0f;
+    float ls = 0.0f;
+    for (int m = 0; m < N; ++m) ls += lane_value(el, m);
+    const float pc = el / ls;
+    const float fv = valid ? static_cast<float>(p.counts[lane]) / (static_cast<float>(p.T) * k) : 0.0f;
+    const float fpc = fv * pc;
+    float fp = 0.0f;
+    for (int m = 0; m < N; ++m) fp += lane_value(fpc, m);
+    dl += p.d_balance / static_cast<float>(p.T) * pc * (fv - fp);
+  }
+  if (valid) {
+    p.dlog[t * N + lane] = dl;
+    if (p.noisy) p.dnz[t * N + lane] = dH * ev * __builtin_amdgcn_rcpf(1.0f + expf(-nz));
+  }
+}
+
+// dx[t] = sum over kept slots of dx_perm[slot] (in slot order) + the router
+// terms sum_n dlog[t,n] W_g[:,n] (+ dnz[t,n] W_noise[:,n]). A block owns
+// kTokB tokens, so each router weight is read once per kTokB tokens.
+constexpr int kTokB = 8;
+__global__ __launch_bounds__(256) void k_bwd_dx(BwdDxParams p) {
+  __shared__ float s_dl[kTokB][64], s_dn[kTokB][64];
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kTokB;
+  const int H = p.H, N = p.N, k = p.k;
+  for (int i = threadIdx.x; i < kTokB * 64; i += 256) {
+    const int tt = i / 64, n = i % 64;
+    const bool ok = t0 + tt < p.T && n < N;
+    s_dl[tt][n] = ok ? p.dlog[(t0 + tt) * N + n] : 0.0f;
+    s_dn[tt][n] = (ok && p.noisy) ? p.dnz[(t0 + tt) * N + n] : 0.0f;
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < H / 4; c += 256) {
+    f32x4_t acc[kTokB];
+#pragma unroll
+    for (int tt = 0; tt < kTokB; ++tt) {
+      acc[tt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      const int64_t t = t0 + tt;
+      if (t >= p.T) continue;
+      for (int j = 0; j < k; ++j) {
+        const int sl = p.slot[t * k + j];
+        if (sl < 0) continue;
+        acc[tt] += *reinterpret_cast<const f32x4_t*>(p.dx_perm + static_cast<int64_t>(sl) * H + c * 4);
+      }
+    }
+    for (int n = 0; n < N; ++n) {
+      f32x4_t wg, wn = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) wg[q] = p.Wg[static_cast<int64_t>(c * 4 + q) * N + n];
+      if (p.noisy)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) wn[q] = p.Wn[static_cast<int64_t>(c * 4 + q) * N + n];
+#pragma unroll
+      for (int tt = 0; tt < kTokB; ++tt)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[tt][q] = fmaf(s_dl[tt][n], wg[q], fmaf(s_dn[tt][n], wn[q], acc[tt][q]));
+    }
+#pragma unroll
+    for (int tt = 0; tt < kTokB; ++tt)
+      if (t0 + tt < p.T) *reinterpret_cast<f32x4_t*>(p.dx + (t0 + tt) * H + c * 4) = acc[tt];
+  }
+}
+
+// Router weight gradients dW_g = x^T dlog and dW_noise = x^T dnz, in two
+// passes for a fixed summation order: pass 1 sums a chunk of kTokW tokens per
+// block into partials [chunk][H][N] (thread = one h, all N), pass 2 adds the
+// chunks in order.
+constexpr int kTokW = 64;
+template <int NMAX, bool NOISY>
+__global__ __launch_bounds__(256) void k_router_wgrad(RouterWgradParams p) {
+  __shared__ float s_dl[kTokW][NMAX], s_dn[NOISY ? kTokW : 1][NMAX];
+  const int h = blockIdx.x * 256 + threadIdx.x;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.y) * kTokW;
+  const int N = p.N;
+  for (int i = threadIdx.x; i < kTokW * NMAX; i += 256) {
+    const int tt = i / NMAX, n = i % NMAX;
+    const bool ok = t0 + tt < p.T && n < N;
+    s_dl[tt][n] = ok ? p.dlog[(t0 + tt) * N + n] : 0.0f;
+    if (NOISY) s_dn[tt][n] = ok ? p.dnz[(t0 + tt) * N + n] : 0.0f;
+  }
+  __syncthreads();
+  if (h >= p.H) return;
+  float a[NMAX], b[NOISY ? NMAX : 1];
+#pragma unroll
+  for (int n = 0; n < NMAX; ++n) {
+    a[n] = 0.0f;
+    if (NOISY) b[n] = 0.0f;
+  }
+  for (int tt = 0; tt < kTokW && t0 + tt < p.T; ++tt) {
+    const float xv = bf16_to_f32(p.x[(t0 + tt) * p.H + h]);
+#pragma unroll
+    for (int n = 0; n < NMAX; ++n) {
+      a[n] = fmaf(xv, s_dl[tt][n], a[n]);
+      if (NOISY) b[n] = fmaf(xv, s_dn[tt][n], b[n]);
+    }
+  }
+  float* out = p.part + (static_cast<int64_t>(blockIdx.y) * p.H + h) * N * (NOISY ? 2 : 1);
+#pragma unroll
+  for (int n = 0; n < NMAX; ++n)
+    if (n < N) {
+      out[n] = a[n];
+      if (NOISY) out[N + n] = b[n];
+    }
+}
+
+__global__ __launch_bounds__(256) void k_router_wgrad_sum(RouterWgradParams p, int chunks) {
+  const int per = p.N * (p.noisy ? 2 : 1);
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= static_cast<int64_t>(p.H) * per) return;
+  float v = 0.0f;
+  for (int c = 0; c < chunks; ++c) v += p.part[static_cast<int64_t>(c) * p.H * per + i];
+  const int64_t h = i / per, n = i % per;
+  if (n < p.N) p.dWg[h * p.N + n] = v;
+  else p.dWn[h * p.N + (n - p.N)] = v;
+}
+
+// Padded row segments for the weight gradients: pad[e] = sum over e' < e of
+// the expert's rows rounded up to 64 (rows clamped to [0, rows_max)).
+__global__ __launch_bounds__(64) void k_pad_offsets(const int32_t* __restrict__ offsets, int N, int rows_max,
+                                                    int32_t* __restrict__ pad) {
+  const int lane = threadIdx.x;
+  int off = 0, cnt = 0;
+  if (lane < N) expert_segment(offsets, lane, rows_max, off, cnt);
+  const int v = (cnt + 63) / 64 * 64;
+  int incl = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int u = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += u;
+  }
+  if (lane == 0) pad[0] = 0;
+  if (lane < N) pad[lane + 1] = incl;
+}
+
+// bf16 transpose through LDS, 64 x 64 per block: dst[c][col(r)] = src[row(r)][c].
+// Plain mode (pad == null): blockIdx.z is a batch; col(r) = dst_col0 + r.
+// Padded mode: the block's 64 output columns lie in one expert's padded
+// segment [pad[e], pad[e+1]); column P maps to the expert's row
+// offsets[e] + (P - pad[e]), zero past its rows; with row_map the source row
+// is row_map[that row] (a gather of x by row_token).
+__global__ __launch_bounds__(256) void k_transpose(TransposeParams p) {
+  __shared__ uint16_t tile[64][66];
+  const int c0 = blockIdx.x * 64;   // source column (destination row) block
+  int64_t r0 = static_cast<int64_t>(blockIdx.y) * 64;
+  const uint16_t* src = p.src + blockIdx.z * p.src_batch;
+  uint16_t* dst = p.dst + blockIdx.z * p.dst_batch;
+  int64_t col0 = p.dst_col0 + r0;
+  int rows = static_cast<int>(min(static_cast<int64_t>(64), p.R - r0));  // valid source rows
+  int64_t srow0 = r0;
+  if (p.pad) {
+    // the expert whose padded segment holds this block's columns
+    const int lane = threadIdx.x & 63;
+    const int64_t P = r0;
+    if (P >= p.pad[p.N]) return;
+    int pe = lane < p.N ? p.pad[lane + 1] : 0x7fffffff;
+    const int e = __popcll(__ballot(lane < p.N && pe <= P));
+    int off = 0, cnt = 0;
+    expert_segment(p.offsets, e, p.rows_max, off, cnt);
+    const int64_t local = P - p.pad[e];
+    srow0 = off + local;
+    rows = static_cast<int>(max(static_cast<int64_t>(0), min(static_cast<int64_t>(64), cnt - local)));
+    col0 = P;
+  }
+  // load 64 source rows x 64 columns (16-byte pieces: 8 per row)
+  for (int i = threadIdx.x; i < 64 * 8; i += 256) {
+    const int rr = i / 8, cc = (i % 8) * 8;
+    u32x4_t v = {0u, 0u, 0u, 0u};
+    if (rr < rows && c0 + cc < p.C) {
+      int64_t sr = srow0 + rr;
+      if (p.row_map) sr = p.row_map[sr];
+      const uint16_t* sp = src + sr * p.src_ld + c0 + cc;
+      if (c0 + cc + 8 <= p.C) {
+        v = *reinterpret_cast<const u32x4_t*>(sp);
+      } else {
+        uint16_t tmp[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        for (int q = 0; c0 + cc + q < p.C; ++q) tmp[q] = sp[q];
+        v = u32x4_t{tmp[0] | (uint32_t(tmp[1]) << 16), tmp[2] | (uint32_t(tmp[3]) << 16),
+                    tmp[4] | (uint32_t(tmp[5]) << 16), tmp[6] | (uint32_t(tmp[7]) << 16)};
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      tile[rr][cc + 2 * q] = static_cast<uint16_t>(v[q]);
+      tile[rr][cc + 2 * q + 1] = static_cast<uint16_t>(v[q] >> 16);
+    }
+  }
+  __syncthreads();
+  // write 64 destination rows (source columns) x 64 columns (source rows)
+  for (int i = threadIdx.x; i < 64 * 8; i += 256) {
+    const int cc = i / 8, rr = (i % 8) * 8;
+    if (c0 + cc >= p.C) continue;
+    uint32_t w[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) w[q] = tile[rr + 2 * q][cc] | (static_cast<uint32_t>(tile[rr + 2 * q + 1][cc]) << 16);
+    uint16_t* dp = dst + static_cast<int64_t>(c0 + cc) * p.dst_ld + col0 + rr;
+    if (p.pad || col0 + rr + 8 <= p.dst_col0 + p.R) {
+      *reinterpret_cast<u32x4_t*>(dp) = u32x4_t{w[0], w[1], w[2], w[3]};
+    } else {
+      for (int q = 0; col0 + rr + q < p.dst_col0 + p.R; ++q) dp[q] = static_cast<uint16_t>(w[q / 2] >> (16 * (q & 1)));
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_bwd_gate(const BwdGateParams& p, hipStream_t s) {
+  if (p.T <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_bwd_gate, dim3(static_cast<unsigned>(p.T)), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dx(const BwdDxParams& p, hipStream_t s) {
+  if (p.T <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_bwd_dx, dim3(static_cast<unsigned>((p.T + kTokB - 1) / kTokB)), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+int router_wgrad_chunks(int64_t T) { return static_cast<int>((T + kTokW - 1) / kTokW); }
+
+hipError_t launch_router_wgrad(const RouterWgradParams& p, hipStream_t s) {
+  if (p.T <= 0) return hipSuccess;
+  const dim3 grid((p.H + 255) / 256, router_wgrad_chunks(p.T));
+#define MOE_RW(NM)                                                                   \
+  do {                                                                               \
+    if (p.noisy) hipLaunchKernelGGL((k_router_wgrad<NM, true>), grid, dim3(256), 0, s, p); \
+    else hipLaunchKernelGGL((k_router_wgrad<NM, false>), grid, dim3(256), 0, s, p);  \
+  } while (0)
+  if (p.N <= 8) MOE_RW(8);
+  else if (p.N <= 16) MOE_RW(16);
+  else if (p.N <= 32) MOE_RW(32);
+  else MOE_RW(64);
+#undef MOE_RW
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t n = static_cast<int64_t>(p.H) * p.N * (p.noisy ? 2 : 1);
+  hipLaunchKernelGGL(k_router_wgrad_sum, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s, p,
+                     router_wgrad_chunks(p.T));
+  return hipGetLastError();
+}
+
+hipError_t launch_pad_offsets(const int32_t* offsets, int N, int rows_max, int32_t* pad, hipStream_t s) {
+  hipLaunchKernelGGL(k_pad_offsets, dim3(1), dim3(64), 0, s, offsets, N, rows_max, pad);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose(const TransposeParams& p, int64_t col_blocks, int batches, hipStream_t s) {
+  if (col_blocks <= 0 || p.C <= 0 || batches <= 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>((p.C + 63) / 64), static_cast<unsigned>(col_blocks),
+                  static_cast<unsigned>(batches));
+  hipLaunchKernelGGL(k_transpose, grid, dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace moe

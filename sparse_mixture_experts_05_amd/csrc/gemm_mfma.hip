@@ -222,10 +222,63 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, const TilePos& tp,
                                          f32x16_t (&acc)[MB][NB]) {
   const int col_l = lane & 31, khalf = lane >> 5;
   const int row_l = wm * WM + khalf * 4;  // this lane's first row in the tile
+  if (!SWIGLU && p.epi == 1) {
+    // SwiGLU backward: the sum is dh; g and u of the same rows come from gu
+    const int64_t ldg = 2 * static_cast<int64_t>(p.Nout);
+    const float* gbase = p.gu + static_cast<int64_t>(tp.ti.row0) * ldg;
+    const __amdgpu_buffer_rsrc_t rg = uniform_rsrc(gbase, static_cast<int64_t>(tp.ti.rows) * ldg * 4);
+    const uint16_t* base = static_cast<const uint16_t*>(p.C) + static_cast<int64_t>(tp.ti.row0) * p.ldc;
+    const __amdgpu_buffer_rsrc_t rc = uniform_rsrc(base, static_cast<int64_t>(tp.ti.rows) * p.ldc * 2);
+    const uint32_t ld = static_cast<uint32_t>(p.ldc) * 2u, lg = static_cast<uint32_t>(ldg) * 4u;
+    const uint32_t uoff_g = static_cast<uint32_t>(p.Nout) * 4u, uoff_c = static_cast<uint32_t>(p.Nout) * 2u;
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const int f = tp.nt * NO + wn * WN + j * 32 + col_l;
+        const bool fv = f < p.Nout;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const uint32_t row = static_cast<uint32_t>(row_l + i * 32 + (r >> 2) * 8 + (r & 3));
+          const uint32_t go = fv ? row * lg + static_cast<uint32_t>(f) * 4u : kStoreOOB;
+          const float g = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rg, go, 0, 0));
+          const float u = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rg, go + uoff_g, 0, 0));
+          const float dh = acc[i][j][r];
+          const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g * -1.4426950408889634f));
+          const float dg = dh * u * (sg * (1.0f + g * (1.0f - sg)));
+          const float du = dh * (g * sg);
+          const uint32_t co = fv ? row * ld + static_cast<uint32_t>(f) * 2u : kStoreOOB;
+          __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(dg), rc, co, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(du), rc, co + uoff_c, 0, 0);
+        }
+      }
+    return;
+  }
   if (SWIGLU) {
     const uint16_t* base = static_cast<const uint16_t*>(p.C) + static_cast<int64_t>(tp.ti.row0) * p.ldc;
     const __amdgpu_buffer_rsrc_t rc = uniform_rsrc(base, static_cast<int64_t>(tp.ti.rows) * p.ldc * 2);
     const uint32_t ld = static_cast<uint32_t>(p.ldc) * 2u;  // bytes per row
+    if (p.gu) {
+      // training: keep g and u (fp32) for the backward's SwiGLU derivative
+      const int64_t ldg = 2 * static_cast<int64_t>(p.Nout);
+      const float* gbase = p.gu + static_cast<int64_t>(tp.ti.row0) * ldg;
+      const __amdgpu_buffer_rsrc_t rg = uniform_rsrc(gbase, static_cast<int64_t>(tp.ti.rows) * ldg * 4);
+      const uint32_t lg = static_cast<uint32_t>(ldg) * 4u, uoff = static_cast<uint32_t>(p.Nout) * 4u;
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB / 2; ++j) {
+          const int f = tp.nt * NO + wn * (WN / 2) + j * 32 + col_l;
+          const uint32_t gb = f < p.Nout ? static_cast<uint32_t>(row_l * ldg + f) * 4u : kStoreOOB;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const uint32_t off = gb + static_cast<uint32_t>(i * 32 + (r >> 2) * 8 + (r & 3)) * lg;
+            const float g = acc[i][j][r], u = acc[i][j + NB / 2][r];
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(g), rg, off, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(u), rg, off + uoff, 0, 0);
+          }
+        }
+    }
 #pragma unroll
     for (int i = 0; i < MB; ++i)
 #pragma unroll
@@ -867,6 +920,45 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_experts_fused(FusedParams fp
   if (fp.stats && ticket == ntot) stats_reduce(fp.st, smem);
 }
 
+// ---- backward GEMMs: one tile per workgroup ----------------------------------------
+
+template <bool GATHER>
+__global__ __launch_bounds__(512) void k_gemm_tiles(GemmParams p) {
+  __shared__ __attribute__((aligned(16))) uint16_t smem[dma_lds_elems<256, 256, 2, 64>()];
+  TilePos tp;
+  if (!decode_tile<256, 256, 64>(p, tp)) return;
+  gemm_tile<256, 256, 4, 2, 2, 64, false, GATHER>(p, tp, smem);
+}
+
+// Per-expert weight gradients: tile (e, mt, nt) sums A[mt rows, seg_e] .
+// B[nt rows, seg_e]^T over expert e's padded column segment seg_e and stores
+// the e-th [M, Nout] block of C. Tiles of one expert run together, four row
+// tiles at a time with the column tile fastest, so they share operand panels.
+__global__ __launch_bounds__(512) void k_gemm_wgrad(GemmParams p, const int32_t* __restrict__ pad_offsets, int M) {
+  __shared__ __attribute__((aligned(16))) uint16_t smem[dma_lds_elems<256, 256, 2, 64>()];
+  constexpr int GM = 4;
+  const int mtn = (M + 255) / 256, ntn = (p.Nout + 255) / 256;
+  const int per_e = mtn * ntn;
+  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  if (L >= per_e * p.N) return;
+  const int e = L / per_e;
+  const int q = L - e * per_e;
+  const int g = q / (GM * ntn);
+  const int gm = min(GM, mtn - g * GM);
+  const int rq = q - g * GM * ntn;
+  TilePos tp{};
+  const int mt = g * GM + rq % gm;
+  tp.nt = __builtin_amdgcn_readfirstlane(rq / gm);
+  tp.ti.expert = 0;
+  tp.ti.row0 = __builtin_amdgcn_readfirstlane(mt * 256);
+  tp.ti.rows = __builtin_amdgcn_readfirstlane(min(256, M - mt * 256));
+  tp.split = __builtin_amdgcn_readfirstlane(e);
+  tp.kb0 = __builtin_amdgcn_readfirstlane(pad_offsets[e]);
+  tp.kb1 = __builtin_amdgcn_readfirstlane(max(tp.kb0, pad_offsets[e + 1]));
+  tp.KT = (tp.kb1 - tp.kb0) / 64;
+  gemm_tile<256, 256, 4, 2, 2, 64, false, false>(p, tp, smem);
+}
+
 // ---- launches --------------------------------------------------------------------
 
 int64_t grid_blocks(const GemmParams& p, int BM, int BN) {
@@ -930,5 +1022,20 @@ hipError_t launch_experts_fused(const FusedParams& fp, hipStream_t s) {
 }
 
 hipError_t launch_gemm_decode(const GemmParams& p, hipStream_t s) { return launch_decode<kDecBM, 128, 3, 4>(p, s); }
+
+hipError_t launch_gemm_tiles(const GemmParams& p, hipStream_t s) {
+  const int64_t blocks = grid_blocks(p, 256, 256);
+  if (blocks <= 0) return hipSuccess;
+  if (p.row_token) hipLaunchKernelGGL(k_gemm_tiles<true>, dim3(static_cast<unsigned>(blocks)), dim3(512), 0, s, p);
+  else hipLaunchKernelGGL(k_gemm_tiles<false>, dim3(static_cast<unsigned>(blocks)), dim3(512), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_wgrad(const GemmParams& p, const int32_t* pad_offsets, int M, hipStream_t s) {
+  const int64_t blocks = static_cast<int64_t>((M + 255) / 256) * ((p.Nout + 255) / 256) * p.N;
+  if (blocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_gemm_wgrad, dim3(static_cast<unsigned>(blocks)), dim3(512), 0, s, p, pad_offsets, M);
+  return hipGetLastError();
+}
 
 }  // namespace moe

@@ -16,6 +16,7 @@ struct RouterParams {
   int64_t T;
   int H, N, k, order, noisy;
   float* logits;          // [T,N] or null
+  float* noise_logits;    // [T,N] x.W_noise (noisy), or null
   int32_t* topk_idx;      // [T,k]
   float* topk_w;          // [T,k]
   int32_t* hist;          // [blocks,N] assignments per expert per block, or null
@@ -111,6 +112,13 @@ struct GemmParams {
   int64_t rows_max;           // upper bound on offsets[N] (grid sizing)
   int64_t a_rows;             // rows of A (bounds of the gathered or permuted operand)
   int swiglu;
+  // training: the swiglu epilogue also stores g and u (fp32) as
+  // gu[r, f] and gu[r, Nout + f] (row stride 2*Nout), when gu is set
+  float* gu;
+  // 1: the SwiGLU backward epilogue of a plain GEMM whose sum is dh[r, f]:
+  // with g, u from gu, C[r, f] = bf16(dh u SiLU'(g)) and
+  // C[r, Nout + f] = bf16(dh SiLU(g)) (C row stride ldc = 2*Nout)
+  int epi;
 };
 // Decode-shaped tiles (few rows per expert), one launch per GEMM.
 hipError_t launch_gemm_decode(const GemmParams& p, hipStream_t s);
@@ -118,6 +126,15 @@ bool gemm_bf16_mfma_supported(int K, int Nout);
 bool gemm_decode_shape(int64_t rows_max, int N);
 void gemm_decode_tile(int* bm, int* bn);
 hipError_t launch_gemm_simple(const GemmParams& p, int bf16, hipStream_t s);
+
+// Backward GEMMs on the same 256 x 256 tile, one tile per workgroup:
+// grouped by expert rows as in the forward (dgrad: dh = dE . Wdown^T-copy,
+// dx = dgu . [Wgate; Wup]^T-copy), or per expert with K over the expert's
+// padded row segment (wgrad: C_e = A[:, seg_e] . B[:, seg_e]^T into the
+// e-th [M, Nout] block of C, c_split_stride = M * Nout). pad_offsets[N+1]:
+// the padded segments, multiples of 64 columns.
+hipError_t launch_gemm_tiles(const GemmParams& p, hipStream_t s);
+hipError_t launch_gemm_wgrad(const GemmParams& p, const int32_t* pad_offsets, int M, hipStream_t s);
 
 // Both expert GEMMs in one persistent launch: g1 is the gate/up GEMM with the
 // SwiGLU epilogue (writing h), g2 the down projection reading h (no K split).
@@ -158,5 +175,71 @@ struct CombineParams {
   int res_splits;
 };
 hipError_t launch_combine(const CombineParams& p, hipStream_t s);
+
+// ---- backward (backward.hip) -------------------------------------------------
+struct BwdGateParams {
+  int64_t T;
+  int H, N, k, order, noisy;
+  float scale;              // s
+  float d_balance;          // upstream gradient of the balance statistic
+  const float* dy;          // [T,H]
+  const float* y_perm;      // [rows][H] expert outputs of the forward
+  const int32_t* slot;      // [T,k]
+  const int32_t* topk_idx;  // [T,k]
+  const float* topk_w;      // [T,k]
+  const float* logits;      // [T,N] clean logits of the forward
+  const float* noise_logits;  // [T,N] (noisy)
+  const float* eps;         // [T,N] (noisy)
+  const int32_t* counts;    // [N] assignments before capacity
+  uint16_t* dE;             // [rows][H] bf16: s w dy at each kept slot's row
+  float* dlog;              // [T,N] gradient of the clean logits
+  float* dnz;               // [T,N] gradient of the noise logits (noisy)
+};
+hipError_t launch_bwd_gate(const BwdGateParams& p, hipStream_t s);
+
+struct BwdDxParams {
+  int64_t T;
+  int H, N, k, noisy;
+  const float* dx_perm;     // [rows][H]
+  const int32_t* slot;      // [T,k]
+  const float* dlog;        // [T,N]
+  const float* dnz;         // [T,N]
+  const float* Wg;          // [H,N]
+  const float* Wn;          // [H,N]
+  float* dx;                // [T,H]
+};
+hipError_t launch_bwd_dx(const BwdDxParams& p, hipStream_t s);
+
+struct RouterWgradParams {
+  int64_t T;
+  int H, N, noisy;
+  const uint16_t* x;        // [T,H] bf16
+  const float* dlog;        // [T,N]
+  const float* dnz;         // [T,N]
+  float* part;              // [router_wgrad_chunks(T)][H][N * (1 + noisy)]
+  float* dWg;               // [H,N]
+  float* dWn;               // [H,N]
+};
+int router_wgrad_chunks(int64_t T);
+hipError_t launch_router_wgrad(const RouterWgradParams& p, hipStream_t s);
+
+hipError_t launch_pad_offsets(const int32_t* offsets, int N, int rows_max, int32_t* pad, hipStream_t s);
+
+struct TransposeParams {
+  const uint16_t* src;
+  int64_t src_ld;           // elements per source row
+  int64_t src_batch;        // elements between batches
+  const int32_t* row_map;   // source row = row_map[row], or null
+  uint16_t* dst;
+  int64_t dst_ld;
+  int64_t dst_batch;
+  int64_t dst_col0;
+  int64_t R;                // source rows (destination columns)
+  int64_t C;                // source columns (destination rows)
+  const int32_t* pad;       // padded mode: [N+1] padded segments
+  const int32_t* offsets;   // padded mode: [N+1] row segments
+  int N, rows_max;
+};
+hipError_t launch_transpose(const TransposeParams& p, int64_t col_blocks, int batches, hipStream_t s);
 
 }  // namespace moe

@@ -174,7 +174,7 @@ moe_status zero_expert_outputs(const moe_cfg* c, int32_t* a, int32_t* b, int32_t
 moe_status run_gemms(const moe_cfg* c, const Layout& L, const void* a, const int32_t* row_token,
                      const int32_t* offsets, const void* Wgate, const void* Wup, const void* Wdown, float* y_perm,
                      int splits, void* ws, bool sched_zeroed, hipStream_t s,
-                     const moe::StatsParams* stats_tail = nullptr) {
+                     const moe::StatsParams* stats_tail = nullptr, float* gu = nullptr) {
   const int bf16 = c->act == MOE_BF16;
   moe::GemmParams g1{};
   g1.A = a;
@@ -195,7 +195,9 @@ moe_status run_gemms(const moe_cfg* c, const Layout& L, const void* a, const int
   g1.rows_max = L.A_max;
   g1.a_rows = row_token ? c->T : c->T * c->k;
   g1.swiglu = 1;
+  g1.gu = gu;
   moe::GemmParams g2 = g1;
+  g2.gu = nullptr;
   g2.A = at<char>(ws, L.h);
   g2.lda = c->F;
   g2.row_token = nullptr;
@@ -245,11 +247,18 @@ struct Residual {
   int splits;
 };
 
+// What a training forward keeps for the backward (in the training workspace).
+struct TrainSave {
+  float* logits;         // [T,N] clean logits
+  float* noise_logits;   // [T,N] (noisy)
+  float* gu;             // [A_max, 2F] g and u
+};
+
 moe_status forward_launch(const moe_cfg* c, const void* x, const float* Wg, const float* Wn, const float* eps,
                           const void* Wgate, const void* Wup, const void* Wdown, void* y, int32_t* topk_idx_opt,
                           float* topk_w_opt, int32_t* kept_opt, int32_t* load_opt, float* importance_opt,
                           float* P_opt, float* balance_opt, float* smooth_load_opt, bool stats, void* ws,
-                          const Residual* res, hipStream_t s) {
+                          const Residual* res, hipStream_t s, const TrainSave* train = nullptr) {
   const Layout L = layout(c);
   int32_t* topk_idx = topk_idx_opt ? topk_idx_opt : at<int32_t>(ws, L.idx);
   float* topk_w = topk_w_opt ? topk_w_opt : at<float>(ws, L.w);
@@ -269,7 +278,8 @@ moe_status forward_launch(const moe_cfg* c, const void* x, const float* Wg, cons
   rp.k = c->k;
   rp.order = c->order;
   rp.noisy = c->noisy;
-  rp.logits = nullptr;
+  rp.logits = train ? train->logits : nullptr;
+  rp.noise_logits = train ? train->noise_logits : nullptr;
   rp.topk_idx = topk_idx;
   rp.topk_w = topk_w;
   rp.hist = at<int32_t>(ws, L.hist);
@@ -282,13 +292,18 @@ moe_status forward_launch(const moe_cfg* c, const void* x, const float* Wg, cons
                             load_opt, importance_opt, P_opt, balance_opt, smooth_load_opt};
   if (stats && !L.fused) MOE_LAUNCH(MOE_KERNEL_STATS, s, moe::launch_stats(sp, s));
   moe::ScatterParams sc{topk_idx, at<int32_t>(ws, L.hist), L.hist_tokens, c->T, c->N, c->k, c->capacity,
-                        (!stats && load_opt) ? load_opt : at<int32_t>(ws, L.counts), kept_opt, offsets, slot,
+                        (!stats && load_opt && !train) ? load_opt : at<int32_t>(ws, L.counts), kept_opt, offsets, slot,
                         row_token, L.fused ? at<int32_t>(ws, L.sched) : nullptr,
                         L.fused ? moe::fused_sched_ints(L.A_max, c->N) : 0};
   MOE_LAUNCH(MOE_KERNEL_SCATTER, s, moe::launch_scatter(sc, s));
+  if (train && !stats && load_opt) {
+    const hipError_t e = hipMemcpyAsync(load_opt, at<int32_t>(ws, L.counts), sizeof(int32_t) * c->N,
+                                        hipMemcpyDeviceToDevice, s);
+    if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "copy of the expert counts failed: %s", hipGetErrorString(e));
+  }
   float* y_perm = at<float>(ws, L.yperm);
   const moe_status st = run_gemms(c, L, x, row_token, offsets, Wgate, Wup, Wdown, y_perm, L.splits, ws, true, s,
-                                  stats && L.fused ? &sp : nullptr);
+                                  stats && L.fused ? &sp : nullptr, train ? train->gu : nullptr);
   if (st != MOE_OK) return st;
   moe::CombineParams cp{y_perm, L.A_max * static_cast<int64_t>(c->H), L.splits, slot, topk_w, y,
                         c->out == MOE_BF16, c->T, c->H, c->k, c->out_scale,
@@ -553,6 +568,254 @@ moe_status moe_forward_residual(const moe_cfg* c, int32_t F_shared, const void* 
   const Residual res{y_s, Ls.A_max * static_cast<int64_t>(c->H), Ls.splits};
   return forward_launch(c, x, Wg, Wn, eps, Wgate, Wup, Wdown, y, topk_idx_opt, topk_w_opt, kept_opt, load_opt,
                         importance_opt, P_opt, balance_opt, smooth_load_opt, stats, ws, &res, s);
+}
+
+}  // extern "C"
+
+// ---- training: forward that keeps what the backward needs, and the backward ----
+namespace {
+
+// The training workspace: the forward's layout, then what the training
+// forward keeps (router logits, g and u) and the backward's buffers.
+struct TrainLayout {
+  Layout L;
+  int64_t A_pad = 0;  // columns of the transposed, per-expert padded copies
+  size_t logits = 0, nlog = 0, gu = 0, dE = 0, pad = 0, dEt = 0, ht = 0, xt = 0, dgu = 0, dgut = 0, WdT = 0,
+         WguT = 0, dxp = 0, dlog = 0, dnz = 0, rwp = 0, total = 0;
+};
+
+TrainLayout train_layout(const moe_cfg* c) {
+  TrainLayout t;
+  t.L = layout(c);
+  const int64_t T = c->T, H = c->H, F = c->F, N = c->N, A = t.L.A_max;
+  t.A_pad = (A + 63) / 64 * 64 + 64 * N;
+  size_t o = t.L.total;
+  auto take = [&](size_t bytes) {
+    const size_t at_ = o;
+    o += up(bytes);
+    return at_;
+  };
+  t.logits = take(T * N * 4);
+  t.nlog = take(T * N * 4);
+  t.gu = take(A * 2 * F * 4);
+  t.dE = take(A * H * 2);
+  t.pad = take((N + 1) * 4);
+  t.dEt = take(H * t.A_pad * 2);
+  t.ht = take(F * t.A_pad * 2);
+  t.xt = take(H * t.A_pad * 2);
+  t.dgu = take(A * 2 * F * 2);
+  t.dgut = take(2 * F * t.A_pad * 2);
+  t.WdT = take(N * F * H * 2);
+  t.WguT = take(N * H * 2 * F * 2);
+  t.dxp = take(A * H * 4);
+  t.dlog = take(T * N * 4);
+  t.dnz = take(T * N * 4);
+  t.rwp = take(static_cast<size_t>(moe::router_wgrad_chunks(T)) * H * N * 2 * 4);
+  t.total = o;
+  return t;
+}
+
+// The backward runs on the persistent-kernel path only: bf16, F % 8 == 0,
+// prefill shapes (more than 48 rows per expert on average).
+moe_status check_train(const moe_cfg* c) {
+  moe_status st = moe_check(c);
+  if (st != MOE_OK) return st;
+  const Layout L = layout(c);
+  if (!L.fused)
+    return fail(MOE_ERR_UNSUPPORTED,
+                "training needs bf16 activations and weights, F %% 8 == 0 and more than 48 rows per expert on "
+                "average (the persistent expert kernel's shapes)");
+  const int64_t A_pad = (L.A_max + 63) / 64 * 64 + 64 * static_cast<int64_t>(c->N);
+  if (A_pad * std::max<int64_t>(c->H, 2 * static_cast<int64_t>(c->F)) >= (int64_t(1) << 30))
+    return fail(MOE_ERR_UNSUPPORTED, "transposed backward operands must stay below 2 GiB");
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_train_workspace_bytes(const moe_cfg* c) {
+  if (check_train(c) != MOE_OK) return 0;
+  return train_layout(c).total;
+}
+
+moe_status moe_forward_train(const moe_cfg* c, const void* x, const float* Wg, const float* Wn, const float* eps,
+                             const void* Wgate, const void* Wup, const void* Wdown, void* y, int32_t* kept_opt,
+                             int32_t* load_opt, float* importance_opt, float* P_opt, float* balance_opt,
+                             float* smooth_load_opt, void* ws, size_t ws_bytes, hipStream_t s) {
+  moe_status st = check_train(c);
+  if (st != MOE_OK) return st;
+  MOE_REQUIRE(!smooth_load_opt || c->noisy, "the smooth load needs the noisy gate (cfg->noisy = 1)");
+  const bool stats = c->want_stats && (load_opt || importance_opt || P_opt || balance_opt || smooth_load_opt);
+  if (c->T == 0) {
+    st = zero_expert_outputs(c, kept_opt, load_opt, nullptr, stats ? importance_opt : nullptr,
+                             stats ? P_opt : nullptr, stats ? balance_opt : nullptr, s);
+    if (st == MOE_OK && stats && smooth_load_opt)
+      st = zero_expert_outputs(c, nullptr, nullptr, nullptr, smooth_load_opt, nullptr, nullptr, s);
+    return st;
+  }
+  MOE_REQUIRE(x && Wg && Wgate && Wup && Wdown && y, "x, Wg, expert weights and y are required");
+  MOE_REQUIRE(!c->noisy || (Wn && eps), "noisy routing needs Wn and eps");
+  MOE_REQUIRE(aligned(x, 16) && aligned(Wg, 16) && (!Wn || aligned(Wn, 16)) && aligned(Wgate, 16) &&
+                  aligned(Wup, 16) && aligned(Wdown, 16) && aligned(y, 16),
+              "x, router and expert weights and y must be 16-byte aligned");
+  const TrainLayout t = train_layout(c);
+  if (ws_bytes < t.total) return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, t.total);
+  MOE_REQUIRE(ws && aligned(ws, 256), "the workspace must be non-NULL and 256-byte aligned");
+  const TrainSave save{at<float>(ws, t.logits), c->noisy ? at<float>(ws, t.nlog) : nullptr, at<float>(ws, t.gu)};
+  return forward_launch(c, x, Wg, Wn, eps, Wgate, Wup, Wdown, y, nullptr, nullptr, kept_opt, load_opt,
+                        importance_opt, P_opt, balance_opt, smooth_load_opt, stats, ws, nullptr, s, &save);
+}
+
+moe_status moe_backward(const moe_cfg* c, const void* x, const float* Wg, const float* Wn, const float* eps,
+                        const void* Wgate, const void* Wup, const void* Wdown, const float* dy, float d_balance,
+                        float* dx, float* dWg, float* dWn_opt, float* dWgate, float* dWup, float* dWdown, void* ws,
+                        size_t ws_bytes, hipStream_t s) {
+  moe_status st = check_train(c);
+  if (st != MOE_OK) return st;
+  MOE_REQUIRE(std::isfinite(d_balance), "d_balance is not finite");
+  MOE_REQUIRE(dx && dWg && dWgate && dWup && dWdown, "dx and every weight gradient are required");
+  MOE_REQUIRE(!c->noisy || dWn_opt, "the noisy gate needs dWn");
+  const int64_t T = c->T, H = c->H, F = c->F, N = c->N;
+  if (T == 0) {
+    hipError_t e = moe::launch_fill_f32(dWg, H * N, 0.0f, s);
+    if (e == hipSuccess && dWn_opt) e = moe::launch_fill_f32(dWn_opt, H * N, 0.0f, s);
+    if (e == hipSuccess) e = moe::launch_fill_f32(dWgate, N * F * H, 0.0f, s);
+    if (e == hipSuccess) e = moe::launch_fill_f32(dWup, N * F * H, 0.0f, s);
+    if (e == hipSuccess) e = moe::launch_fill_f32(dWdown, N * H * F, 0.0f, s);
+    if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "fill launch failed: %s", hipGetErrorString(e));
+    return MOE_OK;
+  }
+  MOE_REQUIRE(x && Wg && Wgate && Wup && Wdown && dy, "x, Wg, expert weights and dy are required");
+  MOE_REQUIRE(!c->noisy || (Wn && eps), "noisy routing needs Wn and eps");
+  MOE_REQUIRE(aligned(x, 16) && aligned(Wg, 16) && aligned(Wgate, 16) && aligned(Wup, 16) && aligned(Wdown, 16) &&
+                  aligned(dy, 16) && aligned(dx, 16) && aligned(dWgate, 16) && aligned(dWup, 16) &&
+                  aligned(dWdown, 16),
+              "inputs and gradients must be 16-byte aligned");
+  const TrainLayout t = train_layout(c);
+  if (ws_bytes < t.total) return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, t.total);
+  MOE_REQUIRE(ws && aligned(ws, 256), "the workspace must be non-NULL and 256-byte aligned");
+  const Layout& L = t.L;
+  const int A = static_cast<int>(L.A_max);
+  const int32_t* offsets = at<int32_t>(ws, L.offsets);
+  int32_t* pad = at<int32_t>(ws, t.pad);
+  uint16_t* dE = at<uint16_t>(ws, t.dE);
+  uint16_t* dgu = at<uint16_t>(ws, t.dgu);
+  float* dlog = at<float>(ws, t.dlog);
+  float* dnz = at<float>(ws, t.dnz);
+  hipError_t e = moe::launch_pad_offsets(offsets, c->N, A, pad, s);
+  if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "pad offsets launch failed: %s", hipGetErrorString(e));
+
+  // gate weights back to the router; dE = s w dy at every kept slot's row
+  moe::BwdGateParams gp{T, c->H, c->N, c->k, c->order, c->noisy, c->out_scale, d_balance, dy,
+                        at<float>(ws, L.yperm), at<int32_t>(ws, L.slot), at<int32_t>(ws, L.idx), at<float>(ws, L.w),
+                        at<float>(ws, t.logits), c->noisy ? at<float>(ws, t.nlog) : nullptr, eps,
+                        at<int32_t>(ws, L.counts), dE, dlog, dnz};
+  MOE_LAUNCH(MOE_KERNEL_BWD_GATE, s, moe::launch_bwd_gate(gp, s));
+
+  // K-contiguous copies for the matrix-core tiles
+  auto tr = [&](const void* src, int64_t src_ld, int64_t src_batch, const int32_t* row_map, void* dst, int64_t dst_ld,
+                int64_t dst_batch, int64_t col0, int64_t R, int64_t C, bool padded, int batches) {
+    moe::TransposeParams tp{static_cast<const uint16_t*>(src), src_ld, src_batch, row_map,
+                            static_cast<uint16_t*>(dst), dst_ld, dst_batch, col0, R, C,
+                            padded ? pad : nullptr, padded ? offsets : nullptr, c->N, A};
+    return moe::launch_transpose(tp, padded ? t.A_pad / 64 : (R + 63) / 64, batches, s);
+  };
+  uint16_t* WdT = at<uint16_t>(ws, t.WdT);
+  uint16_t* WguT = at<uint16_t>(ws, t.WguT);
+  uint16_t* dEt = at<uint16_t>(ws, t.dEt);
+  uint16_t* ht = at<uint16_t>(ws, t.ht);
+  uint16_t* xt = at<uint16_t>(ws, t.xt);
+  uint16_t* dgut = at<uint16_t>(ws, t.dgut);
+  {
+    ProfScope ps_(MOE_KERNEL_BWD_TRANSPOSE, s);
+    e = tr(Wdown, F, H * F, nullptr, WdT, H, F * H, 0, H, F, false, c->N);
+    if (e == hipSuccess) e = tr(Wgate, H, F * H, nullptr, WguT, 2 * F, H * 2 * F, 0, F, H, false, c->N);
+    if (e == hipSuccess) e = tr(Wup, H, F * H, nullptr, WguT, 2 * F, H * 2 * F, F, F, H, false, c->N);
+    if (e == hipSuccess) e = tr(dE, H, 0, nullptr, dEt, t.A_pad, 0, 0, A, H, true, 1);
+    if (e == hipSuccess) e = tr(at<uint16_t>(ws, L.h), F, 0, nullptr, ht, t.A_pad, 0, 0, A, F, true, 1);
+    if (e == hipSuccess) e = tr(x, H, 0, at<int32_t>(ws, L.rowtok), xt, t.A_pad, 0, 0, A, H, true, 1);
+  }
+  if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "transpose launch failed: %s", hipGetErrorString(e));
+
+  // dh = dE . Wdown_e, and the SwiGLU derivative into dg | du (bf16)
+  moe::GemmParams gd{};
+  gd.A = dE;
+  gd.lda = H;
+  gd.offsets = offsets;
+  gd.N = c->N;
+  gd.B0 = WdT;
+  gd.b_expert_stride = F * H;
+  gd.ldb = H;
+  gd.K = c->H;
+  gd.Nout = c->F;
+  gd.C = dgu;
+  gd.ldc = 2 * F;
+  gd.splits = 1;
+  gd.rows_max = A;
+  gd.a_rows = A;
+  gd.gu = at<float>(ws, t.gu);
+  gd.epi = 1;
+  MOE_LAUNCH(MOE_KERNEL_BWD_DGRAD, s, moe::launch_gemm_tiles(gd, s));
+  {
+    ProfScope ps_(MOE_KERNEL_BWD_TRANSPOSE, s);
+    e = tr(dgu, 2 * F, 0, nullptr, dgut, t.A_pad, 0, 0, A, 2 * F, true, 1);
+  }
+  if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "transpose launch failed: %s", hipGetErrorString(e));
+  // dx_perm = dg . Wgate_e + du . Wup_e
+  moe::GemmParams gx{};
+  gx.A = dgu;
+  gx.lda = 2 * F;
+  gx.offsets = offsets;
+  gx.N = c->N;
+  gx.B0 = WguT;
+  gx.b_expert_stride = H * 2 * F;
+  gx.ldb = 2 * F;
+  gx.K = 2 * c->F;
+  gx.Nout = c->H;
+  gx.C = at<float>(ws, t.dxp);
+  gx.ldc = H;
+  gx.splits = 1;
+  gx.rows_max = A;
+  gx.a_rows = A;
+  MOE_LAUNCH(MOE_KERNEL_BWD_DGRAD, s, moe::launch_gemm_tiles(gx, s));
+  // dx = sum of the slots' rows + the router terms
+  moe::BwdDxParams dp{T, c->H, c->N, c->k, c->noisy, at<float>(ws, t.dxp), at<int32_t>(ws, L.slot), dlog, dnz, Wg,
+                      Wn, dx};
+  MOE_LAUNCH(MOE_KERNEL_BWD_DX, s, moe::launch_bwd_dx(dp, s));
+  // weight gradients per expert, K over the expert's padded rows
+  moe::GemmParams gw{};
+  gw.N = c->N;
+  gw.splits = 1;
+  gw.b_expert_stride = 0;
+  gw.A = dEt;
+  gw.lda = t.A_pad;
+  gw.a_rows = H;
+  gw.B0 = ht;
+  gw.ldb = t.A_pad;
+  gw.K = static_cast<int>(t.A_pad);
+  gw.Nout = c->F;
+  gw.C = dWdown;
+  gw.ldc = F;
+  gw.c_split_stride = H * F;
+  MOE_LAUNCH(MOE_KERNEL_BWD_WGRAD, s, moe::launch_gemm_wgrad(gw, pad, c->H, s));
+  gw.A = dgut;
+  gw.a_rows = F;
+  gw.B0 = xt;
+  gw.Nout = c->H;
+  gw.C = dWgate;
+  gw.ldc = H;
+  gw.c_split_stride = F * H;
+  MOE_LAUNCH(MOE_KERNEL_BWD_WGRAD, s, moe::launch_gemm_wgrad(gw, pad, c->F, s));
+  gw.A = dgut + F * t.A_pad;
+  gw.C = dWup;
+  MOE_LAUNCH(MOE_KERNEL_BWD_WGRAD, s, moe::launch_gemm_wgrad(gw, pad, c->F, s));
+  // router weights
+  moe::RouterWgradParams rw{T, c->H, c->N, c->noisy, static_cast<const uint16_t*>(x), dlog, dnz,
+                            at<float>(ws, t.rwp), dWg, dWn_opt};
+  MOE_LAUNCH(MOE_KERNEL_BWD_ROUTER, s, moe::launch_router_wgrad(rw, s));
+  return MOE_OK;
 }
 
 const char* moe_status_str(moe_status s) {

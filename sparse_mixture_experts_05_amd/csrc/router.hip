@@ -145,6 +145,9 @@ __global__ __launch_bounds__(kRouterWaves * kWave) void k_router(RouterParams p)
     // then compares a strict total order, so every lane agrees on the winner
     if (hv != hv) hv = -INFINITY;
     if (p.logits && valid) p.logits[tok * N + lane] = lv;
+    if constexpr (NOISY) {
+      if (p.noise_logits && valid) p.noise_logits[tok * N + lane] = nz;
+    }
 
     // KeepTopK: k rounds of a wave-wide argmax, ties to the lower index
     float cur = valid ? hv : -INFINITY;

@@ -364,6 +364,7 @@ __global__ __launch_bounds__(router_waves<NB16>() * 64) void k_router_mma(Router
     // is a strict total order and exactly k experts are kept
     if (hv != hv) hv = -INFINITY;
     if (p.logits && valid) p.logits[g * N + lane] = lv;
+    if (p.noise_logits && p.noisy && valid) p.noise_logits[g * N + lane] = s_log[t][N + lane];
     // rank: experts with a larger score, or an equal one at a lower index
     int rank = 0;
     for (int m = 0; m < N; ++m) {
