@@ -86,6 +86,11 @@ WORKLOADS = {
     "C2res": ("LLaMA-MoE-3.5B-shape residual (shared-neuron Inter mode) layer: T=4096, hidden 4096, 11008 neurons = "
               "1376 shared + 7 routed experts of 1376, top-2 Mixtral, dropless, s=1",
               lambda synth: synth.make_residual("C2res", 1007, 4096, 4096, 11008, 1376, 7, 2, out_scale=1.0)),
+    "C2train": ("LLaMA-MoE-3.5B (2/8) MoE layer training step (forward that keeps its activations, then the "
+                "backward: dx, router and expert weight gradients, balance-loss gradient 0.01): T=4096, hidden "
+                "4096, 8 experts of 1376, top-2 Mixtral, dropless, s=4", lambda synth: synth.c2()),
+    "C3train": ("LLaMA-MoE-3.5B (4/16) MoE layer training step: T=4096, 16 experts of 688, noisy top-4, stats, "
+                "balance-loss gradient 0.01, s=4", lambda synth: synth.c3()),
     "C5": ("decode-shaped E8T2 layer: T=64 tokens, hidden 4096, 8 experts of 14336, top-2, half the tokens "
            "steered to expert 0, dropless", lambda synth: synth.c5()),
 }
@@ -145,9 +150,17 @@ def main():
                  P=torch.empty(N, dtype=torch.float32, device="cuda"),
                  balance=torch.empty(1, dtype=torch.float32, device="cuda")) if w.want_stats else {}
     Fs = w.shared[0].shape[0] if w.shared is not None else 0
+    train = args.config.endswith("train")
     if Fs:
         shared = [tuple(dev(a) for a in w.shared) for _ in range(len(copies))]
         ws = torch.empty(abi.moe_residual_workspace_bytes(cfg, Fs), dtype=torch.uint8, device="cuda")
+    elif train:
+        ws = torch.empty(abi.moe_train_workspace_bytes(cfg), dtype=torch.uint8, device="cuda")
+        dy = dev(synth.normal_f32(w.meta["seed"], 40, (T, H), 1.0))
+        grads = dict(dx=torch.empty(T, H, device="cuda"), dWg=torch.empty(H, N, device="cuda"),
+                     dWn=torch.empty(H, N, device="cuda") if w.noisy else None,
+                     dWgate=torch.empty(N, F, H, device="cuda"), dWup=torch.empty(N, F, H, device="cuda"),
+                     dWdown=torch.empty(N, H, F, device="cuda"))
     else:
         ws = abi.workspace(cfg)
     stream = torch.cuda.current_stream()
@@ -155,7 +168,13 @@ def main():
     def step(i, d=None):
         j = i % len(copies)
         d = d if d is not None else copies[j]
-        if Fs:
+        if train:
+            abi.moe_forward_train(cfg, d["x"], d["Wg"], d["Wn"], d["eps"], d["Wgate"], d["Wup"], d["Wdown"], y,
+                                  kept=kept, ws=ws, stream=stream, **stats)
+            abi.moe_backward(cfg, d["x"], d["Wg"], d["Wn"], d["eps"], d["Wgate"], d["Wup"], d["Wdown"], dy, 0.01,
+                             grads["dx"], grads["dWg"], grads["dWn"], grads["dWgate"], grads["dWup"],
+                             grads["dWdown"], ws=ws, stream=stream)
+        elif Fs:
             abi.moe_forward_residual(cfg, Fs, d["x"], d["Wg"], d["Wn"], d["eps"], d["Wgate"], d["Wup"], d["Wdown"],
                                      *shared[j], y, kept=kept, ws=ws, stream=stream, **stats)
         else:
@@ -171,6 +190,19 @@ def main():
     torch.cuda.synchronize()
     fused = abi.moe_profile_read()[1] > 0
     dom_id = abi.MOE_KERNEL_EXPERTS if fused else abi.MOE_KERNEL_GEMM1
+    if train:
+        # a training step runs three GEMM kernels of 6*A*H*F flops each (the
+        # forward's experts, the backward's dgrad pair and its three weight
+        # gradients): the dominant one is the slowest of them per step
+        per_step = {}
+        for kid in (abi.MOE_KERNEL_EXPERTS, abi.MOE_KERNEL_BWD_DGRAD, abi.MOE_KERNEL_BWD_WGRAD):
+            abi.moe_profile_select(kid)
+            abi.moe_profile_read()
+            for i in range(4):
+                step(i)
+            torch.cuda.synchronize()
+            per_step[kid] = abi.moe_profile_read()[0] / 4
+        dom_id = max(per_step, key=per_step.get)
     abi.moe_profile_select(-1)
     kept_h = kept.cpu().numpy().astype(np.int64)
     A = int(kept_h.sum())                    # kept (token, expert) rows
@@ -213,16 +245,20 @@ def main():
     # the residual layer launches the expert kernel twice a step (shared
     # slice, then the routed experts): its roofline covers both launches
     dom_avg_s = dom_ms / 1e3 / max(1, dom_n) * (2 if Fs else 1)
+    if train:  # per step: the dgrad kernel launches twice, the weight-gradient kernel three times
+        dom_avg_s = dom_ms / 1e3 / args.steps
 
     # layer roofline over the kept assignments: expert flops on the matrix
     # cores plus the fp32 router, or the bytes of reading x, the router
     # weights, the active experts' weights once, the routing outputs, and
     # writing fp32 y once, whichever takes longer
     eb = 2 if bf16 else 4
-    f_expert = 6.0 * A * H * F + 6.0 * T * H * Fs
+    f_expert = (18.0 if train else 6.0) * A * H * F + 6.0 * T * H * Fs
     f_router = 2.0 * T * H * N * (2 if w.noisy else 1)
     b_alg = (T * H * eb + H * N * 4 * (2 if w.noisy else 1) + (T * N * 4 if w.noisy else 0)
              + active * 3 * F * H * eb + 3 * Fs * H * eb + T * k * 8 + T * H * 4)
+    if train:  # the backward reads dy and the weights again and writes dx and every gradient in fp32
+        b_alg += T * H * 4 + active * 3 * F * H * eb + T * H * 4 + active * 3 * F * H * 4 + H * N * 4 * (2 if w.noisy else 1)
     peak_expert = PEAK_BF16_TFLOPS if bf16 else PEAK_FP32_TFLOPS
     t_compute = f_expert / (peak_expert * 1e12) + f_router / (PEAK_FP32_TFLOPS * 1e12)
     t_mem = b_alg / (PEAK_HBM_GBS * 1e9)
@@ -231,7 +267,12 @@ def main():
     # dominant kernel's algorithmic work per launch: the fused launch does
     # 6*A*H*F flops and reads the active experts' three matrices; the gate/up
     # GEMM alone does 4*A*H*F and reads two of them
-    if fused:
+    if train:
+        dom_name = {abi.MOE_KERNEL_EXPERTS: "experts_fused_forward", abi.MOE_KERNEL_BWD_DGRAD: "backward_dgrad_pair",
+                    abi.MOE_KERNEL_BWD_WGRAD: "backward_weight_gradients"}[dom_id]
+        dom_flops = 6.0 * A * H * F
+        dom_bytes = active * 3 * F * H * eb
+    elif fused:
         dom_name = "experts_gate_up_swiglu_down"
         dom_flops = 6.0 * A * H * F + 6.0 * T * H * Fs
         dom_bytes = active * 3 * F * H * eb + A * H * eb + A * H * 4 + 3 * Fs * H * eb + T * H * eb + T * H * 4
@@ -257,7 +298,10 @@ def main():
         names = {abi.MOE_KERNEL_ROUTER: "router_topk", abi.MOE_KERNEL_STATS: "router_stats",
                  abi.MOE_KERNEL_SCATTER: "permute_scatter", abi.MOE_KERNEL_GEMM1: "gemm1_gate_up_swiglu",
                  abi.MOE_KERNEL_GEMM2: "gemm2_down", abi.MOE_KERNEL_EXPERTS: "experts_fused",
-                 abi.MOE_KERNEL_COMBINE: "combine"}
+                 abi.MOE_KERNEL_COMBINE: "combine", abi.MOE_KERNEL_BWD_GATE: "bwd_gate",
+                 abi.MOE_KERNEL_BWD_TRANSPOSE: "bwd_transposes", abi.MOE_KERNEL_BWD_DGRAD: "bwd_dgrad",
+                 abi.MOE_KERNEL_BWD_DX: "bwd_dx", abi.MOE_KERNEL_BWD_WGRAD: "bwd_wgrad",
+                 abi.MOE_KERNEL_BWD_ROUTER: "bwd_router_wgrad"}
         for kid, name in names.items():
             abi.moe_profile_select(kid)
             for i in range(10):
@@ -265,7 +309,7 @@ def main():
             torch.cuda.synchronize()
             ms, n = abi.moe_profile_read()
             if n:
-                per_kernel[name] = round(ms * 1e3 / n, 2)
+                per_kernel[name] = round(ms * 1e3 / (10 if train else n), 2)  # train: per step
         abi.moe_profile_select(-1)
         # same data every step: weights can stay in the last-level cache
         torch.cuda.synchronize()
