@@ -51,7 +51,7 @@ def load(path: str = None):
     lib.oracle_combine_rows.argtypes = [cfgp, vp, vp, vp, i64, vp, vp, vp]
     lib.oracle_smooth_load.argtypes = [cfgp] + [vp] * 5
     lib.oracle_residual_combine_rows.argtypes = [cfgp, vp, vp, vp, i64, vp, vp, vp, vp]
-    lib.oracle_backward.argtypes = [cfgp] + [vp] * 8 + [ctypes.c_double] + [vp] * 6
+    lib.oracle_backward.argtypes = [cfgp] + [vp] * 8 + [ctypes.c_double, i32] + [vp] * 6
     lib.brute_layer.argtypes = [cfgp] + [vp] * 17
     for f in ("oracle_route", "oracle_stats", "oracle_capacity", "oracle_expert_rows",
               "oracle_combine_tokens", "oracle_combine_rows", "oracle_smooth_load", "oracle_residual_combine_rows",
@@ -236,7 +236,7 @@ def residual_forward(w, tokens=None, nthreads=1, h_round=None, lib=None, E=None,
     return out
 
 
-def backward(w, dy, d_balance=0.0, h_round=None, lib=None):
+def backward(w, dy, d_balance=0.0, h_round=None, lib=None, nthreads=1):
     """Gradients of <dy, y> + d_balance * balance (see moe_oracle.h):
     dict of dx, dWg, dWn, dWgate, dWup, dWdown (double)."""
     lib = lib or load()
@@ -247,7 +247,8 @@ def backward(w, dy, d_balance=0.0, h_round=None, lib=None):
     Wn = w.Wn if w.noisy else None
     eps = w.eps if w.noisy else None
     _check(lib.oracle_backward(ctypes.byref(c), _p(w.x), _p(w.Wg), _p(Wn), _p(eps), _p(w.Wgate), _p(w.Wup),
-                               _p(w.Wdown), _p(np.ascontiguousarray(dy, np.float32)), float(d_balance), _p(o["dx"]),
+                               _p(w.Wdown), _p(np.ascontiguousarray(dy, np.float32)), float(d_balance),
+                               int(nthreads), _p(o["dx"]),
                                _p(o["dWg"]), _p(o["dWn"]), _p(o["dWgate"]), _p(o["dWup"]), _p(o["dWdown"])),
            "oracle_backward")
     return o

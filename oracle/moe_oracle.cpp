@@ -397,7 +397,8 @@ int oracle_residual_combine_rows(const oracle_cfg* c, const double* topk_w, cons
 
 int oracle_backward(const oracle_cfg* c, const void* x, const float* Wg, const float* Wn, const float* eps,
                     const void* Wgate, const void* Wup, const void* Wdown, const float* dy, double d_balance,
-                    double* dx, double* dWg, double* dWn, double* dWgate, double* dWup, double* dWdown) {
+                    int32_t nthreads, double* dx, double* dWg, double* dWn, double* dWgate, double* dWup,
+                    double* dWdown) {
   if (!cfg_ok(c)) return -1;
   if (!dx || !dWg || !dWn || !dWgate || !dWup || !dWdown) return -2;
   if (c->T > 0 && (!x || !Wg || !Wgate || !Wup || !Wdown || !dy)) return -2;
@@ -421,68 +422,79 @@ int oracle_backward(const oracle_cfg* c, const void* x, const float* Wg, const f
   std::vector<int64_t> counts(N), kept(N), offsets(N + 1), slot(T * k), row_token(T * k);
   oracle_capacity(c, idx.data(), counts.data(), kept.data(), offsets.data(), slot.data(), row_token.data());
 
-  std::vector<double> xd(H), nz(N), sp(N), g(F), u(F), hh(F), E(H), dE(H), dh(F), dg(F), du(F), dw(k), dH(N),
-      dlog(N), dn(N), p(N);
-  for (int64_t t = 0; t < T; ++t) {
-    for (int64_t h = 0; h < H; ++h) xd[h] = load_val(x, c->x_dtype, t * H + h);
-    std::fill(dw.begin(), dw.end(), 0.0);
-    for (int64_t j = 0; j < k; ++j) {
-      if (slot[t * k + j] < 0) continue;  /* a dropped slot adds nothing to y: no gradient */
-      const int64_t e = idx[t * k + j];
-      const int64_t wb = e * F * H;
-      /* forward of expert e on this token ([V2] code example, Expert) */
-      for (int64_t f = 0; f < F; ++f) {
-        double a = 0.0, b = 0.0;
-        for (int64_t h = 0; h < H; ++h) {
-          a += xd[h] * load_val(Wgate, c->w_dtype, wb + f * H + h);
-          b += xd[h] * load_val(Wup, c->w_dtype, wb + f * H + h);
+  /* The experts, one expert per task: its kept rows in token order, so each
+   * weight-gradient element sums its rows in token order whatever the thread
+   * count. Each row leaves dw (its gate weight's gradient) and its share of
+   * dx; the token's shares are added in slot order below. */
+  std::vector<double> dwv(T * k, 0.0), dxp(T * k * H, 0.0);
+  for_tokens(N, nthreads, [&](int64_t e) {
+    std::vector<double> xd(H), g(F), u(F), hh(F), E(H), dE(H), dh(F), dg(F), du(F);
+    const int64_t wb = e * F * H;
+    for (int64_t t = 0; t < T; ++t)
+      for (int64_t j = 0; j < k; ++j) {
+        /* a dropped slot adds nothing to y: no gradient */
+        if (idx[t * k + j] != e || slot[t * k + j] < 0) continue;
+        for (int64_t h = 0; h < H; ++h) xd[h] = load_val(x, c->x_dtype, t * H + h);
+        /* forward of expert e on this token ([V2] code example, Expert) */
+        for (int64_t f = 0; f < F; ++f) {
+          double a = 0.0, b = 0.0;
+          for (int64_t h = 0; h < H; ++h) {
+            a += xd[h] * load_val(Wgate, c->w_dtype, wb + f * H + h);
+            b += xd[h] * load_val(Wup, c->w_dtype, wb + f * H + h);
+          }
+          g[f] = a;
+          u[f] = b;
+          double v = oracle_silu(a) * b;
+          if (c->h_round == ORC_H_BF16) v = oracle_round_bf16(v);
+          else if (c->h_round == ORC_H_F32) v = oracle_round_f32(v);
+          hh[f] = v;
         }
-        g[f] = a;
-        u[f] = b;
-        double v = oracle_silu(a) * b;
-        if (c->h_round == ORC_H_BF16) v = oracle_round_bf16(v);
-        else if (c->h_round == ORC_H_F32) v = oracle_round_f32(v);
-        hh[f] = v;
-      }
-      for (int64_t o = 0; o < H; ++o) {
-        double acc = 0.0;
-        for (int64_t f = 0; f < F; ++f) acc += hh[f] * load_val(Wdown, c->w_dtype, wb + o * F + f);
-        E[o] = acc;
-      }
-      /* y_t = s sum_j w_j E_j: dw_j = s <dy_t, E_j>, dE_j = s w_j dy_t */
-      double d = 0.0;
-      for (int64_t o = 0; o < H; ++o) d += static_cast<double>(dy[t * H + o]) * E[o];
-      dw[j] = c->out_scale * d;
-      for (int64_t o = 0; o < H; ++o) dE[o] = rnd(c->out_scale * w[t * k + j] * static_cast<double>(dy[t * H + o]));
-      /* down projection: dWdown_e += dE h^T, dh = Wdown_e^T dE */
-      for (int64_t o = 0; o < H; ++o)
-        for (int64_t f = 0; f < F; ++f) dWdown[wb + o * F + f] += dE[o] * hh[f];
-      for (int64_t f = 0; f < F; ++f) {
-        double acc = 0.0;
-        for (int64_t o = 0; o < H; ++o) acc += dE[o] * load_val(Wdown, c->w_dtype, wb + o * F + f);
-        dh[f] = acc;
-      }
-      /* h = SiLU(g) u: du = dh SiLU(g), dg = dh u SiLU'(g) with
-       * SiLU'(g) = sigma(g) (1 + g (1 - sigma(g))) */
-      for (int64_t f = 0; f < F; ++f) {
-        const double sg = 1.0 / (1.0 + std::exp(-g[f]));
-        du[f] = rnd(dh[f] * oracle_silu(g[f]));
-        dg[f] = rnd(dh[f] * u[f] * sg * (1.0 + g[f] * (1.0 - sg)));
-      }
-      /* gate and up projections: dW += d outer x, dx += W^T d */
-      for (int64_t f = 0; f < F; ++f)
-        for (int64_t h = 0; h < H; ++h) {
-          dWgate[wb + f * H + h] += dg[f] * xd[h];
-          dWup[wb + f * H + h] += du[f] * xd[h];
-          dx[t * H + h] += dg[f] * load_val(Wgate, c->w_dtype, wb + f * H + h) +
-                           du[f] * load_val(Wup, c->w_dtype, wb + f * H + h);
+        for (int64_t o = 0; o < H; ++o) {
+          double acc = 0.0;
+          for (int64_t f = 0; f < F; ++f) acc += hh[f] * load_val(Wdown, c->w_dtype, wb + o * F + f);
+          E[o] = acc;
         }
-    }
-    /* gate weights back to the scores H ([UP] section 3, G = Softmax(KeepTopK(H)))
-     * Mixtral: w = softmax over the kept k scores, dH_j = w_j (dw_j - sum w dw);
-     * ST ([UP] section 5): w_j = p_{idx_j}, p = softmax over all N scores,
-     * dp is dw at the kept indices and 0 elsewhere, dH = p (dp - <p, dp>) */
-    std::fill(dH.begin(), dH.end(), 0.0);
+        /* y_t = s sum_j w_j E_j: dw_j = s <dy_t, E_j>, dE_j = s w_j dy_t */
+        double d = 0.0;
+        for (int64_t o = 0; o < H; ++o) d += static_cast<double>(dy[t * H + o]) * E[o];
+        dwv[t * k + j] = c->out_scale * d;
+        for (int64_t o = 0; o < H; ++o) dE[o] = rnd(c->out_scale * w[t * k + j] * static_cast<double>(dy[t * H + o]));
+        /* down projection: dWdown_e += dE h^T, dh = Wdown_e^T dE */
+        for (int64_t o = 0; o < H; ++o)
+          for (int64_t f = 0; f < F; ++f) dWdown[wb + o * F + f] += dE[o] * hh[f];
+        for (int64_t f = 0; f < F; ++f) {
+          double acc = 0.0;
+          for (int64_t o = 0; o < H; ++o) acc += dE[o] * load_val(Wdown, c->w_dtype, wb + o * F + f);
+          dh[f] = acc;
+        }
+        /* h = SiLU(g) u: du = dh SiLU(g), dg = dh u SiLU'(g) with
+         * SiLU'(g) = sigma(g) (1 + g (1 - sigma(g))) */
+        for (int64_t f = 0; f < F; ++f) {
+          const double sg = 1.0 / (1.0 + std::exp(-g[f]));
+          du[f] = rnd(dh[f] * oracle_silu(g[f]));
+          dg[f] = rnd(dh[f] * u[f] * sg * (1.0 + g[f] * (1.0 - sg)));
+        }
+        /* gate and up projections: dW += d outer x; this row's dx share W^T d */
+        double* dxr = dxp.data() + (t * k + j) * H;
+        for (int64_t f = 0; f < F; ++f)
+          for (int64_t h = 0; h < H; ++h) {
+            dWgate[wb + f * H + h] += dg[f] * xd[h];
+            dWup[wb + f * H + h] += du[f] * xd[h];
+            dxr[h] += dg[f] * load_val(Wgate, c->w_dtype, wb + f * H + h) +
+                      du[f] * load_val(Wup, c->w_dtype, wb + f * H + h);
+          }
+      }
+  });
+
+  /* per token: the gate weights back to the scores and the router logits */
+  std::vector<double> dlog(T * N, 0.0), dnv(T * N, 0.0);
+  for_tokens(T, nthreads, [&](int64_t t) {
+    std::vector<double> dH(N, 0.0), p(N), dp(N, 0.0), xd(H);
+    const double* dw = dwv.data() + t * k;
+    /* [UP] section 3, G = Softmax(KeepTopK(H)). Mixtral: w = softmax over
+     * the kept k scores, dH_j = w_j (dw_j - sum w dw); ST ([UP] section 5):
+     * w_j = p_{idx_j}, p = softmax over all N scores, dp is dw at the kept
+     * indices and 0 elsewhere, dH = p (dp - <p, dp>) */
     const float* Hrow = Hv.data() + t * N;
     if (c->order == ORC_KEEPTOPK_SOFTMAX) {
       double sdot = 0.0;
@@ -494,7 +506,6 @@ int oracle_backward(const oracle_cfg* c, const void* x, const float* Wg, const f
       double den = 0.0;
       for (int64_t i = 0; i < N; ++i) den += (p[i] = std::exp(static_cast<double>(Hrow[i]) - hmax));
       for (int64_t i = 0; i < N; ++i) p[i] /= den;
-      std::vector<double> dp(N, 0.0);
       for (int64_t j = 0; j < k; ++j) dp[idx[t * k + j]] += dw[j];
       double sdot = 0.0;
       for (int64_t i = 0; i < N; ++i) sdot += p[i] * dp[i];
@@ -503,39 +514,50 @@ int oracle_backward(const oracle_cfg* c, const void* x, const float* Wg, const f
     /* balance = sum_i f_i P_i with P_i = mean over tokens of softmax(clean
      * logits) ([V2] gating section): d balance / d logit_t,m =
      * (1/T) p_m (f_m - <f, p>), p = softmax(logits_t) */
-    {
-      double m = -std::numeric_limits<double>::infinity();
-      for (int64_t i = 0; i < N; ++i) m = std::max(m, static_cast<double>(logits[t * N + i]));
-      double den = 0.0;
-      for (int64_t i = 0; i < N; ++i) den += (p[i] = std::exp(static_cast<double>(logits[t * N + i]) - m));
-      double fp = 0.0;
-      for (int64_t i = 0; i < N; ++i) {
-        p[i] /= den;
-        fp += (static_cast<double>(counts[i]) / static_cast<double>(T * k)) * p[i];
-      }
-      for (int64_t i = 0; i < N; ++i)
-        dlog[i] = dH[i] + d_balance / static_cast<double>(T) * p[i] *
-                              (static_cast<double>(counts[i]) / static_cast<double>(T * k) - fp);
+    double m = -std::numeric_limits<double>::infinity();
+    for (int64_t i = 0; i < N; ++i) m = std::max(m, static_cast<double>(logits[t * N + i]));
+    double den = 0.0;
+    for (int64_t i = 0; i < N; ++i) den += (p[i] = std::exp(static_cast<double>(logits[t * N + i]) - m));
+    double fp = 0.0;
+    for (int64_t i = 0; i < N; ++i) {
+      p[i] /= den;
+      fp += (static_cast<double>(counts[i]) / static_cast<double>(T * k)) * p[i];
     }
+    for (int64_t i = 0; i < N; ++i)
+      dlog[t * N + i] = dH[i] + d_balance / static_cast<double>(T) * p[i] *
+                                    (static_cast<double>(counts[i]) / static_cast<double>(T * k) - fp);
     /* H = logits + eps * Softplus(x W_noise): d/dn = dH eps sigmoid(n) */
+    for (int64_t h = 0; h < H; ++h) xd[h] = load_val(x, c->x_dtype, t * H + h);
     if (c->noisy) {
       for (int64_t i = 0; i < N; ++i) {
         double b = 0.0;
         for (int64_t h = 0; h < H; ++h) b += xd[h] * static_cast<double>(Wn[h * N + i]);
-        dn[i] = dH[i] * static_cast<double>(eps[t * N + i]) / (1.0 + std::exp(-b));
+        dnv[t * N + i] = dH[i] * static_cast<double>(eps[t * N + i]) / (1.0 + std::exp(-b));
       }
     }
-    /* logits = x W_g (and the noise logits x W_noise) */
-    for (int64_t h = 0; h < H; ++h)
+    /* dx: the slots' shares in slot order, then the router terms
+     * (logits = x W_g, noise logits = x W_noise) */
+    for (int64_t h = 0; h < H; ++h) {
+      double v = 0.0;
+      for (int64_t j = 0; j < k; ++j) v += dxp[(t * k + j) * H + h];
       for (int64_t i = 0; i < N; ++i) {
-        dWg[h * N + i] += xd[h] * dlog[i];
-        dx[t * H + h] += dlog[i] * static_cast<double>(Wg[h * N + i]);
-        if (c->noisy) {
-          dWn[h * N + i] += xd[h] * dn[i];
-          dx[t * H + h] += dn[i] * static_cast<double>(Wn[h * N + i]);
-        }
+        v += dlog[t * N + i] * static_cast<double>(Wg[h * N + i]);
+        if (c->noisy) v += dnv[t * N + i] * static_cast<double>(Wn[h * N + i]);
       }
-  }
+      dx[t * H + h] = v;
+    }
+  });
+  /* router weights: dWg = x^T dlog, dWn = x^T dn, each element over the
+   * tokens in order */
+  for_tokens(H, nthreads, [&](int64_t h) {
+    for (int64_t t = 0; t < T; ++t) {
+      const double xv = load_val(x, c->x_dtype, t * H + h);
+      for (int64_t i = 0; i < N; ++i) {
+        dWg[h * N + i] += xv * dlog[t * N + i];
+        if (c->noisy) dWn[h * N + i] += xv * dnv[t * N + i];
+      }
+    }
+  });
   return 0;
 }
 

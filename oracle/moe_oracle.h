@@ -140,10 +140,14 @@ int oracle_residual_combine_rows(const oracle_cfg* c, const double* topk_w, cons
  * h_round = ORC_H_BF16 the backward rounds to bf16 where the bf16 layer
  * feeds matrix cores: the expert-output gradient dE = s w dy and the SwiGLU
  * gradients dg, du; otherwise nothing is rounded (exact mode, for finite
- * differences). */
+ * differences). nthreads spreads the experts, then the tokens, then the rows of
+ * dWg over threads; every sum keeps a fixed order (an expert's rows in token
+ * order, a token's slots in slot order, the tokens in order), so the result
+ * does not depend on the thread count. */
 int oracle_backward(const oracle_cfg* c, const void* x, const float* Wg, const float* Wn, const float* eps,
                     const void* Wgate, const void* Wup, const void* Wdown, const float* dy, double d_balance,
-                    double* dx, double* dWg, double* dWn, double* dWgate, double* dWup, double* dWdown);
+                    int32_t nthreads, double* dx, double* dWg, double* dWn, double* dWgate, double* dWup,
+                    double* dWdown);
 
 /* Scalar pieces, exported so tests can pin them against library routines. */
 double oracle_round_bf16(double v);   /* round to nearest bf16, ties to even */

@@ -137,10 +137,13 @@ __global__ __launch_bounds__(256) void k_bwd_gate(BwdGateParams p) {
 
 // dx[t] = sum over kept slots of dx_perm[slot] (in slot order) + the router
 // terms sum_n dlog[t,n] W_g[:,n] (+ dnz[t,n] W_noise[:,n]). A block owns
-// kTokB tokens, so each router weight is read once per kTokB tokens.
-constexpr int kTokB = 8;
+// kTokB tokens, so each router weight row is read once per kTokB tokens; a
+// thread owns 4 consecutive h and reads their W_g rows as 16-byte vectors.
+constexpr int kTokB = 4;
 __global__ __launch_bounds__(256) void k_bwd_dx(BwdDxParams p) {
   __shared__ float s_dl[kTokB][64], s_dn[kTokB][64];
+  __shared__ int s_sl[kTokB][8];
+  static_assert(kTokB * 8 <= 256 && kTokB * 64 <= 1024, "one pass of the staging loops");
   const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kTokB;
   const int H = p.H, N = p.N, k = p.k;
   for (int i = threadIdx.x; i < kTokB * 64; i += 256) {
@@ -149,31 +152,51 @@ __global__ __launch_bounds__(256) void k_bwd_dx(BwdDxParams p) {
     s_dl[tt][n] = ok ? p.dlog[(t0 + tt) * N + n] : 0.0f;
     s_dn[tt][n] = (ok && p.noisy) ? p.dnz[(t0 + tt) * N + n] : 0.0f;
   }
+  for (int i = threadIdx.x; i < kTokB * 8; i += 256) {
+    const int tt = i / 8, j = i % 8;
+    s_sl[tt][j] = (t0 + tt < p.T && j < k) ? p.slot[(t0 + tt) * k + j] : -1;
+  }
   __syncthreads();
+  const bool vec = (N % 4) == 0;
   for (int c = threadIdx.x; c < H / 4; c += 256) {
     f32x4_t acc[kTokB];
 #pragma unroll
     for (int tt = 0; tt < kTokB; ++tt) {
       acc[tt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-      const int64_t t = t0 + tt;
-      if (t >= p.T) continue;
-      for (int j = 0; j < k; ++j) {
-        const int sl = p.slot[t * k + j];
-        if (sl < 0) continue;
-        acc[tt] += *reinterpret_cast<const f32x4_t*>(p.dx_perm + static_cast<int64_t>(sl) * H + c * 4);
+      if (t0 + tt >= p.T) continue;
+      if (k <= 8) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int sl = s_sl[tt][j];
+          if (sl >= 0) acc[tt] += *reinterpret_cast<const f32x4_t*>(p.dx_perm + static_cast<int64_t>(sl) * H + c * 4);
+        }
+      } else {
+        for (int j = 0; j < k; ++j) {
+          const int sl = p.slot[(t0 + tt) * k + j];
+          if (sl >= 0) acc[tt] += *reinterpret_cast<const f32x4_t*>(p.dx_perm + static_cast<int64_t>(sl) * H + c * 4);
+        }
       }
     }
-    for (int n = 0; n < N; ++n) {
-      f32x4_t wg, wn = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int q = 0; q < 4; ++q) wg[q] = p.Wg[static_cast<int64_t>(c * 4 + q) * N + n];
-      if (p.noisy)
+    for (int q = 0; q < 4; ++q) {
+      const int64_t h = c * 4 + q;
+      for (int n0 = 0; n0 < N; n0 += 4) {
+        f32x4_t wg = {0.0f, 0.0f, 0.0f, 0.0f}, wn = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (vec) {
+          wg = *reinterpret_cast<const f32x4_t*>(p.Wg + h * N + n0);
+          if (p.noisy) wn = *reinterpret_cast<const f32x4_t*>(p.Wn + h * N + n0);
+        } else {
+          for (int e = 0; e < 4 && n0 + e < N; ++e) {
+            wg[e] = p.Wg[h * N + n0 + e];
+            if (p.noisy) wn[e] = p.Wn[h * N + n0 + e];
+          }
+        }
 #pragma unroll
-        for (int q = 0; q < 4; ++q) wn[q] = p.Wn[static_cast<int64_t>(c * 4 + q) * N + n];
+        for (int tt = 0; tt < kTokB; ++tt)
 #pragma unroll
-      for (int tt = 0; tt < kTokB; ++tt)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) acc[tt][q] = fmaf(s_dl[tt][n], wg[q], fmaf(s_dn[tt][n], wn[q], acc[tt][q]));
+          for (int e = 0; e < 4; ++e)
+            acc[tt][q] = fmaf(s_dl[tt][n0 + e], wg[e], fmaf(s_dn[tt][n0 + e], wn[e], acc[tt][q]));
+      }
     }
 #pragma unroll
     for (int tt = 0; tt < kTokB; ++tt)
@@ -183,52 +206,115 @@ __global__ __launch_bounds__(256) void k_bwd_dx(BwdDxParams p) {
 
 // Router weight gradients dW_g = x^T dlog and dW_noise = x^T dnz, in two
 // passes for a fixed summation order: pass 1 sums a chunk of kTokW tokens per
-// block into partials [chunk][H][N] (thread = one h, all N), pass 2 adds the
-// chunks in order.
-constexpr int kTokW = 64;
-template <int NMAX, bool NOISY>
-__global__ __launch_bounds__(256) void k_router_wgrad(RouterWgradParams p) {
+// block into partials [chunk][H][N (+N)] (thread = HPT consecutive h with one
+// vector load of x per token, all N), pass 2 adds the chunks in order.
+constexpr int kTokW = 32;
+constexpr int kRwThreads = 128;
+template <int NMAX, bool NOISY, int HPT>
+__global__ __launch_bounds__(kRwThreads) void k_router_wgrad(RouterWgradParams p) {
   __shared__ float s_dl[kTokW][NMAX], s_dn[NOISY ? kTokW : 1][NMAX];
-  const int h = blockIdx.x * 256 + threadIdx.x;
+  const int h0 = (blockIdx.x * kRwThreads + threadIdx.x) * HPT;
   const int64_t t0 = static_cast<int64_t>(blockIdx.y) * kTokW;
   const int N = p.N;
-  for (int i = threadIdx.x; i < kTokW * NMAX; i += 256) {
+  for (int i = threadIdx.x; i < kTokW * NMAX; i += kRwThreads) {
     const int tt = i / NMAX, n = i % NMAX;
     const bool ok = t0 + tt < p.T && n < N;
     s_dl[tt][n] = ok ? p.dlog[(t0 + tt) * N + n] : 0.0f;
     if (NOISY) s_dn[tt][n] = ok ? p.dnz[(t0 + tt) * N + n] : 0.0f;
   }
   __syncthreads();
-  if (h >= p.H) return;
-  float a[NMAX], b[NOISY ? NMAX : 1];
+  if (h0 >= p.H) return;
+  float a[HPT][NMAX], b[HPT][NOISY ? NMAX : 1];
 #pragma unroll
-  for (int n = 0; n < NMAX; ++n) {
-    a[n] = 0.0f;
-    if (NOISY) b[n] = 0.0f;
-  }
-  for (int tt = 0; tt < kTokW && t0 + tt < p.T; ++tt) {
-    const float xv = bf16_to_f32(p.x[(t0 + tt) * p.H + h]);
+  for (int q = 0; q < HPT; ++q)
 #pragma unroll
     for (int n = 0; n < NMAX; ++n) {
-      a[n] = fmaf(xv, s_dl[tt][n], a[n]);
-      if (NOISY) b[n] = fmaf(xv, s_dn[tt][n], b[n]);
+      a[q][n] = 0.0f;
+      if (NOISY) b[q][n] = 0.0f;
+    }
+  const int tn = static_cast<int>(min(static_cast<int64_t>(kTokW), p.T - t0));
+  // x of the next kPre tokens is requested before their products, so the
+  // loads overlap instead of each waiting out a memory round trip
+  constexpr int kPre = 8;
+  for (int tb = 0; tb < tn; tb += kPre) {
+  uint16_t xraw[kPre][HPT];
+#pragma unroll
+  for (int u = 0; u < kPre; ++u) {
+    const int tt = min(tb + u, tn - 1);
+    const uint16_t* xr = p.x + (t0 + tt) * p.H + h0;
+    if constexpr (HPT == 8) {
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(xr);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        xraw[u][2 * q] = static_cast<uint16_t>(v[q]);
+        xraw[u][2 * q + 1] = static_cast<uint16_t>(v[q] >> 16);
+      }
+    } else if constexpr (HPT == 4) {
+      typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+      const u32x2_t v = *reinterpret_cast<const u32x2_t*>(xr);
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        xraw[u][2 * q] = static_cast<uint16_t>(v[q]);
+        xraw[u][2 * q + 1] = static_cast<uint16_t>(v[q] >> 16);
+      }
+    } else if constexpr (HPT == 2) {
+      const uint32_t v = *reinterpret_cast<const uint32_t*>(xr);
+      xraw[u][0] = static_cast<uint16_t>(v);
+      xraw[u][1] = static_cast<uint16_t>(v >> 16);
+    } else {
+      xraw[u][0] = xr[0];
     }
   }
-  float* out = p.part + (static_cast<int64_t>(blockIdx.y) * p.H + h) * N * (NOISY ? 2 : 1);
+  // every value is converted before any use that depends on the token count,
+  // so the compiler keeps the kPre loads issued together
+  float xv[kPre][HPT];
 #pragma unroll
-  for (int n = 0; n < NMAX; ++n)
-    if (n < N) {
-      out[n] = a[n];
-      if (NOISY) out[N + n] = b[n];
-    }
+  for (int u = 0; u < kPre; ++u)
+#pragma unroll
+    for (int q = 0; q < HPT; ++q) xv[u][q] = bf16_to_f32(xraw[u][q]);
+  const int cnt = min(kPre, tn - tb);
+#pragma unroll
+  for (int u = 0; u < kPre; ++u) {
+    const int tt = tb + u;
+    // a token past the chunk's end adds 0 (its slot of the staged gradients is 0)
+    const float live = u < cnt ? 1.0f : 0.0f;
+    const int ts = u < cnt ? tt : 0;
+#pragma unroll
+    for (int q = 0; q < HPT; ++q)
+#pragma unroll
+      for (int n = 0; n < NMAX; ++n) {
+        a[q][n] = fmaf(xv[u][q] * live, s_dl[ts][n], a[q][n]);
+        if (NOISY) b[q][n] = fmaf(xv[u][q] * live, s_dn[ts][n], b[q][n]);
+      }
+  }
+  }
+  const int per = N * (NOISY ? 2 : 1);
+#pragma unroll
+  for (int q = 0; q < HPT; ++q) {
+    float* out = p.part + (static_cast<int64_t>(blockIdx.y) * p.H + h0 + q) * per;
+#pragma unroll
+    for (int n = 0; n < NMAX; ++n)
+      if (n < N) {
+        out[n] = a[q][n];
+        if (NOISY) out[N + n] = b[q][n];
+      }
+  }
 }
 
 __global__ __launch_bounds__(256) void k_router_wgrad_sum(RouterWgradParams p, int chunks) {
   const int per = p.N * (p.noisy ? 2 : 1);
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (i >= static_cast<int64_t>(p.H) * per) return;
+  // the chunks in order, eight loads in flight at a time
   float v = 0.0f;
-  for (int c = 0; c < chunks; ++c) v += p.part[static_cast<int64_t>(c) * p.H * per + i];
+  for (int c0 = 0; c0 < chunks; c0 += 8) {
+    float u[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) u[q] = c0 + q < chunks ? p.part[static_cast<int64_t>(c0 + q) * p.H * per + i] : 0.0f;
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      if (c0 + q < chunks) v += u[q];
+  }
   const int64_t h = i / per, n = i % per;
   if (n < p.N) p.dWg[h * p.N + n] = v;
   else p.dWn[h * p.N + (n - p.N)] = v;
@@ -259,7 +345,7 @@ __global__ __launch_bounds__(64) void k_pad_offsets(const int32_t* __restrict__ 
 // offsets[e] + (P - pad[e]), zero past its rows; with row_map the source row
 // is row_map[that row] (a gather of x by row_token).
 __global__ __launch_bounds__(256) void k_transpose(TransposeParams p) {
-  __shared__ uint16_t tile[64][66];
+  __shared__ uint16_t tile[64][66];  // a row stride of 33 dwords: the column reads hit distinct banks
   const int c0 = blockIdx.x * 64;   // source column (destination row) block
   int64_t r0 = static_cast<int64_t>(blockIdx.y) * 64;
   const uint16_t* src = p.src + blockIdx.z * p.src_batch;
@@ -339,17 +425,23 @@ int router_wgrad_chunks(int64_t T) { return static_cast<int>((T + kTokW - 1) / k
 
 hipError_t launch_router_wgrad(const RouterWgradParams& p, hipStream_t s) {
   if (p.T <= 0) return hipSuccess;
-  const dim3 grid((p.H + 255) / 256, router_wgrad_chunks(p.T));
-#define MOE_RW(NM)                                                                   \
-  do {                                                                               \
-    if (p.noisy) hipLaunchKernelGGL((k_router_wgrad<NM, true>), grid, dim3(256), 0, s, p); \
-    else hipLaunchKernelGGL((k_router_wgrad<NM, false>), grid, dim3(256), 0, s, p);  \
-  } while (0)
-  if (p.N <= 8) MOE_RW(8);
-  else if (p.N <= 16) MOE_RW(16);
-  else if (p.N <= 32) MOE_RW(32);
-  else MOE_RW(64);
+  // h per thread: as many as keep the accumulators within 128 registers
+  // (H % 8 == 0, so every width divides H)
+  const int per = (p.N <= 8 ? 8 : p.N <= 16 ? 16 : p.N <= 32 ? 32 : 64) * (p.noisy ? 2 : 1);
+  const int hpt = per <= 16 ? 8 : per <= 32 ? 4 : per <= 64 ? 2 : 1;
+  const dim3 grid((p.H / hpt + kRwThreads - 1) / kRwThreads, router_wgrad_chunks(p.T));
+#define MOE_RW(NM, NZ, HP) hipLaunchKernelGGL((k_router_wgrad<NM, NZ, HP>), grid, dim3(kRwThreads), 0, s, p)
+  if (p.N <= 8) {
+    if (p.noisy) MOE_RW(8, true, 8); else MOE_RW(8, false, 8);
+  } else if (p.N <= 16) {
+    if (p.noisy) MOE_RW(16, true, 4); else MOE_RW(16, false, 8);
+  } else if (p.N <= 32) {
+    if (p.noisy) MOE_RW(32, true, 2); else MOE_RW(32, false, 4);
+  } else {
+    if (p.noisy) MOE_RW(64, true, 1); else MOE_RW(64, false, 2);
+  }
 #undef MOE_RW
+  (void)hpt;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t n = static_cast<int64_t>(p.H) * p.N * (p.noisy ? 2 : 1);

@@ -248,8 +248,8 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, const TilePos& tp,
           const float dg = dh * u * (sg * (1.0f + g * (1.0f - sg)));
           const float du = dh * (g * sg);
           const uint32_t co = fv ? row * ld + static_cast<uint32_t>(f) * 2u : kStoreOOB;
-          __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(dg), rc, co, 0, 0);
-          __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(du), rc, co + uoff_c, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(dg), rc, co, 0, kHStorePolicy);
+          __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(du), rc, co + uoff_c, 0, kHStorePolicy);
         }
       }
     return;
@@ -778,7 +778,10 @@ __device__ __forceinline__ bool wait_count(int32_t* ctr, int target, int32_t* er
   return true;
 }
 
-template <int BM, int BN, int WGM, int WGN, int STAGES, int BK, bool GATHER>
+// G1_SWIGLU: g1 is the gate/up GEMM with the SwiGLU epilogue (the forward);
+// otherwise g1 is a plain GEMM whose epilogue is g1.epi (the backward's dh
+// with the SwiGLU derivative), and g2 reads its output the same way.
+template <int BM, int BN, int WGM, int WGN, int STAGES, int BK, bool GATHER, bool G1_SWIGLU>
 __global__ __launch_bounds__(WGM * WGN * 64) void k_experts_fused(FusedParams fp) {
   constexpr int kElems = dma_lds_elems<BM, BN, STAGES, BK>();
   // the operand stages and, after them, the broadcast work item: one LDS object
@@ -802,7 +805,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_experts_fused(FusedParams fp
     if (lane >= d) incl += v;
   }
   const int RB = __builtin_amdgcn_readfirstlane(__shfl(incl, 63, 64));
-  const int NT1 = (g1.Nout + BN / 2 - 1) / (BN / 2);
+  const int NT1 = G1_SWIGLU ? (g1.Nout + BN / 2 - 1) / (BN / 2) : (g1.Nout + BN - 1) / BN;
   const int NT2 = (g2.Nout + BN - 1) / BN;
   const int n1 = RB * NT1, ntot = RB * (NT1 + NT2);
   const int G = gridDim.x;
@@ -871,7 +874,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_experts_fused(FusedParams fp
         TilePos tq;
         int rq;
         if (decode(next, tq, rq)) {
-          TileLoader<BM, BN, WGM, WGN, BK, true, GATHER> lq;
+          TileLoader<BM, BN, WGM, WGN, BK, G1_SWIGLU, GATHER> lq;
           lq.init(g1, tq);
           lq.issue_a(a_free, 0);
           lq.issue_b(b_free, 0);
@@ -888,7 +891,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_experts_fused(FusedParams fp
     TilePos tp;
     int rb;
     if (decode(ticket, tp, rb)) {
-      gemm_tile<BM, BN, WGM, WGN, STAGES, BK, true, GATHER>(g1, tp, smem, sbase, pre, hook, reserve);
+      gemm_tile<BM, BN, WGM, WGN, STAGES, BK, G1_SWIGLU, GATHER>(g1, tp, smem, sbase, pre, hook, reserve);
       // publish: every wave waits until its device-scope h stores have
       // completed (the wait also covers the next tile's first loads, issued
       // before the epilogue and needed next anyway), then one count. No L2
@@ -920,27 +923,30 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_experts_fused(FusedParams fp
   if (fp.stats && ticket == ntot) stats_reduce(fp.st, smem);
 }
 
-// ---- backward GEMMs: one tile per workgroup ----------------------------------------
+// ---- backward: weight gradients ------------------------------------------------------
 
-template <bool GATHER>
-__global__ __launch_bounds__(512) void k_gemm_tiles(GemmParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[dma_lds_elems<256, 256, 2, 64>()];
-  TilePos tp;
-  if (!decode_tile<256, 256, 64>(p, tp)) return;
-  gemm_tile<256, 256, 4, 2, 2, 64, false, GATHER>(p, tp, smem);
-}
-
-// Per-expert weight gradients: tile (e, mt, nt) sums A[mt rows, seg_e] .
-// B[nt rows, seg_e]^T over expert e's padded column segment seg_e and stores
-// the e-th [M, Nout] block of C. Tiles of one expert run together, four row
-// tiles at a time with the column tile fastest, so they share operand panels.
-__global__ __launch_bounds__(512) void k_gemm_wgrad(GemmParams p, const int32_t* __restrict__ pad_offsets, int M) {
+// Per-expert weight gradients: tile (e, mt, nt) of GEMM g sums A[mt rows,
+// seg_e] . B[nt rows, seg_e]^T over expert e's padded column segment seg_e
+// and stores the e-th [M, Nout] block of C. One launch runs the tiles of up to
+// three such GEMMs one after the other; within a GEMM the tiles of one expert
+// run together, four row tiles at a time with the column tile fastest, so
+// they share operand panels.
+__global__ __launch_bounds__(512) void k_gemm_wgrad(WgradParams wp) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[dma_lds_elems<256, 256, 2, 64>()];
   constexpr int GM = 4;
+  int L = xcd_remap(blockIdx.x, gridDim.x);
+  // which GEMM (uniform selects on the kernel arguments, no dynamic indexing)
+  auto tiles = [&](int i) {
+    return ((wp.M[i] + 255) / 256) * ((wp.g[i].Nout + 255) / 256) * wp.g[i].N;
+  };
+  const int n0 = tiles(0), n1 = wp.count > 1 ? tiles(1) : 0, n2 = wp.count > 2 ? tiles(2) : 0;
+  if (L >= n0 + n1 + n2) return;
+  const int gi = L < n0 ? 0 : (L < n0 + n1 ? 1 : 2);
+  L -= gi == 0 ? 0 : (gi == 1 ? n0 : n0 + n1);
+  const GemmParams p = gi == 0 ? wp.g[0] : (gi == 1 ? wp.g[1] : wp.g[2]);
+  const int M = gi == 0 ? wp.M[0] : (gi == 1 ? wp.M[1] : wp.M[2]);
   const int mtn = (M + 255) / 256, ntn = (p.Nout + 255) / 256;
   const int per_e = mtn * ntn;
-  const int L = xcd_remap(blockIdx.x, gridDim.x);
-  if (L >= per_e * p.N) return;
   const int e = L / per_e;
   const int q = L - e * per_e;
   const int g = q / (GM * ntn);
@@ -953,8 +959,8 @@ __global__ __launch_bounds__(512) void k_gemm_wgrad(GemmParams p, const int32_t*
   tp.ti.row0 = __builtin_amdgcn_readfirstlane(mt * 256);
   tp.ti.rows = __builtin_amdgcn_readfirstlane(min(256, M - mt * 256));
   tp.split = __builtin_amdgcn_readfirstlane(e);
-  tp.kb0 = __builtin_amdgcn_readfirstlane(pad_offsets[e]);
-  tp.kb1 = __builtin_amdgcn_readfirstlane(max(tp.kb0, pad_offsets[e + 1]));
+  tp.kb0 = __builtin_amdgcn_readfirstlane(wp.pad[e]);
+  tp.kb1 = __builtin_amdgcn_readfirstlane(max(tp.kb0, wp.pad[e + 1]));
   tp.KT = (tp.kb1 - tp.kb0) / 64;
   gemm_tile<256, 256, 4, 2, 2, 64, false, false>(p, tp, smem);
 }
@@ -1015,26 +1021,31 @@ hipError_t launch_experts_fused(const FusedParams& fp, hipStream_t s) {
   // one resident workgroup per compute unit (the LDS stages fill most of a CU)
   const dim3 grid(static_cast<unsigned>(cus > 0 ? cus : 256)), block(4 * 2 * 64);
   if (fp.g1.row_token)
-    hipLaunchKernelGGL((k_experts_fused<kFusedBM, kFusedBN, 4, 2, 2, 64, true>), grid, block, 0, s, fp);
+    hipLaunchKernelGGL((k_experts_fused<kFusedBM, kFusedBN, 4, 2, 2, 64, true, true>), grid, block, 0, s, fp);
   else
-    hipLaunchKernelGGL((k_experts_fused<kFusedBM, kFusedBN, 4, 2, 2, 64, false>), grid, block, 0, s, fp);
+    hipLaunchKernelGGL((k_experts_fused<kFusedBM, kFusedBN, 4, 2, 2, 64, false, true>), grid, block, 0, s, fp);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dgrad_fused(const FusedParams& fp, hipStream_t s) {
+  if (fp.g1.rows_max <= 0) return hipSuccess;
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  const dim3 grid(static_cast<unsigned>(cus > 0 ? cus : 256)), block(4 * 2 * 64);
+  hipLaunchKernelGGL((k_experts_fused<kFusedBM, kFusedBN, 4, 2, 2, 64, false, false>), grid, block, 0, s, fp);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_decode(const GemmParams& p, hipStream_t s) { return launch_decode<kDecBM, 128, 3, 4>(p, s); }
 
-hipError_t launch_gemm_tiles(const GemmParams& p, hipStream_t s) {
-  const int64_t blocks = grid_blocks(p, 256, 256);
+hipError_t launch_gemm_wgrad(const WgradParams& wp, hipStream_t s) {
+  int64_t blocks = 0;
+  for (int i = 0; i < wp.count; ++i)
+    blocks += static_cast<int64_t>((wp.M[i] + 255) / 256) * ((wp.g[i].Nout + 255) / 256) * wp.g[i].N;
   if (blocks <= 0) return hipSuccess;
-  if (p.row_token) hipLaunchKernelGGL(k_gemm_tiles<true>, dim3(static_cast<unsigned>(blocks)), dim3(512), 0, s, p);
-  else hipLaunchKernelGGL(k_gemm_tiles<false>, dim3(static_cast<unsigned>(blocks)), dim3(512), 0, s, p);
-  return hipGetLastError();
-}
-
-hipError_t launch_gemm_wgrad(const GemmParams& p, const int32_t* pad_offsets, int M, hipStream_t s) {
-  const int64_t blocks = static_cast<int64_t>((M + 255) / 256) * ((p.Nout + 255) / 256) * p.N;
-  if (blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_gemm_wgrad, dim3(static_cast<unsigned>(blocks)), dim3(512), 0, s, p, pad_offsets, M);
+  hipLaunchKernelGGL(k_gemm_wgrad, dim3(static_cast<unsigned>(blocks)), dim3(512), 0, s, wp);
   return hipGetLastError();
 }
 

@@ -127,14 +127,18 @@ bool gemm_decode_shape(int64_t rows_max, int N);
 void gemm_decode_tile(int* bm, int* bn);
 hipError_t launch_gemm_simple(const GemmParams& p, int bf16, hipStream_t s);
 
-// Backward GEMMs on the same 256 x 256 tile, one tile per workgroup:
-// grouped by expert rows as in the forward (dgrad: dh = dE . Wdown^T-copy,
-// dx = dgu . [Wgate; Wup]^T-copy), or per expert with K over the expert's
-// padded row segment (wgrad: C_e = A[:, seg_e] . B[:, seg_e]^T into the
-// e-th [M, Nout] block of C, c_split_stride = M * Nout). pad_offsets[N+1]:
+// The backward's weight gradients on the same 256 x 256 tile, one tile per
+// workgroup: per expert with K over the expert's padded row segment,
+// C_e = A[:, seg_e] . B[:, seg_e]^T into the e-th [M, Nout] block of C
+// (c_split_stride = M * Nout), for up to three GEMMs in one launch. pad[N+1]:
 // the padded segments, multiples of 64 columns.
-hipError_t launch_gemm_tiles(const GemmParams& p, hipStream_t s);
-hipError_t launch_gemm_wgrad(const GemmParams& p, const int32_t* pad_offsets, int M, hipStream_t s);
+struct WgradParams {
+  GemmParams g[3];
+  int M[3];
+  int count;
+  const int32_t* pad;  // [N+1]
+};
+hipError_t launch_gemm_wgrad(const WgradParams& wp, hipStream_t s);
 
 // Both expert GEMMs in one persistent launch: g1 is the gate/up GEMM with the
 // SwiGLU epilogue (writing h), g2 the down projection reading h (no K split).
@@ -156,6 +160,9 @@ int fused_error_index();
 int fused_sched_ints(int64_t rows_max, int N);
 bool gemm_fused_supported(int64_t rows_max, int N, int K1, int F);
 hipError_t launch_experts_fused(const FusedParams& fp, hipStream_t s);
+// The backward's dgrad pair in the same persistent kernel: g1 = dh with the
+// SwiGLU-derivative epilogue (epi 1, writing dg|du), g2 = dx reading dg|du.
+hipError_t launch_bwd_dgrad_fused(const FusedParams& fp, hipStream_t s);
 
 // ---- combine (combine.hip) --------------------------------------------------
 struct CombineParams {

@@ -757,13 +757,8 @@ moe_status moe_backward(const moe_cfg* c, const void* x, const float* Wg, const 
   gd.a_rows = A;
   gd.gu = at<float>(ws, t.gu);
   gd.epi = 1;
-  MOE_LAUNCH(MOE_KERNEL_BWD_DGRAD, s, moe::launch_gemm_tiles(gd, s));
-  {
-    ProfScope ps_(MOE_KERNEL_BWD_TRANSPOSE, s);
-    e = tr(dgu, 2 * F, 0, nullptr, dgut, t.A_pad, 0, 0, A, 2 * F, true, 1);
-  }
-  if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "transpose launch failed: %s", hipGetErrorString(e));
-  // dx_perm = dg . Wgate_e + du . Wup_e
+  // dx_perm = dg . Wgate_e + du . Wup_e: in the same persistent launch, each
+  // row block's dx tiles after its dh tiles
   moe::GemmParams gx{};
   gx.A = dgu;
   gx.lda = 2 * F;
@@ -779,13 +774,33 @@ moe_status moe_backward(const moe_cfg* c, const void* x, const float* Wg, const 
   gx.splits = 1;
   gx.rows_max = A;
   gx.a_rows = A;
-  MOE_LAUNCH(MOE_KERNEL_BWD_DGRAD, s, moe::launch_gemm_tiles(gx, s));
+  {
+    int32_t* sched = at<int32_t>(ws, L.sched);
+    e = moe::launch_fill_i32(sched, moe::fused_sched_ints(L.A_max, c->N), 0, s);
+    if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "fill launch failed: %s", hipGetErrorString(e));
+    int spin = moe::kDefaultSpinLimit, extra = 0;
+    {
+      std::lock_guard<std::mutex> lk(g_wait_mu);
+      if (g_wait_spin > 0) spin = g_wait_spin;
+      extra = g_wait_extra;
+    }
+    const moe::FusedParams fp{gd, gx, sched, moe::StatsParams{}, 0, spin, extra};
+    MOE_LAUNCH(MOE_KERNEL_BWD_DGRAD, s, moe::launch_bwd_dgrad_fused(fp, s));
+  }
+  {
+    ProfScope ps_(MOE_KERNEL_BWD_TRANSPOSE, s);
+    e = tr(dgu, 2 * F, 0, nullptr, dgut, t.A_pad, 0, 0, A, 2 * F, true, 1);
+  }
+  if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "transpose launch failed: %s", hipGetErrorString(e));
   // dx = sum of the slots' rows + the router terms
   moe::BwdDxParams dp{T, c->H, c->N, c->k, c->noisy, at<float>(ws, t.dxp), at<int32_t>(ws, L.slot), dlog, dnz, Wg,
                       Wn, dx};
   MOE_LAUNCH(MOE_KERNEL_BWD_DX, s, moe::launch_bwd_dx(dp, s));
   // weight gradients per expert, K over the expert's padded rows
-  moe::GemmParams gw{};
+  moe::WgradParams wp{};
+  wp.pad = pad;
+  wp.count = 3;
+  moe::GemmParams& gw = wp.g[0];
   gw.N = c->N;
   gw.splits = 1;
   gw.b_expert_stride = 0;
@@ -799,18 +814,30 @@ moe_status moe_backward(const moe_cfg* c, const void* x, const float* Wg, const 
   gw.C = dWdown;
   gw.ldc = F;
   gw.c_split_stride = H * F;
-  MOE_LAUNCH(MOE_KERNEL_BWD_WGRAD, s, moe::launch_gemm_wgrad(gw, pad, c->H, s));
-  gw.A = dgut;
-  gw.a_rows = F;
-  gw.B0 = xt;
-  gw.Nout = c->H;
-  gw.C = dWgate;
-  gw.ldc = H;
-  gw.c_split_stride = F * H;
-  MOE_LAUNCH(MOE_KERNEL_BWD_WGRAD, s, moe::launch_gemm_wgrad(gw, pad, c->F, s));
-  gw.A = dgut + F * t.A_pad;
-  gw.C = dWup;
-  MOE_LAUNCH(MOE_KERNEL_BWD_WGRAD, s, moe::launch_gemm_wgrad(gw, pad, c->F, s));
+  wp.M[0] = c->H;
+  wp.g[1] = gw;
+  wp.g[1].A = dgut;
+  wp.g[1].a_rows = F;
+  wp.g[1].B0 = xt;
+  wp.g[1].Nout = c->H;
+  wp.g[1].C = dWgate;
+  wp.g[1].ldc = H;
+  wp.g[1].c_split_stride = F * H;
+  wp.M[1] = c->F;
+  wp.g[2] = wp.g[1];
+  wp.g[2].A = dgut + F * t.A_pad;
+  wp.g[2].C = dWup;
+  wp.M[2] = c->F;
+  // one launch per gradient: each grid's XCD-aware order keeps an expert's
+  // tiles of one GEMM together (one launch for all three measured 6% slower)
+  for (int i = 0; i < 3; ++i) {
+    moe::WgradParams one{};
+    one.g[0] = wp.g[i];
+    one.M[0] = wp.M[i];
+    one.count = 1;
+    one.pad = pad;
+    MOE_LAUNCH(MOE_KERNEL_BWD_WGRAD, s, moe::launch_gemm_wgrad(one, s));
+  }
   // router weights
   moe::RouterWgradParams rw{T, c->H, c->N, c->noisy, static_cast<const uint16_t*>(x), dlog, dnz,
                             at<float>(ws, t.rwp), dWg, dWn_opt};

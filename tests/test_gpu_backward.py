@@ -126,3 +126,21 @@ def test_backward_is_deterministic():
     b = run_train(w, dy, 0.1, d=d)
     for key in a:
         assert np.array_equal(a[key], b[key]), key
+
+
+@pytest.mark.timeout(900)
+def test_full_C2_backward():
+    """The LLaMA-MoE-3.5B (2/8) layer's backward at full size (4096 tokens,
+    hidden 4096, 8 experts of 1376, top-2, s = 4), every element of every
+    gradient against the oracle run on this host's threads."""
+    from gpu_util import oracle_threads
+    w = synth.c2()
+    ora = oracle.route(w)
+    assert np.all(ora["min_gap"] > 1e-6), "a near tie would make the comparison ill-posed"
+    dy = synth.normal_f32(w.meta["seed"], 40, (w.T, w.H), 1.0)
+    d_bal = 0.01
+    g = run_train(w, dy, d_bal)
+    log(f"[backward] C2 oracle on {oracle_threads()} threads")
+    ref = oracle.backward(w, dy, d_bal, nthreads=oracle_threads())
+    for key in ("dx", "dWg", "dWgate", "dWup", "dWdown"):
+        assert_grad(g[key], ref[key], f"C2 {key}")

@@ -125,3 +125,16 @@ def test_B4_bf16_mode_rounds_only_the_operands():
             continue
         err = np.linalg.norm(a[key] - b[key]) / np.linalg.norm(b[key])
         assert 1e-5 < err < 2e-2, (key, err)
+
+
+def test_B5_thread_count_does_not_change_a_bit():
+    """Every sum in the backward keeps a fixed order (an expert's rows in
+    token order, a token's slots in slot order, tokens in order), so the
+    threaded run gives the single-threaded run's bits."""
+    w = synth.make_independent("bwd_thr", 96, 60, 64, 32, 6, 2, noisy=True, order=synth.ST, capacity=18,
+                               out_scale=3.0)
+    dy = synth.normal_f32(96, 30, (w.T, w.H), 1.0)
+    a = oracle.backward(w, dy, 0.2, nthreads=1)
+    b = oracle.backward(w, dy, 0.2, nthreads=5)
+    for key in a:
+        assert np.array_equal(a[key], b[key]), key

@@ -10,6 +10,7 @@ import os
 import shutil
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 import pytest
 
@@ -84,16 +85,16 @@ MUTANTS = [
      "for (int64_t i = 0; i < N; ++i) dH[i] = dp[i] - sdot;"),
     ("bwd_balance_sign", "(static_cast<double>(counts[i]) / static_cast<double>(T * k) - fp);",
      "(fp - static_cast<double>(counts[i]) / static_cast<double>(T * k));"),
-    ("bwd_noise_softplus_not_sigmoid", "dn[i] = dH[i] * static_cast<double>(eps[t * N + i]) / (1.0 + std::exp(-b));",
-     "dn[i] = dH[i] * static_cast<double>(eps[t * N + i]) * oracle_softplus(b);"),
+    ("bwd_noise_softplus_not_sigmoid", "dnv[t * N + i] = dH[i] * static_cast<double>(eps[t * N + i]) / (1.0 + std::exp(-b));",
+     "dnv[t * N + i] = dH[i] * static_cast<double>(eps[t * N + i]) * oracle_softplus(b);"),
     ("bwd_dE_drops_scale", "dE[o] = rnd(c->out_scale * w[t * k + j] * static_cast<double>(dy[t * H + o]));",
      "dE[o] = rnd(w[t * k + j] * static_cast<double>(dy[t * H + o]));"),
-    ("bwd_dw_drops_scale", "dw[j] = c->out_scale * d;", "dw[j] = d;"),
+    ("bwd_dw_drops_scale", "dwv[t * k + j] = c->out_scale * d;", "dwv[t * k + j] = d;"),
     ("bwd_dWdown_transposed", "for (int64_t f = 0; f < F; ++f) dWdown[wb + o * F + f] += dE[o] * hh[f];",
      "for (int64_t f = 0; f < F; ++f) dWdown[wb + f * H + o] += dE[o] * hh[f];"),
-    ("bwd_dropped_slot_gets_gradient", "      if (slot[t * k + j] < 0) continue;  /* a dropped slot adds nothing to y: no gradient */",
-     "      /* mistake: dropped slots handled like kept ones */"),
-    ("bwd_dx_misses_router_term", "        dx[t * H + h] += dlog[i] * static_cast<double>(Wg[h * N + i]);",
+    ("bwd_dropped_slot_gets_gradient", "if (idx[t * k + j] != e || slot[t * k + j] < 0) continue;",
+     "if (idx[t * k + j] != e) continue;"),
+    ("bwd_dx_misses_router_term", "        v += dlog[t * N + i] * static_cast<double>(Wg[h * N + i]);",
      "        (void)0;"),
     ("nan_score_not_ranked_last",
      "if (std::isnan(hv)) hv = -std::numeric_limits<double>::infinity();", "(void)0;"),
@@ -103,20 +104,44 @@ PIN_FILES = ["tests/test_golden.py", "tests/test_oracle_pins.py", "tests/test_or
              "tests/test_oracle_brute.py", "tests/test_oracle_backward.py"]
 
 
-@pytest.mark.parametrize("name,orig,bad", MUTANTS, ids=[m[0] for m in MUTANTS])
-def test_pins_catch_planted_mistake(name, orig, bad, tmp_path):
+def _run_mutant(name, orig, bad, work):
+    """Build the oracle with one planted mistake and run every pin against it
+    in a subprocess; returns (returncode, output tail)."""
     src = open(SRC).read()
-    assert src.count(orig) >= 1, f"mutation anchor for {name} not found"
-    d = tmp_path / "oracle_src"
-    d.mkdir()
+    if src.count(orig) < 1:
+        return None, f"mutation anchor for {name} not found"
+    d = os.path.join(work, name)
+    os.makedirs(d, exist_ok=True)
     for f in ("moe_oracle.h", "brute.cpp"):
-        shutil.copy(os.path.join(ROOT, "oracle", f), d / f)
-    (d / "moe_oracle.cpp").write_text(src.replace(orig, bad, 1))
-    sys.path.insert(0, ROOT)
+        shutil.copy(os.path.join(ROOT, "oracle", f), os.path.join(d, f))
+    with open(os.path.join(d, "moe_oracle.cpp"), "w") as fh:
+        fh.write(src.replace(orig, bad, 1))
     from oracle import build as ob
-    so = str(tmp_path / "liboracle_mut.so")
-    ob.build(out=so, sources_dir=str(d))
-    env = dict(os.environ, MOE_ORACLE_LIB=so)
+    so = os.path.join(d, "liboracle_mut.so")
+    ob.build(out=so, sources_dir=d)
+    env = dict(os.environ, MOE_ORACLE_LIB=so, OMP_NUM_THREADS="1")
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider", *PIN_FILES],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
-    assert r.returncode != 0, f"planted mistake '{name}' survived every pin:\n{r.stdout[-2000:]}"
+    return r.returncode, r.stdout[-2000:]
+
+
+@pytest.fixture(scope="module")
+def mutant_results(request, tmp_path_factory):
+    """Run the selected mutants' pin suites in parallel subprocesses (each is
+    single-threaded), once per session."""
+    wanted = {item.callspec.params["name"] for item in request.session.items
+              if item.originalname == "test_pins_catch_planted_mistake"}
+    sys.path.insert(0, ROOT)
+    work = str(tmp_path_factory.mktemp("mutants"))
+    jobs = [m for m in MUTANTS if m[0] in wanted]
+    workers = max(1, min(8, os.cpu_count() or 1))
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        futs = {m[0]: ex.submit(_run_mutant, m[0], m[1], m[2], work) for m in jobs}
+        return {name: f.result() for name, f in futs.items()}
+
+
+@pytest.mark.parametrize("name,orig,bad", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_planted_mistake(name, orig, bad, mutant_results):
+    rc, tail = mutant_results[name]
+    assert rc is not None, tail
+    assert rc != 0, f"planted mistake '{name}' survived every pin:\n{tail}"
