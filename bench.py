@@ -53,7 +53,7 @@ def parse_args():
 
 
 def counters_traffic():
-    """HBM bytes per GEMM1 launch from the committed rocprofv3 counter summary,
+    """HBM bytes per launch of the fused expert kernel from the committed rocprofv3 counter summary,
     or None if there is none or the kernel source changed since it was taken."""
     if not os.path.exists(COUNTERS_FILE):
         return None
