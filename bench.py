@@ -299,7 +299,7 @@ def main():
                  abi.MOE_KERNEL_SCATTER: "permute_scatter", abi.MOE_KERNEL_GEMM1: "gemm1_gate_up_swiglu",
                  abi.MOE_KERNEL_GEMM2: "gemm2_down", abi.MOE_KERNEL_EXPERTS: "experts_fused",
                  abi.MOE_KERNEL_COMBINE: "combine", abi.MOE_KERNEL_BWD_GATE: "bwd_gate",
-                 abi.MOE_KERNEL_BWD_TRANSPOSE: "bwd_transposes", abi.MOE_KERNEL_BWD_DGRAD: "bwd_dgrad",
+                 abi.MOE_KERNEL_BWD_DGRAD: "bwd_dgrad",
                  abi.MOE_KERNEL_BWD_DX: "bwd_dx", abi.MOE_KERNEL_BWD_WGRAD: "bwd_wgrad",
                  abi.MOE_KERNEL_BWD_ROUTER: "bwd_router_wgrad"}
         for kid, name in names.items():

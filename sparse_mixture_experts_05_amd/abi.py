@@ -22,8 +22,7 @@ MOE_F32, MOE_BF16 = 0, 1
 MOE_TOPK_THEN_SOFTMAX, MOE_SOFTMAX_THEN_TOPK = 0, 1
 (MOE_KERNEL_ROUTER, MOE_KERNEL_HIST, MOE_KERNEL_SCATTER, MOE_KERNEL_GATHER, MOE_KERNEL_GEMM1,
  MOE_KERNEL_GEMM2, MOE_KERNEL_COMBINE, MOE_KERNEL_STATS, MOE_KERNEL_EXPERTS, MOE_KERNEL_BWD_GATE,
- MOE_KERNEL_BWD_TRANSPOSE, MOE_KERNEL_BWD_DGRAD, MOE_KERNEL_BWD_DX, MOE_KERNEL_BWD_WGRAD,
- MOE_KERNEL_BWD_ROUTER) = range(15)
+ MOE_KERNEL_BWD_DGRAD, MOE_KERNEL_BWD_DX, MOE_KERNEL_BWD_WGRAD, MOE_KERNEL_BWD_ROUTER) = range(14)
 
 EXPORTED = ["moe_capacity", "moe_check", "moe_workspace_bytes", "moe_route", "moe_permute",
             "moe_grouped_swiglu", "moe_combine", "moe_forward", "moe_status_str", "moe_last_error",

@@ -7,10 +7,9 @@
 //
 // The kernels here move and reduce data; the four expert GEMMs of the
 // backward (dh = dE Wdown, dx = dg Wgate + du Wup, and the weight gradients)
-// run on the matrix-core tiles of gemm_mfma.hip, whose operands must be
-// K-contiguous: k_transpose writes the transposed copies they need, with each
-// expert's rows padded to a multiple of 64 columns for the weight gradients
-// (whose K runs over an expert's rows).
+// run on the matrix-core tiles of gemm_mfma.hip, which read the operands whose
+// rows are K rows (the weights, and every operand of the weight gradients) in
+// place, through gfx950's transposing LDS reads.
 #include "common.h"
 #include "kernels.h"
 
@@ -320,93 +319,6 @@ __global__ __launch_bounds__(256) void k_router_wgrad_sum(RouterWgradParams p, i
   else p.dWn[h * p.N + (n - p.N)] = v;
 }
 
-// Padded row segments for the weight gradients: pad[e] = sum over e' < e of
-// the expert's rows rounded up to 64 (rows clamped to [0, rows_max)).
-__global__ __launch_bounds__(64) void k_pad_offsets(const int32_t* __restrict__ offsets, int N, int rows_max,
-                                                    int32_t* __restrict__ pad) {
-  const int lane = threadIdx.x;
-  int off = 0, cnt = 0;
-  if (lane < N) expert_segment(offsets, lane, rows_max, off, cnt);
-  const int v = (cnt + 63) / 64 * 64;
-  int incl = v;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int u = __shfl_up(incl, d, 64);
-    if (lane >= d) incl += u;
-  }
-  if (lane == 0) pad[0] = 0;
-  if (lane < N) pad[lane + 1] = incl;
-}
-
-// bf16 transpose through LDS, 64 x 64 per block: dst[c][col(r)] = src[row(r)][c].
-// Plain mode (pad == null): blockIdx.z is a batch; col(r) = dst_col0 + r.
-// Padded mode: the block's 64 output columns lie in one expert's padded
-// segment [pad[e], pad[e+1]); column P maps to the expert's row
-// offsets[e] + (P - pad[e]), zero past its rows; with row_map the source row
-// is row_map[that row] (a gather of x by row_token).
-__global__ __launch_bounds__(256) void k_transpose(TransposeParams p) {
-  __shared__ uint16_t tile[64][66];  // a row stride of 33 dwords: the column reads hit distinct banks
-  const int c0 = blockIdx.x * 64;   // source column (destination row) block
-  int64_t r0 = static_cast<int64_t>(blockIdx.y) * 64;
-  const uint16_t* src = p.src + blockIdx.z * p.src_batch;
-  uint16_t* dst = p.dst + blockIdx.z * p.dst_batch;
-  int64_t col0 = p.dst_col0 + r0;
-  int rows = static_cast<int>(min(static_cast<int64_t>(64), p.R - r0));  // valid source rows
-  int64_t srow0 = r0;
-  if (p.pad) {
-    // the expert whose padded segment holds this block's columns
-    const int lane = threadIdx.x & 63;
-    const int64_t P = r0;
-    if (P >= p.pad[p.N]) return;
-    int pe = lane < p.N ? p.pad[lane + 1] : 0x7fffffff;
-    const int e = __popcll(__ballot(lane < p.N && pe <= P));
-    int off = 0, cnt = 0;
-    expert_segment(p.offsets, e, p.rows_max, off, cnt);
-    const int64_t local = P - p.pad[e];
-    srow0 = off + local;
-    rows = static_cast<int>(max(static_cast<int64_t>(0), min(static_cast<int64_t>(64), cnt - local)));
-    col0 = P;
-  }
-  // load 64 source rows x 64 columns (16-byte pieces: 8 per row)
-  for (int i = threadIdx.x; i < 64 * 8; i += 256) {
-    const int rr = i / 8, cc = (i % 8) * 8;
-    u32x4_t v = {0u, 0u, 0u, 0u};
-    if (rr < rows && c0 + cc < p.C) {
-      int64_t sr = srow0 + rr;
-      if (p.row_map) sr = p.row_map[sr];
-      const uint16_t* sp = src + sr * p.src_ld + c0 + cc;
-      if (c0 + cc + 8 <= p.C) {
-        v = *reinterpret_cast<const u32x4_t*>(sp);
-      } else {
-        uint16_t tmp[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        for (int q = 0; c0 + cc + q < p.C; ++q) tmp[q] = sp[q];
-        v = u32x4_t{tmp[0] | (uint32_t(tmp[1]) << 16), tmp[2] | (uint32_t(tmp[3]) << 16),
-                    tmp[4] | (uint32_t(tmp[5]) << 16), tmp[6] | (uint32_t(tmp[7]) << 16)};
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      tile[rr][cc + 2 * q] = static_cast<uint16_t>(v[q]);
-      tile[rr][cc + 2 * q + 1] = static_cast<uint16_t>(v[q] >> 16);
-    }
-  }
-  __syncthreads();
-  // write 64 destination rows (source columns) x 64 columns (source rows)
-  for (int i = threadIdx.x; i < 64 * 8; i += 256) {
-    const int cc = i / 8, rr = (i % 8) * 8;
-    if (c0 + cc >= p.C) continue;
-    uint32_t w[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) w[q] = tile[rr + 2 * q][cc] | (static_cast<uint32_t>(tile[rr + 2 * q + 1][cc]) << 16);
-    uint16_t* dp = dst + static_cast<int64_t>(c0 + cc) * p.dst_ld + col0 + rr;
-    if (p.pad || col0 + rr + 8 <= p.dst_col0 + p.R) {
-      *reinterpret_cast<u32x4_t*>(dp) = u32x4_t{w[0], w[1], w[2], w[3]};
-    } else {
-      for (int q = 0; col0 + rr + q < p.dst_col0 + p.R; ++q) dp[q] = static_cast<uint16_t>(w[q / 2] >> (16 * (q & 1)));
-    }
-  }
-}
-
 }  // namespace
 
 hipError_t launch_bwd_gate(const BwdGateParams& p, hipStream_t s) {
@@ -447,19 +359,6 @@ hipError_t launch_router_wgrad(const RouterWgradParams& p, hipStream_t s) {
   const int64_t n = static_cast<int64_t>(p.H) * p.N * (p.noisy ? 2 : 1);
   hipLaunchKernelGGL(k_router_wgrad_sum, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s, p,
                      router_wgrad_chunks(p.T));
-  return hipGetLastError();
-}
-
-hipError_t launch_pad_offsets(const int32_t* offsets, int N, int rows_max, int32_t* pad, hipStream_t s) {
-  hipLaunchKernelGGL(k_pad_offsets, dim3(1), dim3(64), 0, s, offsets, N, rows_max, pad);
-  return hipGetLastError();
-}
-
-hipError_t launch_transpose(const TransposeParams& p, int64_t col_blocks, int batches, hipStream_t s) {
-  if (col_blocks <= 0 || p.C <= 0 || batches <= 0) return hipSuccess;
-  const dim3 grid(static_cast<unsigned>((p.C + 63) / 64), static_cast<unsigned>(col_blocks),
-                  static_cast<unsigned>(batches));
-  hipLaunchKernelGGL(k_transpose, grid, dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

@@ -137,6 +137,51 @@ __device__ __forceinline__ void frag_rows(int wm, int wn, int lane, int (&arow)[
   }
 }
 
+// ---- K-outer operands (the backward) ---------------------------------------
+//
+// The backward's GEMMs read operands whose rows are K rows: the expert
+// weights as B of the input gradients (dh = dE . Wdown_e reads Wdown_e[h][f]
+// with K = h; dx = dg . Wgate_e + du . Wup_e reads Wgate_e[f][h] with K = f),
+// and every operand of the weight gradients, whose K is an expert's rows
+// (dWdown_e = dE^T h, dWgate_e = dg^T x, dWup_e = du^T x). Such a "KN"
+// operand is staged as it lies in memory: BK rows of the tile's 256 M (or N)
+// columns, 512 bytes per LDS row. The MFMA operand wants 8 consecutive K of
+// one column per lane; gfx950's transposing LDS read (ds_read_b64_tr_b16)
+// gives each lane of a 16-lane group 4 consecutive rows of its column, so two
+// reads make one operand. Lane i of a group points at row i / 4 of the four
+// rows, columns 4 (i % 4) .. 4 (i % 4) + 3 of the group's 16.
+//
+// Bank conflicts: the LDS serves a 64-bit read 32 lanes at a time over 64
+// banks. Those 32 lanes cover 4 rows x 32 columns; rows 512 bytes apart fall
+// on the same banks, so 16-byte chunk c of row k is stored at chunk
+// c ^ (4 (k & 3)): the 4 rows' 4 chunks then occupy 16 distinct chunk slots of
+// one 256-byte window. The row-wise direct-to-LDS writes pick their global
+// chunk with the same XOR.
+constexpr int kKnCols = 256;  // columns of a KN LDS row (the tile's M or N extent)
+
+__device__ __forceinline__ int kn_off(int k, int col) {
+  return k * kKnCols + ((((col >> 3) ^ ((k & 3) << 2))) << 3) + (col & 7);
+}
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
+// Lane offset (elements, within a KN stage) of the transposing reads of the
+// 32-column block at column c0, K slice ks = 0 (add ks * 16 * kKnCols for
+// slice ks, 4 * kKnCols for the second read).
+__device__ __forceinline__ int kn_frag_off(int c0, int lane) {
+  const int k = (lane >> 5) * 8 + ((lane & 15) >> 2);
+  return kn_off(k, c0 + (lane & 16) + 4 * (lane & 3));
+}
+
+__device__ __forceinline__ bf16x8_t kn_frag(const uint16_t* __restrict__ st, int off) {
+  const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(st + off));
+  const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(st + off + 4 * kKnCols));
+  typedef short s16x8_t __attribute__((ext_vector_type(8)));
+  const s16x8_t v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
 // A wave's operand fragments for the K loop, in two register sets: the LDS
 // reads of one K slice are in flight while the MFMAs of the previous slice
 // run. A stage's last slice lands in set 1 and its MFMAs wait for the next
@@ -145,7 +190,7 @@ __device__ __forceinline__ void frag_rows(int wm, int wn, int lane, int (&arow)[
 // blocks hold rows of the expert (wave-uniform), and the rest of an expert's
 // last, partly filled tile is skipped, MFMAs and operand reads alike; full
 // tiles take the branch-free copy.
-template <int MB, int NB, int BK, bool PARTIAL>
+template <int MB, int NB, int BK, bool PARTIAL, bool AKN = false, bool BKN = false>
 struct FragPipe {
   static constexpr int KS = BK / 16;
   static_assert(KS % 2 == 0, "a stage's last slice must land in set 1");
@@ -162,12 +207,19 @@ struct FragPipe {
   __device__ __forceinline__ void load(const uint16_t* __restrict__ a, const uint16_t* __restrict__ b,
                                        const int (&arow)[MB], const int (&brow)[NB], int khalf, int ks, int buf,
                                        int live) {
+    // TN: arow/brow are LDS rows; KN: lane offsets of the transposing reads
     const int chunk = ks * 2 + khalf;
 #pragma unroll
     for (int i = 0; i < MB; ++i)
-      if (!PARTIAL || i < live) af[buf][i] = *reinterpret_cast<const bf16x8_t*>(&a[swz<BK>(arow[i], chunk)]);
+      if (!PARTIAL || i < live) {
+        if constexpr (AKN) af[buf][i] = kn_frag(a, arow[i] + ks * 16 * kKnCols);
+        else af[buf][i] = *reinterpret_cast<const bf16x8_t*>(&a[swz<BK>(arow[i], chunk)]);
+      }
 #pragma unroll
-    for (int j = 0; j < NB; ++j) bfr[buf][j] = *reinterpret_cast<const bf16x8_t*>(&b[swz<BK>(brow[j], chunk)]);
+    for (int j = 0; j < NB; ++j) {
+      if constexpr (BKN) bfr[buf][j] = kn_frag(b, brow[j] + ks * 16 * kKnCols);
+      else bfr[buf][j] = *reinterpret_cast<const bf16x8_t*>(&b[swz<BK>(brow[j], chunk)]);
+    }
   }
 
   __device__ __forceinline__ void mma(int buf, f32x16_t (&acc)[MB][NB], int live) {
@@ -371,12 +423,11 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 // two stages are disjoint, so it does not hold the current stage's LDS reads
 // until the just-issued loads land (the explicit waits and barrier at the top
 // of each step order the stages).
-template <int MB, int NB, int BK, bool PARTIAL, class Issue>
+template <int MB, int NB, class Issue, class Pipe>
 __device__ __forceinline__ void dma_step(Issue& issue, bool do_issue, int kt_next, const uint16_t* __restrict__ a_cur,
                                          const uint16_t* __restrict__ b_cur, uint16_t* __restrict__ a_nxt,
                                          uint16_t* __restrict__ b_nxt, const int (&arow)[MB], const int (&brow)[NB],
-                                         int khalf, f32x16_t (&acc)[MB][NB], int live,
-                                         FragPipe<MB, NB, BK, PARTIAL>& fp) {
+                                         int khalf, f32x16_t (&acc)[MB][NB], int live, Pipe& fp) {
   if (do_issue) issue(a_nxt, b_nxt, kt_next);
   fp.stage(a_cur, b_cur, arow, brow, khalf, acc, live);
 }
@@ -472,6 +523,134 @@ struct TileLoader {
   }
 };
 
+// One KN operand's loads: BK rows x 256 columns per stage, 2 rows per 1-KB
+// segment, NW waves each filling BK / 2 / NW segments. Lane q of a segment
+// holds row q / 32 at physical chunk q % 32, i.e. logical chunk
+// (q % 32) ^ (4 (row & 3)); row & 3 is the same for every segment of a wave,
+// so one column offset per lane serves all of its loads.
+//   rows: K row k reads source row k (plain), map[k] (gather), or for a
+//   split operand row k of src0 when k < ksplit and row k - ksplit of src1
+//   (ksplit even, so both rows of a segment come from one source).
+// Gather: the 64 map entries of a K step go into a two-slot LDS ring with one
+// direct-to-LDS load by wave 0, a step ahead (so no vector register waits on
+// a map load, and the compiler places no wait on the stage loads before the
+// MFMAs). Step kt reads slot kt & 1; the load for step kt + 1 overwrites the
+// slot of step kt - 1, which every wave read before the barrier of the step
+// in which it is issued.
+template <int NW, int BK, bool GATHER>
+struct KnOperand {
+  static constexpr int I = BK / 2 / NW;  // segments a wave fills per stage
+  static_assert(I * 2 * NW == BK, "KN segments must divide among waves");
+  static_assert(!GATHER || BK == 64, "a map ring slot holds one 64-row K step");
+  __amdgpu_buffer_rsrc_t r0, r1, rmap;
+  uint32_t colb;     // this lane's byte offset within a row, or kOOB (columns past the extent)
+  uint32_t ldbytes;  // bytes per source row
+  int wave, half, kb1, ksplit;
+  int* ring;         // gather: [2][64] source rows of K steps (LDS)
+
+  __device__ __forceinline__ void init(const void* src0, const void* src1, int64_t src_rows, int64_t ld, int col0,
+                                       int cols, int kend, int ksplit_, const int32_t* map, int* ring_) {
+    const int lane = threadIdx.x & 63;
+    wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    half = lane >> 5;
+    const int key = ((2 * wave + half) & 3) << 2;
+    const int c = (lane & 31) ^ key;
+    colb = c * 8 < cols ? static_cast<uint32_t>(col0 + c * 8) * 2u : kOOB;
+    ldbytes = static_cast<uint32_t>(ld) * 2u;
+    kb1 = kend;
+    ksplit = ksplit_;
+    ring = ring_;
+    r0 = uniform_rsrc(src0, src_rows * ld * 2);
+    r1 = uniform_rsrc(src1 ? src1 : src0, src_rows * ld * 2);
+    if constexpr (GATHER) rmap = uniform_rsrc(map, static_cast<int64_t>(kend) * 4);  // map[k] reads 0 for k >= kend
+  }
+
+  __device__ __forceinline__ int row(int s, int kb) const { return kb + 2 * s + half; }
+
+  // gather: wave 0 loads the map entries of the K step at kb into ring slot
+  // `slot` (entries past the K range read as 0)
+  __device__ __forceinline__ void fetch(int kb, int slot) const {
+    if constexpr (GATHER) {
+      if (wave == 0) {
+        const uint32_t vo = static_cast<uint32_t>(kb + (threadIdx.x & 63)) * 4u;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rmap, (lds_ptr_t)(ring + slot * 64), 4, vo, 0, 0, 0);
+      }
+    }
+  }
+
+  __device__ __forceinline__ void issue(uint16_t* dst, int kb, int slot) const {
+#pragma unroll
+    for (int i = 0; i < I; ++i) {
+      const int s = i * NW + wave;
+      const int k = row(s, kb);
+      const bool second = kb + 2 * s >= ksplit;  // wave-uniform
+      int src;
+      // an LDS read (the address space said explicitly, so it is no flat load)
+      if constexpr (GATHER) src = ((__attribute__((address_space(3))) const int*)ring)[slot * 64 + 2 * s + half];
+      else src = second ? k - ksplit : k;
+      const uint32_t vo = (k < kb1 && colb != kOOB) ? static_cast<uint32_t>(src) * ldbytes + colb : kOOB;
+      if (second)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r1, (lds_ptr_t)(dst + s * 512), 16, vo, 0, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r0, (lds_ptr_t)(dst + s * 512), 16, vo, 0, 0, 0);
+    }
+  }
+};
+
+// The backward's tile loads. LAY 1 (input gradients): A is the usual
+// K-contiguous row operand (dE, or dg | du, rows of the tile's expert); B is
+// KN, the expert's weights, split at g.ksplit between B0 and B1 (Wgate and
+// Wup). LAY 2 (weight gradients): both KN over the expert's rows
+// [kb0, kb1) of the permuted order; A's columns are the tile's M rows
+// (ti.row0 .. + ti.rows), B's the tile's N columns; B rows are gathered
+// through row_token when it is set (x for dWgate and dWup).
+template <int BM, int BN, int WGM, int WGN, int BK, int LAY, bool BGATHER>
+struct BwdLoader {
+  static constexpr int NW = WGM * WGN;
+  static_assert(BM == kKnCols && BN == kKnCols, "KN stages hold 256 columns");
+  using Tn = TileLoader<BM, BN, WGM, WGN, BK, false, false>;
+  using KnA = KnOperand<NW, BK, false>;
+  using KnB = KnOperand<NW, BK, BGATHER>;
+  static constexpr int LPS = (LAY == 1 ? Tn::IA : KnA::I) + KnB::I;
+  static constexpr int NO = BN;
+  Tn ta;
+  KnA ka;
+  KnB kb;
+  int kb0;
+
+  // ring: BGATHER's map ring ([2][64] int32 of LDS, not used otherwise). With
+  // BGATHER, init loads the first K step's map entries and waits for them at
+  // a workgroup barrier, so every wave must call it.
+  __device__ __forceinline__ void init(const GemmParams& p, const TilePos& tp, int* ring = nullptr) {
+    kb0 = tp.kb0;
+    if constexpr (LAY == 1) {
+      ta.init(p, tp);  // its A rows; its B part is not used
+      const uint16_t* b0 = static_cast<const uint16_t*>(p.B0) + tp.ti.expert * p.b_expert_stride;
+      const uint16_t* b1 = p.B1 ? static_cast<const uint16_t*>(p.B1) + tp.ti.expert * p.b_expert_stride : b0;
+      kb.init(b0, b1, p.b_rows, p.ldb, tp.nt * BN, p.Nout - tp.nt * BN, tp.kb1, p.ksplit, nullptr, nullptr);
+    } else {
+      ka.init(p.A, nullptr, p.a_rows, p.lda, tp.ti.row0, tp.ti.rows, tp.kb1, 1 << 30, nullptr, nullptr);
+      kb.init(p.B0, nullptr, p.b_rows, p.ldb, tp.nt * BN, p.Nout - tp.nt * BN, tp.kb1, 1 << 30, p.row_token, ring);
+      if constexpr (BGATHER) {
+        kb.fetch(kb0, 0);
+        wait_vm<0>();
+        __syncthreads();
+      }
+    }
+  }
+
+  __device__ __forceinline__ void issue_a(uint16_t* a_dst, int kt) {
+    if constexpr (LAY == 1) ta.issue_a(a_dst, kt);
+    else ka.issue(a_dst, kb0 + kt * BK, 0);
+  }
+  // K step kt's B rows; with BGATHER, also the map entries of step kt + 1
+  // (steps are issued in order, one per K step)
+  __device__ __forceinline__ void issue_b(uint16_t* b_dst, int kt) {
+    kb.issue(b_dst, kb0 + kt * BK, kt & 1);
+    if constexpr (BGATHER) kb.fetch(kb0 + (kt + 1) * BK, (kt + 1) & 1);
+  }
+};
+
 // LDS stage addresses of the operand stages in `smem`.
 template <int BM, int BN, int BK>
 __device__ __forceinline__ uint16_t* stage_a(uint16_t* smem, int st) { return smem + st * (BM + BN) * BK; }
@@ -496,12 +675,19 @@ struct NoReserve {
 // a shorter tile); after the MFMAs of the last K step are issued, hook(a, b,
 // buf) may issue loads into stage buffer buf (at a, b), which no wave reads
 // any more; the epilogue follows.
+//
+// LAY 0: both operands K-contiguous (the forward); LAY 1 and 2: the
+// backward's K-outer operands (BwdLoader), B (LAY 1) or both (LAY 2) staged
+// as KN and read with the transposing LDS reads; BGATHER gathers LAY 2's B
+// rows through row_token.
 template <int BM, int BN, int WGM, int WGN, int STAGES, int BK, bool SWIGLU, bool GATHER, class Hook = NoHook,
-          class Reserve = NoReserve>
+          class Reserve = NoReserve, int LAY = 0, bool BGATHER = false>
 __device__ __forceinline__ void gemm_tile(const GemmParams& p, const TilePos& tp, uint16_t* smem, int sbase = 0,
                                           int pre = 0, Hook&& hook = Hook{}, Reserve&& reserve = Reserve{},
                                           bool poison = false) {
-  using Loader = TileLoader<BM, BN, WGM, WGN, BK, SWIGLU, GATHER>;
+  static_assert(LAY == 0 || (!SWIGLU && !GATHER && BK == 64), "the backward's tiles are plain");
+  using Loader = std::conditional_t<LAY == 0, TileLoader<BM, BN, WGM, WGN, BK, SWIGLU, GATHER>,
+                                    BwdLoader<BM, BN, WGM, WGN, BK, LAY, BGATHER>>;
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int MB = WM / 32, NB = WN / 32;
   constexpr int LPS = Loader::LPS;
@@ -520,7 +706,8 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const TilePos& tp
   const int wm = wave % WGM, wn = wave / WGM;
 
   Loader ld;
-  ld.init(p, tp);
+  if constexpr (LAY == 0) ld.init(p, tp);
+  else ld.init(p, tp, reinterpret_cast<int*>(smem + dma_lds_elems<BM, BN, STAGES, BK>()));
   auto issue = [&](uint16_t* a_dst, uint16_t* b_dst, int kt) {
     ld.issue_a(a_dst, kt);
     ld.issue_b(b_dst, kt);
@@ -530,6 +717,14 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const TilePos& tp
   zero_acc(acc);
   int arow[MB], brow[NB];
   frag_rows<WM, WN, MB, NB, BN, SWIGLU>(wm, wn, lane, arow, brow);
+  if constexpr (LAY == 2) {
+#pragma unroll
+    for (int i = 0; i < MB; ++i) arow[i] = kn_frag_off(wm * WM + i * 32, lane);
+  }
+  if constexpr (LAY >= 1) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j) brow[j] = kn_frag_off(wn * WN + j * 32, lane);
+  }
   const int khalf = lane >> 5;
   // 32-row blocks of this wave that hold rows of the tile; none when all of
   // the wave's output columns lie past Nout (an expert's last column tile)
@@ -548,7 +743,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const TilePos& tp
   // partly filled tile's empty row blocks
   const int kt_reserve = max(0, tp.KT - 3);
   auto kloop = [&](auto partial) {
-    FragPipe<MB, NB, BK, decltype(partial)::value> fp;
+    FragPipe<MB, NB, BK, decltype(partial)::value, LAY == 2, LAY >= 1> fp;
     fp.init();
     for (int kt = 0; kt < tp.KT; ++kt) {
       const int later = min(STAGES - 2, tp.KT - 1 - kt);
@@ -556,8 +751,8 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const TilePos& tp
       lds_barrier();  // stage kt is complete for every wave; stage kt-1 is free
       if (kt == kt_reserve) reserve();
       const int st = (sbase + kt) % STAGES, nx = (sbase + kt + STAGES - 1) % STAGES;
-      dma_step<MB, NB, BK, decltype(partial)::value>(issue, kt + STAGES - 1 < tp.KT, kt + STAGES - 1, sA(st), sB(st),
-                                                     sA(nx), sB(nx), arow, brow, khalf, acc, live, fp);
+      dma_step<MB, NB>(issue, kt + STAGES - 1 < tp.KT, kt + STAGES - 1, sA(st), sB(st), sA(nx), sB(nx), arow, brow,
+                       khalf, acc, live, fp);
     }
     fp.mma(1, acc, live);  // the last stage's last slice
   };
@@ -791,6 +986,12 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_experts_fused(FusedParams fp
   const GemmParams& g1 = fp.g1;
   const GemmParams& g2 = fp.g2;
   const int lane = threadIdx.x & 63;
+  // the forward's operands are K-contiguous; the backward's weights are KN
+  constexpr int LAY = G1_SWIGLU ? 0 : 1;
+  using Loader1 = std::conditional_t<LAY == 0, TileLoader<BM, BN, WGM, WGN, BK, G1_SWIGLU, GATHER>,
+                                     BwdLoader<BM, BN, WGM, WGN, BK, 1, false>>;
+  using Loader2 = std::conditional_t<LAY == 0, TileLoader<BM, BN, WGM, WGN, BK, false, false>,
+                                     BwdLoader<BM, BN, WGM, WGN, BK, 1, false>>;
 
   // per-expert row blocks (lane e = expert e), inclusive scan over lanes
   // (clamped to the rows the workspace holds, so RB never exceeds the row
@@ -874,13 +1075,13 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_experts_fused(FusedParams fp
         TilePos tq;
         int rq;
         if (decode(next, tq, rq)) {
-          TileLoader<BM, BN, WGM, WGN, BK, G1_SWIGLU, GATHER> lq;
+          Loader1 lq;
           lq.init(g1, tq);
           lq.issue_a(a_free, 0);
           lq.issue_b(b_free, 0);
           npre = 2;
         } else {
-          TileLoader<BM, BN, WGM, WGN, BK, false, false> lq;
+          Loader2 lq;
           lq.init(g2, tq);
           lq.issue_b(b_free, 0);
           npre = 1;
@@ -891,7 +1092,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_experts_fused(FusedParams fp
     TilePos tp;
     int rb;
     if (decode(ticket, tp, rb)) {
-      gemm_tile<BM, BN, WGM, WGN, STAGES, BK, G1_SWIGLU, GATHER>(g1, tp, smem, sbase, pre, hook, reserve);
+      gemm_tile<BM, BN, WGM, WGN, STAGES, BK, G1_SWIGLU, GATHER, decltype(hook)&, decltype(reserve)&, LAY>(
+          g1, tp, smem, sbase, pre, hook, reserve);
       // publish: every wave waits until its device-scope h stores have
       // completed (the wait also covers the next tile's first loads, issued
       // before the epilogue and needed next anyway), then one count. No L2
@@ -912,7 +1114,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_experts_fused(FusedParams fp
       }
       __syncthreads();
       const bool poison = __builtin_amdgcn_readfirstlane(s_item[1]) != 0;
-      gemm_tile<BM, BN, WGM, WGN, STAGES, BK, false, false>(g2, tp, smem, sbase, pre, hook, reserve, poison);
+      gemm_tile<BM, BN, WGM, WGN, STAGES, BK, false, false, decltype(hook)&, decltype(reserve)&, LAY>(
+          g2, tp, smem, sbase, pre, hook, reserve, poison);
     }
     ticket = next;
     sbase = nsbase;
@@ -925,29 +1128,24 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_experts_fused(FusedParams fp
 
 // ---- backward: weight gradients ------------------------------------------------------
 
-// Per-expert weight gradients: tile (e, mt, nt) of GEMM g sums A[mt rows,
-// seg_e] . B[nt rows, seg_e]^T over expert e's padded column segment seg_e
-// and stores the e-th [M, Nout] block of C. One launch runs the tiles of up to
-// three such GEMMs one after the other; within a GEMM the tiles of one expert
-// run together, four row tiles at a time with the column tile fastest, so
-// they share operand panels.
+// Per-expert weight gradients: tile (e, mt, nt) of GEMM g sums, over expert
+// e's rows r of the permuted order (K, in order, 64 at a time; rows past the
+// expert's end read as zero), A[r][mt cols] x B[r][nt cols], both operands
+// K-outer (KN), and stores the e-th [M, Nout] block of C. The tiles of one
+// expert run together, four row tiles at a time with the column tile fastest,
+// so they share operand panels. BGATHER: B's row r is row row_token[r] of x.
+template <bool BGATHER>
 __global__ __launch_bounds__(512) void k_gemm_wgrad(WgradParams wp) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[dma_lds_elems<256, 256, 2, 64>()];
+  // the operand stages, then the gather's map ring ([2][64] int32)
+  __shared__ __attribute__((aligned(16))) uint16_t smem[dma_lds_elems<256, 256, 2, 64>() + 2 * 64 * 2];
   constexpr int GM = 4;
-  int L = xcd_remap(blockIdx.x, gridDim.x);
-  // which GEMM (uniform selects on the kernel arguments, no dynamic indexing)
-  auto tiles = [&](int i) {
-    return ((wp.M[i] + 255) / 256) * ((wp.g[i].Nout + 255) / 256) * wp.g[i].N;
-  };
-  const int n0 = tiles(0), n1 = wp.count > 1 ? tiles(1) : 0, n2 = wp.count > 2 ? tiles(2) : 0;
-  if (L >= n0 + n1 + n2) return;
-  const int gi = L < n0 ? 0 : (L < n0 + n1 ? 1 : 2);
-  L -= gi == 0 ? 0 : (gi == 1 ? n0 : n0 + n1);
-  const GemmParams p = gi == 0 ? wp.g[0] : (gi == 1 ? wp.g[1] : wp.g[2]);
-  const int M = gi == 0 ? wp.M[0] : (gi == 1 ? wp.M[1] : wp.M[2]);
+  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  const GemmParams& p = wp.g;
+  const int M = wp.M;
   const int mtn = (M + 255) / 256, ntn = (p.Nout + 255) / 256;
   const int per_e = mtn * ntn;
   const int e = L / per_e;
+  if (e >= p.N) return;
   const int q = L - e * per_e;
   const int g = q / (GM * ntn);
   const int gm = min(GM, mtn - g * GM);
@@ -959,10 +1157,12 @@ __global__ __launch_bounds__(512) void k_gemm_wgrad(WgradParams wp) {
   tp.ti.row0 = __builtin_amdgcn_readfirstlane(mt * 256);
   tp.ti.rows = __builtin_amdgcn_readfirstlane(min(256, M - mt * 256));
   tp.split = __builtin_amdgcn_readfirstlane(e);
-  tp.kb0 = __builtin_amdgcn_readfirstlane(wp.pad[e]);
-  tp.kb1 = __builtin_amdgcn_readfirstlane(max(tp.kb0, wp.pad[e + 1]));
-  tp.KT = (tp.kb1 - tp.kb0) / 64;
-  gemm_tile<256, 256, 4, 2, 2, 64, false, false>(p, tp, smem);
+  int off = 0, cnt = 0;
+  expert_segment(p.offsets, e, static_cast<int>(p.rows_max), off, cnt);
+  tp.kb0 = __builtin_amdgcn_readfirstlane(off);
+  tp.kb1 = __builtin_amdgcn_readfirstlane(off + cnt);
+  tp.KT = (cnt + 63) / 64;
+  gemm_tile<256, 256, 4, 2, 2, 64, false, false, NoHook, NoReserve, 2, BGATHER>(p, tp, smem);
 }
 
 // ---- launches --------------------------------------------------------------------
@@ -1041,11 +1241,12 @@ hipError_t launch_bwd_dgrad_fused(const FusedParams& fp, hipStream_t s) {
 hipError_t launch_gemm_decode(const GemmParams& p, hipStream_t s) { return launch_decode<kDecBM, 128, 3, 4>(p, s); }
 
 hipError_t launch_gemm_wgrad(const WgradParams& wp, hipStream_t s) {
-  int64_t blocks = 0;
-  for (int i = 0; i < wp.count; ++i)
-    blocks += static_cast<int64_t>((wp.M[i] + 255) / 256) * ((wp.g[i].Nout + 255) / 256) * wp.g[i].N;
+  const int64_t blocks = static_cast<int64_t>((wp.M + 255) / 256) * ((wp.g.Nout + 255) / 256) * wp.g.N;
   if (blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_gemm_wgrad, dim3(static_cast<unsigned>(blocks)), dim3(512), 0, s, wp);
+  if (wp.g.row_token)
+    hipLaunchKernelGGL(k_gemm_wgrad<true>, dim3(static_cast<unsigned>(blocks)), dim3(512), 0, s, wp);
+  else
+    hipLaunchKernelGGL(k_gemm_wgrad<false>, dim3(static_cast<unsigned>(blocks)), dim3(512), 0, s, wp);
   return hipGetLastError();
 }
 

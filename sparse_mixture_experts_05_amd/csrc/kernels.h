@@ -119,6 +119,11 @@ struct GemmParams {
   // with g, u from gu, C[r, f] = bf16(dh u SiLU'(g)) and
   // C[r, Nout + f] = bf16(dh SiLU(g)) (C row stride ldc = 2*Nout)
   int epi;
+  // the backward's K-outer ("KN") B operand: row k of the K range is row k of
+  // B0 when k < ksplit, else row k - ksplit of B1 (each b_rows rows of ldb
+  // elements per expert); the N columns are contiguous within a row
+  int64_t b_rows;
+  int ksplit;
 };
 // Decode-shaped tiles (few rows per expert), one launch per GEMM.
 hipError_t launch_gemm_decode(const GemmParams& p, hipStream_t s);
@@ -128,15 +133,15 @@ void gemm_decode_tile(int* bm, int* bn);
 hipError_t launch_gemm_simple(const GemmParams& p, int bf16, hipStream_t s);
 
 // The backward's weight gradients on the same 256 x 256 tile, one tile per
-// workgroup: per expert with K over the expert's padded row segment,
-// C_e = A[:, seg_e] . B[:, seg_e]^T into the e-th [M, Nout] block of C
-// (c_split_stride = M * Nout), for up to three GEMMs in one launch. pad[N+1]:
-// the padded segments, multiples of 64 columns.
+// workgroup: per expert e, K over the expert's rows r in [offsets[e],
+// offsets[e+1]) of the permuted order, C_e[m][n] = sum_r A[r][m] B[r'][n] into
+// the e-th [M, Nout] block of C (c_split_stride = M * Nout). Both operands are
+// K-outer: A rows of lda elements (a_rows of them), the M columns contiguous;
+// B rows of ldb elements (b_rows of them), r' = row_token[r] when row_token is
+// set, else r.
 struct WgradParams {
-  GemmParams g[3];
-  int M[3];
-  int count;
-  const int32_t* pad;  // [N+1]
+  GemmParams g;
+  int M;
 };
 hipError_t launch_gemm_wgrad(const WgradParams& wp, hipStream_t s);
 
@@ -230,23 +235,5 @@ struct RouterWgradParams {
 int router_wgrad_chunks(int64_t T);
 hipError_t launch_router_wgrad(const RouterWgradParams& p, hipStream_t s);
 
-hipError_t launch_pad_offsets(const int32_t* offsets, int N, int rows_max, int32_t* pad, hipStream_t s);
-
-struct TransposeParams {
-  const uint16_t* src;
-  int64_t src_ld;           // elements per source row
-  int64_t src_batch;        // elements between batches
-  const int32_t* row_map;   // source row = row_map[row], or null
-  uint16_t* dst;
-  int64_t dst_ld;
-  int64_t dst_batch;
-  int64_t dst_col0;
-  int64_t R;                // source rows (destination columns)
-  int64_t C;                // source columns (destination rows)
-  const int32_t* pad;       // padded mode: [N+1] padded segments
-  const int32_t* offsets;   // padded mode: [N+1] row segments
-  int N, rows_max;
-};
-hipError_t launch_transpose(const TransposeParams& p, int64_t col_blocks, int batches, hipStream_t s);
 
 }  // namespace moe

@@ -579,16 +579,13 @@ namespace {
 // forward keeps (router logits, g and u) and the backward's buffers.
 struct TrainLayout {
   Layout L;
-  int64_t A_pad = 0;  // columns of the transposed, per-expert padded copies
-  size_t logits = 0, nlog = 0, gu = 0, dE = 0, pad = 0, dEt = 0, ht = 0, xt = 0, dgu = 0, dgut = 0, WdT = 0,
-         WguT = 0, dxp = 0, dlog = 0, dnz = 0, rwp = 0, total = 0;
+  size_t logits = 0, nlog = 0, gu = 0, dE = 0, dgu = 0, dxp = 0, dlog = 0, dnz = 0, rwp = 0, total = 0;
 };
 
 TrainLayout train_layout(const moe_cfg* c) {
   TrainLayout t;
   t.L = layout(c);
   const int64_t T = c->T, H = c->H, F = c->F, N = c->N, A = t.L.A_max;
-  t.A_pad = (A + 63) / 64 * 64 + 64 * N;
   size_t o = t.L.total;
   auto take = [&](size_t bytes) {
     const size_t at_ = o;
@@ -599,14 +596,7 @@ TrainLayout train_layout(const moe_cfg* c) {
   t.nlog = take(T * N * 4);
   t.gu = take(A * 2 * F * 4);
   t.dE = take(A * H * 2);
-  t.pad = take((N + 1) * 4);
-  t.dEt = take(H * t.A_pad * 2);
-  t.ht = take(F * t.A_pad * 2);
-  t.xt = take(H * t.A_pad * 2);
   t.dgu = take(A * 2 * F * 2);
-  t.dgut = take(2 * F * t.A_pad * 2);
-  t.WdT = take(N * F * H * 2);
-  t.WguT = take(N * H * 2 * F * 2);
   t.dxp = take(A * H * 4);
   t.dlog = take(T * N * 4);
   t.dnz = take(T * N * 4);
@@ -625,9 +615,6 @@ moe_status check_train(const moe_cfg* c) {
     return fail(MOE_ERR_UNSUPPORTED,
                 "training needs bf16 activations and weights, F %% 8 == 0 and more than 48 rows per expert on "
                 "average (the persistent expert kernel's shapes)");
-  const int64_t A_pad = (L.A_max + 63) / 64 * 64 + 64 * static_cast<int64_t>(c->N);
-  if (A_pad * std::max<int64_t>(c->H, 2 * static_cast<int64_t>(c->F)) >= (int64_t(1) << 30))
-    return fail(MOE_ERR_UNSUPPORTED, "transposed backward operands must stay below 2 GiB");
   return MOE_OK;
 }
 
@@ -699,13 +686,11 @@ moe_status moe_backward(const moe_cfg* c, const void* x, const float* Wg, const 
   const Layout& L = t.L;
   const int A = static_cast<int>(L.A_max);
   const int32_t* offsets = at<int32_t>(ws, L.offsets);
-  int32_t* pad = at<int32_t>(ws, t.pad);
   uint16_t* dE = at<uint16_t>(ws, t.dE);
   uint16_t* dgu = at<uint16_t>(ws, t.dgu);
   float* dlog = at<float>(ws, t.dlog);
   float* dnz = at<float>(ws, t.dnz);
-  hipError_t e = moe::launch_pad_offsets(offsets, c->N, A, pad, s);
-  if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "pad offsets launch failed: %s", hipGetErrorString(e));
+  hipError_t e = hipSuccess;
 
   // gate weights back to the router; dE = s w dy at every kept slot's row
   moe::BwdGateParams gp{T, c->H, c->N, c->k, c->order, c->noisy, c->out_scale, d_balance, dy,
@@ -714,40 +699,18 @@ moe_status moe_backward(const moe_cfg* c, const void* x, const float* Wg, const 
                         at<int32_t>(ws, L.counts), dE, dlog, dnz};
   MOE_LAUNCH(MOE_KERNEL_BWD_GATE, s, moe::launch_bwd_gate(gp, s));
 
-  // K-contiguous copies for the matrix-core tiles
-  auto tr = [&](const void* src, int64_t src_ld, int64_t src_batch, const int32_t* row_map, void* dst, int64_t dst_ld,
-                int64_t dst_batch, int64_t col0, int64_t R, int64_t C, bool padded, int batches) {
-    moe::TransposeParams tp{static_cast<const uint16_t*>(src), src_ld, src_batch, row_map,
-                            static_cast<uint16_t*>(dst), dst_ld, dst_batch, col0, R, C,
-                            padded ? pad : nullptr, padded ? offsets : nullptr, c->N, A};
-    return moe::launch_transpose(tp, padded ? t.A_pad / 64 : (R + 63) / 64, batches, s);
-  };
-  uint16_t* WdT = at<uint16_t>(ws, t.WdT);
-  uint16_t* WguT = at<uint16_t>(ws, t.WguT);
-  uint16_t* dEt = at<uint16_t>(ws, t.dEt);
-  uint16_t* ht = at<uint16_t>(ws, t.ht);
-  uint16_t* xt = at<uint16_t>(ws, t.xt);
-  uint16_t* dgut = at<uint16_t>(ws, t.dgut);
-  {
-    ProfScope ps_(MOE_KERNEL_BWD_TRANSPOSE, s);
-    e = tr(Wdown, F, H * F, nullptr, WdT, H, F * H, 0, H, F, false, c->N);
-    if (e == hipSuccess) e = tr(Wgate, H, F * H, nullptr, WguT, 2 * F, H * 2 * F, 0, F, H, false, c->N);
-    if (e == hipSuccess) e = tr(Wup, H, F * H, nullptr, WguT, 2 * F, H * 2 * F, F, F, H, false, c->N);
-    if (e == hipSuccess) e = tr(dE, H, 0, nullptr, dEt, t.A_pad, 0, 0, A, H, true, 1);
-    if (e == hipSuccess) e = tr(at<uint16_t>(ws, L.h), F, 0, nullptr, ht, t.A_pad, 0, 0, A, F, true, 1);
-    if (e == hipSuccess) e = tr(x, H, 0, at<int32_t>(ws, L.rowtok), xt, t.A_pad, 0, 0, A, H, true, 1);
-  }
-  if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "transpose launch failed: %s", hipGetErrorString(e));
-
-  // dh = dE . Wdown_e, and the SwiGLU derivative into dg | du (bf16)
+  // dh = dE . Wdown_e (B = Wdown_e[h][f], K = h, read in place), and the
+  // SwiGLU derivative into dg | du (bf16)
   moe::GemmParams gd{};
   gd.A = dE;
   gd.lda = H;
   gd.offsets = offsets;
   gd.N = c->N;
-  gd.B0 = WdT;
-  gd.b_expert_stride = F * H;
-  gd.ldb = H;
+  gd.B0 = Wdown;
+  gd.b_expert_stride = H * F;
+  gd.ldb = F;
+  gd.b_rows = H;
+  gd.ksplit = c->H;
   gd.K = c->H;
   gd.Nout = c->F;
   gd.C = dgu;
@@ -757,16 +720,20 @@ moe_status moe_backward(const moe_cfg* c, const void* x, const float* Wg, const 
   gd.a_rows = A;
   gd.gu = at<float>(ws, t.gu);
   gd.epi = 1;
-  // dx_perm = dg . Wgate_e + du . Wup_e: in the same persistent launch, each
-  // row block's dx tiles after its dh tiles
+  // dx_perm = dg . Wgate_e + du . Wup_e: K runs over the 2F columns of dg | du,
+  // B row k is Wgate_e row k (k < F) or Wup_e row k - F; in the same
+  // persistent launch, each row block's dx tiles after its dh tiles
   moe::GemmParams gx{};
   gx.A = dgu;
   gx.lda = 2 * F;
   gx.offsets = offsets;
   gx.N = c->N;
-  gx.B0 = WguT;
-  gx.b_expert_stride = H * 2 * F;
-  gx.ldb = 2 * F;
+  gx.B0 = Wgate;
+  gx.B1 = Wup;
+  gx.b_expert_stride = F * H;
+  gx.ldb = H;
+  gx.b_rows = F;
+  gx.ksplit = c->F;
   gx.K = 2 * c->F;
   gx.Nout = c->H;
   gx.C = at<float>(ws, t.dxp);
@@ -787,57 +754,48 @@ moe_status moe_backward(const moe_cfg* c, const void* x, const float* Wg, const 
     const moe::FusedParams fp{gd, gx, sched, moe::StatsParams{}, 0, spin, extra};
     MOE_LAUNCH(MOE_KERNEL_BWD_DGRAD, s, moe::launch_bwd_dgrad_fused(fp, s));
   }
-  {
-    ProfScope ps_(MOE_KERNEL_BWD_TRANSPOSE, s);
-    e = tr(dgu, 2 * F, 0, nullptr, dgut, t.A_pad, 0, 0, A, 2 * F, true, 1);
-  }
-  if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "transpose launch failed: %s", hipGetErrorString(e));
   // dx = sum of the slots' rows + the router terms
   moe::BwdDxParams dp{T, c->H, c->N, c->k, c->noisy, at<float>(ws, t.dxp), at<int32_t>(ws, L.slot), dlog, dnz, Wg,
                       Wn, dx};
   MOE_LAUNCH(MOE_KERNEL_BWD_DX, s, moe::launch_bwd_dx(dp, s));
-  // weight gradients per expert, K over the expert's padded rows
-  moe::WgradParams wp{};
-  wp.pad = pad;
-  wp.count = 3;
-  moe::GemmParams& gw = wp.g[0];
-  gw.N = c->N;
-  gw.splits = 1;
-  gw.b_expert_stride = 0;
-  gw.A = dEt;
-  gw.lda = t.A_pad;
-  gw.a_rows = H;
-  gw.B0 = ht;
-  gw.ldb = t.A_pad;
-  gw.K = static_cast<int>(t.A_pad);
-  gw.Nout = c->F;
-  gw.C = dWdown;
-  gw.ldc = F;
-  gw.c_split_stride = H * F;
-  wp.M[0] = c->H;
-  wp.g[1] = gw;
-  wp.g[1].A = dgut;
-  wp.g[1].a_rows = F;
-  wp.g[1].B0 = xt;
-  wp.g[1].Nout = c->H;
-  wp.g[1].C = dWgate;
-  wp.g[1].ldc = H;
-  wp.g[1].c_split_stride = F * H;
-  wp.M[1] = c->F;
-  wp.g[2] = wp.g[1];
-  wp.g[2].A = dgut + F * t.A_pad;
-  wp.g[2].C = dWup;
-  wp.M[2] = c->F;
-  // one launch per gradient: each grid's XCD-aware order keeps an expert's
-  // tiles of one GEMM together (one launch for all three measured 6% slower)
-  for (int i = 0; i < 3; ++i) {
-    moe::WgradParams one{};
-    one.g[0] = wp.g[i];
-    one.M[0] = wp.M[i];
-    one.count = 1;
-    one.pad = pad;
-    MOE_LAUNCH(MOE_KERNEL_BWD_WGRAD, s, moe::launch_gemm_wgrad(one, s));
-  }
+  // weight gradients per expert, K over the expert's rows of the permuted
+  // order; one launch per gradient, each grid's XCD-aware order keeping an
+  // expert's tiles together
+  moe::WgradParams wd{};
+  moe::GemmParams& w0 = wd.g;
+  w0.offsets = offsets;
+  w0.N = c->N;
+  w0.rows_max = A;
+  w0.splits = 1;
+  w0.A = dE;  // dWdown_e[h][f] = sum_r dE[r][h] h[r][f]
+  w0.lda = H;
+  w0.a_rows = A;
+  w0.B0 = at<uint16_t>(ws, L.h);
+  w0.ldb = F;
+  w0.b_rows = A;
+  w0.Nout = c->F;
+  w0.C = dWdown;
+  w0.ldc = F;
+  w0.c_split_stride = H * F;
+  wd.M = c->H;
+  moe::WgradParams wg = wd;  // dWgate_e[f][h] = sum_r dg[r][f] x[row_token[r]][h]
+  wg.g.A = dgu;
+  wg.g.lda = 2 * F;
+  wg.g.B0 = x;
+  wg.g.ldb = H;
+  wg.g.b_rows = T;
+  wg.g.row_token = at<int32_t>(ws, L.rowtok);
+  wg.g.Nout = c->H;
+  wg.g.C = dWgate;
+  wg.g.ldc = H;
+  wg.g.c_split_stride = F * H;
+  wg.M = c->F;
+  moe::WgradParams wu = wg;  // dWup_e: the du half of dg | du
+  wu.g.A = dgu + F;
+  wu.g.C = dWup;
+  MOE_LAUNCH(MOE_KERNEL_BWD_WGRAD, s, moe::launch_gemm_wgrad(wd, s));
+  MOE_LAUNCH(MOE_KERNEL_BWD_WGRAD, s, moe::launch_gemm_wgrad(wg, s));
+  MOE_LAUNCH(MOE_KERNEL_BWD_WGRAD, s, moe::launch_gemm_wgrad(wu, s));
   // router weights
   moe::RouterWgradParams rw{T, c->H, c->N, c->noisy, static_cast<const uint16_t*>(x), dlog, dnz,
                             at<float>(ws, t.rwp), dWg, dWn_opt};
