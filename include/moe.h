@@ -276,9 +276,9 @@ enum {
   MOE_KERNEL_STATS = 7,
   MOE_KERNEL_EXPERTS = 8,  /* both expert GEMMs in one persistent launch (bf16, prefill shapes) */
   MOE_KERNEL_BWD_GATE = 9,       /* backward: gate weights to the router, dE */
-  MOE_KERNEL_BWD_DGRAD = 10,     /* backward: dh with the SwiGLU derivative, and dx of the experts */
+  MOE_KERNEL_BWD_DGRAD = 10,     /* backward: dh with the SwiGLU derivative, dx of the experts, and dWdown */
   MOE_KERNEL_BWD_DX = 11,        /* backward: dx gathered back to tokens, with the router terms */
-  MOE_KERNEL_BWD_WGRAD = 12,     /* backward: expert weight gradients */
+  MOE_KERNEL_BWD_WGRAD = 12,     /* backward: the weight gradients dWgate and dWup */
   MOE_KERNEL_BWD_ROUTER = 13,    /* backward: router and noise weight gradients */
   MOE_KERNEL_COUNT = 14
 };

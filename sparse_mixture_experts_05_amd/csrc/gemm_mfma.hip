@@ -1008,24 +1008,68 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_experts_fused(FusedParams fp
   const int RB = __builtin_amdgcn_readfirstlane(__shfl(incl, 63, 64));
   const int NT1 = G1_SWIGLU ? (g1.Nout + BN / 2 - 1) / (BN / 2) : (g1.Nout + BN - 1) / BN;
   const int NT2 = (g2.Nout + BN - 1) / BN;
-  const int n1 = RB * NT1, ntot = RB * (NT1 + NT2);
+  const int n1 = RB * NT1, n2 = RB * NT2;
   const int G = gridDim.x;
   const int S = min(n1, G);  // tickets below S are remapped XCD-aware
+  // the backward's third GEMM (tiles that never wait): P of its n3 tiles go
+  // right after the g1 tiles, to keep the compute units that the first round
+  // of g1 tiles leaves free busy until those finish (about (G - n1) units, each
+  // for a g1 tile's K steps over a g3 tile's), and the rest after the g2
+  // tiles, where they fill the last round
+  constexpr bool W3 = !G1_SWIGLU;
+  int n3 = 0, P = 0, mt3 = 0, nt3 = 0;
+  if constexpr (W3) {
+    if (fp.g3.N > 0) {
+      mt3 = (fp.m3 + BM - 1) / BM;
+      nt3 = (fp.g3.Nout + BN - 1) / BN;
+      n3 = mt3 * nt3 * fp.g3.N;
+      const int kt1 = (g1.K + BK - 1) / BK;
+      const int kt3 = max(1, static_cast<int>((fp.g3.rows_max / max(1, fp.g3.N) + BK - 1) / BK));
+      P = min(n3, max(0, G - n1) * max(1, kt1 / kt3));
+    }
+  }
+  const int ntot = n1 + n2 + n3;
 
-  // tile of ticket t: gate/up (returns true) or down, its row block and position
+  // tile of ticket t: 0 a gate/up (g1) tile, 1 a down (g2) tile, 2 a g3 tile;
+  // its row block (types 0 and 1) and position
   auto decode = [&](int t, TilePos& tp, int& rb) {
     const int it = t < S ? xcd_remap(t, S) : t;
     tp = TilePos{};
-    if (it < n1) {
+    if (W3 && n3 > 0 && (it >= n1 + P + n2 || (it >= n1 && it < n1 + P))) {
+      // g3 tile j: expert e, four M tiles at a time with the N tile fastest
+      const int j = it < n1 + P ? it - n1 : it - n1 - n2;
+      constexpr int GM3 = 4;
+      const int per_e = mt3 * nt3;
+      const int e = j / per_e;
+      const int q = j - e * per_e;
+      const int g = q / (GM3 * nt3);
+      const int gm = min(GM3, mt3 - g * GM3);
+      const int rq = q - g * GM3 * nt3;
+      const int mt = g * GM3 + rq % gm;
+      tp.nt = __builtin_amdgcn_readfirstlane(rq / gm);
+      tp.ti.expert = 0;
+      tp.ti.row0 = __builtin_amdgcn_readfirstlane(mt * BM);
+      tp.ti.rows = __builtin_amdgcn_readfirstlane(min(BM, fp.m3 - mt * BM));
+      tp.split = __builtin_amdgcn_readfirstlane(e);
+      const int off = __builtin_amdgcn_readfirstlane(__shfl(eoff, e, 64));
+      const int cnt = __builtin_amdgcn_readfirstlane(__shfl(ecnt, e, 64));
+      tp.kb0 = off;
+      tp.kb1 = off + cnt;
+      tp.KT = (cnt + BK - 1) / BK;
+      rb = -1;
+      return 2;
+    }
+    const int it2 = (W3 && it >= n1 + P) ? it - P : it;  // g1 and g2 tickets without the first g3 tiles
+    if (it2 < n1) {
       // gate/up tiles go expert by expert, in groups of at most GM of the
       // expert's row blocks (split evenly), column tile by column tile with the
       // row block fastest: the tiles of a group share their weight panels, and
       // an expert's last, partly filled row block rides along with the others
-      const int e = __popcll(__ballot(incl * NT1 <= it));  // expert of the tile
+      const int e = __popcll(__ballot(incl * NT1 <= it2));  // expert of the tile
       const int rb0 = __builtin_amdgcn_readfirstlane(__shfl(incl - etl, e, 64));
       const int R = __builtin_amdgcn_readfirstlane(__shfl(etl, e, 64));
       const int ng = (R + GM - 1) / GM, base = R / ng, extra = R % ng;
-      int q = it - rb0 * NT1;  // tile within the expert
+      int q = it2 - rb0 * NT1;  // tile within the expert
       int g0 = 0, gm = base + (extra > 0 ? 1 : 0);
       for (int g = 0; q >= gm * NT1; ++g) {  // find the group (ng is small)
         q -= gm * NT1;
@@ -1037,15 +1081,15 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_experts_fused(FusedParams fp
       tp.ti = row_block<BM>(rb, eoff, ecnt, etl, incl);
       tp.kb1 = g1.K;
       tp.KT = (g1.K + BK - 1) / BK;
-      return true;
+      return 0;
     }
-    const int j = it - n1;
+    const int j = it2 - n1;
     rb = j / NT2;
     tp.nt = j % NT2;
     tp.ti = row_block<BM>(rb, eoff, ecnt, etl, incl);
     tp.kb1 = g2.K;
     tp.KT = (g2.K + BK - 1) / BK;
-    return false;
+    return 1;
   };
 
   if (threadIdx.x == 0) *s_item = atomicAdd(&fp.sched[kSchedTicket], 1);
@@ -1057,11 +1101,13 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_experts_fused(FusedParams fp
     // enough that the queue still balances the tail, early enough that the
     // atomic's latency hides); it reaches the workgroup after the K loop,
     // where the hook issues the next tile's first stage into the free stage
-    // buffer: all of it for a gate/up tile, only the weights for a down tile,
-    // whose h rows may not be ready. A reserved ticket is larger than the
-    // running one, so a workgroup that waits in a down tile holds only down
-    // tickets: every gate/up ticket still runs in or is reserved by a
-    // workgroup that waits on nothing.
+    // buffer: all of it for a gate/up (or g3) tile, only the weights for a
+    // down tile, whose h rows may not be ready. Every gate/up ticket is
+    // smaller than every down ticket, g3 tiles wait on nothing, and a
+    // workgroup reserves its next ticket only after its own wait: so a
+    // workgroup that waits in a down tile holds no other ticket, and every
+    // gate/up ticket still runs in or is reserved by a workgroup that waits on
+    // nothing.
     int reserved = ntot;  // "none" unless reserve() runs
     auto reserve = [&]() {
       if (threadIdx.x == 0) reserved = atomicAdd(&fp.sched[kSchedTicket], 1);
@@ -1074,24 +1120,36 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_experts_fused(FusedParams fp
       if (next < ntot) {
         TilePos tq;
         int rq;
-        if (decode(next, tq, rq)) {
+        const int ty = decode(next, tq, rq);
+        if (ty == 0) {
           Loader1 lq;
           lq.init(g1, tq);
           lq.issue_a(a_free, 0);
           lq.issue_b(b_free, 0);
           npre = 2;
-        } else {
+        } else if (ty == 1) {
           Loader2 lq;
           lq.init(g2, tq);
           lq.issue_b(b_free, 0);
           npre = 1;
+        } else if constexpr (W3) {
+          BwdLoader<BM, BN, WGM, WGN, BK, 2, false> lq;
+          lq.init(fp.g3, tq);
+          lq.issue_a(a_free, 0);
+          lq.issue_b(b_free, 0);
+          npre = 2;
         }
         nsbase = fb;
       }
     };
     TilePos tp;
     int rb;
-    if (decode(ticket, tp, rb)) {
+    const int ty = decode(ticket, tp, rb);
+    if (W3 && ty == 2) {
+      if constexpr (W3)
+        gemm_tile<BM, BN, WGM, WGN, STAGES, BK, false, false, decltype(hook)&, decltype(reserve)&, 2>(
+            fp.g3, tp, smem, sbase, pre, hook, reserve);
+    } else if (ty == 0) {
       gemm_tile<BM, BN, WGM, WGN, STAGES, BK, G1_SWIGLU, GATHER, decltype(hook)&, decltype(reserve)&, LAY>(
           g1, tp, smem, sbase, pre, hook, reserve);
       // publish: every wave waits until its device-scope h stores have

@@ -159,6 +159,12 @@ struct FusedParams {
   int stats;       // 1: reduce them (in the workgroup that draws the first ticket past the end)
   int spin_limit;
   int wait_extra;
+  // the backward only: a third GEMM whose tiles never wait (the weight
+  // gradient dWdown, laid out as for launch_gemm_wgrad with M = m3), run from
+  // the same queue to fill the compute units the dependent tiles leave idle;
+  // none when g3.N == 0
+  GemmParams g3;
+  int m3;
 };
 constexpr int kDefaultSpinLimit = 1 << 22;  // about a second of polling
 int fused_error_index();

@@ -741,33 +741,16 @@ moe_status moe_backward(const moe_cfg* c, const void* x, const float* Wg, const 
   gx.splits = 1;
   gx.rows_max = A;
   gx.a_rows = A;
-  {
-    int32_t* sched = at<int32_t>(ws, L.sched);
-    e = moe::launch_fill_i32(sched, moe::fused_sched_ints(L.A_max, c->N), 0, s);
-    if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "fill launch failed: %s", hipGetErrorString(e));
-    int spin = moe::kDefaultSpinLimit, extra = 0;
-    {
-      std::lock_guard<std::mutex> lk(g_wait_mu);
-      if (g_wait_spin > 0) spin = g_wait_spin;
-      extra = g_wait_extra;
-    }
-    const moe::FusedParams fp{gd, gx, sched, moe::StatsParams{}, 0, spin, extra};
-    MOE_LAUNCH(MOE_KERNEL_BWD_DGRAD, s, moe::launch_bwd_dgrad_fused(fp, s));
-  }
-  // dx = sum of the slots' rows + the router terms
-  moe::BwdDxParams dp{T, c->H, c->N, c->k, c->noisy, at<float>(ws, t.dxp), at<int32_t>(ws, L.slot), dlog, dnz, Wg,
-                      Wn, dx};
-  MOE_LAUNCH(MOE_KERNEL_BWD_DX, s, moe::launch_bwd_dx(dp, s));
-  // weight gradients per expert, K over the expert's rows of the permuted
-  // order; one launch per gradient, each grid's XCD-aware order keeping an
-  // expert's tiles together
+  // dWdown_e[h][f] = sum over the expert's rows r of dE[r][h] h[r][f], both
+  // operands K-outer: it needs nothing from this launch, so its tiles run
+  // from the same queue and fill the units the dependent dx tiles leave idle
   moe::WgradParams wd{};
   moe::GemmParams& w0 = wd.g;
   w0.offsets = offsets;
   w0.N = c->N;
   w0.rows_max = A;
   w0.splits = 1;
-  w0.A = dE;  // dWdown_e[h][f] = sum_r dE[r][h] h[r][f]
+  w0.A = dE;
   w0.lda = H;
   w0.a_rows = A;
   w0.B0 = at<uint16_t>(ws, L.h);
@@ -778,6 +761,26 @@ moe_status moe_backward(const moe_cfg* c, const void* x, const float* Wg, const 
   w0.ldc = F;
   w0.c_split_stride = H * F;
   wd.M = c->H;
+  {
+    int32_t* sched = at<int32_t>(ws, L.sched);
+    e = moe::launch_fill_i32(sched, moe::fused_sched_ints(L.A_max, c->N), 0, s);
+    if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "fill launch failed: %s", hipGetErrorString(e));
+    int spin = moe::kDefaultSpinLimit, extra = 0;
+    {
+      std::lock_guard<std::mutex> lk(g_wait_mu);
+      if (g_wait_spin > 0) spin = g_wait_spin;
+      extra = g_wait_extra;
+    }
+    const moe::FusedParams fp{gd, gx, sched, moe::StatsParams{}, 0, spin, extra, wd.g, wd.M};
+    MOE_LAUNCH(MOE_KERNEL_BWD_DGRAD, s, moe::launch_bwd_dgrad_fused(fp, s));
+  }
+  // dx = sum of the slots' rows + the router terms
+  moe::BwdDxParams dp{T, c->H, c->N, c->k, c->noisy, at<float>(ws, t.dxp), at<int32_t>(ws, L.slot), dlog, dnz, Wg,
+                      Wn, dx};
+  MOE_LAUNCH(MOE_KERNEL_BWD_DX, s, moe::launch_bwd_dx(dp, s));
+  // the other weight gradients per expert, K over the expert's rows of the
+  // permuted order; one launch per gradient, each grid's XCD-aware order
+  // keeping an expert's tiles together
   moe::WgradParams wg = wd;  // dWgate_e[f][h] = sum_r dg[r][f] x[row_token[r]][h]
   wg.g.A = dgu;
   wg.g.lda = 2 * F;
@@ -793,7 +796,6 @@ moe_status moe_backward(const moe_cfg* c, const void* x, const float* Wg, const 
   moe::WgradParams wu = wg;  // dWup_e: the du half of dg | du
   wu.g.A = dgu + F;
   wu.g.C = dWup;
-  MOE_LAUNCH(MOE_KERNEL_BWD_WGRAD, s, moe::launch_gemm_wgrad(wd, s));
   MOE_LAUNCH(MOE_KERNEL_BWD_WGRAD, s, moe::launch_gemm_wgrad(wg, s));
   MOE_LAUNCH(MOE_KERNEL_BWD_WGRAD, s, moe::launch_gemm_wgrad(wu, s));
   // router weights
