@@ -203,12 +203,129 @@ __global__ __launch_bounds__(256) void k_bwd_dx(BwdDxParams p) {
   }
 }
 
+// The same sums for N (times two when noisy) of at most 32 router columns and
+// at most KM slots, with the router weights read once per kTokX tokens: a
+// block owns kTokX tokens and 1024 columns of H (256 threads, 4 consecutive h
+// each), and each thread keeps its 4 rows of W_g (and W_noise) in registers.
+// The slot rows of kU tokens are requested together as buffer loads (a
+// dropped slot's offset is out of range and reads zeros), a batch ahead.
+// Per element the order is that of k_bwd_dx: the slots in order, then the
+// router terms in expert order (the clean gate skips the noise terms, which
+// add zeros there).
+constexpr int kTokX = 32;
+template <int NM, bool NOISY, int KM>
+__global__ __launch_bounds__(256) void k_bwd_dx_regs(BwdDxParams p) {
+  constexpr int kU = KM <= 2 ? 4 : 2;
+  __shared__ float s_dl[kTokX][NM], s_dn[NOISY ? kTokX : 1][NM];
+  __shared__ int s_sl[kTokX][KM];
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kTokX;
+  const int H = p.H, N = p.N, k = p.k;
+  for (int i = threadIdx.x; i < kTokX * NM; i += 256) {
+    const int tt = i / NM, n = i % NM;
+    const bool ok = t0 + tt < p.T && n < N;
+    s_dl[tt][n] = ok ? p.dlog[(t0 + tt) * N + n] : 0.0f;
+    if (NOISY) s_dn[tt][n] = ok ? p.dnz[(t0 + tt) * N + n] : 0.0f;
+  }
+  for (int i = threadIdx.x; i < kTokX * KM; i += 256) {
+    const int tt = i / KM, j = i % KM;
+    s_sl[tt][j] = (t0 + tt < p.T && j < k) ? p.slot[(t0 + tt) * k + j] : -1;
+  }
+  const int h0 = (blockIdx.y * 256 + threadIdx.x) * 4;
+  const bool hv = h0 < H;  // H % 4 == 0
+  // the thread's 4 rows of W are 4 N contiguous floats: 16-byte loads when
+  // N % 4 == 0 (columns past N read as zero through the range check)
+  float wg[4][NM], wn[NOISY ? 4 : 1][NM];
+  if (N % 4 == 0) {
+    const __amdgpu_buffer_rsrc_t rg = uniform_rsrc(p.Wg, static_cast<int64_t>(H) * N * 4);
+    const __amdgpu_buffer_rsrc_t rn = uniform_rsrc(NOISY ? p.Wn : p.Wg, static_cast<int64_t>(H) * N * 4);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int n = 0; n < NM; n += 4) {
+        const uint32_t off = (hv && n < N) ? static_cast<uint32_t>((h0 + q) * N + n) * 4u : kOOB;
+        const f32x4_t a = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rg, off, 0, 0));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) wg[q][n + e] = a[e];
+        if (NOISY) {
+          const f32x4_t b = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rn, off, 0, 0));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) wn[q][n + e] = b[e];
+        }
+      }
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int n = 0; n < NM; ++n) {
+        const bool ok = hv && n < N;
+        wg[q][n] = ok ? p.Wg[static_cast<int64_t>(h0 + q) * N + n] : 0.0f;
+        if (NOISY) wn[q][n] = ok ? p.Wn[static_cast<int64_t>(h0 + q) * N + n] : 0.0f;
+      }
+  }
+  const __amdgpu_buffer_rsrc_t rp = uniform_rsrc(p.dx_perm, p.rows * H * 4);
+  __syncthreads();
+  if (!hv) return;
+  const int tend = static_cast<int>(min(static_cast<int64_t>(kTokX), p.T - t0));
+  // double-buffered: the slot rows of the next kU tokens are requested before
+  // this batch is summed and stored
+  f32x4_t v[2][kU][KM];
+  auto load = [&](f32x4_t (&dst)[kU][KM], int tb) {
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+#pragma unroll
+      for (int j = 0; j < KM; ++j) {
+        const int sl = tb + u < tend ? s_sl[tb + u][j] : -1;
+        const uint32_t off = sl >= 0 ? (static_cast<uint32_t>(sl) * static_cast<uint32_t>(H) + h0) * 4u : kOOB;
+        dst[u][j] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rp, off, 0, 0));
+      }
+  };
+  auto finish = [&](const f32x4_t (&src)[kU][KM], int tb) {
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      if (tb + u >= tend) break;
+      const int tt = tb + u;
+      f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int j = 0; j < KM; ++j) acc += src[u][j];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int n = 0; n < NM; ++n)
+          acc[q] = NOISY ? fmaf(s_dl[tt][n], wg[q][n], fmaf(s_dn[tt][n], wn[q][n], acc[q]))
+                         : fmaf(s_dl[tt][n], wg[q][n], acc[q]);
+      *reinterpret_cast<f32x4_t*>(p.dx + (t0 + tt) * H + h0) = acc;
+    }
+  };
+  load(v[0], 0);
+  for (int tb = 0; tb < tend; tb += 2 * kU) {
+    load(v[1], tb + kU);
+    finish(v[0], tb);
+    if (tb + 2 * kU < tend) load(v[0], tb + 2 * kU);
+    finish(v[1], tb + kU);
+  }
+}
+
 // Router weight gradients dW_g = x^T dlog and dW_noise = x^T dnz, in two
 // passes for a fixed summation order: pass 1 sums a chunk of kTokW tokens per
 // block into partials [chunk][H][N (+N)] (thread = HPT consecutive h with one
 // vector load of x per token, all N), pass 2 adds the chunks in order.
 constexpr int kTokW = 32;
 constexpr int kRwThreads = 128;
+
+// v[0..HPT)[n] to dst[0..HPT) with 16-byte (or narrower) vector stores
+template <int HPT, int NM>
+__device__ __forceinline__ void store_run(float* dst, const float (&v)[HPT][NM], int n) {
+  if constexpr (HPT >= 4) {
+#pragma unroll
+    for (int q = 0; q < HPT; q += 4)
+      *reinterpret_cast<f32x4_t*>(dst + q) = f32x4_t{v[q][n], v[q + 1][n], v[q + 2][n], v[q + 3][n]};
+  } else if constexpr (HPT == 2) {
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    *reinterpret_cast<f32x2_t*>(dst) = f32x2_t{v[0][n], v[1][n]};
+  } else {
+    dst[0] = v[0][n];
+  }
+}
 template <int NMAX, bool NOISY, int HPT>
 __global__ __launch_bounds__(kRwThreads) void k_router_wgrad(RouterWgradParams p) {
   __shared__ float s_dl[kTokW][NMAX], s_dn[NOISY ? kTokW : 1][NMAX];
@@ -287,22 +404,21 @@ __global__ __launch_bounds__(kRwThreads) void k_router_wgrad(RouterWgradParams p
       }
   }
   }
+  // partials [chunk][column][H]: a lane stores its HPT consecutive h of one
+  // column as one vector, so a wave's store covers contiguous memory
   const int per = N * (NOISY ? 2 : 1);
+  float* out = p.part + static_cast<int64_t>(blockIdx.y) * per * p.H + h0;
 #pragma unroll
-  for (int q = 0; q < HPT; ++q) {
-    float* out = p.part + (static_cast<int64_t>(blockIdx.y) * p.H + h0 + q) * per;
-#pragma unroll
-    for (int n = 0; n < NMAX; ++n)
-      if (n < N) {
-        out[n] = a[q][n];
-        if (NOISY) out[N + n] = b[q][n];
-      }
-  }
+  for (int n = 0; n < NMAX; ++n)
+    if (n < N) {
+      store_run<HPT>(out + static_cast<int64_t>(n) * p.H, a, n);
+      if (NOISY) store_run<HPT>(out + static_cast<int64_t>(N + n) * p.H, b, n);
+    }
 }
 
 __global__ __launch_bounds__(256) void k_router_wgrad_sum(RouterWgradParams p, int chunks) {
   const int per = p.N * (p.noisy ? 2 : 1);
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;  // column * H + h
   if (i >= static_cast<int64_t>(p.H) * per) return;
   // the chunks in order, eight loads in flight at a time
   float v = 0.0f;
@@ -314,7 +430,7 @@ __global__ __launch_bounds__(256) void k_router_wgrad_sum(RouterWgradParams p, i
     for (int q = 0; q < 8; ++q)
       if (c0 + q < chunks) v += u[q];
   }
-  const int64_t h = i / per, n = i % per;
+  const int64_t n = i / p.H, h = i % p.H;
   if (n < p.N) p.dWg[h * p.N + n] = v;
   else p.dWn[h * p.N + (n - p.N)] = v;
 }
@@ -329,6 +445,21 @@ hipError_t launch_bwd_gate(const BwdGateParams& p, hipStream_t s) {
 
 hipError_t launch_bwd_dx(const BwdDxParams& p, hipStream_t s) {
   if (p.T <= 0) return hipSuccess;
+  if (p.k <= 4 && p.N <= (p.noisy ? 16 : 32)) {
+    const dim3 grid(static_cast<unsigned>((p.T + kTokX - 1) / kTokX), static_cast<unsigned>((p.H / 4 + 255) / 256));
+#define MOE_DX(NM, NZ)                                                                         \
+  do {                                                                                         \
+    if (p.k <= 2) hipLaunchKernelGGL((k_bwd_dx_regs<NM, NZ, 2>), grid, dim3(256), 0, s, p);    \
+    else hipLaunchKernelGGL((k_bwd_dx_regs<NM, NZ, 4>), grid, dim3(256), 0, s, p);             \
+  } while (0)
+    if (p.noisy) {
+      if (p.N <= 8) MOE_DX(8, true); else MOE_DX(16, true);
+    } else {
+      if (p.N <= 8) MOE_DX(8, false); else if (p.N <= 16) MOE_DX(16, false); else MOE_DX(32, false);
+    }
+#undef MOE_DX
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(k_bwd_dx, dim3(static_cast<unsigned>((p.T + kTokB - 1) / kTokB)), dim3(256), 0, s, p);
   return hipGetLastError();
 }

@@ -219,6 +219,7 @@ struct BwdDxParams {
   int64_t T;
   int H, N, k, noisy;
   const float* dx_perm;     // [rows][H]
+  int64_t rows;             // rows of dx_perm
   const int32_t* slot;      // [T,k]
   const float* dlog;        // [T,N]
   const float* dnz;         // [T,N]
@@ -234,7 +235,7 @@ struct RouterWgradParams {
   const uint16_t* x;        // [T,H] bf16
   const float* dlog;        // [T,N]
   const float* dnz;         // [T,N]
-  float* part;              // [router_wgrad_chunks(T)][H][N * (1 + noisy)]
+  float* part;              // [router_wgrad_chunks(T)][N * (1 + noisy)][H]
   float* dWg;               // [H,N]
   float* dWn;               // [H,N]
 };

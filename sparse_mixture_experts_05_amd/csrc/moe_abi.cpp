@@ -775,8 +775,8 @@ moe_status moe_backward(const moe_cfg* c, const void* x, const float* Wg, const 
     MOE_LAUNCH(MOE_KERNEL_BWD_DGRAD, s, moe::launch_bwd_dgrad_fused(fp, s));
   }
   // dx = sum of the slots' rows + the router terms
-  moe::BwdDxParams dp{T, c->H, c->N, c->k, c->noisy, at<float>(ws, t.dxp), at<int32_t>(ws, L.slot), dlog, dnz, Wg,
-                      Wn, dx};
+  moe::BwdDxParams dp{T, c->H, c->N, c->k, c->noisy, at<float>(ws, t.dxp), L.A_max, at<int32_t>(ws, L.slot), dlog,
+                      dnz, Wg, Wn, dx};
   MOE_LAUNCH(MOE_KERNEL_BWD_DX, s, moe::launch_bwd_dx(dp, s));
   // the other weight gradients per expert, K over the expert's rows of the
   // permuted order; one launch per gradient, each grid's XCD-aware order
