@@ -33,6 +33,12 @@ CASES = {
                                                         noisy=True, capacity=110, out_scale=2.0),
     "noisy_k4_n16": lambda: synth.make_independent("bwd_k4", 103, 520, 512, 192, 16, 4, noisy=True, out_scale=4.0),
     "skewed_empty_expert": lambda: _skew_empty(),
+    # top-6 of 40 noisy experts: the general dx gather (k > 4) and the widest
+    # router-gradient path (64 columns, noise)
+    "wide_k6_n40_noisy": lambda: synth.make_independent("bwd_k6", 105, 400, 256, 128, 40, 6, noisy=True,
+                                                        out_scale=2.0),
+    # 24 clean experts, top-3, F not a multiple of 64
+    "n24_k3_ragged": lambda: synth.make_independent("bwd_n24", 106, 420, 384, 136, 24, 3),
 }
 
 
