@@ -191,9 +191,10 @@ def main():
     fused = abi.moe_profile_read()[1] > 0
     dom_id = abi.MOE_KERNEL_EXPERTS if fused else abi.MOE_KERNEL_GEMM1
     if train:
-        # a training step runs three GEMM kernels of 6*A*H*F flops each (the
-        # forward's experts, the backward's dgrad pair and its three weight
-        # gradients): the dominant one is the slowest of them per step
+        # a training step runs three expert-GEMM kernels: the forward's experts
+        # (6*A*H*F flops), the backward's input-gradient launch with dWdown
+        # (8*A*H*F) and the dWgate and dWup launches (2*A*H*F each): the
+        # dominant one is the slowest of them per step
         per_step = {}
         for kid in (abi.MOE_KERNEL_EXPERTS, abi.MOE_KERNEL_BWD_DGRAD, abi.MOE_KERNEL_BWD_WGRAD):
             abi.moe_profile_select(kid)
@@ -268,10 +269,14 @@ def main():
     # 6*A*H*F flops and reads the active experts' three matrices; the gate/up
     # GEMM alone does 4*A*H*F and reads two of them
     if train:
-        dom_name = {abi.MOE_KERNEL_EXPERTS: "experts_fused_forward", abi.MOE_KERNEL_BWD_DGRAD: "backward_dgrad_pair",
-                    abi.MOE_KERNEL_BWD_WGRAD: "backward_weight_gradients"}[dom_id]
-        dom_flops = 6.0 * A * H * F
-        dom_bytes = active * 3 * F * H * eb
+        dom_name = {abi.MOE_KERNEL_EXPERTS: "experts_fused_forward",
+                    abi.MOE_KERNEL_BWD_DGRAD: "backward_input_gradients_and_dWdown",
+                    abi.MOE_KERNEL_BWD_WGRAD: "backward_dWgate_dWup"}[dom_id]
+        # per launch
+        dom_flops = {abi.MOE_KERNEL_EXPERTS: 6.0, abi.MOE_KERNEL_BWD_DGRAD: 8.0,
+                     abi.MOE_KERNEL_BWD_WGRAD: 2.0}[dom_id] * A * H * F
+        dom_bytes = {abi.MOE_KERNEL_EXPERTS: 3, abi.MOE_KERNEL_BWD_DGRAD: 3,
+                     abi.MOE_KERNEL_BWD_WGRAD: 0}[dom_id] * active * F * H * eb + A * H * eb
     elif fused:
         dom_name = "experts_gate_up_swiglu_down"
         dom_flops = 6.0 * A * H * F + 6.0 * T * H * Fs
