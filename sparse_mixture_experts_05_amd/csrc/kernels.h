@@ -171,8 +171,10 @@ int fused_error_index();
 int fused_sched_ints(int64_t rows_max, int N);
 bool gemm_fused_supported(int64_t rows_max, int N, int K1, int F);
 hipError_t launch_experts_fused(const FusedParams& fp, hipStream_t s);
-// The backward's dgrad pair in the same persistent kernel: g1 = dh with the
-// SwiGLU-derivative epilogue (epi 1, writing dg|du), g2 = dx reading dg|du.
+// The backward's input gradients in the same persistent kernel: g1 = dh with
+// the SwiGLU-derivative epilogue (epi 1, writing dg|du), g2 = dx reading
+// dg|du, both with the weights as K-outer B operands; g3 (dWdown) fills the
+// queue's idle units.
 hipError_t launch_bwd_dgrad_fused(const FusedParams& fp, hipStream_t s);
 
 // ---- combine (combine.hip) --------------------------------------------------
