@@ -157,6 +157,7 @@ moe_status moe_grouped_swiglu(const moe_cfg* cfg, const void* x_perm_or_x, const
  * LLaMA-MoE v2 article, rescaling section):
  *   y[t] = s * sum_{j=0..k-1, slot[t,j] >= 0} topk_w[t,j] * y_perm[slot[t,j]]
  * summed in j order in fp32; a token with every slot dropped gets y = 0.
+ *   y_perm [T*k,H] fp32; a slot at or past T*k counts as dropped.
  *   y [T,H] cfg->out. Needs no workspace. */
 moe_status moe_combine(const moe_cfg* cfg, const float* y_perm, const int32_t* slot, const float* topk_w,
                        void* y, hipStream_t stream);
@@ -293,6 +294,24 @@ moe_status moe_profile_read(double* total_ms, int64_t* launches);
  * restores normal operation. Process-wide, host only; MOE_ERR_INVALID for
  * wait_extra < 0. */
 moe_status moe_debug_set_wait(int32_t spin_limit, int32_t wait_extra);
+
+/* Bounds checks. Every index that data can steer (a slot, a row_token entry,
+ * the offsets) is guarded in every build: an out-of-range value is dropped or
+ * clamped, never followed. The debug build, libmoe_debug.so (compiled with
+ * -DMOE_DEBUG; moe_debug_build() returns 1 there, 0 in libmoe.so), also
+ * records each guard that fires by setting a bit of a 32-bit word in the
+ * workspace at byte offset moe_debug_word_offset(cfg) (0 for an invalid
+ * cfg; the same offset in the residual and training workspaces):
+ *   1 a kept slot's row at or past T*k (scatter), 2 a row_token entry
+ *   outside x (moe_permute's gather), 4 a slot past y_perm (combine),
+ *   8 offsets outside [0, rows] or decreasing (expert GEMMs), 16 a slot past
+ *   the rows in the backward.
+ * The library never clears the word; the caller zeroes it. On valid input no
+ * bit is set. The release build never writes it. For tests and debugging;
+ * the debug build is as fast as the release build up to the atomics of
+ * guards that fire. */
+int32_t moe_debug_build(void);
+size_t moe_debug_word_offset(const moe_cfg* cfg);
 
 #ifdef __cplusplus
 }

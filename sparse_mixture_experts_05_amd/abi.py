@@ -7,6 +7,7 @@ there is no fallback: without the built library every call raises.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 from dataclasses import dataclass
@@ -16,6 +17,7 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
+DEBUG_LIB_PATH = os.path.join(_HERE, "libmoe_debug.so")  # the same ABI with recorded bounds checks
 
 MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_DEVICE = range(5)
 MOE_F32, MOE_BF16 = 0, 1
@@ -28,7 +30,8 @@ EXPORTED = ["moe_capacity", "moe_check", "moe_workspace_bytes", "moe_route", "mo
             "moe_grouped_swiglu", "moe_combine", "moe_forward", "moe_status_str", "moe_last_error",
             "moe_profile_select", "moe_profile_read", "moe_debug_set_wait", "moe_forward_noalloc",
             "moe_noalloc_scratch_bytes", "moe_forward_residual", "moe_residual_workspace_bytes",
-            "moe_train_workspace_bytes", "moe_forward_train", "moe_backward"]
+            "moe_train_workspace_bytes", "moe_forward_train", "moe_backward", "moe_debug_build",
+            "moe_debug_word_offset"]
 
 
 class moe_cfg(ctypes.Structure):
@@ -99,6 +102,10 @@ def load_library(path: Optional[str] = None):
     lib.moe_noalloc_scratch_bytes.restype = sz
     lib.moe_debug_set_wait.argtypes = [i32, i32]
     lib.moe_debug_set_wait.restype = i32
+    lib.moe_debug_build.argtypes = []
+    lib.moe_debug_build.restype = i32
+    lib.moe_debug_word_offset.argtypes = [cfgp]
+    lib.moe_debug_word_offset.restype = sz
     if path is None:
         _lib = lib
     return lib
@@ -280,3 +287,24 @@ def moe_profile_read():
 
 def moe_debug_set_wait(spin_limit: int, wait_extra: int):
     _check(load_library().moe_debug_set_wait(int(spin_limit), int(wait_extra)), "moe_debug_set_wait")
+
+
+def moe_debug_build() -> bool:
+    return bool(load_library().moe_debug_build())
+
+
+def moe_debug_word_offset(cfg: MoEConfig) -> int:
+    return int(load_library().moe_debug_word_offset(ctypes.byref(cfg.c())))
+
+
+@contextlib.contextmanager
+def use_library(path: str):
+    """Route every call of this module through the library at `path` (for
+    example DEBUG_LIB_PATH) inside the block."""
+    global _lib
+    saved = load_library()
+    _lib = load_library(path)
+    try:
+        yield _lib
+    finally:
+        _lib = saved

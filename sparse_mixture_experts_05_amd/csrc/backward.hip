@@ -52,7 +52,7 @@ __global__ __launch_bounds__(256) void k_bwd_gate(BwdGateParams p) {
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       const int j = j0 + q;
-      sl[q] = j < k ? p.slot[t * k + j] : -1;
+      sl[q] = j < k ? checked_slot(p.slot[t * k + j], p.rows, p.dbg, kDbgBwdSlot) : -1;
       wj[q] = j < k ? p.topk_w[t * k + j] : 0.0f;
       acc[q] = 0.0f;
     }
@@ -153,7 +153,7 @@ __global__ __launch_bounds__(256) void k_bwd_dx(BwdDxParams p) {
   }
   for (int i = threadIdx.x; i < kTokB * 8; i += 256) {
     const int tt = i / 8, j = i % 8;
-    s_sl[tt][j] = (t0 + tt < p.T && j < k) ? p.slot[(t0 + tt) * k + j] : -1;
+    s_sl[tt][j] = (t0 + tt < p.T && j < k) ? checked_slot(p.slot[(t0 + tt) * k + j], p.rows, p.dbg, kDbgBwdSlot) : -1;
   }
   __syncthreads();
   const bool vec = (N % 4) == 0;
@@ -171,7 +171,7 @@ __global__ __launch_bounds__(256) void k_bwd_dx(BwdDxParams p) {
         }
       } else {
         for (int j = 0; j < k; ++j) {
-          const int sl = p.slot[(t0 + tt) * k + j];
+          const int sl = checked_slot(p.slot[(t0 + tt) * k + j], p.rows, p.dbg, kDbgBwdSlot);
           if (sl >= 0) acc[tt] += *reinterpret_cast<const f32x4_t*>(p.dx_perm + static_cast<int64_t>(sl) * H + c * 4);
         }
       }
@@ -228,7 +228,7 @@ __global__ __launch_bounds__(256) void k_bwd_dx_regs(BwdDxParams p) {
   }
   for (int i = threadIdx.x; i < kTokX * KM; i += 256) {
     const int tt = i / KM, j = i % KM;
-    s_sl[tt][j] = (t0 + tt < p.T && j < k) ? p.slot[(t0 + tt) * k + j] : -1;
+    s_sl[tt][j] = (t0 + tt < p.T && j < k) ? checked_slot(p.slot[(t0 + tt) * k + j], p.rows, p.dbg, kDbgBwdSlot) : -1;
   }
   const int h0 = (blockIdx.y * 256 + threadIdx.x) * 4;
   const bool hv = h0 < H;  // H % 4 == 0

@@ -80,7 +80,7 @@ __device__ __forceinline__ void token_any(const CombineParams& p, int64_t t, int
   for (int64_t c = lane; c < H4; c += nl) {
     f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
     for (int j = 0; j < k; ++j) {
-      const int sl = p.slot[t * k + j];
+      const int sl = checked_slot(p.slot[t * k + j], p.rows, p.dbg, kDbgCombineSlot);
       if (sl < 0) continue;
       const float w = p.topk_w[t * k + j];
       const float* src = p.y_perm + static_cast<int64_t>(sl) * p.H + c * 4;

@@ -29,7 +29,7 @@ __global__ __launch_bounds__(256) void k_combine(CombineParams p) {
   float w[KMAX];
 #pragma unroll
   for (int j = 0; j < KMAX; ++j) {
-    sl[j] = j < k ? p.slot[t * k + j] : -1;
+    sl[j] = j < k ? checked_slot(p.slot[t * k + j], p.rows, p.dbg, kDbgCombineSlot) : -1;
     w[j] = j < k ? p.topk_w[t * k + j] : 0.0f;
   }
 #pragma unroll 4

@@ -76,12 +76,66 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* base,
 // device-side offsets, clamped to [0, rows_max): offsets that a caller
 // passes in (or that disagree with the row bound the workspace was sized
 // for) can then never move a tile's loads or stores past its buffers.
+// Bounds invariants. Every index that data can steer is guarded in every
+// build (the access is skipped or clamped); a debug build (-DMOE_DEBUG) also
+// records a guard that fires by raising `bit` of the workspace's debug word
+// (dbg may be null: nothing recorded). On valid data no guard fires.
+constexpr int kDbgScatterRow = 1;   // a kept slot's row at or past T*k
+constexpr int kDbgGatherRow = 2;    // a row_token entry outside x's rows
+constexpr int kDbgCombineSlot = 4;  // a slot at or past y_perm's rows
+constexpr int kDbgOffsets = 8;      // offsets outside [0, rows_max] or decreasing
+constexpr int kDbgBwdSlot = 16;     // the backward: a slot at or past the rows
+__device__ __forceinline__ void debug_flag(int32_t* dbg, int bit) {
+#ifdef MOE_DEBUG
+  if (dbg) __hip_atomic_fetch_or(dbg, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#else
+  (void)dbg;
+  (void)bit;
+#endif
+}
+
+// A slot of a buffer of `rows` rows: the slot itself when it is in range,
+// else -1 (a dropped slot), raising `bit`.
+__device__ __forceinline__ int checked_slot(int s, int64_t rows, int32_t* dbg, int bit) {
+  if (s >= rows) {
+    debug_flag(dbg, bit);
+    return -1;
+  }
+  return s;
+}
+
 __device__ __forceinline__ void expert_segment(const int32_t* __restrict__ offsets, int e, int rows_max, int& off,
-                                               int& cnt) {
-  const int a = min(max(offsets[e], 0), rows_max);
-  const int b = min(max(offsets[e + 1], a), rows_max);
+                                               int& cnt, int32_t* dbg = nullptr) {
+  const int o0 = offsets[e], o1 = offsets[e + 1];
+  const int a = min(max(o0, 0), rows_max);
+  const int b = min(max(o1, a), rows_max);
+  if (a != o0 || b != o1) debug_flag(dbg, kDbgOffsets);
   off = a;
   cnt = b - a;
+}
+
+// Lane e < N of a wave: expert e's segment [off, off + cnt), with the offsets
+// clamped to [0, rows_max] and made non-decreasing (a running maximum over
+// the experts before it), so that the segments never overlap and together
+// hold at most rows_max rows whatever a caller passes; lanes >= N get empty
+// segments. Valid offsets come back unchanged; any other raises kDbgOffsets.
+// Every lane of the wave must call it.
+__device__ __forceinline__ void expert_segment_wave(const int32_t* __restrict__ offsets, int N, int rows_max,
+                                                    int& off, int& cnt, int32_t* dbg = nullptr) {
+  const int lane = threadIdx.x & 63;
+  const bool v = lane < N;
+  const int o0 = v ? offsets[lane] : 0, o1 = v ? offsets[lane + 1] : 0;
+  const int a = min(max(o0, 0), rows_max);
+  int A = v ? a : 0;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int u = __shfl_up(A, d, 64);
+    if (lane >= d) A = max(A, u);
+  }
+  const int B = max(A, min(max(o1, 0), rows_max));
+  if (v && (A != o0 || B != o1)) debug_flag(dbg, kDbgOffsets);
+  off = v ? A : 0;
+  cnt = v ? B - A : 0;
 }
 
 struct TileInfo {
@@ -95,10 +149,10 @@ struct TileInfo {
 // counts locates the expert. Returns false past the last tile.
 template <int BM>
 __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ offsets, int N, int rows_max, int mt,
-                                          TileInfo& ti) {
+                                          TileInfo& ti, int32_t* dbg = nullptr) {
   const int lane = threadIdx.x & 63;
   int off = 0, cnt = 0;
-  if (lane < N) expert_segment(offsets, lane, rows_max, off, cnt);
+  expert_segment_wave(offsets, N, rows_max, off, cnt, dbg);
   const int tl = (cnt + BM - 1) / BM;
   int incl = tl;
 #pragma unroll

@@ -83,7 +83,7 @@ __device__ __forceinline__ bool decode_tile(const GemmParams& p, TilePos& tp) {
   const int ntiles = (p.Nout + NO - 1) / NO;
   // per-expert m-tile counts (lane e = expert e), inclusive scan over lanes
   int eoff = 0, ecnt = 0;
-  if (lane < p.N) expert_segment(p.offsets, lane, static_cast<int>(p.rows_max), eoff, ecnt);
+  expert_segment_wave(p.offsets, p.N, static_cast<int>(p.rows_max), eoff, ecnt, p.dbg);
   const int etl = (ecnt + BM - 1) / BM;
   int incl = etl;
 #pragma unroll
@@ -997,7 +997,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_experts_fused(FusedParams fp
   // (clamped to the rows the workspace holds, so RB never exceeds the row
   // blocks the queue counters were sized for)
   int eoff = 0, ecnt = 0;
-  if (lane < g1.N) expert_segment(g1.offsets, lane, static_cast<int>(g1.rows_max), eoff, ecnt);
+  expert_segment_wave(g1.offsets, g1.N, static_cast<int>(g1.rows_max), eoff, ecnt, g1.dbg);
   const int etl = (ecnt + BM - 1) / BM;
   int incl = etl;
 #pragma unroll
@@ -1005,6 +1005,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_experts_fused(FusedParams fp
     const int v = __shfl_up(incl, d, 64);
     if (lane >= d) incl += v;
   }
+  // the segments do not overlap and hold at most rows_max rows, so RB stays
+  // within the ceil(rows_max / BM) + N row blocks the queue counters hold
   const int RB = __builtin_amdgcn_readfirstlane(__shfl(incl, 63, 64));
   const int NT1 = G1_SWIGLU ? (g1.Nout + BN / 2 - 1) / (BN / 2) : (g1.Nout + BN - 1) / BN;
   const int NT2 = (g2.Nout + BN - 1) / BN;
@@ -1216,7 +1218,7 @@ __global__ __launch_bounds__(512) void k_gemm_wgrad(WgradParams wp) {
   tp.ti.rows = __builtin_amdgcn_readfirstlane(min(256, M - mt * 256));
   tp.split = __builtin_amdgcn_readfirstlane(e);
   int off = 0, cnt = 0;
-  expert_segment(p.offsets, e, static_cast<int>(p.rows_max), off, cnt);
+  expert_segment(p.offsets, e, static_cast<int>(p.rows_max), off, cnt, p.dbg);
   tp.kb0 = __builtin_amdgcn_readfirstlane(off);
   tp.kb1 = __builtin_amdgcn_readfirstlane(off + cnt);
   tp.KT = (cnt + 63) / 64;

@@ -30,7 +30,7 @@ __global__ __launch_bounds__(256) void k_gemm_simple(GemmParams p) {
   const int mt = bid % mtiles;
   const int split = bid / mtiles;
   TileInfo ti;
-  if (!find_tile<TM>(p.offsets, p.N, static_cast<int>(p.rows_max), mt, ti)) return;
+  if (!find_tile<TM>(p.offsets, p.N, static_cast<int>(p.rows_max), mt, ti, p.dbg)) return;
 
   const int kper = (p.K + p.splits - 1) / p.splits;
   const int kb0 = split * kper;

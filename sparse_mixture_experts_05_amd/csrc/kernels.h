@@ -74,6 +74,7 @@ struct ScatterParams {
   int32_t* row_token;       // [T*k]
   int32_t* zero;            // [zero_n] set to 0 by block 0 (the expert kernel's queue counters), or null
   int zero_n;
+  int32_t* dbg;             // debug word, or null
 };
 hipError_t launch_scatter(const ScatterParams& p, hipStream_t s);
 
@@ -85,6 +86,7 @@ struct GatherParams {
   int64_t rows_max;       // T*k
   int H, N, elem_bytes;
   int64_t T;              // rows of x
+  int32_t* dbg;           // debug word, or null
 };
 hipError_t launch_gather(const GatherParams& p, hipStream_t s);
 
@@ -124,6 +126,7 @@ struct GemmParams {
   // elements per expert); the N columns are contiguous within a row
   int64_t b_rows;
   int ksplit;
+  int32_t* dbg;               // debug word, or null
 };
 // Decode-shaped tiles (few rows per expert), one launch per GEMM.
 hipError_t launch_gemm_decode(const GemmParams& p, hipStream_t s);
@@ -193,6 +196,8 @@ struct CombineParams {
   const float* residual;     // [res_splits][T][H]: added unscaled, y = residual + s * sum; or null
   int64_t res_split_stride;  // elements
   int res_splits;
+  int64_t rows;              // rows of y_perm (per split); a slot at or past it adds nothing
+  int32_t* dbg;              // debug word, or null
 };
 hipError_t launch_combine(const CombineParams& p, hipStream_t s);
 
@@ -214,6 +219,8 @@ struct BwdGateParams {
   uint16_t* dE;             // [rows][H] bf16: s w dy at each kept slot's row
   float* dlog;              // [T,N] gradient of the clean logits
   float* dnz;               // [T,N] gradient of the noise logits (noisy)
+  int64_t rows;             // rows of y_perm and dE; a slot at or past it is skipped
+  int32_t* dbg;             // debug word, or null
 };
 hipError_t launch_bwd_gate(const BwdGateParams& p, hipStream_t s);
 
@@ -228,6 +235,7 @@ struct BwdDxParams {
   const float* Wg;          // [H,N]
   const float* Wn;          // [H,N]
   float* dx;                // [T,H]
+  int32_t* dbg;             // debug word, or null
 };
 hipError_t launch_bwd_dx(const BwdDxParams& p, hipStream_t s);
 

@@ -83,7 +83,7 @@ struct Layout {
   bool mfma = false;
   bool fused = false;    // both expert GEMMs in one persistent launch
   size_t hist = 0, stat = 0, h = 0, yperm = 0, idx = 0, w = 0, slot = 0, rowtok = 0, counts = 0, kept = 0,
-         offsets = 0, sched = 0, total = 0;
+         offsets = 0, sched = 0, dbg = 0, total = 0;
 };
 
 bool use_mfma(const moe_cfg* c) { return c->act == MOE_BF16 && c->F % 8 == 0; }
@@ -130,6 +130,7 @@ Layout layout(const moe_cfg* c) {
   L.kept = take(static_cast<size_t>(c->N) * 4);
   L.offsets = take(static_cast<size_t>(c->N + 1) * 4);
   L.sched = take(L.fused ? static_cast<size_t>(moe::fused_sched_ints(L.A_max, c->N)) * 4 : 0);
+  L.dbg = take(4);  // the debug word (written by debug builds only)
   L.total = o;
   return L;
 }
@@ -174,7 +175,7 @@ moe_status zero_expert_outputs(const moe_cfg* c, int32_t* a, int32_t* b, int32_t
 moe_status run_gemms(const moe_cfg* c, const Layout& L, const void* a, const int32_t* row_token,
                      const int32_t* offsets, const void* Wgate, const void* Wup, const void* Wdown, float* y_perm,
                      int splits, void* ws, bool sched_zeroed, hipStream_t s,
-                     const moe::StatsParams* stats_tail = nullptr, float* gu = nullptr) {
+                     const moe::StatsParams* stats_tail = nullptr, float* gu = nullptr, int32_t* dbg = nullptr) {
   const int bf16 = c->act == MOE_BF16;
   moe::GemmParams g1{};
   g1.A = a;
@@ -196,6 +197,7 @@ moe_status run_gemms(const moe_cfg* c, const Layout& L, const void* a, const int
   g1.a_rows = row_token ? c->T : c->T * c->k;
   g1.swiglu = 1;
   g1.gu = gu;
+  g1.dbg = dbg ? dbg : at<int32_t>(ws, L.dbg);
   moe::GemmParams g2 = g1;
   g2.gu = nullptr;
   g2.A = at<char>(ws, L.h);
@@ -294,7 +296,7 @@ moe_status forward_launch(const moe_cfg* c, const void* x, const float* Wg, cons
   moe::ScatterParams sc{topk_idx, at<int32_t>(ws, L.hist), L.hist_tokens, c->T, c->N, c->k, c->capacity,
                         (!stats && load_opt && !train) ? load_opt : at<int32_t>(ws, L.counts), kept_opt, offsets, slot,
                         row_token, L.fused ? at<int32_t>(ws, L.sched) : nullptr,
-                        L.fused ? moe::fused_sched_ints(L.A_max, c->N) : 0};
+                        L.fused ? moe::fused_sched_ints(L.A_max, c->N) : 0, at<int32_t>(ws, L.dbg)};
   MOE_LAUNCH(MOE_KERNEL_SCATTER, s, moe::launch_scatter(sc, s));
   if (train && !stats && load_opt) {
     const hipError_t e = hipMemcpyAsync(load_opt, at<int32_t>(ws, L.counts), sizeof(int32_t) * c->N,
@@ -308,7 +310,8 @@ moe_status forward_launch(const moe_cfg* c, const void* x, const float* Wg, cons
   moe::CombineParams cp{y_perm, L.A_max * static_cast<int64_t>(c->H), L.splits, slot, topk_w, y,
                         c->out == MOE_BF16, c->T, c->H, c->k, c->out_scale,
                         L.fused ? at<int32_t>(ws, L.sched) + moe::fused_error_index() : nullptr,
-                        res ? res->y : nullptr, res ? res->split_stride : 0, res ? res->splits : 0};
+                        res ? res->y : nullptr, res ? res->split_stride : 0, res ? res->splits : 0, L.A_max,
+                        at<int32_t>(ws, L.dbg)};
   MOE_LAUNCH(MOE_KERNEL_COMBINE, s, moe::launch_combine(cp, s));
   return MOE_OK;
 }
@@ -438,10 +441,11 @@ moe_status moe_permute(const moe_cfg* c, const void* x, const int32_t* topk_idx,
   moe::HistParams hp{topk_idx, c->T, c->N, c->k, L.hist_tokens, at<int32_t>(ws, L.hist)};
   MOE_LAUNCH(MOE_KERNEL_HIST, s, moe::launch_hist(hp, s));
   moe::ScatterParams sp{topk_idx, at<int32_t>(ws, L.hist), L.hist_tokens, c->T, c->N, c->k, c->capacity,
-                        counts, nullptr, offsets, slot, row_token};
+                        counts, nullptr, offsets, slot, row_token, nullptr, 0, at<int32_t>(ws, L.dbg)};
   MOE_LAUNCH(MOE_KERNEL_SCATTER, s, moe::launch_scatter(sp, s));
   if (x_perm) {
-    moe::GatherParams gp{x, x_perm, row_token, offsets, c->T * c->k, c->H, c->N, c->act == MOE_BF16 ? 2 : 4, c->T};
+    moe::GatherParams gp{x,   x_perm, row_token, offsets, c->T * c->k, c->H, c->N, c->act == MOE_BF16 ? 2 : 4,
+                         c->T, at<int32_t>(ws, L.dbg)};
     MOE_LAUNCH(MOE_KERNEL_GATHER, s, moe::launch_gather(gp, s));
   }
   return MOE_OK;
@@ -469,7 +473,8 @@ moe_status moe_combine(const moe_cfg* c, const float* y_perm, const int32_t* slo
   if (c->T == 0) return MOE_OK;
   MOE_REQUIRE(y_perm && slot && topk_w && y, "y_perm, slot, topk_w and y are required");
   MOE_REQUIRE(aligned(y_perm, 16) && aligned(y, 16), "y_perm and y must be 16-byte aligned");
-  moe::CombineParams cp{y_perm, 0, 1, slot, topk_w, y, c->out == MOE_BF16, c->T, c->H, c->k, c->out_scale, nullptr};
+  moe::CombineParams cp{y_perm, 0, 1, slot, topk_w, y, c->out == MOE_BF16, c->T, c->H, c->k, c->out_scale,
+                        nullptr, nullptr, 0, 0, c->T * c->k, nullptr};
   MOE_LAUNCH(MOE_KERNEL_COMBINE, s, moe::launch_combine(cp, s));
   return MOE_OK;
 }
@@ -563,7 +568,8 @@ moe_status moe_forward_residual(const moe_cfg* c, int32_t F_shared, const void* 
   if (e == hipSuccess) e = moe::launch_fill_i32(offsets_s + 1, 1, static_cast<int32_t>(c->T), s);
   if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "fill launch failed: %s", hipGetErrorString(e));
   float* y_s = at<float>(ws_s, Ls.yperm);
-  st = run_gemms(&sc, Ls, x, nullptr, offsets_s, Ws_gate, Ws_up, Ws_down, y_s, Ls.splits, ws_s, false, s);
+  st = run_gemms(&sc, Ls, x, nullptr, offsets_s, Ws_gate, Ws_up, Ws_down, y_s, Ls.splits, ws_s, false, s, nullptr,
+                 nullptr, at<int32_t>(ws, L.dbg));
   if (st != MOE_OK) return st;
   const Residual res{y_s, Ls.A_max * static_cast<int64_t>(c->H), Ls.splits};
   return forward_launch(c, x, Wg, Wn, eps, Wgate, Wup, Wdown, y, topk_idx_opt, topk_w_opt, kept_opt, load_opt,
@@ -696,7 +702,7 @@ moe_status moe_backward(const moe_cfg* c, const void* x, const float* Wg, const 
   moe::BwdGateParams gp{T, c->H, c->N, c->k, c->order, c->noisy, c->out_scale, d_balance, dy,
                         at<float>(ws, L.yperm), at<int32_t>(ws, L.slot), at<int32_t>(ws, L.idx), at<float>(ws, L.w),
                         at<float>(ws, t.logits), c->noisy ? at<float>(ws, t.nlog) : nullptr, eps,
-                        at<int32_t>(ws, L.counts), dE, dlog, dnz};
+                        at<int32_t>(ws, L.counts), dE, dlog, dnz, L.A_max, at<int32_t>(ws, L.dbg)};
   MOE_LAUNCH(MOE_KERNEL_BWD_GATE, s, moe::launch_bwd_gate(gp, s));
 
   // dh = dE . Wdown_e (B = Wdown_e[h][f], K = h, read in place), and the
@@ -720,6 +726,7 @@ moe_status moe_backward(const moe_cfg* c, const void* x, const float* Wg, const 
   gd.a_rows = A;
   gd.gu = at<float>(ws, t.gu);
   gd.epi = 1;
+  gd.dbg = at<int32_t>(ws, L.dbg);
   // dx_perm = dg . Wgate_e + du . Wup_e: K runs over the 2F columns of dg | du,
   // B row k is Wgate_e row k (k < F) or Wup_e row k - F; in the same
   // persistent launch, each row block's dx tiles after its dh tiles
@@ -741,6 +748,7 @@ moe_status moe_backward(const moe_cfg* c, const void* x, const float* Wg, const 
   gx.splits = 1;
   gx.rows_max = A;
   gx.a_rows = A;
+  gx.dbg = gd.dbg;
   // dWdown_e[h][f] = sum over the expert's rows r of dE[r][h] h[r][f], both
   // operands K-outer: it needs nothing from this launch, so its tiles run
   // from the same queue and fill the units the dependent dx tiles leave idle
@@ -760,6 +768,7 @@ moe_status moe_backward(const moe_cfg* c, const void* x, const float* Wg, const 
   w0.C = dWdown;
   w0.ldc = F;
   w0.c_split_stride = H * F;
+  w0.dbg = gd.dbg;
   wd.M = c->H;
   {
     int32_t* sched = at<int32_t>(ws, L.sched);
@@ -775,8 +784,8 @@ moe_status moe_backward(const moe_cfg* c, const void* x, const float* Wg, const 
     MOE_LAUNCH(MOE_KERNEL_BWD_DGRAD, s, moe::launch_bwd_dgrad_fused(fp, s));
   }
   // dx = sum of the slots' rows + the router terms
-  moe::BwdDxParams dp{T, c->H, c->N, c->k, c->noisy, at<float>(ws, t.dxp), L.A_max, at<int32_t>(ws, L.slot), dlog,
-                      dnz, Wg, Wn, dx};
+  moe::BwdDxParams dp{T,  c->H, c->N, c->k, c->noisy, at<float>(ws, t.dxp), L.A_max, at<int32_t>(ws, L.slot), dlog,
+                      dnz, Wg, Wn, dx, gd.dbg};
   MOE_LAUNCH(MOE_KERNEL_BWD_DX, s, moe::launch_bwd_dx(dp, s));
   // the other weight gradients per expert, K over the expert's rows of the
   // permuted order; one launch per gradient, each grid's XCD-aware order
@@ -824,6 +833,19 @@ moe_status moe_debug_set_wait(int32_t spin_limit, int32_t wait_extra) {
   g_wait_spin = spin_limit;
   g_wait_extra = wait_extra;
   return MOE_OK;
+}
+
+int32_t moe_debug_build(void) {
+#ifdef MOE_DEBUG
+  return 1;
+#else
+  return 0;
+#endif
+}
+
+size_t moe_debug_word_offset(const moe_cfg* c) {
+  if (moe_check(c) != MOE_OK) return 0;
+  return layout(c).dbg;
 }
 
 moe_status moe_profile_select(int32_t kernel_id) {

@@ -159,7 +159,9 @@ __global__ __launch_bounds__(kScatterThreads) void k_scatter(ScatterParams p) {
           rank = s_base[e] + woff + pre[j];
         }
         const int64_t row = ve ? static_cast<int64_t>(s_off[e]) + rank : -1;
-        const bool keep = ve && (p.capacity < 0 || rank < p.capacity) && row < T * k;
+        const bool fits = ve && (p.capacity < 0 || rank < p.capacity);
+        if (fits && row >= T * k) debug_flag(p.dbg, kDbgScatterRow);
+        const bool keep = fits && row < T * k;
         p.slot[t * k + j] = keep ? static_cast<int32_t>(row) : -1;
         if (keep) p.row_token[row] = static_cast<int32_t>(t);
       }
@@ -181,6 +183,7 @@ __global__ __launch_bounds__(256) void k_gather(GatherParams p) {
   const int64_t row_bytes = static_cast<int64_t>(p.H) * p.elem_bytes;
   char* d = static_cast<char*>(p.x_perm) + r * row_bytes;
   if (src < 0 || src >= p.T) {  // never from the scatter; a guard against a row index outside x
+    debug_flag(p.dbg, kDbgGatherRow);
     for (int64_t o = lane * 16; o < row_bytes; o += 64 * 16) *reinterpret_cast<u32x4_t*>(d + o) = u32x4_t{0, 0, 0, 0};
     return;
   }
