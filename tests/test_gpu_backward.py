@@ -39,6 +39,10 @@ CASES = {
                                                         out_scale=2.0),
     # 24 clean experts, top-3, F not a multiple of 64
     "n24_k3_ragged": lambda: synth.make_independent("bwd_n24", 106, 420, 384, 136, 24, 3),
+    # H and F off multiples of 64: ragged K steps of dh (K = H) and of dx,
+    # whose K switches from Wgate to Wup inside a step (K = 2F, at F = 200)
+    "ragged_h328_f200": lambda: synth.make_independent("bwd_rag", 107, 400, 328, 200, 8, 2, noisy=True,
+                                                       out_scale=4.0),
 }
 
 
