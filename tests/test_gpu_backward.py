@@ -154,3 +154,30 @@ def test_full_C2_backward():
     ref = oracle.backward(w, dy, d_bal, nthreads=oracle_threads())
     for key in ("dx", "dWg", "dWgate", "dWup", "dWdown"):
         assert_grad(g[key], ref[key], f"C2 {key}")
+
+
+def test_autograd_function_matches_the_abi():
+    """MoEFunction under torch autograd gives moe_backward's gradients: the
+    fp32 ones (router and noise weights) bit for bit, the bf16 inputs'
+    (x, expert weights) as the same fp32 gradients rounded to bf16."""
+    from sparse_mixture_experts_05_amd import MoEFunction
+    w = CASES["noisy_k4_n16"]()
+    dy = synth.normal_f32(w.meta["seed"], 40, (w.T, w.H), 1.0)
+    ref = run_train(w, dy, 0.37)
+    d = upload(w)
+    leaves = {k: d[k].clone().requires_grad_(True) for k in ("x", "Wg", "Wn", "Wgate", "Wup", "Wdown")}
+    cfg = synth_cfg(w)
+    cfg.want_stats = True
+    y, bal = MoEFunction.apply(leaves["x"], leaves["Wg"], leaves["Wn"], d["eps"], leaves["Wgate"], leaves["Wup"],
+                               leaves["Wdown"], cfg)
+    loss = (y * dev(dy)).sum() + 0.37 * bal.sum()
+    loss.backward()
+    torch.cuda.synchronize()
+    assert np.array_equal(host(y.detach()), ref["y"])
+    assert np.array_equal(host(leaves["Wg"].grad), ref["dWg"])
+    assert np.array_equal(host(leaves["Wn"].grad), ref["dWn"])
+    for key, name in (("x", "dx"), ("Wgate", "dWgate"), ("Wup", "dWup"), ("Wdown", "dWdown")):
+        got = leaves[key].grad
+        assert got.dtype == torch.bfloat16
+        want = torch.from_numpy(np.ascontiguousarray(ref[name])).cuda().to(torch.bfloat16)
+        assert torch.equal(got, want), key
