@@ -1,5 +1,6 @@
 /*
- * CPU ORACLE for the top-k MoE SwiGLU layer forward pass.
+ * CPU ORACLE for the top-k MoE SwiGLU layer: the forward pass, the
+ * shared-neuron (residual) layer, the smooth gate load, and the backward.
  *
  * TEST INFRASTRUCTURE ONLY. This is the plain, slow, obviously-correct
  * reference the GPU path is checked against. Only the test suite, the smoke
@@ -22,7 +23,13 @@
  *   [V2]  "LLaMA-MoE v2" article: gating-mechanism section (noisy gate,
  *         balance loss L = lambda * sum f_i P_i), rescaling section
  *         (y = N/k * sum G_i E_i), and its code example (SwiGLU expert
- *         down(SiLU(gate x) * up x), noise = randn * softplus(noise_linear)).
+ *         down(SiLU(gate x) * up x), noise = randn * softplus(noise_linear)),
+ *         and its shared-neuron partitioning (an always-active slice).
+ *   [HUB] LLaMA-MoE hub page: the expert-construction list (Inter / Inner
+ *         shared neurons), the gate choices (TopK Noisy Gate; Switch) and the
+ *         Gate Load monitor, and continual pre-training (the backward).
+ *   The smooth gate load follows the noisy top-k gate's original paper
+ *   (Shazeer et al. 2017), which the hub page names.
  *
  * Parity status: every function here is pinned by CPU tests (brute force on
  * tiny inputs, closed forms, library routines, invariants); none is
