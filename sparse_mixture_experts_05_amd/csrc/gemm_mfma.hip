@@ -283,18 +283,28 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, const TilePos& tp,
     const __amdgpu_buffer_rsrc_t rc = uniform_rsrc(base, static_cast<int64_t>(tp.ti.rows) * p.ldc * 2);
     const uint32_t ld = static_cast<uint32_t>(p.ldc) * 2u, lg = static_cast<uint32_t>(ldg) * 4u;
     const uint32_t uoff_g = static_cast<uint32_t>(p.Nout) * 4u, uoff_c = static_cast<uint32_t>(p.Nout) * 2u;
+    // a block's 32 loads of g and u are issued before its stores: the stores
+    // may alias them as far as the compiler knows, so loads placed after a
+    // store would each wait out a memory round trip (issuing them a block
+    // ahead as well gained nothing more)
 #pragma unroll
     for (int i = 0; i < MB; ++i)
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
         const int f = tp.nt * NO + wn * WN + j * 32 + col_l;
         const bool fv = f < p.Nout;
+        float gv[16], uv[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const uint32_t row = static_cast<uint32_t>(row_l + i * 32 + (r >> 2) * 8 + (r & 3));
           const uint32_t go = fv ? row * lg + static_cast<uint32_t>(f) * 4u : kStoreOOB;
-          const float g = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rg, go, 0, 0));
-          const float u = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rg, go + uoff_g, 0, 0));
+          gv[r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rg, go, 0, 0));
+          uv[r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rg, go + uoff_g, 0, 0));
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const uint32_t row = static_cast<uint32_t>(row_l + i * 32 + (r >> 2) * 8 + (r & 3));
+          const float g = gv[r], u = uv[r];
           const float dh = acc[i][j][r];
           const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g * -1.4426950408889634f));
           const float dg = dh * u * (sg * (1.0f + g * (1.0f - sg)));
