@@ -118,7 +118,8 @@ size_t moe_workspace_bytes(const moe_cfg* cfg);
  *   is taken again; kth_excluding is the k-th highest score of the other
  *   experts (-inf when k = N).
  *   ws: a workspace of moe_workspace_bytes(cfg) is required when statistics
- *   are requested; otherwise it may be NULL.
+ *   are requested or x is bf16 (the matrix-core router keeps its partial
+ *   logits, one set per chunk of H, there); otherwise it may be NULL.
  *   Returns MOE_ERR_WORKSPACE when it is too small. */
 moe_status moe_route(const moe_cfg* cfg, const void* x, const float* Wg, const float* Wn, const float* eps,
                      float* logits_opt, int32_t* topk_idx, float* topk_w, int32_t* load_opt,

@@ -22,6 +22,8 @@ struct RouterParams {
   int32_t* hist;          // [blocks,N] assignments per expert per block, or null
   float* stat_part;       // [blocks,3N] importance, sum of softmax(logits), smooth load; or null
   int smooth;             // 1: fill the smooth-load partials (noisy gate only)
+  float* part;            // bf16 x: router_part_floats(T, H, N, noisy) fp32 of workspace, the
+                          // per-chunk partial logits
 };
 constexpr int kStatsPerExpert = 3;  // importance, softmax(logits) sum, smooth load
 // Tokens handled by one router block; the permutation scatter reads the
@@ -30,6 +32,8 @@ int router_tokens_per_block(int N, int noisy, int act_bf16);
 int router_blocks(int64_t T, int N, int noisy, int act_bf16);
 hipError_t launch_router(const RouterParams& p, hipStream_t s);
 hipError_t launch_router_mma(const RouterParams& p, hipStream_t s);
+// Floats of the matrix-core router's partial logits (one set per chunk of H).
+int64_t router_part_floats(int64_t T, int H, int N, int noisy);
 
 // Fixed-order reduction of the router's per-block statistics.
 struct StatsParams {

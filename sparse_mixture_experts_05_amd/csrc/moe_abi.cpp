@@ -83,7 +83,7 @@ struct Layout {
   bool mfma = false;
   bool fused = false;    // both expert GEMMs in one persistent launch
   size_t hist = 0, stat = 0, h = 0, yperm = 0, idx = 0, w = 0, slot = 0, rowtok = 0, counts = 0, kept = 0,
-         offsets = 0, sched = 0, dbg = 0, total = 0;
+         offsets = 0, sched = 0, dbg = 0, rpart = 0, total = 0;
 };
 
 bool use_mfma(const moe_cfg* c) { return c->act == MOE_BF16 && c->F % 8 == 0; }
@@ -131,6 +131,7 @@ Layout layout(const moe_cfg* c) {
   L.offsets = take(static_cast<size_t>(c->N + 1) * 4);
   L.sched = take(L.fused ? static_cast<size_t>(moe::fused_sched_ints(L.A_max, c->N)) * 4 : 0);
   L.dbg = take(4);  // the debug word (written by debug builds only)
+  L.rpart = take(c->act == MOE_BF16 ? static_cast<size_t>(moe::router_part_floats(T, c->H, c->N, c->noisy)) * 4 : 0);
   L.total = o;
   return L;
 }
@@ -287,6 +288,7 @@ moe_status forward_launch(const moe_cfg* c, const void* x, const float* Wg, cons
   rp.hist = at<int32_t>(ws, L.hist);
   rp.stat_part = stats ? at<float>(ws, L.stat) : nullptr;
   rp.smooth = stats && smooth_load_opt ? 1 : 0;
+  rp.part = at<float>(ws, L.rpart);
   MOE_LAUNCH(MOE_KERNEL_ROUTER, s, moe::launch_router(rp, s));
   // statistics: reduced by the persistent expert kernel once its queue is
   // empty when that kernel runs, else by a launch of their own
@@ -394,7 +396,10 @@ moe_status moe_route(const moe_cfg* c, const void* x, const float* Wg, const flo
   MOE_REQUIRE(x && Wg && topk_idx && topk_w, "x, Wg, topk_idx and topk_w are required");
   MOE_REQUIRE(!c->noisy || (Wn && eps), "noisy routing needs Wn and eps");
   MOE_REQUIRE(aligned(x, 16) && aligned(Wg, 16) && (!Wn || aligned(Wn, 16)), "x, Wg and Wn must be 16-byte aligned");
-  if (stats) {
+  // the workspace holds the statistics' partials and the matrix-core
+  // router's partial logits
+  const bool need_ws = stats || c->act == MOE_BF16;
+  if (need_ws) {
     st = check_ws(c, ws, ws_bytes);
     if (st != MOE_OK) return st;
   }
@@ -417,6 +422,7 @@ moe_status moe_route(const moe_cfg* c, const void* x, const float* Wg, const flo
   rp.hist = stats ? at<int32_t>(ws, L.hist) : nullptr;
   rp.stat_part = stats ? at<float>(ws, L.stat) : nullptr;
   rp.smooth = stats && smooth_load_opt ? 1 : 0;
+  rp.part = c->act == MOE_BF16 ? at<float>(ws, L.rpart) : nullptr;
   MOE_LAUNCH(MOE_KERNEL_ROUTER, s, moe::launch_router(rp, s));
   if (stats) {
     moe::StatsParams sp{at<int32_t>(ws, L.hist), at<float>(ws, L.stat), L.hist_blocks, c->T, c->N, c->k,

@@ -6,32 +6,29 @@
 // round-to-nearest-even leaves a remainder that the next part holds exactly),
 // so every product x * W_i of a bf16 activation is exact in fp32 and
 // v_mfma_f32_16x16x32_bf16 forms x.W with fp32 accumulation. The hi part and
-// the two lower parts go to separate accumulators and the waves of a block
-// each cover a share of H, which keeps the accumulated rounding error near
-// that of a plain fp32 dot product.
+// the two lower parts go to separate accumulators, and every sum covers a
+// short run of H, which keeps the accumulated rounding error near that of a
+// plain fp32 dot product.
 //
-// A block owns 16 tokens and walks H in chunks through two LDS buffers: while
-// the waves split and multiply chunk c, the fp32 weight rows and x of chunk
-// c + 1 are in flight, and they are written to the other buffer (transposed,
-// so that a lane reads its eight operand values of one column with two
-// 16-byte reads) before the barrier that ends the chunk.
+// Two launches. k_router_part splits H into chunks: a block owns 64 or 128
+// tokens and one chunk, each of its 8 waves a run of 32 to 128 rows of the
+// chunk. A wave loads its rows' weights straight into the MFMA B-operand
+// pattern (8 rows of one column per lane), splits them in registers and
+// multiplies them with the x fragments of all the block's tokens; the 8
+// waves' sums are added in wave order through LDS, and the chunk's partial
+// logits go to the workspace. Every compute unit therefore splits only a
+// chunk of the weights, not all of them. k_router_select adds a token's
+// partials in chunk order and takes the routing decisions.
 //
-// With at most 8 router columns, half the 16 columns of the MFMA B operand
-// would be zero, so they are "folded": columns 8..15 carry the same 8 router
-// columns for the next 32 rows of H, and the A rows 8..15 carry the same 8
-// tokens at those rows. The diagonal 8 x 8 blocks of the product are the two
-// halves of the dot products; the off-diagonal blocks are not used. Every
-// lane then splits weight values that are used, which halves the splitting
-// work per row of H.
-//
-// After the product, one wave per token applies the noise term, KeepTopK and
-// the gate of the chosen order: a lane's rank is the number of experts with a
+// The selection: one wave per token applies the noise term, KeepTopK and the
+// gate of the chosen order: a lane's rank is the number of experts with a
 // larger score, or an equal score and a lower index ("Llama 3 Meets MoE"
 // review, section 3: ties to the lower expert index; a NaN score counts as
 // -inf), and the experts of rank < k are kept in rank order (Mixtral:
-// softmax over the kept scores; ST: softmax over all scores, section 5). Threads of the block then sum the
-// per-expert counts, gate weights and softmax(logit) values over the block's
-// tokens in token order for the permutation and the balance statistics.
+// softmax over the kept scores; ST: softmax over all scores, section 5).
+// Threads of the block then sum the per-expert counts, gate weights and
+// softmax(logit) values over the block's 16 tokens in token order for the
+// permutation and the balance statistics.
 #include "common.h"
 #include "kernels.h"
 
@@ -45,36 +42,40 @@ namespace moe {
 
 namespace {
 
-constexpr int kTok = 16;  // tokens per block (M of the MFMA)
-// waves per block, each over 1/W of a chunk's rows: more waves for fewer
-// output columns, fewer when the partial sums of every wave would not fit
+constexpr int kTok = 16;        // tokens per selection block (the permutation's histogram granularity)
+constexpr int kPartWaves = 8;   // waves of a partial-product block
+constexpr int kStepRows = 32;   // rows of H per MFMA step (the K of v_mfma_f32_16x16x32_bf16)
+
+// token tiles of 16 per partial block: a wave's accumulators stay at 64
+// registers for every column count
 template <int NB16>
-constexpr int router_waves() { return NB16 <= 2 ? 16 : (NB16 <= 4 ? 8 : 4); }
+constexpr int part_tiles() { return 8 / NB16; }
 
-constexpr int kWFloats = 16 * 1024;  // fp32 weights of one chunk (64 KB); two buffers
-constexpr int kWPad = 4;             // floats of padding per LDS column
-constexpr int kWBuf = kWFloats + kWPad * 128;  // one buffer, up to 128 padded columns
-
-// 16-byte x loads per lane per chunk (two chunks stay in registers): folded
-// chunks give a wave two steps of two A fragments; otherwise the buffer holds
-// at most two steps per wave
-template <bool FOLD>
-constexpr int router_xl() { return FOLD ? 4 : 2; }
-
-// Rows of H one MFMA step covers: 32, or 64 when the columns are folded.
-template <bool FOLD>
-constexpr int unit_rows() { return FOLD ? 64 : 32; }
-
-// Rows of H per chunk: whole steps for every wave, within one buffer for all
-// n2 columns and within the lanes' x registers.
-template <int NB16, bool FOLD>
-int router_chunk_rows(int H, int n2) {
-  const int unit = unit_rows<FOLD>() * router_waves<NB16>();
-  const int max_units = FOLD ? router_xl<FOLD>() / 2 : router_xl<FOLD>();
-  int rows = kWFloats / n2 / unit * unit;
-  rows = std::min(rows, max_units * unit);
-  rows = std::max(rows, unit);
-  return std::min(rows, (H + unit - 1) / unit * unit);
+// The partial-product grid: NB16 column tiles of 16 (1, 2, 4 or 8); KS MFMA
+// steps per wave, so chunks of 256 * KS rows of H; token groups of
+// 16 * part_tiles rows. More steps per wave when there are many token groups
+// (fewer, longer chunks), fewer when there are few (more blocks for a short
+// batch).
+struct PartShape {
+  int nb16, ks, chunk_rows, chunks, groups;
+};
+PartShape part_shape(int64_t T, int H, int N, int noisy) {
+  PartShape s;
+  const int n2 = N * (noisy ? 2 : 1);
+  s.nb16 = n2 <= 16 ? 1 : (n2 <= 32 ? 2 : (n2 <= 64 ? 4 : 8));
+  const int tb = 16 * (8 / s.nb16);
+  s.groups = static_cast<int>((T + tb - 1) / tb);
+  // the longest chunks (at most 8 / nb16 steps per wave, for the weight
+  // registers) that still give at least 512 blocks, two per compute unit: a
+  // block makes one pass, so a second resident block is what overlaps one
+  // block's loads with another's products
+  for (s.ks = std::min(4, 8 / s.nb16); s.ks > 1; s.ks /= 2) {
+    const int chunks = (H + kPartWaves * kStepRows * s.ks - 1) / (kPartWaves * kStepRows * s.ks);
+    if (static_cast<int64_t>(s.groups) * chunks >= 512) break;
+  }
+  s.chunk_rows = kPartWaves * kStepRows * s.ks;
+  s.chunks = (H + s.chunk_rows - 1) / s.chunk_rows;
+  return s;
 }
 
 // Exact three-way bf16 split of eight fp32 values, two at a time: the
@@ -101,326 +102,260 @@ __device__ __forceinline__ float lane_value(float v, int m) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), m));
 }
 
-// SHORT: H fits in the two buffers; the weights are staged first, then all
-// of x is requested at once.
-template <int NB16, bool FOLD, bool SHORT>
-__global__ __launch_bounds__(router_waves<NB16>() * 64) void k_router_mma(RouterParams p, int hc) {
-  constexpr int kWaves = router_waves<NB16>();
-  constexpr int kThreads = kWaves * 64;
-  constexpr int NC = NB16 * 16;
-  constexpr int kXL = router_xl<FOLD>();
-  constexpr int UR = unit_rows<FOLD>();
-  constexpr int AF = FOLD ? 2 : 1;        // A fragments per step (token halves when folded)
-  constexpr int kU = kXL / AF;            // most steps of one wave in one chunk
-  constexpr int kP = kWFloats / 4 / kThreads;  // most 16-byte weight pieces per thread per chunk
-  static_assert(!FOLD || NB16 == 1, "folding is for at most 8 columns");
-  // the weight chunks; after the product, the per-wave partial sums
-  __shared__ __attribute__((aligned(16))) float s_w[2 * kWBuf];
-  static_assert(kWaves * kTok * NC <= 2 * kWBuf, "partials fit in the weight buffers");
-  __shared__ float s_log[kTok][NC];  // clean logits, then noise logits
+// Partial logits of one chunk of H for one token group: part[chunk][t][c]
+// = sum over the chunk's rows h of x[t][h] * W[h][c], W_g as columns [0, N)
+// and W_noise as [N, 2N).
+template <int NB16, int KS, bool NOISY>
+__global__ __launch_bounds__(kPartWaves * 64) void k_router_part(RouterParams p) {
+  constexpr int TT = part_tiles<NB16>();
+  constexpr int TB = 16 * TT;
+  constexpr int NC = 16 * NB16;
+  constexpr int CR = kPartWaves * kStepRows * KS;
+  __shared__ float s_red[kPartWaves][TB][NC];  // 64 KB
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int N = p.N, H = p.H, k = p.k;
+  const int N = p.N, H = p.H;
+  const int n2 = N * (NOISY ? 2 : 1);
   const int64_t T = p.T;
-  const int64_t tok0 = static_cast<int64_t>(blockIdx.x) * kTok;
-  const uint16_t* __restrict__ x = static_cast<const uint16_t*>(p.x);
-  const int n2 = N * (p.noisy ? 2 : 1);  // real columns; the padding stays zero
+  const int64_t tok0 = static_cast<int64_t>(blockIdx.x) * TB;
+  const int chunk = blockIdx.y;
+  const int tv = static_cast<int>(T - tok0 < TB ? T - tok0 : TB);  // tokens of this block
+  const int h0 = chunk * CR + wave * (kStepRows * KS);                // this wave's first row of H
 
-  // MFMA roles: A row / B column `row`, K group `kg` (8 of the step's rows).
-  // Folded, row bit 3 selects the upper 32 rows of the 64-row step on both
-  // sides, and A row r of token half th is token 8 * th + (r & 7).
+  // MFMA roles: A row / B column `row`, K group `kg` (rows 8 kg .. 8 kg + 7
+  // of the step)
   const int row = lane & 15, kg = lane >> 4;
-  const int koff = FOLD ? 32 * (row >> 3) + 8 * kg : 8 * kg;
-  const int bcol = FOLD ? (row & 7) : row;
   // x rows of this block through a buffer descriptor: a load past the rows
-  // or past H (offset kOOB) returns zeros, so every lane issues the same loads
-  // in every chunk and the waits for them are exact
-  const int tv = static_cast<int>(T - tok0 < kTok ? T - tok0 : kTok);  // tokens of this block
+  // or past H (offset kOOB) returns zeros
+  const uint16_t* __restrict__ x = static_cast<const uint16_t*>(p.x);
   const __amdgpu_buffer_rsrc_t rx = uniform_rsrc(x + tok0 * H, static_cast<int64_t>(tv) * H * 2);
-  int trow[AF];
+  bf16x8_t a[KS][TT];
 #pragma unroll
-  for (int th = 0; th < AF; ++th) trow[th] = FOLD ? 8 * th + (row & 7) : row;
-  // f / N for the weight pieces' rows: a multiply-high by ceil(2^32 / N),
-  // exact for f < 2^32 / N (f stays below a chunk's hc * N floats); N = 1,
-  // whose multiplier does not fit 32 bits, is the identity
-  const uint32_t n_inv = N > 1 ? 0xFFFFFFFFu / static_cast<uint32_t>(N) + 1u : 0u;
-  auto div_n = [&](int f) { return N > 1 ? static_cast<int>(__umulhi(static_cast<uint32_t>(f), n_inv)) : f; };
-  // the noise draws of this wave's tokens, requested now so that their
-  // latency hides behind the product
-  constexpr int kTW = (kTok + kWaves - 1) / kWaves;  // tokens per wave in the gate step
-  float eps_pre[kTW];
+  for (int s = 0; s < KS; ++s)
 #pragma unroll
-  for (int i = 0; i < kTW; ++i) {
-    const int t = wave + i * kWaves;
-    eps_pre[i] = (p.noisy && lane < N && t < kTok && tok0 + t < T) ? p.eps[(tok0 + t) * N + lane] : 0.0f;
-  }
-  const int wu = hc / UR / kWaves;  // this wave's steps per chunk
-  const int hcp = hc + kWPad;       // LDS column stride: column j holds the chunk's rows contiguous
-
-  f32x4_mma_t acc_hi[NB16][AF], acc_lo[NB16][AF];
-#pragma unroll
-  for (int c = 0; c < NB16; ++c)
-#pragma unroll
-    for (int th = 0; th < AF; ++th)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) acc_hi[c][th][r] = acc_lo[c][th][r] = 0.0f;
-
-  // 16-byte weight loads need aligned pointers and whole rows per piece
-  const bool vec = (reinterpret_cast<uintptr_t>(p.Wg) & 15) == 0 &&
-                   (!p.noisy || (reinterpret_cast<uintptr_t>(p.Wn) & 15) == 0) && N % 4 == 0;
+    for (int t = 0; t < TT; ++t) {
+      const int kk = h0 + s * kStepRows + 8 * kg, tr = 16 * t + row;
+      const uint32_t off = (kk < H && tr < tv) ? static_cast<uint32_t>(tr * H + kk) * 2u : kOOB;
+      a[s][t] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0));
+    }
+  // the weights in the B pattern: lane (row, kg) of column tile c takes
+  // column 16 c + row at the step's rows 8 kg .. 8 kg + 7. A lane's column
+  // lies in W_g or in W_noise: each matrix is read through its own
+  // descriptor, the other load's offset is out of range and reads zero, as
+  // do columns past n2 and rows past H.
   const int64_t w_bytes = static_cast<int64_t>(H) * N * 4;
-  const __amdgpu_buffer_rsrc_t rw[2] = {uniform_rsrc(p.Wg, w_bytes), uniform_rsrc(p.noisy ? p.Wn : p.Wg, w_bytes)};
-  // weight piece j of this thread: matrix (W_g, or W_noise for the upper half
-  // of the pieces when noisy) and 16-byte piece index within the chunk
-  auto piece = [&](int j, int& m, int& q) {
-    m = (p.noisy && j >= kP / 2) ? 1 : 0;
-    q = threadIdx.x + (j - m * (kP / 2)) * kThreads;
-  };
-
-  f32x4_t wbuf[kP], wbuf2[kP];
-  bf16x8_t a_cur[kXL], a_nxt[kXL];  // x of this chunk and of the next
-  // a chunk's weight rows, W_g as columns [0, N) and W_noise as [N, 2N), in
-  // 16-byte pieces
-  auto load_w = [&](int h0, f32x4_t (&wb)[kP]) {
-    const int hn = min(hc, H - h0);
-    const int c4 = vec ? hn * N / 4 : 0;
+  const __amdgpu_buffer_rsrc_t rg = uniform_rsrc(p.Wg, w_bytes);
+  const __amdgpu_buffer_rsrc_t rn = uniform_rsrc(NOISY ? p.Wn : p.Wg, w_bytes);
+  float wv[KS][NB16][8];
 #pragma unroll
-    for (int j = 0; j < kP; ++j) {
-      int m, q;
-      piece(j, m, q);
-      const uint32_t off = q < c4 ? static_cast<uint32_t>(h0 * N + 4 * q) * 4u : kOOB;
-      wb[j] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw[m], off, 0, 0));
-    }
-  };
-  auto load_x = [&](int h0, bf16x8_t (&a)[kXL]) {
+  for (int c = 0; c < NB16; ++c) {
+    const int col = 16 * c + row;
 #pragma unroll
-    for (int u = 0; u < kU; ++u)
+    for (int s = 0; s < KS; ++s)
 #pragma unroll
-      for (int th = 0; th < AF; ++th) {
-        const int kk = h0 + (wave * wu + u) * UR + koff;
-        const bool ok = u < wu && kk < H && trow[th] < tv;
-        const uint32_t off = ok ? static_cast<uint32_t>(trow[th] * H + kk) * 2u : kOOB;
-        a[u * AF + th] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0));
+      for (int e = 0; e < 8; ++e) {
+        const int h = h0 + s * kStepRows + 8 * kg + e;
+        const uint32_t og = (col < N && h < H) ? static_cast<uint32_t>(h * N + col) * 4u : kOOB;
+        wv[s][c][e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, og, 0, 0));
       }
-  };
-  // transposed stores of the pieces, and what they do not cover (an
-  // unaligned pointer, N % 4 != 0) straight from global memory
-  auto store_w = [&](int h0, float* sb, const f32x4_t (&wb)[kP]) {
-    const int hn = min(hc, H - h0);
-    const int cnt = hn * N, c4 = vec ? cnt / 4 : 0;
+  }
+  if (NOISY) {
 #pragma unroll
-    for (int j = 0; j < kP; ++j) {
-      int m, q;
-      piece(j, m, q);
-      if (q < c4) {
-        const int f = 4 * q, r = div_n(f), n = f - r * N + m * N;  // row and first column of the piece
+    for (int c = 0; c < NB16; ++c) {
+      const int col = 16 * c + row;
+      const bool in_n = col >= N && col < n2;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sb[(n + e) * hcp + r] = wb[j][e];
-      }
-    }
-    for (int m = 0; m < (p.noisy ? 2 : 1); ++m) {
-      const float* src = (m == 0 ? p.Wg : p.Wn) + static_cast<int64_t>(h0) * N;
-      for (int i = 4 * c4 + threadIdx.x; i < cnt; i += kThreads) {
-        const int r = div_n(i);
-        sb[(i - r * N + m * N) * hcp + r] = src[i];
-      }
-    }
-  };
-  auto compute = [&](int h0, const float* sb, const bf16x8_t (&a)[kXL]) {
-    const int hn = min(hc, H - h0);  // weight rows in this chunk; the rest hold stale values
+      for (int s = 0; s < KS; ++s)
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      if (u < wu) {
-        const int kl = (wave * wu + u) * UR + koff;  // row within the chunk
-#pragma unroll
-        for (int c = 0; c < NB16; ++c) {
-          const int col = c * 16 + bcol;
-          float wv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-          if (col < n2) {
-            // col * hcp + kl is a multiple of 4 floats
-            const f32x4_t* src = reinterpret_cast<const f32x4_t*>(sb) + ((col * hcp + kl) >> 2);
-            const f32x4_t lo = src[0], hi = src[1];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              wv[e] = lo[e];
-              wv[4 + e] = hi[e];
-            }
-            if (hn < hc) {
-#pragma unroll
-              for (int e = 0; e < 8; ++e)
-                if (kl + e >= hn) wv[e] = 0.0f;
-            }
-          }
-          bf16x8_t w1, w2, w3;
-          split3(wv, w1, w2, w3);
-#pragma unroll
-          for (int th = 0; th < AF; ++th) {
-            const bf16x8_t af = a[u * AF + th];
-            acc_hi[c][th] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, w1, acc_hi[c][th], 0, 0, 0);
-            acc_lo[c][th] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, w2, acc_lo[c][th], 0, 0, 0);
-            acc_lo[c][th] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, w3, acc_lo[c][th], 0, 0, 0);
-          }
+        for (int e = 0; e < 8; ++e) {
+          const int h = h0 + s * kStepRows + 8 * kg + e;
+          const uint32_t on = (in_n && h < H) ? static_cast<uint32_t>(h * N + col - N) * 4u : kOOB;
+          wv[s][c][e] += __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rn, on, 0, 0));
         }
-      }
-      __builtin_amdgcn_sched_barrier(0);  // one step's operands live at a time
-    }
-  };
-
-  if constexpr (SHORT) {
-    // Both chunks' weights are requested first and stored; x follows. Every
-    // block reads the same weights, and their first reads from memory would
-    // otherwise queue behind the whole of x.
-    load_w(0, wbuf);
-    load_w(hc, wbuf2);
-    store_w(0, s_w, wbuf);
-    store_w(hc, s_w + kWBuf, wbuf2);
-    __syncthreads();
-    load_x(0, a_cur);
-    load_x(hc, a_nxt);
-    compute(0, s_w, a_cur);
-    if (hc < H) compute(hc, s_w + kWBuf, a_nxt);
-    __syncthreads();
-  } else {
-    // software pipeline over the chunks: chunk c + 1 loads while chunk c
-    // computes, and is stored to the other buffer before the barrier that
-    // ends chunk c
-    load_w(0, wbuf);
-    load_x(0, a_cur);
-    store_w(0, s_w, wbuf);
-    // chunk 0's x has landed too: no load is pending where the loop starts,
-    // so the waits inside it count only the next chunk's loads
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    for (int h0 = 0, c = 0; h0 < H; h0 += hc, ++c) {
-      const bool more = h0 + hc < H;
-      if (more) {
-        load_w(h0 + hc, wbuf);
-        load_x(h0 + hc, a_nxt);
-      }
-      compute(h0, s_w + (c & 1) * kWBuf, a_cur);
-      if (more) store_w(h0 + hc, s_w + ((c + 1) & 1) * kWBuf, wbuf);
-      __syncthreads();
-#pragma unroll
-      for (int i = 0; i < kXL; ++i) a_cur[i] = a_nxt[i];
     }
   }
 
-  // lane holds output rows 4 * kg + r and column `row` of each product
-  if constexpr (FOLD) {
-    // the diagonal blocks: rows 0..7 x columns 0..7 (lower 32 rows of each
-    // step) and rows 8..15 x columns 8..15 (upper 32 rows)
-    float (*s_part)[2][kTok][8] = reinterpret_cast<float (*)[2][kTok][8]>(s_w);
-    const int half = kg >> 1;
-    if (half == (row >> 3)) {
+  f32x4_mma_t acc_hi[TT][NB16], acc_lo[TT][NB16];
 #pragma unroll
-      for (int th = 0; th < AF; ++th)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          s_part[wave][half][8 * th + ((4 * kg + r) & 7)][row & 7] = acc_hi[0][th][r] + acc_lo[0][th][r];
-    }
-    __syncthreads();
-    for (int i = threadIdx.x; i < kTok * 8; i += kThreads) {
-      const int t = i / 8, c = i % 8;
-      float v = s_part[0][0][t][c] + s_part[0][1][t][c];
-#pragma unroll
-      for (int w = 1; w < kWaves; ++w) v += s_part[w][0][t][c] + s_part[w][1][t][c];
-      s_log[t][c] = v;
-    }
-  } else {
-    float (*s_part)[kTok][NC] = reinterpret_cast<float (*)[kTok][NC]>(s_w);
+  for (int t = 0; t < TT; ++t)
 #pragma unroll
     for (int c = 0; c < NB16; ++c)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) s_part[wave][kg * 4 + r][c * 16 + row] = acc_hi[c][0][r] + acc_lo[c][0][r];
-    __syncthreads();
-    for (int i = threadIdx.x; i < kTok * NC; i += kThreads) {
-      const int t = i / NC, c = i % NC;
-      float v = s_part[0][t][c];
+      for (int r = 0; r < 4; ++r) acc_hi[t][c][r] = acc_lo[t][c][r] = 0.0f;
 #pragma unroll
-      for (int w = 1; w < kWaves; ++w) v += s_part[w][t][c];
-      s_log[t][c] = v;
-    }
-  }
-  __syncthreads();
-
-  // one wave per token, lane n holding expert n: noise, KeepTopK, gates
-  __shared__ float s_sel[kTok][64];  // gate weight of expert n if kept, else 0
-  __shared__ int s_take[kTok][64];   // 1 if expert n is among the token's top k
-  __shared__ float s_p[kTok][64];    // softmax of the clean logits
-  __shared__ float s_sl[kTok][64];   // smooth-load probability of expert n
-  const bool valid = lane < N;
+  for (int s = 0; s < KS; ++s)
 #pragma unroll
-  for (int i = 0; i < kTW; ++i) {
-    const int t = wave + i * kWaves;
-    const int64_t g = tok0 + t;
-    if (t >= kTok || g >= T) break;  // wave-uniform
-    const float lv = valid ? s_log[t][lane] : -INFINITY;
-    float hv = lv;
-    // H_i = (x W_g)_i + StandardNormal() * Softplus((x W_noise)_i), the
-    // normal draw being the input eps[t, i]
-    const float sp = (p.noisy && valid) ? softplus(s_log[t][N + lane]) : 1.0f;
-    if (p.noisy && valid) hv = fmaf(eps_pre[i], sp, lv);
-    // a NaN score counts as -inf in KeepTopK and the gates, so the rank below
-    // is a strict total order and exactly k experts are kept
-    if (hv != hv) hv = -INFINITY;
-    if (p.logits && valid) p.logits[g * N + lane] = lv;
-    if (p.noise_logits && p.noisy && valid) p.noise_logits[g * N + lane] = s_log[t][N + lane];
-    // rank: experts with a larger score, or an equal one at a lower index
-    int rank = 0;
-    for (int m = 0; m < N; ++m) {
-      const float sm = lane_value(hv, m);
-      rank += (sm > hv || (sm == hv && m < lane)) ? 1 : 0;
-    }
-    const bool kept = valid && rank < k;
-    const float hmax = lane_value(hv, static_cast<int>(__builtin_ctzll(__ballot(valid && rank == 0))));
-    // Mixtral order: softmax over the kept scores; ST: over all N scores.
-    // The denominator adds the terms in expert order.
-    const float ex = (p.order == 0 ? kept : valid) ? expf(hv - hmax) : 0.0f;
-    float den = 0.0f;
-    for (int m = 0; m < N; ++m) den += lane_value(ex, m);
-    const float wgt = kept ? ex / den : 0.0f;
-    if (kept) {
-      p.topk_idx[g * k + rank] = lane;
-      p.topk_w[g * k + rank] = wgt;
-    }
-    s_take[t][lane] = kept ? 1 : 0;
-    s_sel[t][lane] = wgt;
-    if (p.stat_part) {
-      float lmax = -INFINITY;
-      for (int m = 0; m < N; ++m) lmax = fmaxf(lmax, lane_value(lv, m));
-      const float el = valid ? expf(lv - lmax) : 0.0f;
-      float ls = 0.0f;
-      for (int m = 0; m < N; ++m) ls += lane_value(el, m);
-      s_p[t][lane] = el / ls;
-      if (p.smooth) {
-        // smooth load (Shazeer et al. 2017, the TopK Noisy Gate the LLaMA-MoE
-        // hub page names): the chance that expert i stays in the top k when
-        // only its own draw is taken again, Phi((clean logit - k-th highest
-        // other score) / Softplus(noise logit)); the k-th highest other score
-        // is the score of rank k for a kept expert, of rank k - 1 otherwise
-        // (-inf when no expert has rank k)
-        const uint64_t bk1 = __ballot(valid && rank == k - 1), bk = __ballot(valid && rank == k);
-        const float v1 = lane_value(hv, static_cast<int>(__builtin_ctzll(bk1)));
-        const float v2 = bk ? lane_value(hv, static_cast<int>(__builtin_ctzll(bk))) : -INFINITY;
-        const float z = (lv - (kept ? v2 : v1)) / sp;
-        s_sl[t][lane] = valid ? 0.5f * erfcf(z * -0.70710678118654752f) : 0.0f;
+    for (int c = 0; c < NB16; ++c) {
+      bf16x8_t w1, w2, w3;
+      split3(wv[s][c], w1, w2, w3);
+#pragma unroll
+      for (int t = 0; t < TT; ++t) {
+        acc_hi[t][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s][t], w1, acc_hi[t][c], 0, 0, 0);
+        acc_lo[t][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s][t], w2, acc_lo[t][c], 0, 0, 0);
+        acc_lo[t][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s][t], w3, acc_lo[t][c], 0, 0, 0);
       }
     }
+
+  // lane holds output rows 4 kg + r and column `row` of each product; the
+  // waves' sums are added in wave order
+#pragma unroll
+  for (int t = 0; t < TT; ++t)
+#pragma unroll
+    for (int c = 0; c < NB16; ++c)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s_red[wave][16 * t + 4 * kg + r][16 * c + row] = acc_hi[t][c][r] + acc_lo[t][c][r];
+  __syncthreads();
+  float* __restrict__ dst = p.part + (static_cast<int64_t>(chunk) * T + tok0) * n2;
+  for (int i = threadIdx.x; i < tv * n2; i += kPartWaves * 64) {
+    const int t = i / n2, c = i - t * n2;
+    float v = s_red[0][t][c];
+#pragma unroll
+    for (int w = 1; w < kPartWaves; ++w) v += s_red[w][t][c];
+    dst[i] = v;
   }
+}
+
+// Sums of the chunks' partial logits in chunk order, then the noise term,
+// KeepTopK, the gates and the block's statistics, for 16 tokens per block.
+// A token takes a group of NM lanes (NM >= N, a power of two), lane e of the
+// group holding expert e, so a wave holds 64 / NM tokens; the experts'
+// values move within a group by lane shuffles. Every load is requested up
+// front (out-of-range offsets read zero), every lane runs the same
+// instructions (a token past the batch computes on zeros and stores
+// nothing), and every global store comes after the block's last barrier.
+template <int NM>
+__global__ __launch_bounds__(NM / 4 * 64) void k_router_select(RouterParams p, int chunks) {
+  constexpr int kTPW = 64 / NM;  // tokens per wave
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int base = lane & ~(NM - 1), e = lane & (NM - 1);  // the group's first lane; this lane's expert
+  const int t = wave * kTPW + base / NM;                   // this group's token within the block
+  const int N = p.N, k = p.k;
+  const int n2 = N * (p.noisy ? 2 : 1);
+  const int64_t T = p.T;
+  const int64_t tok0 = static_cast<int64_t>(blockIdx.x) * kTok;
+  const int tv = static_cast<int>(T - tok0 < kTok ? T - tok0 : kTok);
+  const bool live = t < tv;
+  const bool valid = e < N;
+  const int64_t g = tok0 + t;
+  const uint64_t gmask = NM == 64 ? ~0ull : ((1ull << NM) - 1) << base;
+  // the lowest lane of this group where pred holds (one must)
+  auto first = [&](bool pred) { return static_cast<int>(__builtin_ctzll(__ballot(pred) & gmask)); };
+
+  // the noise draw and the partial logits of expert e (column e of W_g,
+  // column N + e of W_noise), sixteen chunks' worth at a time
+  const __amdgpu_buffer_rsrc_t re = uniform_rsrc(p.noisy ? p.eps : p.part, p.noisy ? T * N * 4 : 0);
+  const float epsv = __builtin_bit_cast(
+      float, __builtin_amdgcn_raw_buffer_load_b32(
+                 re, (p.noisy && valid && live) ? static_cast<uint32_t>(g * N + e) * 4u : kOOB, 0, 0));
+  const __amdgpu_buffer_rsrc_t rp = uniform_rsrc(p.part, static_cast<int64_t>(chunks) * T * n2 * 4);
+  const uint32_t cs = static_cast<uint32_t>(T * n2) * 4u;  // bytes of one chunk's partials
+  const bool lok = valid && live, nok = p.noisy && valid && live;
+  const uint32_t ol = static_cast<uint32_t>(g * n2 + e) * 4u, on = ol + static_cast<uint32_t>(N) * 4u;
+  float lv = 0.0f, nv = 0.0f;
+  for (int ch0 = 0; ch0 < chunks; ch0 += 16) {
+    float ql[16], qn[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const bool c_ok = ch0 + j < chunks;
+      const uint32_t co = static_cast<uint32_t>(ch0 + j) * cs;
+      ql[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rp, (c_ok && lok) ? co + ol : kOOB, 0, 0));
+      qn[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rp, (c_ok && nok) ? co + on : kOOB, 0, 0));
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      lv += ql[j];
+      nv += qn[j];
+    }
+  }
+
+  if (!valid) lv = -INFINITY;
+  float hv = lv;
+  // H_i = (x W_g)_i + StandardNormal() * Softplus((x W_noise)_i), the
+  // normal draw being the input eps[t, i]
+  const float sp = (p.noisy && valid) ? softplus(nv) : 1.0f;
+  if (p.noisy && valid) hv = fmaf(epsv, sp, lv);
+  // a NaN score counts as -inf in KeepTopK and the gates, so the rank below
+  // is a strict total order and exactly k experts are kept
+  if (hv != hv) hv = -INFINITY;
+  // rank: experts with a larger score, or an equal one at a lower index
+  int rank = 0;
+#pragma unroll
+  for (int m = 0; m < NM; ++m) {
+    const float sm = __shfl(hv, base + m);
+    if (m < N) rank += (sm > hv || (sm == hv && m < e)) ? 1 : 0;
+  }
+  const bool kept = valid && rank < k;
+  const float hmax = __shfl(hv, first(valid && rank == 0));
+  // Mixtral order: softmax over the kept scores; ST: over all N scores.
+  // The denominator adds the terms in expert order.
+  const float ex = (p.order == 0 ? kept : valid) ? expf(hv - hmax) : 0.0f;
+  float den = 0.0f;
+#pragma unroll
+  for (int m = 0; m < NM; ++m) {
+    const float v = __shfl(ex, base + m);
+    if (m < N) den += v;
+  }
+  const float wgt = kept ? ex / den : 0.0f;
+  float pv = 0.0f, slv = 0.0f;
+  if (p.stat_part) {
+    float lmax = -INFINITY;
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      const float v = __shfl(lv, base + m);
+      if (m < N) lmax = fmaxf(lmax, v);
+    }
+    const float el = valid ? expf(lv - lmax) : 0.0f;
+    float ls = 0.0f;
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      const float v = __shfl(el, base + m);
+      if (m < N) ls += v;
+    }
+    pv = el / ls;
+    if (p.smooth) {
+      // smooth load (Shazeer et al. 2017, the TopK Noisy Gate the LLaMA-MoE
+      // hub page names): the chance that expert i stays in the top k when
+      // only its own draw is taken again, Phi((clean logit - k-th highest
+      // other score) / Softplus(noise logit)); the k-th highest other score
+      // is the score of rank k for a kept expert, of rank k - 1 otherwise
+      // (-inf when no expert has rank k)
+      const float v1 = __shfl(hv, first(valid && rank == k - 1));
+      const bool has_k = (__ballot(valid && rank == k) & gmask) != 0;
+      const float v2 = has_k ? __shfl(hv, first(valid && rank == k)) : -INFINITY;
+      const float z = (lv - (kept ? v2 : v1)) / sp;
+      slv = valid ? 0.5f * erfcf(z * -0.70710678118654752f) : 0.0f;
+    }
+  }
+  // tokens past the batch and lanes past N add zeros to the block's sums
+  __shared__ float s_sel[kTok][NM];  // gate weight of expert e if kept, else 0
+  __shared__ int s_take[kTok][NM];   // 1 if expert e is among the token's top k
+  __shared__ float s_p[kTok][NM];    // softmax of the clean logits
+  __shared__ float s_sl[kTok][NM];   // smooth-load probability of expert e
+  s_take[t][e] = (live && kept) ? 1 : 0;
+  s_sel[t][e] = live ? wgt : 0.0f;
+  s_p[t][e] = live ? pv : 0.0f;
+  s_sl[t][e] = live ? slv : 0.0f;
   __syncthreads();
 
+  if (live && valid) {
+    if (p.logits) p.logits[g * N + e] = lv;
+    if (p.noise_logits && p.noisy) p.noise_logits[g * N + e] = nv;
+    if (kept) {
+      p.topk_idx[g * k + rank] = e;
+      p.topk_w[g * k + rank] = wgt;
+    }
+  }
   // per-block sums over the tokens, in token order
   if (p.hist && threadIdx.x < N) {
     const int n = threadIdx.x;
     int cnt = 0;
     float imp = 0.0f, ps = 0.0f, sl = 0.0f;
 #pragma unroll
-    for (int t = 0; t < kTok; ++t) {
-      const bool ok = t < tv;
-      cnt += ok ? s_take[t][n] : 0;
-      imp += ok ? s_sel[t][n] : 0.0f;
-      ps += ok ? s_p[t][n] : 0.0f;
-      sl += (ok && p.smooth) ? s_sl[t][n] : 0.0f;
+    for (int u = 0; u < kTok; ++u) {
+      cnt += s_take[u][n];
+      imp += s_sel[u][n];
+      ps += s_p[u][n];
+      sl += s_sl[u][n];
     }
     p.hist[static_cast<int64_t>(blockIdx.x) * N + n] = cnt;
     if (p.stat_part) {
@@ -434,31 +369,48 @@ __global__ __launch_bounds__(router_waves<NB16>() * 64) void k_router_mma(Router
 
 }  // namespace
 
+int64_t router_part_floats(int64_t T, int H, int N, int noisy) {
+  const PartShape sh = part_shape(T, H, N, noisy);
+  return static_cast<int64_t>(sh.chunks) * T * N * (noisy ? 2 : 1);
+}
+
 hipError_t launch_router_mma(const RouterParams& p, hipStream_t s) {
-  const int n2 = p.N * (p.noisy ? 2 : 1);
-  const dim3 grid(static_cast<unsigned>((p.T + kTok - 1) / kTok));
-#define MOE_ROUTER_MMA(NB, FOLD, SHORT)                                                                \
-  do {                                                                                                 \
-    const int hc = router_chunk_rows<NB, FOLD>(p.H, n2);                                               \
-    if (SHORT && 2 * hc >= p.H)                                                                        \
-      hipLaunchKernelGGL((k_router_mma<NB, FOLD, SHORT>), grid, dim3(router_waves<NB>() * 64), 0, s, p, hc); \
-    else                                                                                               \
-      hipLaunchKernelGGL((k_router_mma<NB, FOLD, false>), grid, dim3(router_waves<NB>() * 64), 0, s, p, hc); \
+  const PartShape sh = part_shape(p.T, p.H, p.N, p.noisy);
+  const dim3 grid(static_cast<unsigned>(sh.groups), static_cast<unsigned>(sh.chunks)), block(kPartWaves * 64);
+#define MOE_ROUTER_PART(NB, KS)                                                    \
+  do {                                                                             \
+    if (p.noisy)                                                                   \
+      hipLaunchKernelGGL((k_router_part<NB, KS, true>), grid, block, 0, s, p);     \
+    else                                                                           \
+      hipLaunchKernelGGL((k_router_part<NB, KS, false>), grid, block, 0, s, p);    \
   } while (0)
-  switch ((n2 + 15) / 16) {
-    case 1:
-      if (n2 <= 8) MOE_ROUTER_MMA(1, true, true);
-      else MOE_ROUTER_MMA(1, false, true);
-      break;
-    case 2: MOE_ROUTER_MMA(2, false, true); break;
-    case 3: MOE_ROUTER_MMA(3, false, false); break;
-    case 4: MOE_ROUTER_MMA(4, false, false); break;
-    case 5: MOE_ROUTER_MMA(5, false, false); break;
-    case 6: MOE_ROUTER_MMA(6, false, false); break;
-    case 7: MOE_ROUTER_MMA(7, false, false); break;
-    default: MOE_ROUTER_MMA(8, false, false); break;
+  switch (sh.nb16 * 10 + sh.ks) {
+    case 11: MOE_ROUTER_PART(1, 1); break;
+    case 12: MOE_ROUTER_PART(1, 2); break;
+    case 14: MOE_ROUTER_PART(1, 4); break;
+    case 21: MOE_ROUTER_PART(2, 1); break;
+    case 22: MOE_ROUTER_PART(2, 2); break;
+    case 24: MOE_ROUTER_PART(2, 4); break;
+    case 41: MOE_ROUTER_PART(4, 1); break;
+    case 42: MOE_ROUTER_PART(4, 2); break;
+    default: MOE_ROUTER_PART(8, 1); break;
   }
-#undef MOE_ROUTER_MMA
+#undef MOE_ROUTER_PART
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 sgrid(static_cast<unsigned>((p.T + kTok - 1) / kTok));
+#define MOE_ROUTER_SELECT(NM) hipLaunchKernelGGL(k_router_select<NM>, sgrid, dim3(NM / 4 * 64), 0, s, p, sh.chunks)
+  if (p.N <= 4)
+    MOE_ROUTER_SELECT(4);
+  else if (p.N <= 8)
+    MOE_ROUTER_SELECT(8);
+  else if (p.N <= 16)
+    MOE_ROUTER_SELECT(16);
+  else if (p.N <= 32)
+    MOE_ROUTER_SELECT(32);
+  else
+    MOE_ROUTER_SELECT(64);
+#undef MOE_ROUTER_SELECT
   return hipGetLastError();
 }
 
