@@ -307,7 +307,7 @@ __global__ __launch_bounds__(256) void k_bwd_dx_regs(BwdDxParams p) {
 
 // Router weight gradients dW_g = x^T dlog and dW_noise = x^T dnz, in two
 // passes for a fixed summation order: pass 1 sums a chunk of kTokW tokens per
-// block into partials [chunk][H][N (+N)] (thread = HPT consecutive h with one
+// block into partials [chunk][N (+N)][H] (thread = HPT consecutive h with one
 // vector load of x per token, all N), pass 2 adds the chunks in order.
 constexpr int kTokW = 32;
 constexpr int kRwThreads = 128;
@@ -416,23 +416,37 @@ __global__ __launch_bounds__(kRwThreads) void k_router_wgrad(RouterWgradParams p
     }
 }
 
-__global__ __launch_bounds__(256) void k_router_wgrad_sum(RouterWgradParams p, int chunks) {
+// Pass 2: each output's chunks in order. Four threads share an output, each
+// adding a contiguous quarter of the chunks (sixteen loads in flight), and
+// the quarters are added in order.
+constexpr int kSumQ = 4;
+__global__ __launch_bounds__(64 * kSumQ) void k_router_wgrad_sum(RouterWgradParams p, int chunks) {
+  __shared__ float s_q[kSumQ][64];
   const int per = p.N * (p.noisy ? 2 : 1);
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;  // column * H + h
-  if (i >= static_cast<int64_t>(p.H) * per) return;
-  // the chunks in order, eight loads in flight at a time
+  const int64_t total = static_cast<int64_t>(p.H) * per;
+  const int q = threadIdx.x >> 6, o = threadIdx.x & 63;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 64 + o;  // column * H + h
+  const int cq = (chunks + kSumQ - 1) / kSumQ;
+  const int c0 = q * cq, c1 = min(chunks, c0 + cq);
   float v = 0.0f;
-  for (int c0 = 0; c0 < chunks; c0 += 8) {
-    float u[8];
+  if (i < total) {
+    for (int cb = c0; cb < c1; cb += 16) {
+      float u[16];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) u[q] = c0 + q < chunks ? p.part[static_cast<int64_t>(c0 + q) * p.H * per + i] : 0.0f;
+      for (int j = 0; j < 16; ++j) u[j] = cb + j < c1 ? p.part[static_cast<int64_t>(cb + j) * total + i] : 0.0f;
 #pragma unroll
-    for (int q = 0; q < 8; ++q)
-      if (c0 + q < chunks) v += u[q];
+      for (int j = 0; j < 16; ++j) v += u[j];
+    }
   }
+  s_q[q][o] = v;
+  __syncthreads();
+  if (q != 0 || i >= total) return;
+  float r = s_q[0][o];
+#pragma unroll
+  for (int w = 1; w < kSumQ; ++w) r += s_q[w][o];
   const int64_t n = i / p.H, h = i % p.H;
-  if (n < p.N) p.dWg[h * p.N + n] = v;
-  else p.dWn[h * p.N + (n - p.N)] = v;
+  if (n < p.N) p.dWg[h * p.N + n] = r;
+  else p.dWn[h * p.N + (n - p.N)] = r;
 }
 
 }  // namespace
@@ -488,7 +502,7 @@ hipError_t launch_router_wgrad(const RouterWgradParams& p, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t n = static_cast<int64_t>(p.H) * p.N * (p.noisy ? 2 : 1);
-  hipLaunchKernelGGL(k_router_wgrad_sum, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s, p,
+  hipLaunchKernelGGL(k_router_wgrad_sum, dim3(static_cast<unsigned>((n + 63) / 64)), dim3(64 * kSumQ), 0, s, p,
                      router_wgrad_chunks(p.T));
   return hipGetLastError();
 }
