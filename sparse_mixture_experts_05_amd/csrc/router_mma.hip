@@ -53,9 +53,7 @@ constexpr int part_tiles() { return 8 / NB16; }
 
 // The partial-product grid: NB16 column tiles of 16 (1, 2, 4 or 8); KS MFMA
 // steps per wave, so chunks of 256 * KS rows of H; token groups of
-// 16 * part_tiles rows. More steps per wave when there are many token groups
-// (fewer, longer chunks), fewer when there are few (more blocks for a short
-// batch).
+// 16 * part_tiles rows.
 struct PartShape {
   int nb16, ks, chunk_rows, chunks, groups;
 };
@@ -65,14 +63,11 @@ PartShape part_shape(int64_t T, int H, int N, int noisy) {
   s.nb16 = n2 <= 16 ? 1 : (n2 <= 32 ? 2 : (n2 <= 64 ? 4 : 8));
   const int tb = 16 * (8 / s.nb16);
   s.groups = static_cast<int>((T + tb - 1) / tb);
-  // the longest chunks (at most 8 / nb16 steps per wave, for the weight
-  // registers) that still give at least 512 blocks, two per compute unit: a
-  // block makes one pass, so a second resident block is what overlaps one
-  // block's loads with another's products
-  for (s.ks = std::min(4, 8 / s.nb16); s.ks > 1; s.ks /= 2) {
-    const int chunks = (H + kPartWaves * kStepRows * s.ks - 1) / (kPartWaves * kStepRows * s.ks);
-    if (static_cast<int64_t>(s.groups) * chunks >= 512) break;
-  }
+  // nb16 steps per wave (at most 8 / nb16, for the weight registers): a
+  // block then reads 64 KB of x (128 / nb16 tokens of 256 * nb16 rows), the
+  // size that ran fastest at 8, 32 and 8 router columns over 4096 and 8192
+  // tokens (measured against half and twice the chunk length)
+  s.ks = std::min(s.nb16, 8 / s.nb16);
   s.chunk_rows = kPartWaves * kStepRows * s.ks;
   s.chunks = (H + s.chunk_rows - 1) / s.chunk_rows;
   return s;
@@ -384,15 +379,10 @@ hipError_t launch_router_mma(const RouterParams& p, hipStream_t s) {
     else                                                                           \
       hipLaunchKernelGGL((k_router_part<NB, KS, false>), grid, block, 0, s, p);    \
   } while (0)
-  switch (sh.nb16 * 10 + sh.ks) {
-    case 11: MOE_ROUTER_PART(1, 1); break;
-    case 12: MOE_ROUTER_PART(1, 2); break;
-    case 14: MOE_ROUTER_PART(1, 4); break;
-    case 21: MOE_ROUTER_PART(2, 1); break;
-    case 22: MOE_ROUTER_PART(2, 2); break;
-    case 24: MOE_ROUTER_PART(2, 4); break;
-    case 41: MOE_ROUTER_PART(4, 1); break;
-    case 42: MOE_ROUTER_PART(4, 2); break;
+  switch (sh.nb16) {  // steps per wave: part_shape's choice for each column count
+    case 1: MOE_ROUTER_PART(1, 1); break;
+    case 2: MOE_ROUTER_PART(2, 2); break;
+    case 4: MOE_ROUTER_PART(4, 2); break;
     default: MOE_ROUTER_PART(8, 1); break;
   }
 #undef MOE_ROUTER_PART
