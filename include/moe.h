@@ -84,7 +84,11 @@ typedef struct {
  * cf < 0 or a result above INT32_MAX. Host only. */
 int32_t moe_capacity(int64_t T, int32_t N, int32_t k, double cf, int32_t count_assignments);
 
-/* Validates cfg on the host; never touches the device. */
+/* Validates cfg on the host; never touches the device. Shapes are bounded so
+ * that every operand is addressed with 32-bit byte offsets: T*H, T*k*F, T*k*H
+ * and F*H below 2^29 elements, and for bf16 activations the router's partial
+ * logits (T*N*(1+noisy) per 256-512-row chunk of H) below 2^29 floats;
+ * beyond them it returns MOE_ERR_UNSUPPORTED. */
 moe_status moe_check(const moe_cfg* cfg);
 
 /* Workspace bytes that any entry point below needs for cfg (0 if cfg is

@@ -368,6 +368,11 @@ moe_status moe_check(const moe_cfg* c) {
   if (c->T * static_cast<int64_t>(c->H) >= lim || Tk * static_cast<int64_t>(c->F) >= lim ||
       Tk * static_cast<int64_t>(c->H) >= lim || static_cast<int64_t>(c->F) * c->H >= lim)
     return fail(MOE_ERR_UNSUPPORTED, "T*H, T*k*F, T*k*H and F*H must stay below 2^29 elements");
+  // the matrix-core router's partial logits (one T x N(1 + noisy) set per
+  // chunk of H) and the noise draws are addressed the same way
+  if (c->act == MOE_BF16 && moe::router_part_floats(c->T, c->H, c->N, c->noisy) >= lim)
+    return fail(MOE_ERR_UNSUPPORTED, "the router's partial logits (T*N*(1+noisy) per chunk of H) must stay below "
+                                     "2^29 floats");
   return MOE_OK;
 }
 

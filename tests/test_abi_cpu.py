@@ -73,6 +73,18 @@ def test_check_rejects(abi, kw, code):
     assert abi.moe_workspace_bytes(cfg(abi, **kw)) == 0
 
 
+def test_check_bounds_the_router_partials(abi):
+    """The bf16 router keeps T x N(1 + noisy) partial logits per chunk of H,
+    addressed with 32-bit offsets: a shape within the other limits whose
+    partials would reach 2^29 floats is rejected for bf16 activations only
+    (2^25 tokens, H = 8, 64 noisy experts: one chunk of 2^25 x 128 floats)."""
+    big = dict(T=1 << 25, H=8, F=8, N=64, k=1, noisy=True)
+    assert abi.moe_check(cfg(abi, **big)) == abi.MOE_ERR_UNSUPPORTED
+    assert b"partial logits" in abi.load_library().moe_last_error()
+    assert abi.moe_check(cfg(abi, act="f32", wt="f32", **big)) == abi.MOE_OK
+    assert abi.moe_check(cfg(abi, **dict(big, T=1 << 21))) == abi.MOE_OK
+
+
 def test_workspace_grows_with_the_problem(abi):
     a = abi.moe_workspace_bytes(cfg(abi, T=64))
     b = abi.moe_workspace_bytes(cfg(abi, T=128))
