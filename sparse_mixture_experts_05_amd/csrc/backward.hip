@@ -32,53 +32,10 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   return ((red[0] + red[1]) + red[2]) + red[3];
 }
 
-// One token per block: dw_j = s <dy_t, E_j> over the kept slots (E_j is the
-// y_perm row of slot j), dE_j = bf16(s w_j dy_t) into the slot's row, then one
-// wave takes the gate weights back to the scores and the router logits:
-//   Mixtral (softmax over the kept scores): dH = w_j (dw_j - sum w dw) at idx_j;
-//   ST (softmax over all scores): dH = p (dp - <p, dp>), dp = dw at idx_j;
-//   balance: dlogit += d_balance / T * p_clean (f - <f, p_clean>), f = load/(T k);
-//   noise: dn = dH * eps * sigmoid(noise logit).
-__global__ __launch_bounds__(256) void k_bwd_gate(BwdGateParams p) {
-  __shared__ float red[4];
-  __shared__ float s_dw[64];
-  const int64_t t = blockIdx.x;
-  const int H = p.H, k = p.k, N = p.N;
-  const float s = p.scale;
-  const float* dy = p.dy + t * H;
-  for (int j0 = 0; j0 < k; j0 += 8) {
-    int sl[8];
-    float wj[8], acc[8];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int j = j0 + q;
-      sl[q] = j < k ? checked_slot(p.slot[t * k + j], p.rows, p.dbg, kDbgBwdSlot) : -1;
-      wj[q] = j < k ? p.topk_w[t * k + j] : 0.0f;
-      acc[q] = 0.0f;
-    }
-    for (int c = threadIdx.x; c < H / 4; c += 256) {
-      const f32x4_t d = *reinterpret_cast<const f32x4_t*>(dy + c * 4);
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        if (sl[q] < 0) continue;
-        const f32x4_t e = *reinterpret_cast<const f32x4_t*>(p.y_perm + static_cast<int64_t>(sl[q]) * H + c * 4);
-        acc[q] = fmaf(d[0], e[0], fmaf(d[1], e[1], fmaf(d[2], e[2], fmaf(d[3], e[3], acc[q]))));
-        const float sw = s * wj[q];
-        const uint32_t lo = f32_to_bf16(sw * d[0]) | (static_cast<uint32_t>(f32_to_bf16(sw * d[1])) << 16);
-        const uint32_t hi = f32_to_bf16(sw * d[2]) | (static_cast<uint32_t>(f32_to_bf16(sw * d[3])) << 16);
-        typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-        *reinterpret_cast<u32x2_t*>(p.dE + static_cast<int64_t>(sl[q]) * H + c * 4) = u32x2_t{lo, hi};
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      if (j0 + q >= k) break;
-      const float v = block_sum(acc[q], red);  // same value on every thread
-      if (threadIdx.x == 0) s_dw[j0 + q] = sl[q] >= 0 ? s * v : 0.0f;
-    }
-  }
-  __syncthreads();
-  if (threadIdx.x >= 64) return;
+// The gate weights' gradients (s_dw, per slot) back to the router logits:
+// the block's first wave, lane n holding expert n.
+__device__ __forceinline__ void gate_to_logits(const BwdGateParams& p, int64_t t, const float* s_dw) {
+  const int k = p.k, N = p.N;
   const int lane = threadIdx.x;
   const bool valid = lane < N;
   // this lane's expert among the token's top k (the slot index j), if any
@@ -132,6 +89,95 @@ __global__ __launch_bounds__(256) void k_bwd_gate(BwdGateParams p) {
     p.dlog[t * N + lane] = dl;
     if (p.noisy) p.dnz[t * N + lane] = dH * ev * __builtin_amdgcn_rcpf(1.0f + expf(-nz));
   }
+}
+
+// One token per block: dw_j = s <dy_t, E_j> over the kept slots (E_j is the
+// y_perm row of slot j), dE_j = bf16(s w_j dy_t) into the slot's row, then one
+// wave takes the gate weights back to the scores and the router logits:
+//   Mixtral (softmax over the kept scores): dH = w_j (dw_j - sum w dw) at idx_j;
+//   ST (softmax over all scores): dH = p (dp - <p, dp>), dp = dw at idx_j;
+//   balance: dlogit += d_balance / T * p_clean (f - <f, p_clean>), f = load/(T k);
+//   noise: dn = dH * eps * sigmoid(noise logit).
+template <int KM>  // k <= KM
+__global__ __launch_bounds__(256) void k_bwd_gate(BwdGateParams p) {
+  __shared__ float red[4][KM];
+  __shared__ float s_dw[64];
+  const int64_t t = blockIdx.x;
+  const int H = p.H, k = p.k, N = p.N;
+  const float s = p.scale;
+  // the token's slots and gate weights, all requested before any is used
+  const __amdgpu_buffer_rsrc_t rs = uniform_rsrc(p.slot + t * k, static_cast<int64_t>(k) * 4);
+  const __amdgpu_buffer_rsrc_t rw = uniform_rsrc(p.topk_w + t * k, static_cast<int64_t>(k) * 4);
+  int sl[KM];
+  float wj[KM], acc[KM];
+#pragma unroll
+  for (int q = 0; q < KM; ++q) {
+    sl[q] = static_cast<int>(__builtin_amdgcn_raw_buffer_load_b32(rs, q * 4u, 0, 0));
+    wj[q] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rw, q * 4u, 0, 0));
+  }
+#pragma unroll
+  for (int q = 0; q < KM; ++q) {
+    sl[q] = q < k ? checked_slot(sl[q], p.rows, p.dbg, kDbgBwdSlot) : -1;
+    acc[q] = 0.0f;
+  }
+  // dy and the kept slots' y_perm rows of up to kP columns of 4 per thread are
+  // all requested before any dE store: a load issued after a store would wait
+  // for that store too. A dropped slot's offsets are out of range (its rows
+  // read zeros, its stores are dropped).
+  constexpr int kP = KM <= 4 ? 4 : 2;
+  const __amdgpu_buffer_rsrc_t rdy = uniform_rsrc(p.dy + t * H, static_cast<int64_t>(H) * 4);
+  const __amdgpu_buffer_rsrc_t ry = uniform_rsrc(p.y_perm, p.rows * H * 4);
+  const __amdgpu_buffer_rsrc_t rd = uniform_rsrc(p.dE, p.rows * H * 2);
+  const int nc = H / 4;
+  for (int c0 = threadIdx.x; c0 < nc; c0 += kP * 256) {
+    f32x4_t d[kP], e[kP][KM];
+#pragma unroll
+    for (int i = 0; i < kP; ++i) {
+      const int c = c0 + i * 256;
+      const bool cv = c < nc;
+      d[i] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rdy, cv ? c * 16u : kOOB, 0, 0));
+#pragma unroll
+      for (int q = 0; q < KM; ++q) {
+        const uint32_t off = (cv && sl[q] >= 0) ? (static_cast<uint32_t>(sl[q]) * H + c * 4) * 4u : kOOB;
+        e[i][q] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ry, off, 0, 0));
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kP; ++i) {
+      const int c = c0 + i * 256;
+      const bool cv = c < nc;
+#pragma unroll
+      for (int q = 0; q < KM; ++q) {
+        acc[q] = fmaf(d[i][0], e[i][q][0], fmaf(d[i][1], e[i][q][1], fmaf(d[i][2], e[i][q][2], fmaf(d[i][3], e[i][q][3], acc[q]))));
+        const float sw = s * wj[q];
+        const uint32_t lo = f32_to_bf16(sw * d[i][0]) | (static_cast<uint32_t>(f32_to_bf16(sw * d[i][1])) << 16);
+        const uint32_t hi = f32_to_bf16(sw * d[i][2]) | (static_cast<uint32_t>(f32_to_bf16(sw * d[i][3])) << 16);
+        typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+        const uint32_t off = (cv && sl[q] >= 0) ? (static_cast<uint32_t>(sl[q]) * H + c * 4) * 2u : kOOB;
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{lo, hi}, rd, off, 0, 0);
+      }
+    }
+  }
+  // dw_j = s <dy, E_j>: each wave's sums, then the four waves in order
+  const int wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int q = 0; q < KM; ++q) {
+    const float v = wave_sum(acc[q]);
+    if ((threadIdx.x & 63) == 0) red[wave][q] = v;
+  }
+  __syncthreads();
+  if (threadIdx.x < KM) {
+    const int q = threadIdx.x;
+    const float v = ((red[0][q] + red[1][q]) + red[2][q]) + red[3][q];
+    int sq = -1;
+#pragma unroll
+    for (int u = 0; u < KM; ++u)
+      if (u == q) sq = sl[u];
+    if (q < k) s_dw[q] = sq >= 0 ? s * v : 0.0f;
+  }
+  __syncthreads();
+  if (threadIdx.x >= 64) return;
+  gate_to_logits(p, t, s_dw);
 }
 
 // dx[t] = sum over kept slots of dx_perm[slot] (in slot order) + the router
@@ -449,11 +495,59 @@ __global__ __launch_bounds__(64 * kSumQ) void k_router_wgrad_sum(RouterWgradPara
   else p.dWn[h * p.N + (n - p.N)] = r;
 }
 
+// Any k (up to 64): slots in groups of eight, loads as they come.
+__global__ __launch_bounds__(256) void k_bwd_gate_any(BwdGateParams p) {
+  __shared__ float red[4];
+  __shared__ float s_dw[64];
+  const int64_t t = blockIdx.x;
+  const int H = p.H, k = p.k, N = p.N;
+  const float s = p.scale;
+  const float* dy = p.dy + t * H;
+  for (int j0 = 0; j0 < k; j0 += 8) {
+    int sl[8];
+    float wj[8], acc[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int j = j0 + q;
+      sl[q] = j < k ? checked_slot(p.slot[t * k + j], p.rows, p.dbg, kDbgBwdSlot) : -1;
+      wj[q] = j < k ? p.topk_w[t * k + j] : 0.0f;
+      acc[q] = 0.0f;
+    }
+    for (int c = threadIdx.x; c < H / 4; c += 256) {
+      const f32x4_t d = *reinterpret_cast<const f32x4_t*>(dy + c * 4);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        if (sl[q] < 0) continue;
+        const f32x4_t e = *reinterpret_cast<const f32x4_t*>(p.y_perm + static_cast<int64_t>(sl[q]) * H + c * 4);
+        acc[q] = fmaf(d[0], e[0], fmaf(d[1], e[1], fmaf(d[2], e[2], fmaf(d[3], e[3], acc[q]))));
+        const float sw = s * wj[q];
+        const uint32_t lo = f32_to_bf16(sw * d[0]) | (static_cast<uint32_t>(f32_to_bf16(sw * d[1])) << 16);
+        const uint32_t hi = f32_to_bf16(sw * d[2]) | (static_cast<uint32_t>(f32_to_bf16(sw * d[3])) << 16);
+        typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+        *reinterpret_cast<u32x2_t*>(p.dE + static_cast<int64_t>(sl[q]) * H + c * 4) = u32x2_t{lo, hi};
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      if (j0 + q >= k) break;
+      const float v = block_sum(acc[q], red);  // same value on every thread
+      if (threadIdx.x == 0) s_dw[j0 + q] = sl[q] >= 0 ? s * v : 0.0f;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x >= 64) return;
+  gate_to_logits(p, t, s_dw);
+}
+
 }  // namespace
 
 hipError_t launch_bwd_gate(const BwdGateParams& p, hipStream_t s) {
   if (p.T <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_bwd_gate, dim3(static_cast<unsigned>(p.T)), dim3(256), 0, s, p);
+  const dim3 grid(static_cast<unsigned>(p.T)), block(256);
+  if (p.k <= 2) hipLaunchKernelGGL(k_bwd_gate<2>, grid, block, 0, s, p);
+  else if (p.k <= 4) hipLaunchKernelGGL(k_bwd_gate<4>, grid, block, 0, s, p);
+  else if (p.k <= 8) hipLaunchKernelGGL(k_bwd_gate<8>, grid, block, 0, s, p);
+  else hipLaunchKernelGGL(k_bwd_gate_any, grid, block, 0, s, p);
   return hipGetLastError();
 }
 

@@ -43,6 +43,10 @@ CASES = {
     # whose K switches from Wgate to Wup inside a step (K = 2F, at F = 200)
     "ragged_h328_f200": lambda: synth.make_independent("bwd_rag", 107, 400, 328, 200, 8, 2, noisy=True,
                                                        out_scale=4.0),
+    # top-12 of 16 noisy experts: more than eight slots per token (the gate
+    # backward's general form, slots in groups of eight)
+    "k12_n16_noisy": lambda: synth.make_independent("bwd_k12", 108, 300, 256, 64, 16, 12, noisy=True,
+                                                    out_scale=16 / 12),
 }
 
 
