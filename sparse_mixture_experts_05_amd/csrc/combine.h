@@ -1,5 +1,5 @@
-// Gate-weighted combine of one token's kept expert rows, shared by the
-// standalone combine kernel and the persistent expert kernel.
+// Gate-weighted combine of one token's kept expert rows: the forms the
+// combine kernel uses for split-K partial rows and for more than eight slots.
 //
 // y[t] = s * sum_{j=0..k-1, slot[t,j] >= 0} w[t,j] * y_perm[slot[t,j]]
 // ("Llama 3 Meets MoE" review, section 3, MoE output; LLaMA-MoE v2 article,

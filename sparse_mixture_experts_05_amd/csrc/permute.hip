@@ -188,8 +188,21 @@ __global__ __launch_bounds__(256) void k_gather(GatherParams p) {
     return;
   }
   const char* s = static_cast<const char*>(p.x) + src * row_bytes;
-  for (int64_t o = lane * 16; o < row_bytes; o += 64 * 16)
-    *reinterpret_cast<u32x4_t*>(d + o) = *reinterpret_cast<const u32x4_t*>(s + o);
+  // eight 16-byte pieces per lane are loaded before they are stored: a load
+  // issued after a store would also wait for that store
+  for (int64_t o0 = lane * 16; o0 < row_bytes; o0 += 8 * 64 * 16) {
+    u32x4_t v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int64_t o = o0 + i * 64 * 16;
+      v[i] = o < row_bytes ? *reinterpret_cast<const u32x4_t*>(s + o) : u32x4_t{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int64_t o = o0 + i * 64 * 16;
+      if (o < row_bytes) *reinterpret_cast<u32x4_t*>(d + o) = v[i];
+    }
+  }
 }
 
 }  // namespace
