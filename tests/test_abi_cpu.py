@@ -135,6 +135,9 @@ def test_entry_points_reject_bad_arguments_before_launch(abi):
     # workspace too small
     assert lib.moe_permute(ctypes.byref(c), fake, fake, fake, fake, fake, fake, null, fake, 16,
                            null) == abi.MOE_ERR_WORKSPACE
+    # bf16 routing keeps its partial logits in the workspace: none given
+    assert lib.moe_route(ctypes.byref(c), fake, fake, null, null, null, fake, fake, null, null, null, null,
+                         null, null, 0, null) == abi.MOE_ERR_WORKSPACE
     assert lib.moe_forward(ctypes.byref(c), fake, fake, null, null, fake, fake, fake, fake, null, null, null,
                            null, null, null, null, null, fake, 16, null) == abi.MOE_ERR_WORKSPACE
     # misaligned workspace
