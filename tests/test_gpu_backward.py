@@ -160,6 +160,25 @@ def test_full_C2_backward():
         assert_grad(g[key], ref[key], f"C2 {key}")
 
 
+@pytest.mark.timeout(900)
+def test_full_C3_backward():
+    """The LLaMA-MoE-3.5B (4/16) layer's backward at full size (4096 tokens,
+    16 experts of 688, noisy top-4, s = 4): the router, noise and expert
+    weight gradients and dx, every element against the oracle (the paths of
+    four slots per token and 32 router columns at full size)."""
+    from gpu_util import oracle_threads
+    w = synth.c3()
+    ora = oracle.route(w)
+    assert np.all(ora["min_gap"] > 1e-6), "a near tie would make the comparison ill-posed"
+    dy = synth.normal_f32(w.meta["seed"], 40, (w.T, w.H), 1.0)
+    d_bal = 0.01
+    g = run_train(w, dy, d_bal)
+    log(f"[backward] C3 oracle on {oracle_threads()} threads")
+    ref = oracle.backward(w, dy, d_bal, nthreads=oracle_threads())
+    for key in ("dx", "dWg", "dWn", "dWgate", "dWup", "dWdown"):
+        assert_grad(g[key], ref[key], f"C3 {key}")
+
+
 def test_autograd_function_matches_the_abi():
     """MoEFunction under torch autograd gives moe_backward's gradients: the
     fp32 ones (router and noise weights) bit for bit, the bf16 inputs'
