@@ -63,7 +63,7 @@ __global__ __launch_bounds__(kScatterThreads) void k_scatter(ScatterParams p) {
   {
     const int64_t nel = nhb * N;
     const int64_t split = hb0 * N;  // elements before this block's first histogram row
-    constexpr int U = 8;  // loads in flight per thread before their adds
+    constexpr int U = 16;  // loads in flight per thread before their adds (4096 counts in one round trip)
     if (kScatterThreads % N == 0) {
       // every element this thread reads is a count of expert tid % N: sum in
       // registers, then one LDS add per counter instead of one per element
