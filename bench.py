@@ -193,7 +193,7 @@ def main():
     if train:
         # a training step runs three expert-GEMM kernels: the forward's experts
         # (6*A*H*F flops), the backward's input-gradient launch with dWdown
-        # (8*A*H*F) and the dWgate and dWup launches (2*A*H*F each): the
+        # (8*A*H*F) and the launch of dWgate and dWup (4*A*H*F): the
         # dominant one is the slowest of them per step
         per_step = {}
         for kid in (abi.MOE_KERNEL_EXPERTS, abi.MOE_KERNEL_BWD_DGRAD, abi.MOE_KERNEL_BWD_WGRAD):
@@ -274,7 +274,7 @@ def main():
                     abi.MOE_KERNEL_BWD_WGRAD: "backward_dWgate_dWup"}[dom_id]
         # per launch
         dom_flops = {abi.MOE_KERNEL_EXPERTS: 6.0, abi.MOE_KERNEL_BWD_DGRAD: 8.0,
-                     abi.MOE_KERNEL_BWD_WGRAD: 2.0}[dom_id] * A * H * F
+                     abi.MOE_KERNEL_BWD_WGRAD: 4.0}[dom_id] * A * H * F
         dom_bytes = {abi.MOE_KERNEL_EXPERTS: 3, abi.MOE_KERNEL_BWD_DGRAD: 3,
                      abi.MOE_KERNEL_BWD_WGRAD: 0}[dom_id] * active * F * H * eb + A * H * eb
     elif fused:

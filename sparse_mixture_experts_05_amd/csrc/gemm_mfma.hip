@@ -1204,15 +1204,18 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_experts_fused(FusedParams fp
 // K-outer (KN), and stores the e-th [M, Nout] block of C. The tiles of one
 // expert run together, four row tiles at a time with the column tile fastest,
 // so they share operand panels. BGATHER: B's row r is row row_token[r] of x.
+// With a second gradient (C2), an expert's m-tiles are the first gradient's
+// then the second's, and all of them share the expert's B panels.
 template <bool BGATHER>
 __global__ __launch_bounds__(512) void k_gemm_wgrad(WgradParams wp) {
   // the operand stages, then the gather's map ring ([2][64] int32)
   __shared__ __attribute__((aligned(16))) uint16_t smem[dma_lds_elems<256, 256, 2, 64>() + 2 * 64 * 2];
   constexpr int GM = 4;
   const int L = xcd_remap(blockIdx.x, gridDim.x);
-  const GemmParams& p = wp.g;
+  GemmParams p = wp.g;
   const int M = wp.M;
-  const int mtn = (M + 255) / 256, ntn = (p.Nout + 255) / 256;
+  const int mt1 = (M + 255) / 256, ntn = (p.Nout + 255) / 256;
+  const int mtn = wp.C2 ? 2 * mt1 : mt1;
   const int per_e = mtn * ntn;
   const int e = L / per_e;
   if (e >= p.N) return;
@@ -1221,7 +1224,12 @@ __global__ __launch_bounds__(512) void k_gemm_wgrad(WgradParams wp) {
   const int gm = min(GM, mtn - g * GM);
   const int rq = q - g * GM * ntn;
   TilePos tp{};
-  const int mt = g * GM + rq % gm;
+  int mt = g * GM + rq % gm;
+  if (mt >= mt1) {  // a tile of the second gradient
+    mt -= mt1;
+    p.A = static_cast<const uint16_t*>(p.A) + wp.a2_col;
+    p.C = wp.C2;
+  }
   tp.nt = __builtin_amdgcn_readfirstlane(rq / gm);
   tp.ti.expert = 0;
   tp.ti.row0 = __builtin_amdgcn_readfirstlane(mt * 256);
@@ -1311,7 +1319,8 @@ hipError_t launch_bwd_dgrad_fused(const FusedParams& fp, hipStream_t s) {
 hipError_t launch_gemm_decode(const GemmParams& p, hipStream_t s) { return launch_decode<kDecBM, 128, 3, 4>(p, s); }
 
 hipError_t launch_gemm_wgrad(const WgradParams& wp, hipStream_t s) {
-  const int64_t blocks = static_cast<int64_t>((wp.M + 255) / 256) * ((wp.g.Nout + 255) / 256) * wp.g.N;
+  const int64_t blocks =
+      static_cast<int64_t>((wp.M + 255) / 256) * (wp.C2 ? 2 : 1) * ((wp.g.Nout + 255) / 256) * wp.g.N;
   if (blocks <= 0) return hipSuccess;
   if (wp.g.row_token)
     hipLaunchKernelGGL(k_gemm_wgrad<true>, dim3(static_cast<unsigned>(blocks)), dim3(512), 0, s, wp);

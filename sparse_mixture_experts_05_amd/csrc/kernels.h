@@ -145,10 +145,14 @@ hipError_t launch_gemm_simple(const GemmParams& p, int bf16, hipStream_t s);
 // the e-th [M, Nout] block of C (c_split_stride = M * Nout). Both operands are
 // K-outer: A rows of lda elements (a_rows of them), the M columns contiguous;
 // B rows of ldb elements (b_rows of them), r' = row_token[r] when row_token is
-// set, else r.
+// set, else r. With C2 set, the same launch also runs a second gradient of
+// the same shape whose A columns start a2_col elements further along each
+// row and whose output is C2 (its m-tiles follow the first one's).
 struct WgradParams {
   GemmParams g;
   int M;
+  void* C2;
+  int64_t a2_col;
 };
 hipError_t launch_gemm_wgrad(const WgradParams& wp, hipStream_t s);
 

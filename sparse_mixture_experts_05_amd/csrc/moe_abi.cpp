@@ -799,8 +799,8 @@ moe_status moe_backward(const moe_cfg* c, const void* x, const float* Wg, const 
                       dnz, Wg, Wn, dx, gd.dbg};
   MOE_LAUNCH(MOE_KERNEL_BWD_DX, s, moe::launch_bwd_dx(dp, s));
   // the other weight gradients per expert, K over the expert's rows of the
-  // permuted order; one launch per gradient, each grid's XCD-aware order
-  // keeping an expert's tiles together
+  // permuted order, both in one launch whose XCD-aware order keeps an
+  // expert's tiles (which share its gathered x panels) together
   moe::WgradParams wg = wd;  // dWgate_e[f][h] = sum_r dg[r][f] x[row_token[r]][h]
   wg.g.A = dgu;
   wg.g.lda = 2 * F;
@@ -813,11 +813,9 @@ moe_status moe_backward(const moe_cfg* c, const void* x, const float* Wg, const 
   wg.g.ldc = H;
   wg.g.c_split_stride = F * H;
   wg.M = c->F;
-  moe::WgradParams wu = wg;  // dWup_e: the du half of dg | du
-  wu.g.A = dgu + F;
-  wu.g.C = dWup;
+  wg.C2 = dWup;  // dWup_e: the du half of dg | du
+  wg.a2_col = F;
   MOE_LAUNCH(MOE_KERNEL_BWD_WGRAD, s, moe::launch_gemm_wgrad(wg, s));
-  MOE_LAUNCH(MOE_KERNEL_BWD_WGRAD, s, moe::launch_gemm_wgrad(wu, s));
   // router weights
   moe::RouterWgradParams rw{T, c->H, c->N, c->noisy, static_cast<const uint16_t*>(x), dlog, dnz,
                             at<float>(ws, t.rwp), dWg, dWn_opt};
