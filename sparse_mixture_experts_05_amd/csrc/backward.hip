@@ -103,6 +103,8 @@ __global__ __launch_bounds__(256) void k_bwd_gate(BwdGateParams p) {
   __shared__ float red[4][KM];
   __shared__ float s_dw[64];
   const int64_t t = blockIdx.x;
+  if (t == 0 && p.zero)
+    for (int i = threadIdx.x; i < p.zero_n; i += 256) p.zero[i] = 0;
   const int H = p.H, k = p.k, N = p.N;
   const float s = p.scale;
   // the token's slots and gate weights, all requested before any is used
@@ -500,6 +502,8 @@ __global__ __launch_bounds__(256) void k_bwd_gate_any(BwdGateParams p) {
   __shared__ float red[4];
   __shared__ float s_dw[64];
   const int64_t t = blockIdx.x;
+  if (t == 0 && p.zero)
+    for (int i = threadIdx.x; i < p.zero_n; i += 256) p.zero[i] = 0;
   const int H = p.H, k = p.k, N = p.N;
   const float s = p.scale;
   const float* dy = p.dy + t * H;

@@ -229,6 +229,8 @@ struct BwdGateParams {
   float* dnz;               // [T,N] gradient of the noise logits (noisy)
   int64_t rows;             // rows of y_perm and dE; a slot at or past it is skipped
   int32_t* dbg;             // debug word, or null
+  int32_t* zero;            // zero_n int32 that block 0 sets to 0 (the next launch's queue), or null
+  int zero_n;
 };
 hipError_t launch_bwd_gate(const BwdGateParams& p, hipStream_t s);
 

@@ -707,13 +707,16 @@ moe_status moe_backward(const moe_cfg* c, const void* x, const float* Wg, const 
   uint16_t* dgu = at<uint16_t>(ws, t.dgu);
   float* dlog = at<float>(ws, t.dlog);
   float* dnz = at<float>(ws, t.dnz);
-  hipError_t e = hipSuccess;
 
   // gate weights back to the router; dE = s w dy at every kept slot's row
   moe::BwdGateParams gp{T, c->H, c->N, c->k, c->order, c->noisy, c->out_scale, d_balance, dy,
                         at<float>(ws, L.yperm), at<int32_t>(ws, L.slot), at<int32_t>(ws, L.idx), at<float>(ws, L.w),
                         at<float>(ws, t.logits), c->noisy ? at<float>(ws, t.nlog) : nullptr, eps,
                         at<int32_t>(ws, L.counts), dE, dlog, dnz, L.A_max, at<int32_t>(ws, L.dbg)};
+  // its first workgroup also zeroes the queue of the persistent launch below
+  int32_t* sched = at<int32_t>(ws, L.sched);
+  gp.zero = sched;
+  gp.zero_n = moe::fused_sched_ints(L.A_max, c->N);
   MOE_LAUNCH(MOE_KERNEL_BWD_GATE, s, moe::launch_bwd_gate(gp, s));
 
   // dh = dE . Wdown_e (B = Wdown_e[h][f], K = h, read in place), and the
@@ -782,9 +785,6 @@ moe_status moe_backward(const moe_cfg* c, const void* x, const float* Wg, const 
   w0.dbg = gd.dbg;
   wd.M = c->H;
   {
-    int32_t* sched = at<int32_t>(ws, L.sched);
-    e = moe::launch_fill_i32(sched, moe::fused_sched_ints(L.A_max, c->N), 0, s);
-    if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "fill launch failed: %s", hipGetErrorString(e));
     int spin = moe::kDefaultSpinLimit, extra = 0;
     {
       std::lock_guard<std::mutex> lk(g_wait_mu);
