@@ -93,8 +93,13 @@ __device__ __forceinline__ bool decode_tile(const GemmParams& p, TilePos& tp) {
   }
   const int mtot = __shfl(incl, 63, 64);
   const int per_split = mtot * ntiles;
-  int L = xcd_remap(blockIdx.x, gridDim.x);
-  if (L >= per_split * p.splits) return false;
+  // the grid is an upper bound on the tiles: the first `real` workgroups take
+  // them, remapped over those alone, so the tiles spread over all 8 XCDs
+  // (remapped over the whole grid, they would crowd onto the first XCDs and
+  // leave the others only workgroups without a tile)
+  const int real = min(per_split * p.splits, static_cast<int>(gridDim.x));
+  if (static_cast<int>(blockIdx.x) >= real) return false;
+  int L = xcd_remap(blockIdx.x, real);
   tp.split = L / per_split;
   L -= tp.split * per_split;
   const int g = L / (GM * ntiles);
