@@ -946,10 +946,11 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_decode(GemmParams p) {
 // ticket order: first every gate/up tile (expert by expert, a group of the
 // expert's row blocks at a time), then the down tiles in row-block order, so
 // the down tiles of the first row blocks fill the compute units that the last
-// round of gate/up tiles leaves idle. The first tickets are remapped as the
-// separate launch remaps blockIdx: workgroups start in dispatch order, dealt
+// round of gate/up tiles leaves idle. Workgroup b's first ticket is b, and
+// the first tickets are remapped as blockIdx would be: workgroups are dealt
 // round-robin to the 8 XCDs, so the first round's tiles that share weight
-// panels land on one XCD and its L2. A down tile waits, with a bounded spin,
+// panels land on one XCD and its L2; the queue then hands out tickets from
+// the grid size on. A down tile waits, with a bounded spin,
 // on its row block's count of finished gate/up tiles; all gate/up tickets
 // come before any down ticket, so every tile it waits on is already running
 // in, or reserved by, a workgroup that waits on nothing, and the wait always
@@ -1109,9 +1110,11 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_experts_fused(FusedParams fp
     return 1;
   };
 
-  if (threadIdx.x == 0) *s_item = atomicAdd(&fp.sched[kSchedTicket], 1);
-  __syncthreads();
-  int ticket = __builtin_amdgcn_readfirstlane(*s_item);
+  // the first round's tickets are the workgroups' own indices (workgroup b
+  // runs on XCD b % 8, which the remap of the first S tickets relies on; an
+  // atomic draw would hand them out in whatever order the XCDs arrive); the
+  // queue hands out the tickets from G on
+  int ticket = static_cast<int>(blockIdx.x);
   int sbase = 0, pre = 0;  // stage buffer of K step 0, and how much of it is already loading
   while (ticket < ntot) {
     // The next ticket is reserved three K steps before this tile ends (late
@@ -1127,7 +1130,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_experts_fused(FusedParams fp
     // nothing.
     int reserved = ntot;  // "none" unless reserve() runs
     auto reserve = [&]() {
-      if (threadIdx.x == 0) reserved = atomicAdd(&fp.sched[kSchedTicket], 1);
+      if (threadIdx.x == 0) reserved = G + atomicAdd(&fp.sched[kSchedTicket], 1);
     };
     int next = ntot, nsbase = 0, npre = 0;
     auto hook = [&](uint16_t* a_free, uint16_t* b_free, int fb) {
