@@ -1127,7 +1127,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_experts_fused(FusedParams fp
     // workgroup reserves its next ticket only after its own wait: so a
     // workgroup that waits in a down tile holds no other ticket, and every
     // gate/up ticket still runs in or is reserved by a workgroup that waits on
-    // nothing.
+    // nothing (a first-round gate/up ticket belongs to a workgroup of smaller
+    // index than any first-round down ticket's, dispatched before it).
     int reserved = ntot;  // "none" unless reserve() runs
     auto reserve = [&]() {
       if (threadIdx.x == 0) reserved = G + atomicAdd(&fp.sched[kSchedTicket], 1);
