@@ -17,6 +17,11 @@ namespace moe {
 
 namespace {
 
+// Cache policy of the loads of data a launch reads exactly once and that no
+// later launch of the step reads again (dy, y_perm and dx_perm rows): the nt
+// bit, as for the stores of dx.
+constexpr int kReadOnce = 2;
+
 __device__ __forceinline__ float lane_value(float v, int m) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), m));
 }
@@ -137,11 +142,11 @@ __global__ __launch_bounds__(256) void k_bwd_gate(BwdGateParams p) {
     for (int i = 0; i < kP; ++i) {
       const int c = c0 + i * 256;
       const bool cv = c < nc;
-      d[i] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rdy, cv ? c * 16u : kOOB, 0, 0));
+      d[i] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rdy, cv ? c * 16u : kOOB, 0, kReadOnce));
 #pragma unroll
       for (int q = 0; q < KM; ++q) {
         const uint32_t off = (cv && sl[q] >= 0) ? (static_cast<uint32_t>(sl[q]) * H + c * 4) * 4u : kOOB;
-        e[i][q] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ry, off, 0, 0));
+        e[i][q] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ry, off, 0, kReadOnce));
       }
     }
 #pragma unroll
@@ -324,7 +329,7 @@ __global__ __launch_bounds__(256) void k_bwd_dx_regs(BwdDxParams p) {
       for (int j = 0; j < KM; ++j) {
         const int sl = tb + u < tend ? s_sl[tb + u][j] : -1;
         const uint32_t off = sl >= 0 ? (static_cast<uint32_t>(sl) * static_cast<uint32_t>(H) + h0) * 4u : kOOB;
-        dst[u][j] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rp, off, 0, 0));
+        dst[u][j] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rp, off, 0, kReadOnce));
       }
   };
   auto finish = [&](const f32x4_t (&src)[kU][KM], int tb) {
@@ -341,7 +346,7 @@ __global__ __launch_bounds__(256) void k_bwd_dx_regs(BwdDxParams p) {
         for (int n = 0; n < NM; ++n)
           acc[q] = NOISY ? fmaf(s_dl[tt][n], wg[q][n], fmaf(s_dn[tt][n], wn[q][n], acc[q]))
                          : fmaf(s_dl[tt][n], wg[q][n], acc[q]);
-      *reinterpret_cast<f32x4_t*>(p.dx + (t0 + tt) * H + h0) = acc;
+      __builtin_nontemporal_store(acc, reinterpret_cast<f32x4_t*>(p.dx + (t0 + tt) * H + h0));
     }
   };
   load(v[0], 0);

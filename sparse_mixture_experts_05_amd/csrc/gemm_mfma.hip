@@ -267,6 +267,9 @@ constexpr uint32_t kStoreOOB = 0x80000000u;
 // waiting for its stores instead of writing back the whole L2. y_perm (or its
 // split partials) is read only by a later launch and uses the default policy.
 constexpr int kHStorePolicy = 16, kYStorePolicy = 0;
+// Weight gradients (the tiles with both operands K-outer) are read by no
+// later launch of the step: non-temporal stores (the nt bit).
+constexpr int kGradStorePolicy = 2;
 
 // SiLU(z) = z * sigmoid(z) with the hardware exp2 and reciprocal, each within
 // about one ulp of fp32, far below the bf16 rounding of h that follows.
@@ -274,7 +277,7 @@ __device__ __forceinline__ float silu_fast(float z) {
   return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z * -1.4426950408889634f));
 }
 
-template <int WM, int WN, int MB, int NB, bool SWIGLU>
+template <int WM, int WN, int MB, int NB, bool SWIGLU, int CPOL = kYStorePolicy>
 __device__ __forceinline__ void epilogue(const GemmParams& p, const TilePos& tp, int wm, int wn, int lane, int NO,
                                          f32x16_t (&acc)[MB][NB]) {
   const int col_l = lane & 31, khalf = lane >> 5;
@@ -382,7 +385,7 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, const TilePos& tp,
           const float v = acc[i][j][r];
           __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rc,
                                                 cb + static_cast<uint32_t>(i * 32 + (r >> 2) * 8 + (r & 3)) * ld, 0,
-                                                kYStorePolicy);
+                                                CPOL);
         }
       }
   }
@@ -785,7 +788,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const TilePos& tp
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = __builtin_nanf("");
   }
-  epilogue<WM, WN, MB, NB, SWIGLU>(p, tp, wm, wn, lane, NO, acc);
+  epilogue<WM, WN, MB, NB, SWIGLU, LAY == 2 ? kGradStorePolicy : kYStorePolicy>(p, tp, wm, wn, lane, NO, acc);
 }
 
 // ---- decode-shaped tiles: a long K step per weight row -----------------------
