@@ -270,6 +270,10 @@ constexpr int kHStorePolicy = 16, kYStorePolicy = 0;
 // Weight gradients (the tiles with both operands K-outer) are read by no
 // later launch of the step: non-temporal stores (the nt bit).
 constexpr int kGradStorePolicy = 2;
+// The training forward's saved g and u are read only by the backward's
+// input-gradient launch, several launches later, and there only once: their
+// stores and loads are non-temporal as well.
+constexpr int kSaveStorePolicy = 2, kSaveLoadPolicy = 2;
 
 // SiLU(z) = z * sigmoid(z) with the hardware exp2 and reciprocal, each within
 // about one ulp of fp32, far below the bf16 rounding of h that follows.
@@ -306,8 +310,8 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, const TilePos& tp,
         for (int r = 0; r < 16; ++r) {
           const uint32_t row = static_cast<uint32_t>(row_l + i * 32 + (r >> 2) * 8 + (r & 3));
           const uint32_t go = fv ? row * lg + static_cast<uint32_t>(f) * 4u : kStoreOOB;
-          gv[r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rg, go, 0, 0));
-          uv[r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rg, go + uoff_g, 0, 0));
+          gv[r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rg, go, 0, kSaveLoadPolicy));
+          uv[r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rg, go + uoff_g, 0, kSaveLoadPolicy));
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -344,8 +348,8 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, const TilePos& tp,
           for (int r = 0; r < 16; ++r) {
             const uint32_t off = gb + static_cast<uint32_t>(i * 32 + (r >> 2) * 8 + (r & 3)) * lg;
             const float g = acc[i][j][r], u = acc[i][j + NB / 2][r];
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(g), rg, off, 0, 0);
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(u), rg, off + uoff, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(g), rg, off, 0, kSaveStorePolicy);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(u), rg, off + uoff, 0, kSaveStorePolicy);
           }
         }
     }
